@@ -1,0 +1,219 @@
+/*
+ * k2spmv.h -- C ABI of a k^2-tree SpMV library for the AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * The operations follow Tosoni & Mencagli, "A GPU Engine for Sparse
+ * Matrix-Vector Products on k^2-Tree-Compressed Graphs" (arXiv:2611.03610v1):
+ *   - the k^2-tree with k = 2 of a Boolean matrix (Sec. 2.1),
+ *   - the semiring products y = A x and y^T = x^T A (Sec. 2.2, Table 1,
+ *     Sec. 3.6), for one vector or a row-major batch (Sec. 3.6),
+ *   - the level-synchronous traversal with child offsets from popcount
+ *     prefix sums seeded by a sampled directory (Sec. 3, Algorithm 1,
+ *     Sec. 3.2), tiled so that its scratch is fixed before a product runs
+ *     (Sec. 3.4), and the optional cached last internal level (Sec. 3.5),
+ *   - the device memory of a product, known after construction and before
+ *     any kernel runs (Sec. 1 and Sec. 3.4).
+ *
+ * Conventions
+ *   - Every call returns a k2_status and never throws.  Invalid input is
+ *     rejected before anything is written.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are HIP
+ *     device memory (for instance from torch.empty(..., device="cuda")).
+ *   - Streams are passed as void* and are hipStream_t values; NULL means the
+ *     default (null) stream.
+ *   - A matrix is n_rows x n_cols; the tree pads it to n x n, n = 2^l,
+ *     l = max(2, ceil(log2(max(n_rows, n_cols)))).  Padding costs nothing.
+ *   - Vectors are row-major: a batch of B vectors over n entries is n*B
+ *     elements, entry i of vector v at [i*B + v].  Right product: x has
+ *     n_cols*B elements and y n_rows*B; left product: swapped.
+ *   - Products overwrite y (it starts from the semiring zero).
+ */
+#ifndef K2SPMV_H
+#define K2SPMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    K2_OK = 0,
+    K2_E_INVALID_ARG = 1,     /* null pointer, bad enum, batch 0, ... */
+    K2_E_INDEX_RANGE = 2,     /* an edge index >= its dimension */
+    K2_E_ARENA_TOO_SMALL = 3, /* arena smaller than the estimate */
+    K2_E_HOST_OOM = 4,        /* host allocation failed */
+    K2_E_HIP = 5,             /* a HIP runtime call failed (see k2_last_hip_error) */
+    K2_E_UNSUPPORTED = 6      /* size or option outside what this build handles */
+} k2_status;
+
+/* Table 1 of the pages: plus-times (w = 1, atomic add), Boolean (or-and,
+   contribution [x_j != 0], atomic max on the bit patterns of 0 and 1),
+   tropical (min-plus, w = 1, contribution 1 + x_j rounded to fp32, atomic
+   min on bit patterns; x must be >= 0 or +inf, zero element +inf).
+   K2_BOOLEAN_U32X32 packs 32 Boolean vectors per uint32 word (bit v of word
+   i is entry i of vector v) and accumulates with bitwise or. */
+typedef enum {
+    K2_PLUS_TIMES_F32 = 0,
+    K2_BOOLEAN_F32 = 1,
+    K2_BOOLEAN_U32X32 = 2,
+    K2_TROPICAL_F32 = 3
+} k2_semiring;
+
+/* Sec. 3.6: the left product reads the same tree and swaps the decoded
+   coordinates at the leaves, so cell (r, c) adds x_r to y_c. */
+typedef enum { K2_RIGHT = 0, K2_LEFT = 1 } k2_direction;
+
+/* Which traversal a product uses (Sec. 3.5).  AUTO: the cached last internal
+   level when the matrix holds it, else the tree-only descent. */
+typedef enum { K2_MODE_AUTO = 0, K2_MODE_TREE_ONLY = 1, K2_MODE_CACHED = 2 } k2_mode;
+
+typedef struct {
+    /* Tiled descent (Sec. 3.4): a tile is a contiguous node range whose
+       subtree holds at most tile_nodes nodes on every level; one workgroup
+       descends a tile with its frontier in LDS.  256..4096, power of 2.
+       Default 2048. */
+    uint32_t tile_nodes;
+    /* Host-side top (Sec. 3.4): the device starts from the deepest level with
+       at most host_top_max nodes (never below the last internal level).
+       Default 65536. */
+    uint32_t host_top_max;
+    /* Keep the Morton codes of the last internal level on the device, 8 bytes
+       per node (Sec. 3.5, "k2+F").  Default 0. */
+    int32_t cache_last_level;
+    int32_t reserved;
+} k2_plan_opts;
+
+/* Device bytes of a matrix and of one product, by part; 'arena' is what
+   k2_matrix_create needs, 'vectors' the caller's x and y for the semiring
+   and batch asked about, 'total' = arena + vectors. */
+typedef struct {
+    uint64_t tree;        /* signatures of the levels the device reads */
+    uint64_t directory;   /* one uint32 per 256 nodes of each internal level */
+    uint64_t top_codes;   /* Morton codes of the tile starts (host top + splits) */
+    uint64_t tiles;       /* the tile plan */
+    uint64_t cached_codes;/* 8 bytes per node of the last internal level, or 0 */
+    uint64_t scratch;     /* transient product memory (0: frontiers live in LDS) */
+    uint64_t alignment;   /* padding between parts */
+    uint64_t arena;       /* sum of the above */
+    uint64_t vectors;     /* x and y */
+    uint64_t total;       /* arena + vectors */
+} k2_mem_breakdown;
+
+typedef struct {
+    uint32_t n_rows, n_cols;
+    uint32_t levels;      /* l */
+    uint32_t top_level;   /* d0 for the default plan options */
+    uint64_t nnz;         /* distinct non-zeros */
+    uint64_t nodes;       /* all levels */
+} k2_tree_info_t;
+
+typedef struct k2_tree k2_tree;
+typedef struct k2_matrix k2_matrix;
+
+/* Fill 'opts' with the defaults above. */
+k2_status k2_plan_defaults(k2_plan_opts *opts);
+
+/* Build the tree of the Boolean matrix whose non-zeros are the pairs
+   (rows[e], cols[e]), e < n_edges (host arrays; copied, not kept).
+   Duplicate pairs count once.  n_threads = 0 uses the host's cores (at most
+   64).  *out is a host object owned by the caller (k2_tree_free).
+   Errors: K2_E_INVALID_ARG (null pointer with n_edges > 0, n_rows or n_cols
+   zero), K2_E_INDEX_RANGE (rows[e] >= n_rows or cols[e] >= n_cols),
+   K2_E_UNSUPPORTED (a level with 2^32 or more nodes), K2_E_HOST_OOM.
+   (Sec. 2.1; construction on the host as in Sec. 5.1.) */
+k2_status k2_build(const uint32_t *rows, const uint32_t *cols, uint64_t n_edges,
+                   uint32_t n_rows, uint32_t n_cols, uint32_t n_threads, k2_tree **out);
+
+void k2_tree_free(k2_tree *tree);
+
+/* Sizes of a tree (host). */
+k2_status k2_tree_info(const k2_tree *tree, k2_tree_info_t *out);
+
+/* Node count of every level, nodes[0..levels-1] (host array). */
+k2_status k2_tree_level_nodes(const k2_tree *tree, uint64_t *nodes);
+
+/* Canonical export of level 'level' (Sec. 2.1: one signature per nibble, in
+   level order): node i's signature in bits 4*(i%16)..4*(i%16)+3 of word
+   i/16, unused high nibbles zero.  'words' is a host array of n_words >=
+   ceil(nodes/16) entries.  Errors: K2_E_INVALID_ARG. */
+k2_status k2_tree_level_words(const k2_tree *tree, uint32_t level, uint64_t *words,
+                              uint64_t n_words);
+
+/* Sampled directory of internal level 'level' (Sec. 3.2, S = 256): entry k
+   is the offset in level+1 of the first child of node 256*k.  'out' is a host
+   array of ceil(nodes/256) entries.  Errors: K2_E_INVALID_ARG (leaf level). */
+k2_status k2_tree_directory(const k2_tree *tree, uint32_t level, uint32_t *out, uint64_t n_out);
+
+/* Device bytes of a matrix created with 'opts' plus the x and y of a product
+   over 'semiring' with 'batch' vectors (words, for K2_BOOLEAN_U32X32).
+   Host only: no HIP call.  The arena k2_matrix_create needs is out->arena.
+   (Sec. 1 and 3.4: memory fixed by the tree and the tile size.) */
+k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts,
+                                   k2_semiring semiring, uint32_t batch,
+                                   k2_mem_breakdown *out);
+
+/* The tile plan a matrix created with 'opts' would use (host only, no HIP
+   call; Sec. 3.4): the host-top level d0, the number of tiles and of tile
+   start codes.  Errors: K2_E_INVALID_ARG. */
+k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *top_level,
+                       uint64_t *n_tiles, uint64_t *n_codes);
+
+/* The tiles themselves, in depth-first order: tiles[4k..4k+3] = (first node,
+   node count, level, index of the first node's code in 'codes'); 'codes' are
+   Morton codes (row bit above column bit per level, 2*level bits).  Host
+   arrays of 4*n_tiles and n_codes entries (from k2_plan_info).
+   Errors: K2_E_INVALID_ARG. */
+k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *tiles,
+                        uint64_t n_tiles, uint64_t *codes, uint64_t n_codes);
+
+/* Upload a tree into the caller's device arena (d_arena, arena_bytes >=
+   estimate's arena; 256-byte aligned) on 'stream' and return a matrix handle.
+   The library allocates no device memory; the arena must outlive the matrix.
+   If opts->cache_last_level, the codes of the last internal level are
+   computed on the device here.  The call synchronizes 'stream' before it
+   returns.  Errors: K2_E_INVALID_ARG, K2_E_ARENA_TOO_SMALL, K2_E_HIP. */
+k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *d_arena,
+                           uint64_t arena_bytes, void *stream, k2_matrix **out);
+
+/* y = A x (K2_RIGHT) or y^T = x^T A (K2_LEFT) over 'semiring' for 'batch'
+   row-major vectors (Algorithm 1), asynchronously on 'stream'.  d_x and d_y
+   are device arrays of the lengths given at the top of this file (float, or
+   uint32 for K2_BOOLEAN_U32X32); they must not overlap.  y is overwritten.
+   'mode' picks the traversal (k2_mode).  Errors (nothing launched):
+   K2_E_INVALID_ARG (null, batch 0, bad enum, K2_MODE_CACHED without cached
+   codes), K2_E_HIP (launch failure). */
+k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semiring,
+                  uint32_t batch, int32_t mode, const void *d_x, void *d_y, void *stream);
+
+/* Release the handle (the arena stays the caller's). */
+k2_status k2_matrix_destroy(k2_matrix *matrix);
+
+/* Description of the plan a matrix uses (host): levels, top level, tile
+   count, whether codes are cached. */
+k2_status k2_matrix_info(const k2_matrix *matrix, uint32_t *top_level, uint64_t *n_tiles,
+                         int32_t *cached);
+
+/* Copy level 'level' of the device-resident tree back to the host in the
+   export layout of k2_tree_level_words (synchronous; for verification).
+   Levels above the top level are not on the device: K2_E_INVALID_ARG. */
+k2_status k2_matrix_level_words(const k2_matrix *matrix, uint32_t level, uint64_t *words,
+                                uint64_t n_words, void *stream);
+
+/* Copy the cached last-internal-level codes back to the host (synchronous),
+   codes[i] = Morton code of node i of level l-2 (row bit above column bit
+   at every level).  Errors: K2_E_INVALID_ARG if not cached. */
+k2_status k2_matrix_cached_codes(const k2_matrix *matrix, uint64_t *codes, uint64_t n_codes,
+                                 void *stream);
+
+const char *k2_status_string(k2_status status);
+
+/* Text of the last HIP error this thread saw (empty string if none). */
+const char *k2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K2SPMV_H */

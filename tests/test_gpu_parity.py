@@ -1,0 +1,139 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Element by element on the same seeded inputs: bit-exact for the tree bits,
+the Boolean and the tropical semirings; plus-times within relative 1e-5 of
+the oracle's fp64 value (absolute 1e-6 below 0.1).  Covers both directions,
+batches, both traversals (tiled descent and cached last level), several tile
+sizes, rectangular and degenerate matrices.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import (ALL_SEMIRINGS, ORC_DIR, ORC_SEMIRING, check_parity, from_device,
+                           make_x, to_device)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tree_graph_spmv_amd  # noqa: F401  (fails loudly if the library is missing)
+    return torch.device("cuda:0")
+
+
+def run_all(k2, rows, cols, n_rows, n_cols, dev, semirings=ALL_SEMIRINGS, batches=(1, 3),
+            tiles=(256, 2048), modes=("tree", "cached"), seed=0, label=""):
+    tree = k2.Tree(rows, cols, n_rows, n_cols)
+    ref = oracle.OracleTree(rows, cols, n_rows, n_cols)
+    assert tree.nnz == ref.nnz
+    for d in range(tree.levels):
+        assert np.array_equal(tree.level_words(d), ref.level_words(d)), f"{label} level {d}"
+    rng = np.random.default_rng(seed)
+    for tile in tiles:
+        opts = k2.plan_defaults(tile_nodes=tile, cache_last_level=1 if "cached" in modes else 0)
+        m = k2.Matrix(tree, opts, device=dev)
+        for mode, sr, direction, B in itertools.product(modes, semirings, ("right", "left"),
+                                                        batches):
+            n_in = n_cols if direction == "right" else n_rows
+            x = make_x(rng, sr, n_in, B)
+            y = m.spmv(to_device(x, dev), direction=direction, semiring=sr, batch=B, mode=mode)
+            torch.cuda.synchronize()
+            want = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
+            check_parity(from_device(y, sr), want, sr,
+                         f"{label} tile={tile} {mode} {sr} {direction} B={B}")
+
+
+def test_fig1(dev, fig1):
+    import tree_graph_spmv_amd as k2
+    pairs = [tuple(int(v) for v in p.split(",")) for p in fig1["cells"].split()]
+    r = np.array([p[0] for p in pairs], np.uint32)
+    c = np.array([p[1] for p in pairs], np.uint32)
+    run_all(k2, r, c, 8, 8, dev, batches=(1, 3, 8), tiles=(256,), label="fig1")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_small_random(dev, seed):
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(100 + seed)
+    n_rows, n_cols = int(rng.integers(1, 300)), int(rng.integers(1, 300))
+    density = [0.0, 0.002, 0.02, 0.2, 0.7, 1.0][seed]
+    mask = rng.random((n_rows, n_cols)) < density
+    r, c = np.nonzero(mask)
+    run_all(k2, r.astype(np.uint32), c.astype(np.uint32), n_rows, n_cols, dev,
+            batches=(1, 2, 5, 64, 70), seed=seed, label=f"random{seed}")
+
+
+def test_degenerate(dev):
+    import tree_graph_spmv_amd as k2
+    # empty, single cell in a corner, identity, all-ones
+    run_all(k2, np.zeros(0, np.uint32), np.zeros(0, np.uint32), 5, 7, dev, label="empty")
+    run_all(k2, np.array([1000], np.uint32), np.array([3], np.uint32), 1001, 4, dev,
+            label="single")
+    idx = np.arange(777, dtype=np.uint32)
+    run_all(k2, idx, idx, 777, 777, dev, label="identity")
+    rr, cc = np.meshgrid(np.arange(64), np.arange(64), indexing="ij")
+    run_all(k2, rr.ravel().astype(np.uint32), cc.ravel().astype(np.uint32), 64, 64, dev,
+            label="dense")
+
+
+def test_rmat_s12_e32k(dev):
+    """R-MAT 2^12, 32,768 distinct edges: the whole product, every variant."""
+    import tree_graph_spmv_amd as k2
+    rows, cols, n = synth.workload_edges("rmat_s12_e32k")
+    run_all(k2, rows, cols, n, n, dev, batches=(1, 4), tiles=(256, 1024, 4096),
+            label="rmat_s12_e32k")
+
+
+def test_device_tree_and_cached_codes(dev):
+    """The device copy of every level equals the canonical export, and the
+    cached codes of the last internal level are the nodes' Morton codes."""
+    import tree_graph_spmv_amd as k2
+    rows, cols = synth.rmat(14, 100000, seed=9)
+    n = 2 ** 14
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    nodes = ref.level_nodes()
+    m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1, tile_nodes=512), device=dev)
+    for d in range(m.top_level, tree.levels):
+        assert np.array_equal(m.device_level_words(d, nodes[d]), ref.level_words(d)), d
+    # codes of level l-2 by expanding the oracle's signatures in level order
+    codes = np.zeros(1, np.uint64)
+    for d in range(tree.levels - 2):
+        sig = ref.signatures(d)
+        nxt = []
+        for i, s in enumerate(sig.tolist()):
+            for b in range(4):
+                if s >> b & 1:
+                    nxt.append((int(codes[i]) << 2) | b)
+        codes = np.array(nxt, np.uint64)
+    got = m.cached_codes(nodes[tree.levels - 2])
+    assert np.array_equal(got, codes)
+
+
+def test_web_n20_d16(dev):
+    """Web-like 2^20 (about 15M distinct edges): right and left plus-times,
+    tree-only and cached, against the oracle's full product."""
+    import tree_graph_spmv_amd as k2
+    rows, cols, n = synth.workload_edges("web_n20_d16")
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    for d in range(tree.levels):
+        assert np.array_equal(tree.level_words(d), ref.level_words(d)), d
+    x = synth.workload_x("web_n20_d16", n)
+    m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    xd = to_device(x, dev)
+    for direction in ("right", "left"):
+        want = ref.spmv(x, oracle.PLUS_TIMES, ORC_DIR[direction], 1, threads=16)
+        for mode in ("tree", "cached"):
+            y = m.spmv(xd, direction=direction, mode=mode)
+            torch.cuda.synchronize()
+            check_parity(from_device(y, "plus_times"), want, "plus_times",
+                         f"web_n20_d16 {direction} {mode}")

@@ -1,0 +1,268 @@
+"""k^2-tree SpMV on AMD Instinct MI355X: Python binding of libk2spmv.so.
+
+Argument marshalling only: every step of a product runs in the library's HIP
+kernels.  torch supplies device memory (the arena and the vectors) and
+streams.  The C functions keep their names (``k2_build``, ``k2_spmv``, ...);
+the classes ``Tree`` and ``Matrix`` wrap the handles.
+
+The library must have been built (``python -m tree_graph_spmv_amd._build`` or
+``__graft_entry__.build()``); importing this package raises if it is missing,
+and there is no fallback of any kind.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libk2spmv.so")
+
+K2_OK, K2_E_INVALID_ARG, K2_E_INDEX_RANGE, K2_E_ARENA_TOO_SMALL, K2_E_HOST_OOM, K2_E_HIP, \
+    K2_E_UNSUPPORTED = range(7)
+K2_PLUS_TIMES_F32, K2_BOOLEAN_F32, K2_BOOLEAN_U32X32, K2_TROPICAL_F32 = range(4)
+K2_RIGHT, K2_LEFT = 0, 1
+K2_MODE_AUTO, K2_MODE_TREE_ONLY, K2_MODE_CACHED = 0, 1, 2
+
+SEMIRINGS = {"plus_times": K2_PLUS_TIMES_F32, "boolean": K2_BOOLEAN_F32,
+             "boolean_u32": K2_BOOLEAN_U32X32, "tropical": K2_TROPICAL_F32}
+DIRECTIONS = {"right": K2_RIGHT, "left": K2_LEFT}
+MODES = {"auto": K2_MODE_AUTO, "tree": K2_MODE_TREE_ONLY, "cached": K2_MODE_CACHED}
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("tile_nodes", ctypes.c_uint32), ("host_top_max", ctypes.c_uint32),
+                ("cache_last_level", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MemBreakdown(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("tree", "directory", "top_codes", "tiles", "cached_codes", "scratch",
+                 "alignment", "arena", "vectors", "total")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class TreeInfo(ctypes.Structure):
+    _fields_ = [("n_rows", ctypes.c_uint32), ("n_cols", ctypes.c_uint32),
+                ("levels", ctypes.c_uint32), ("top_level", ctypes.c_uint32),
+                ("nnz", ctypes.c_uint64), ("nodes", ctypes.c_uint64)]
+
+
+class K2Error(RuntimeError):
+    def __init__(self, status, where):
+        msg = lib().k2_status_string(status).decode()
+        if status == K2_E_HIP:
+            msg += " (" + lib().k2_last_hip_error().decode() + ")"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+# name -> (restype, argtypes)
+_VP = ctypes.c_void_p
+_U32P = ctypes.POINTER(ctypes.c_uint32)
+_U64P = ctypes.POINTER(ctypes.c_uint64)
+_SIGS = {
+    "k2_plan_defaults": (ctypes.c_int, [ctypes.POINTER(PlanOpts)]),
+    "k2_build": (ctypes.c_int, [_U32P, _U32P, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32,
+                                ctypes.c_uint32, ctypes.POINTER(_VP)]),
+    "k2_tree_free": (None, [_VP]),
+    "k2_tree_info": (ctypes.c_int, [_VP, ctypes.POINTER(TreeInfo)]),
+    "k2_tree_level_nodes": (ctypes.c_int, [_VP, _U64P]),
+    "k2_tree_level_words": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P, ctypes.c_uint64]),
+    "k2_tree_directory": (ctypes.c_int, [_VP, ctypes.c_uint32, _U32P, ctypes.c_uint64]),
+    "k2_estimate_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_int,
+                                                ctypes.c_uint32, ctypes.POINTER(MemBreakdown)]),
+    "k2_plan_info": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _U32P, _U64P, _U64P]),
+    "k2_plan_tiles": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _U32P, ctypes.c_uint64, _U64P,
+                                     ctypes.c_uint64]),
+    "k2_matrix_create": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _VP, ctypes.c_uint64, _VP,
+                                        ctypes.POINTER(_VP)]),
+    "k2_spmv": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int32,
+                               _VP, _VP, _VP]),
+    "k2_matrix_destroy": (ctypes.c_int, [_VP]),
+    "k2_matrix_info": (ctypes.c_int, [_VP, _U32P, _U64P, ctypes.POINTER(ctypes.c_int32)]),
+    "k2_matrix_level_words": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P, ctypes.c_uint64, _VP]),
+    "k2_matrix_cached_codes": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
+    "k2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "k2_last_hip_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """The loaded libk2spmv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m tree_graph_spmv_amd._build`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status, where):
+    if status != K2_OK:
+        raise K2Error(status, where)
+
+
+def _u32(a):
+    a = np.ascontiguousarray(a, dtype=np.uint32)
+    return a, a.ctypes.data_as(_U32P)
+
+
+def plan_defaults(**kw):
+    o = PlanOpts()
+    _check(lib().k2_plan_defaults(ctypes.byref(o)), "k2_plan_defaults")
+    for k, v in kw.items():
+        setattr(o, k, int(v))
+    return o
+
+
+class Tree:
+    """Host k^2-tree (k2_build)."""
+
+    def __init__(self, rows, cols, n_rows, n_cols, n_threads=0):
+        r, rp = _u32(rows)
+        c, cp = _u32(cols)
+        if r.shape != c.shape:
+            raise ValueError("rows and cols differ in length")
+        h = _VP()
+        _check(lib().k2_build(rp, cp, r.size, int(n_rows), int(n_cols), int(n_threads),
+                              ctypes.byref(h)), "k2_build")
+        self._h = h
+        info = TreeInfo()
+        _check(lib().k2_tree_info(h, ctypes.byref(info)), "k2_tree_info")
+        self.n_rows, self.n_cols = int(info.n_rows), int(info.n_cols)
+        self.levels, self.nnz, self.nodes = int(info.levels), int(info.nnz), int(info.nodes)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.k2_tree_free(h)
+            self._h = None
+
+    def level_nodes(self):
+        out = np.zeros(self.levels, np.uint64)
+        _check(lib().k2_tree_level_nodes(self._h, out.ctypes.data_as(_U64P)), "k2_tree_level_nodes")
+        return [int(v) for v in out]
+
+    def level_words(self, level):
+        n = self.level_nodes()[level]
+        out = np.zeros((n + 15) // 16, np.uint64)
+        _check(lib().k2_tree_level_words(self._h, level, out.ctypes.data_as(_U64P), out.size),
+               "k2_tree_level_words")
+        return out
+
+    def directory(self, level):
+        n = self.level_nodes()[level]
+        out = np.zeros((n + 255) // 256, np.uint32)
+        _check(lib().k2_tree_directory(self._h, level, out.ctypes.data_as(_U32P), out.size),
+               "k2_tree_directory")
+        return out
+
+    def estimate(self, opts=None, semiring="plus_times", batch=1):
+        opts = opts or plan_defaults()
+        m = MemBreakdown()
+        _check(lib().k2_estimate_device_bytes(self._h, ctypes.byref(opts), SEMIRINGS[semiring],
+                                              int(batch), ctypes.byref(m)),
+               "k2_estimate_device_bytes")
+        return m.as_dict()
+
+    def plan(self, opts=None):
+        """(top_level, tiles (n,4) uint32, codes uint64) of the tile plan."""
+        opts = opts or plan_defaults()
+        top = ctypes.c_uint32()
+        nt = ctypes.c_uint64()
+        nc = ctypes.c_uint64()
+        _check(lib().k2_plan_info(self._h, ctypes.byref(opts), ctypes.byref(top), ctypes.byref(nt),
+                                  ctypes.byref(nc)), "k2_plan_info")
+        tiles = np.zeros((max(nt.value, 1), 4), np.uint32)
+        codes = np.zeros(max(nc.value, 1), np.uint64)
+        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), tiles.ctypes.data_as(_U32P),
+                                   nt.value, codes.ctypes.data_as(_U64P), nc.value), "k2_plan_tiles")
+        return int(top.value), tiles[:nt.value], codes[:nc.value]
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return _VP(stream.cuda_stream)
+
+
+class Matrix:
+    """A tree resident in a device arena allocated through torch."""
+
+    def __init__(self, tree, opts=None, device="cuda", stream=None):
+        import torch
+        self.opts = opts or plan_defaults()
+        est = tree.estimate(self.opts)
+        self.arena_bytes = est["arena"]
+        # 256-byte aligned view of a torch allocation
+        raw = torch.empty(self.arena_bytes + 256, dtype=torch.uint8, device=device)
+        shift = (-raw.data_ptr()) % 256
+        self._raw = raw
+        self.arena_ptr = raw.data_ptr() + shift
+        self.device = raw.device
+        self.n_rows, self.n_cols, self.levels = tree.n_rows, tree.n_cols, tree.levels
+        h = _VP()
+        _check(lib().k2_matrix_create(tree.handle, ctypes.byref(self.opts), _VP(self.arena_ptr),
+                                      self.arena_bytes, _stream_handle(stream), ctypes.byref(h)),
+               "k2_matrix_create")
+        self._h = h
+        top = ctypes.c_uint32()
+        nt = ctypes.c_uint64()
+        cached = ctypes.c_int32()
+        _check(lib().k2_matrix_info(h, ctypes.byref(top), ctypes.byref(nt), ctypes.byref(cached)),
+               "k2_matrix_info")
+        self.top_level, self.n_tiles, self.cached = int(top.value), int(nt.value), bool(cached.value)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.k2_matrix_destroy(h)
+            self._h = None
+
+    def spmv(self, x, y=None, direction="right", semiring="plus_times", batch=1, mode="auto",
+             stream=None):
+        """y = A x ('right') or x^T A ('left'); x, y torch device tensors."""
+        import torch
+        d = DIRECTIONS[direction]
+        n_in = self.n_cols if d == K2_RIGHT else self.n_rows
+        n_out = self.n_rows if d == K2_RIGHT else self.n_cols
+        dtype = torch.int32 if semiring == "boolean_u32" else torch.float32
+        if x.dtype != dtype or x.numel() != n_in * batch or not x.is_contiguous():
+            raise ValueError(f"x must be a contiguous {dtype} tensor of {n_in * batch} elements")
+        if x.device != self.device:
+            raise ValueError("x is on another device")
+        if y is None:
+            y = torch.empty(n_out * batch, dtype=dtype, device=self.device)
+        elif y.dtype != dtype or y.numel() != n_out * batch or not y.is_contiguous():
+            raise ValueError(f"y must be a contiguous {dtype} tensor of {n_out * batch} elements")
+        _check(lib().k2_spmv(self._h, d, SEMIRINGS[semiring], int(batch), MODES[mode],
+                             _VP(x.data_ptr()), _VP(y.data_ptr()), _stream_handle(stream)),
+               "k2_spmv")
+        return y
+
+    def device_level_words(self, level, n_nodes, stream=None):
+        out = np.zeros((n_nodes + 15) // 16, np.uint64)
+        _check(lib().k2_matrix_level_words(self._h, level, out.ctypes.data_as(_U64P), out.size,
+                                           _stream_handle(stream)), "k2_matrix_level_words")
+        return out
+
+    def cached_codes(self, n_nodes, stream=None):
+        out = np.zeros(max(n_nodes, 1), np.uint64)
+        _check(lib().k2_matrix_cached_codes(self._h, out.ctypes.data_as(_U64P), n_nodes,
+                                            _stream_handle(stream)), "k2_matrix_cached_codes")
+        return out[:n_nodes]

@@ -1,0 +1,387 @@
+// k2_api.cpp -- the C ABI declared in include/k2spmv.h.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <new>
+#include <string>
+#include <thread>
+
+#include "k2_internal.h"
+
+struct k2_tree {
+    k2::HostTree t;
+};
+
+struct k2_matrix {
+    k2::Matrix m;
+};
+
+namespace k2 {
+k2_status build_tree(const uint32_t *rows, const uint32_t *cols, uint64_t m, uint32_t n_rows,
+                     uint32_t n_cols, int nt, HostTree *out);
+
+static thread_local std::string g_hip_error;
+
+void set_hip_error(int err, const char *where) {
+    g_hip_error = std::string(where) + ": " + hip_error_text(err);
+}
+}  // namespace k2
+
+using namespace k2;
+
+namespace {
+
+bool valid_opts(const k2_plan_opts &o) {
+    if (o.tile_nodes < 256 || o.tile_nodes > 4096) return false;
+    if (o.tile_nodes & (o.tile_nodes - 1)) return false;
+    return true;
+}
+
+uint64_t vector_bytes(const HostTree &t, uint32_t batch) {
+    return (uint64_t(t.n_rows) + uint64_t(t.n_cols)) * uint64_t(batch) * 4ull;
+}
+
+k2_status estimate(const HostTree &t, const k2_plan_opts &o, Plan *plan, Layout *lay) {
+    k2_status st = make_plan(t, o, plan);
+    if (st != K2_OK) return st;
+    bool cached = o.cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
+    layout_for(t, plan->top_level, plan->codes.size(), plan->tiles.size(), cached, lay);
+    return K2_OK;
+}
+
+#define HIP_TRY(call, where)                                        \
+    do {                                                            \
+        hipError_t e_ = (call);                                     \
+        if (e_ != hipSuccess) {                                     \
+            set_hip_error(int(e_), where);                          \
+            return K2_E_HIP;                                        \
+        }                                                           \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+k2_status k2_plan_defaults(k2_plan_opts *opts) {
+    if (!opts) return K2_E_INVALID_ARG;
+    opts->tile_nodes = 2048;
+    opts->host_top_max = 1u << 16;
+    opts->cache_last_level = 0;
+    opts->reserved = 0;
+    return K2_OK;
+}
+
+k2_status k2_build(const uint32_t *rows, const uint32_t *cols, uint64_t n_edges, uint32_t n_rows,
+                   uint32_t n_cols, uint32_t n_threads, k2_tree **out) {
+    if (!out) return K2_E_INVALID_ARG;
+    *out = nullptr;
+    if (n_rows == 0 || n_cols == 0) return K2_E_INVALID_ARG;
+    if (n_edges > 0 && (!rows || !cols)) return K2_E_INVALID_ARG;
+    int nt = int(n_threads);
+    if (nt <= 0) nt = int(std::min<unsigned>(64, std::max(1u, std::thread::hardware_concurrency())));
+    nt = std::min(nt, 64);
+    k2_tree *t = new (std::nothrow) k2_tree();
+    if (!t) return K2_E_HOST_OOM;
+    k2_status st;
+    try {
+        st = build_tree(rows, cols, n_edges, n_rows, n_cols, nt, &t->t);
+    } catch (const std::bad_alloc &) {
+        st = K2_E_HOST_OOM;
+    }
+    if (st != K2_OK) {
+        delete t;
+        return st;
+    }
+    *out = t;
+    return K2_OK;
+}
+
+void k2_tree_free(k2_tree *tree) { delete tree; }
+
+k2_status k2_tree_info(const k2_tree *tree, k2_tree_info_t *out) {
+    if (!tree || !out) return K2_E_INVALID_ARG;
+    const HostTree &t = tree->t;
+    out->n_rows = t.n_rows;
+    out->n_cols = t.n_cols;
+    out->levels = uint32_t(t.levels);
+    out->top_level = uint32_t(top_level_for(t, 1u << 16));
+    out->nnz = t.nnz;
+    uint64_t n = 0;
+    for (uint64_t v : t.nodes) n += v;
+    out->nodes = n;
+    return K2_OK;
+}
+
+k2_status k2_tree_level_nodes(const k2_tree *tree, uint64_t *nodes) {
+    if (!tree || !nodes) return K2_E_INVALID_ARG;
+    std::copy(tree->t.nodes.begin(), tree->t.nodes.end(), nodes);
+    return K2_OK;
+}
+
+k2_status k2_tree_level_words(const k2_tree *tree, uint32_t level, uint64_t *words, uint64_t n_words) {
+    if (!tree || !words || level >= uint32_t(tree->t.levels)) return K2_E_INVALID_ARG;
+    const std::vector<uint64_t> &w = tree->t.words[level];
+    if (n_words < w.size()) return K2_E_INVALID_ARG;
+    std::copy(w.begin(), w.end(), words);
+    std::fill(words + w.size(), words + n_words, 0ull);
+    return K2_OK;
+}
+
+k2_status k2_tree_directory(const k2_tree *tree, uint32_t level, uint32_t *out, uint64_t n_out) {
+    if (!tree || !out || level + 1 >= uint32_t(tree->t.levels)) return K2_E_INVALID_ARG;
+    const std::vector<uint32_t> &D = tree->t.dir[level];
+    if (n_out < D.size()) return K2_E_INVALID_ARG;
+    std::copy(D.begin(), D.end(), out);
+    return K2_OK;
+}
+
+k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts,
+                                   k2_semiring semiring, uint32_t batch, k2_mem_breakdown *out) {
+    if (!tree || !opts || !out || batch == 0) return K2_E_INVALID_ARG;
+    if (int(semiring) < 0 || int(semiring) > 3 || !valid_opts(*opts)) return K2_E_INVALID_ARG;
+    Plan plan;
+    Layout lay;
+    k2_status st;
+    try {
+        st = estimate(tree->t, *opts, &plan, &lay);
+    } catch (const std::bad_alloc &) {
+        return K2_E_HOST_OOM;
+    }
+    if (st != K2_OK) return st;
+    *out = lay.mem;
+    out->vectors = vector_bytes(tree->t, batch);
+    out->total = out->arena + out->vectors;
+    return K2_OK;
+}
+
+k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *top_level,
+                       uint64_t *n_tiles, uint64_t *n_codes) {
+    if (!tree || !opts || !valid_opts(*opts)) return K2_E_INVALID_ARG;
+    Plan plan;
+    k2_status st;
+    try {
+        st = make_plan(tree->t, *opts, &plan);
+    } catch (const std::bad_alloc &) {
+        return K2_E_HOST_OOM;
+    }
+    if (st != K2_OK) return st;
+    if (top_level) *top_level = uint32_t(plan.top_level);
+    if (n_tiles) *n_tiles = plan.tiles.size();
+    if (n_codes) *n_codes = plan.codes.size();
+    return K2_OK;
+}
+
+k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *tiles,
+                        uint64_t n_tiles, uint64_t *codes, uint64_t n_codes) {
+    if (!tree || !opts || !valid_opts(*opts)) return K2_E_INVALID_ARG;
+    Plan plan;
+    k2_status st;
+    try {
+        st = make_plan(tree->t, *opts, &plan);
+    } catch (const std::bad_alloc &) {
+        return K2_E_HOST_OOM;
+    }
+    if (st != K2_OK) return st;
+    if (n_tiles < plan.tiles.size() || n_codes < plan.codes.size()) return K2_E_INVALID_ARG;
+    if ((!tiles && !plan.tiles.empty()) || (!codes && !plan.codes.empty())) return K2_E_INVALID_ARG;
+    for (size_t k = 0; k < plan.tiles.size(); ++k) {
+        tiles[4 * k + 0] = plan.tiles[k].first;
+        tiles[4 * k + 1] = plan.tiles[k].count;
+        tiles[4 * k + 2] = plan.tiles[k].level;
+        tiles[4 * k + 3] = plan.tiles[k].code_off;
+    }
+    std::copy(plan.codes.begin(), plan.codes.end(), codes);
+    return K2_OK;
+}
+
+k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *d_arena,
+                           uint64_t arena_bytes, void *stream, k2_matrix **out) {
+    if (!tree || !opts || !out || !d_arena) return K2_E_INVALID_ARG;
+    *out = nullptr;
+    if (!valid_opts(*opts) || (reinterpret_cast<uintptr_t>(d_arena) & 255)) return K2_E_INVALID_ARG;
+    const HostTree &t = tree->t;
+    k2_matrix *mx = new (std::nothrow) k2_matrix();
+    if (!mx) return K2_E_HOST_OOM;
+    Matrix &m = mx->m;
+    k2_status st;
+    try {
+        st = estimate(t, *opts, &m.plan, &m.layout);
+    } catch (const std::bad_alloc &) {
+        st = K2_E_HOST_OOM;
+    }
+    if (st != K2_OK) {
+        delete mx;
+        return st;
+    }
+    if (arena_bytes < m.layout.mem.arena) {
+        delete mx;
+        return K2_E_ARENA_TOO_SMALL;
+    }
+    m.arena = static_cast<char *>(d_arena);
+    m.n_rows = t.n_rows;
+    m.n_cols = t.n_cols;
+    m.levels = t.levels;
+    m.nodes = t.nodes;
+    m.cached = opts->cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
+    std::memset(&m.dev, 0, sizeof(m.dev));
+    m.dev.levels = t.levels;
+    m.dev.top_level = m.plan.top_level;
+    hipStream_t st_h = static_cast<hipStream_t>(stream);
+    auto fail = [&](k2_status s) {
+        delete mx;
+        return s;
+    };
+    for (int d = 0; d < t.levels; ++d) m.dev.nodes[d] = uint32_t(t.nodes[d]);
+    for (int d = m.plan.top_level; d < t.levels; ++d) {
+        char *p = m.arena + m.layout.words_off[d];
+        m.dev.words[d] = reinterpret_cast<const uint64_t *>(p);
+        if (!t.words[d].empty()) {
+            hipError_t e = hipMemcpyAsync(p, t.words[d].data(), t.words[d].size() * 8,
+                                          hipMemcpyHostToDevice, st_h);
+            if (e != hipSuccess) {
+                set_hip_error(int(e), "upload tree");
+                return fail(K2_E_HIP);
+            }
+        }
+    }
+    for (int d = m.plan.top_level; d + 1 < t.levels; ++d) {
+        char *p = m.arena + m.layout.dir_off[d];
+        m.dev.dir[d] = reinterpret_cast<const uint32_t *>(p);
+        if (!t.dir[d].empty()) {
+            hipError_t e = hipMemcpyAsync(p, t.dir[d].data(), t.dir[d].size() * 4,
+                                          hipMemcpyHostToDevice, st_h);
+            if (e != hipSuccess) {
+                set_hip_error(int(e), "upload directory");
+                return fail(K2_E_HIP);
+            }
+        }
+    }
+    m.d_codes = reinterpret_cast<const uint64_t *>(m.arena + m.layout.codes_off);
+    m.d_tiles = reinterpret_cast<const Tile *>(m.arena + m.layout.tiles_off);
+    if (!m.plan.codes.empty()) {
+        hipError_t e = hipMemcpyAsync(const_cast<uint64_t *>(m.d_codes), m.plan.codes.data(),
+                                      m.plan.codes.size() * 8, hipMemcpyHostToDevice, st_h);
+        if (e != hipSuccess) {
+            set_hip_error(int(e), "upload tile codes");
+            return fail(K2_E_HIP);
+        }
+    }
+    if (!m.plan.tiles.empty()) {
+        hipError_t e = hipMemcpyAsync(const_cast<Tile *>(m.d_tiles), m.plan.tiles.data(),
+                                      m.plan.tiles.size() * sizeof(Tile), hipMemcpyHostToDevice, st_h);
+        if (e != hipSuccess) {
+            set_hip_error(int(e), "upload tiles");
+            return fail(K2_E_HIP);
+        }
+    }
+    if (m.cached) {
+        m.d_cached = reinterpret_cast<uint64_t *>(m.arena + m.layout.cached_off);
+        int e = launch_descent(m, K2_RIGHT, K2_BOOLEAN_U32X32, 1, nullptr, nullptr, m.d_cached, stream);
+        if (e != hipSuccess) {
+            set_hip_error(e, "cache last internal level");
+            return fail(K2_E_HIP);
+        }
+    }
+    hipError_t e = hipStreamSynchronize(st_h);
+    if (e != hipSuccess) {
+        set_hip_error(int(e), "matrix create");
+        return fail(K2_E_HIP);
+    }
+    *out = mx;
+    return K2_OK;
+}
+
+k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semiring, uint32_t batch,
+                  int32_t mode, const void *d_x, void *d_y, void *stream) {
+    if (!matrix || !d_x || !d_y || batch == 0) return K2_E_INVALID_ARG;
+    if (int(direction) != K2_RIGHT && int(direction) != K2_LEFT) return K2_E_INVALID_ARG;
+    if (int(semiring) < 0 || int(semiring) > 3) return K2_E_INVALID_ARG;
+    Matrix &m = matrix->m;
+    if (mode == K2_MODE_AUTO) mode = m.cached ? K2_MODE_CACHED : K2_MODE_TREE_ONLY;
+    if (mode != K2_MODE_TREE_ONLY && mode != K2_MODE_CACHED) return K2_E_INVALID_ARG;
+    const bool empty = m.nodes[m.levels - 2] == 0;
+    if (mode == K2_MODE_CACHED && !m.cached && !empty) return K2_E_INVALID_ARG;
+    const uint64_t n_out = direction == K2_RIGHT ? m.n_rows : m.n_cols;
+    const uint64_t n_in = direction == K2_RIGHT ? m.n_cols : m.n_rows;
+    {   // x and y must not overlap
+        const char *xb = static_cast<const char *>(d_x), *yb = static_cast<const char *>(d_y);
+        const uint64_t xl = n_in * batch * 4, yl = n_out * batch * 4;
+        if (xb < yb + yl && yb < xb + xl) return K2_E_INVALID_ARG;
+    }
+    const uint32_t zero = semiring == K2_TROPICAL_F32 ? 0x7F800000u : 0u;
+    int e = launch_fill(d_y, n_out * batch, zero, stream);
+    if (e != hipSuccess) {
+        set_hip_error(e, "fill");
+        return K2_E_HIP;
+    }
+    if (empty) return K2_OK;
+    e = (mode == K2_MODE_CACHED)
+            ? launch_cached(m, direction, semiring, batch, d_x, d_y, stream)
+            : launch_descent(m, direction, semiring, batch, d_x, d_y, nullptr, stream);
+    if (e != hipSuccess) {
+        set_hip_error(e, "spmv");
+        return K2_E_HIP;
+    }
+    return K2_OK;
+}
+
+k2_status k2_matrix_destroy(k2_matrix *matrix) {
+    if (!matrix) return K2_E_INVALID_ARG;
+    delete matrix;
+    return K2_OK;
+}
+
+k2_status k2_matrix_info(const k2_matrix *matrix, uint32_t *top_level, uint64_t *n_tiles,
+                         int32_t *cached) {
+    if (!matrix) return K2_E_INVALID_ARG;
+    if (top_level) *top_level = uint32_t(matrix->m.plan.top_level);
+    if (n_tiles) *n_tiles = matrix->m.plan.tiles.size();
+    if (cached) *cached = matrix->m.cached ? 1 : 0;
+    return K2_OK;
+}
+
+k2_status k2_matrix_level_words(const k2_matrix *matrix, uint32_t level, uint64_t *words,
+                                uint64_t n_words, void *stream) {
+    if (!matrix || !words) return K2_E_INVALID_ARG;
+    const Matrix &m = matrix->m;
+    if (level >= uint32_t(m.levels) || int(level) < m.plan.top_level) return K2_E_INVALID_ARG;
+    const uint64_t nw = (m.nodes[level] + 15) / 16;
+    if (n_words < nw) return K2_E_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (nw) HIP_TRY(hipMemcpyAsync(words, m.dev.words[level], nw * 8, hipMemcpyDeviceToHost, st),
+                    "read tree");
+    HIP_TRY(hipStreamSynchronize(st), "read tree");
+    std::fill(words + nw, words + n_words, 0ull);
+    return K2_OK;
+}
+
+k2_status k2_matrix_cached_codes(const k2_matrix *matrix, uint64_t *codes, uint64_t n_codes,
+                                 void *stream) {
+    if (!matrix || !codes) return K2_E_INVALID_ARG;
+    const Matrix &m = matrix->m;
+    if (!m.cached) return K2_E_INVALID_ARG;
+    const uint64_t n = m.nodes[m.levels - 2];
+    if (n_codes < n) return K2_E_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    HIP_TRY(hipMemcpyAsync(codes, m.d_cached, n * 8, hipMemcpyDeviceToHost, st), "read codes");
+    HIP_TRY(hipStreamSynchronize(st), "read codes");
+    return K2_OK;
+}
+
+const char *k2_status_string(k2_status status) {
+    switch (status) {
+    case K2_OK: return "ok";
+    case K2_E_INVALID_ARG: return "invalid argument";
+    case K2_E_INDEX_RANGE: return "edge index out of range";
+    case K2_E_ARENA_TOO_SMALL: return "device arena smaller than the estimate";
+    case K2_E_HOST_OOM: return "host out of memory";
+    case K2_E_HIP: return "HIP runtime error";
+    case K2_E_UNSUPPORTED: return "unsupported size or option";
+    }
+    return "unknown status";
+}
+
+const char *k2_last_hip_error(void) { return g_hip_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// k2_internal.h -- structures shared by the host runtime and the HIP kernels.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/k2spmv.h"
+
+namespace k2 {
+
+constexpr int kMaxLevels = 32;     // n <= 2^32
+constexpr uint32_t kDirBlock = 256;  // directory sample S (Sec. 3.2)
+constexpr uint32_t kWordsPerBlock = kDirBlock / 16;
+
+// Host tree: per level, node count and packed signatures (16 per word, node i
+// at bits 4*(i%16)); per internal level, the S = 256 directory.
+struct HostTree {
+    uint32_t n_rows = 0, n_cols = 0;
+    int levels = 0;
+    uint64_t nnz = 0;
+    std::vector<uint64_t> nodes;                 // [levels]
+    std::vector<std::vector<uint64_t>> words;    // [levels][ceil(nodes/16)]
+    std::vector<std::vector<uint32_t>> dir;      // [levels-1][ceil(nodes/256)]
+};
+
+inline unsigned nibble(const std::vector<uint64_t> &w, uint64_t i) {
+    return unsigned(w[i >> 4] >> ((i & 15) * 4)) & 0xFu;
+}
+
+// Offset in level d+1 of the first child of node i of level d, from the
+// directory plus the popcounts of the words before i in its block.
+uint64_t child_offset(const HostTree &t, int d, uint64_t i);
+
+// One tile of the descent: 'count' consecutive nodes of level 'level'
+// starting at node 'first', whose codes are codes[code_off .. code_off+count).
+struct Tile {
+    uint32_t first;
+    uint32_t count;
+    uint32_t level;
+    uint32_t code_off;
+};
+static_assert(sizeof(Tile) == 16, "tile layout");
+
+// The plan of a matrix: host top level, tiles in depth-first order and the
+// codes their first level starts from.
+struct Plan {
+    int top_level = 0;                 // d0
+    uint32_t tile_nodes = 0;
+    std::vector<uint64_t> codes;       // tile start codes
+    std::vector<Tile> tiles;
+};
+
+k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
+int top_level_for(const HostTree &t, uint32_t host_top_max);
+
+// Arena layout of a matrix (byte offsets from the arena base).
+struct Layout {
+    uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
+    uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
+    uint64_t codes_off = 0, tiles_off = 0, cached_off = 0;
+    k2_mem_breakdown mem = {};
+};
+
+void layout_for(const HostTree &t, int top_level, uint64_t n_codes, uint64_t n_tiles, bool cached,
+                Layout *out);
+
+// ------------------------------------------------------------ device view
+
+// Everything a kernel needs to address the tree, passed by value.
+struct DevTree {
+    const uint64_t *words[kMaxLevels];   // per level (nullptr above the top)
+    const uint32_t *dir[kMaxLevels];     // per internal level
+    uint32_t nodes[kMaxLevels];
+    int levels;
+    int top_level;
+};
+
+struct Matrix {
+    DevTree dev;
+    HostTree const *host_shape = nullptr;  // not kept; shape copied below
+    uint32_t n_rows = 0, n_cols = 0;
+    int levels = 0;
+    std::vector<uint64_t> nodes;
+    Plan plan;
+    Layout layout;
+    char *arena = nullptr;
+    const uint64_t *d_codes = nullptr;   // tile start codes
+    const Tile *d_tiles = nullptr;
+    uint64_t *d_cached = nullptr;        // last internal level codes or null
+    bool cached = false;
+};
+
+// Kernel launchers (k2_device.hip).  Return hipError_t as int.
+int launch_fill(void *y, uint64_t n_words32, uint32_t value, void *stream);
+int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
+                   uint64_t *emit_codes, void *stream);
+int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
+                  void *stream);
+const char *hip_error_text(int err);
+
+void set_hip_error(int err, const char *where);
+
+}  // namespace k2
