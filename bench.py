@@ -1,0 +1,255 @@
+"""Benchmark: k^2-tree SpMV on one MI355X.
+
+Default workload: web-like graph, 2^27 vertices, ~1.2G distinct edges (mean
+out-degree 9, 85% of targets within +-4096 of the source), last internal level
+cached, plus-times over a batch of 8 fp32 vectors; one step = one right and one
+left product (fill + cached-level leaf kernel each).  Inputs are resident in
+HBM before the timed region starts.
+
+Prints one JSON line: edges/s over the step (both products), the dominant
+kernel's roofline (algorithmic bytes per launch over its HIP-event duration),
+device bytes (estimate vs measured) and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E, published
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="web_n27_d9")
+    p.add_argument("--mode", default=None, help="tree or cached (default: the workload's)")
+    p.add_argument("--tile-nodes", type=int, default=2048)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-stride", type=int, default=32,
+                   help="oracle sample: the edges whose source is a multiple of this")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a 1 GiB device copy (counter calibration) and exit")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "tree_graph_spmv_amd", "csrc", "k2_device.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(nodes, top, n_in, n_out, batch, mode, elem=4):
+    """Bytes a product's main kernel must move: matrix structure read once,
+    x read once, y read and written once (the atomics' read-modify-write)."""
+    L = len(nodes)
+    vec = elem * n_in * batch + 2 * elem * n_out * batch
+    if mode == "cached":
+        n2, n1 = nodes[L - 2], nodes[L - 1]
+        struct = 8 * n2 + 8 * ((n2 + 15) // 16) + 4 * ((n2 + 255) // 256) + 8 * ((n1 + 15) // 16)
+    else:
+        struct = sum(8 * ((nodes[d] + 15) // 16) for d in range(top, L))
+        struct += sum(4 * ((nodes[d] + 255) // 256) for d in range(top, L - 1))
+        struct += 8 * nodes[top]
+    return struct + vec, struct, vec
+
+
+def copy_probe():
+    import torch
+    a = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": a.numel() * 4, "copy_probe_bytes_written":
+                      a.numel() * 4, "launches": 5}))
+
+
+ORACLE_SEMIRING = {"plus_times": 0, "boolean": 1, "boolean_u32": 2, "tropical": 3}
+
+
+def cpu_baseline(rows, cols, n, x_by_dir, batch, directions, stride, semiring):
+    """The oracle, as it is, on the edges whose source is a multiple of
+    'stride' (same dimensions, same x): one product per direction."""
+    import numpy as np
+
+    import oracle
+    sel = (rows % stride) == 0
+    r, c = rows[sel], cols[sel]
+    threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = max(1, min(int(threads), 64))
+    t0 = time.perf_counter()
+    tree = oracle.OracleTree(r, c, n, n)
+    build_s = time.perf_counter() - t0
+    total_s = 0.0
+    for d in directions:
+        t0 = time.perf_counter()
+        tree.spmv(x_by_dir[d], ORACLE_SEMIRING[semiring], oracle.RIGHT if d == "right" else oracle.LEFT,
+                  batch, threads=threads)
+        total_s += time.perf_counter() - t0
+    products = len(directions)
+    return {"value": tree.nnz * products / total_s, "unit": "edges/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"edges with source % {stride} == 0 ({tree.nnz} distinct of the workload's), "
+                       f"same 2^{int(np.log2(n))} dimensions and x; one {' and one '.join(directions)}"
+                       f" product, batch {batch}; oracle build {build_s:.1f} s "
+                       f"not counted"),
+            "seconds": total_s}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import numpy as np
+    import torch
+
+    import synth
+    import tree_graph_spmv_amd as k2
+
+    w = synth.WORKLOADS[args.workload]
+    mode = args.mode or ("cached" if w["cached"] else "tree")
+    batch = w["batch"]
+    semiring = w["semiring"]
+    directions = list(w["directions"])
+    dev = torch.device("cuda:0")
+
+    t0 = time.perf_counter()
+    rows, cols, n = synth.workload_edges(args.workload)
+    gen_s = time.perf_counter() - t0
+    log(f"generated {len(rows)} edges in {gen_s:.1f}s")
+    t0 = time.perf_counter()
+    tree = k2.Tree(rows, cols, n, n)
+    build_s = time.perf_counter() - t0
+    nodes = tree.level_nodes()
+    log(f"built: nnz={tree.nnz} nodes={tree.nodes} levels={tree.levels} in {build_s:.1f}s")
+
+    opts = k2.plan_defaults(tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"))
+    est = tree.estimate(opts, semiring=semiring, batch=batch)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    t0 = time.perf_counter()
+    m = k2.Matrix(tree, opts, device=dev)
+    xs, ys = {}, {}
+    for d in directions:
+        n_in = n   # square workloads
+        xh = synth.workload_x(args.workload, n_in, seed_offset=0 if d == "right" else 1)
+        xs[d] = torch.from_numpy(xh.view(np.int32) if xh.dtype == np.uint32 else xh).to(dev)
+        ys[d] = torch.empty(n * batch, dtype=xs[d].dtype, device=dev)
+    torch.cuda.synchronize()
+    create_s = time.perf_counter() - t0
+    for d in directions:   # one product each before measuring memory
+        m.spmv(xs[d], ys[d], direction=d, semiring=semiring, batch=batch, mode=mode)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    measured = free0 - free1
+    log(f"matrix created in {create_s:.1f}s; device bytes estimate {est['total']} measured {measured}")
+
+    def step():
+        for d in directions:
+            m.spmv(xs[d], ys[d], direction=d, semiring=semiring, batch=batch, mode=mode)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # Timed region.  HIP events on the product stream bracket the fill and the
+    # main kernel of every product; reading them waits for that product, which
+    # adds a host round trip per product to ms_per_step (tens of microseconds).
+    m.set_timing(True)
+    fills = {d: [] for d in directions}
+    mains = {d: [] for d in directions}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for d in directions:
+            m.spmv(xs[d], ys[d], direction=d, semiring=semiring, batch=batch, mode=mode)
+            f_ms, k_ms = m.last_timing()
+            fills[d].append(f_ms)
+            mains[d].append(k_ms)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    m.set_timing(False)
+    ms_per_step = 1000.0 * elapsed / args.steps
+    log(f"{args.steps} steps in {elapsed:.3f}s")
+
+    per_dir = {}
+    for d in directions:
+        alg, struct, vec = algorithmic_bytes(nodes, m.top_level, n, n, batch, mode)
+        k_ms = statistics.mean(mains[d])
+        f_ms = statistics.mean(fills[d])
+        per_dir[d] = {"kernel_ms": k_ms, "kernel_ms_median": statistics.median(mains[d]),
+                      "fill_ms": f_ms,
+                      "edges_per_s": tree.nnz / ((k_ms + f_ms) / 1000.0),
+                      "edges_per_s_per_vector": tree.nnz * batch / ((k_ms + f_ms) / 1000.0),
+                      "alg_bytes": alg, "alg_struct_bytes": struct, "alg_vector_bytes": vec,
+                      "alg_gbs": alg / (k_ms / 1000.0) / 1e9}
+
+    dom = "right" if "right" in per_dir else directions[0]
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            tj = json.load(f)
+        key = f"{args.workload}:{mode}:{dom}"
+        if tj.get("kernel_source") == kernel_source_hash() and key in tj.get("per_launch_bytes", {}):
+            traffic = tj["per_launch_bytes"][key]
+    achieved = per_dir[dom]["alg_gbs"]
+    result = {
+        "metric": "edges/sec and achieved HBM GB/s (% of peak) per SpMV, right & left, 1 GPU",
+        "value": tree.nnz * len(directions) / (ms_per_step / 1000.0),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if semiring != "boolean_u32" else "u32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "vertices": n, "edges": tree.nnz,
+                   "tree_nodes": tree.nodes, "levels": tree.levels, "batch": batch,
+                   "semiring": semiring, "mode": mode, "directions": directions,
+                   "tile_nodes": args.tile_nodes},
+        "roofline": {"kernel": f"{'cached_kernel' if mode == 'cached' else 'descent_kernel'} "
+                               f"({dom} product)",
+                     "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": traffic},
+        "per_direction": per_dir,
+        "device_bytes": {"estimate": est["total"], "estimate_arena": est["arena"],
+                         "measured": int(measured)},
+        "setup_s": {"generate": gen_s, "build": build_s, "create": create_s},
+        "kernel_source": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a sample)")
+        xh = {d: xs[d].cpu().numpy() for d in directions}
+        xh = {d: (v.view(np.uint32) if v.dtype == np.int32 else v) for d, v in xh.items()}
+        result["cpu_baseline"] = cpu_baseline(rows, cols, n, xh, batch, directions,
+                                              args.cpu_sample_stride, semiring)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

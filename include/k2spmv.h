@@ -69,6 +69,11 @@ typedef enum { K2_RIGHT = 0, K2_LEFT = 1 } k2_direction;
    level when the matrix holds it, else the tree-only descent. */
 typedef enum { K2_MODE_AUTO = 0, K2_MODE_TREE_ONLY = 1, K2_MODE_CACHED = 2 } k2_mode;
 
+/* Flag or-ed into the mode of k2_spmv: skip the fill and accumulate into the
+   caller's y (y = y (+) A x), for products summed over several matrices or
+   steps that update a running vector. */
+#define K2_SPMV_ACCUMULATE 0x100
+
 typedef struct {
     /* Tiled descent (Sec. 3.4): a tile is a contiguous node range whose
        subtree holds at most tile_nodes nodes on every level; one workgroup
@@ -82,7 +87,18 @@ typedef struct {
     /* Keep the Morton codes of the last internal level on the device, 8 bytes
        per node (Sec. 3.5, "k2+F").  Default 0. */
     int32_t cache_last_level;
-    int32_t reserved;
+    /* Workgroup order: 1 gives each of the MI355X's 8 XCDs (own L2 each)
+       contiguous node ranges instead of round-robin neighbours, so the y
+       lines a Z-order region touches stay in one L2.  Default 0 (measured
+       slower on the web-like 2^27 workload). */
+    int32_t xcd_remap;
+    /* Output windows: a tile inside a dense Q x Q quadrant accumulates its
+       outputs in LDS and adds them to y once, where Q is the largest power
+       of 2 with Q * window_batch <= window_elems (at most 16384 elements of
+       4 bytes; 0 disables).  Products with more than window_batch vectors
+       use direct atomics everywhere.  Defaults 0 (off) and 8. */
+    uint32_t window_elems;
+    uint32_t window_batch;
 } k2_plan_opts;
 
 /* Device bytes of a matrix and of one product, by part; 'arena' is what
@@ -154,19 +170,21 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
                                    k2_semiring semiring, uint32_t batch,
                                    k2_mem_breakdown *out);
 
-/* The tile plan a matrix created with 'opts' would use (host only, no HIP
-   call; Sec. 3.4): the host-top level d0, the number of tiles and of tile
-   start codes.  Errors: K2_E_INVALID_ARG. */
+/* The tile plans a matrix created with 'opts' would use (host only, no HIP
+   call; Sec. 3.4): the host-top level d0, the number of descent tiles, of
+   cached-level tiles and of tile start codes.  Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *top_level,
-                       uint64_t *n_tiles, uint64_t *n_codes);
+                       uint64_t *n_tiles, uint64_t *n_cached_tiles, uint64_t *n_codes);
 
-/* The tiles themselves, in depth-first order: tiles[4k..4k+3] = (first node,
-   node count, level, index of the first node's code in 'codes'); 'codes' are
-   Morton codes (row bit above column bit per level, 2*level bits).  Host
-   arrays of 4*n_tiles and n_codes entries (from k2_plan_info).
-   Errors: K2_E_INVALID_ARG. */
-k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *tiles,
-                        uint64_t n_tiles, uint64_t *codes, uint64_t n_codes);
+/* The tiles themselves, in depth-first order; which = 0: descent tiles (and
+   their start codes), 1: cached-level tiles ('codes' unused).
+   tiles[8k..8k+7] = (first node, node count, level, index of the first
+   node's code in 'codes', window row, window column, log2 of the window side
+   or 0xFFFFFFFF for no window, 0).  'codes' are Morton codes (row bit above
+   column bit per level, 2*level bits).  Host arrays of 8*n_tiles and n_codes
+   entries (from k2_plan_info).  Errors: K2_E_INVALID_ARG. */
+k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
+                        uint32_t *tiles, uint64_t n_tiles, uint64_t *codes, uint64_t n_codes);
 
 /* Upload a tree into the caller's device arena (d_arena, arena_bytes >=
    estimate's arena; 256-byte aligned) on 'stream' and return a matrix handle.
@@ -181,11 +199,21 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
    row-major vectors (Algorithm 1), asynchronously on 'stream'.  d_x and d_y
    are device arrays of the lengths given at the top of this file (float, or
    uint32 for K2_BOOLEAN_U32X32); they must not overlap.  y is overwritten.
-   'mode' picks the traversal (k2_mode).  Errors (nothing launched):
+   'mode' picks the traversal (k2_mode), optionally or-ed with
+   K2_SPMV_ACCUMULATE.  Errors (nothing launched):
    K2_E_INVALID_ARG (null, batch 0, bad enum, K2_MODE_CACHED without cached
    codes), K2_E_HIP (launch failure). */
 k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semiring,
                   uint32_t batch, int32_t mode, const void *d_x, void *d_y, void *stream);
+
+/* Kernel timing (HIP events on the product's stream).  While enabled, every
+   k2_spmv records an event before the fill, between the fill and the main
+   kernel, and after the main kernel; k2_matrix_last_timing waits for the
+   last product and returns the fill and main-kernel durations in ms (the
+   fill time is 0 under K2_SPMV_ACCUMULATE).  Errors: K2_E_INVALID_ARG
+   (timing off or no product yet), K2_E_HIP. */
+k2_status k2_matrix_set_timing(k2_matrix *matrix, int32_t enable);
+k2_status k2_matrix_last_timing(k2_matrix *matrix, float *fill_ms, float *kernel_ms);
 
 /* Release the handle (the arena stays the caller's). */
 k2_status k2_matrix_destroy(k2_matrix *matrix);

@@ -29,16 +29,19 @@ def dev():
     return torch.device("cuda:0")
 
 
+PLAN_VARIANTS = (dict(), dict(window_elems=0), dict(host_top_max=4, window_elems=4096, window_batch=4))
+
+
 def run_all(k2, rows, cols, n_rows, n_cols, dev, semirings=ALL_SEMIRINGS, batches=(1, 3),
-            tiles=(256, 2048), modes=("tree", "cached"), seed=0, label=""):
+            tiles=(256, 2048), modes=("tree", "cached"), seed=0, label="", variants=PLAN_VARIANTS):
     tree = k2.Tree(rows, cols, n_rows, n_cols)
     ref = oracle.OracleTree(rows, cols, n_rows, n_cols)
     assert tree.nnz == ref.nnz
     for d in range(tree.levels):
         assert np.array_equal(tree.level_words(d), ref.level_words(d)), f"{label} level {d}"
     rng = np.random.default_rng(seed)
-    for tile in tiles:
-        opts = k2.plan_defaults(tile_nodes=tile, cache_last_level=1 if "cached" in modes else 0)
+    for tile, var in itertools.product(tiles, variants):
+        opts = k2.plan_defaults(tile_nodes=tile, cache_last_level=1 if "cached" in modes else 0, **var)
         m = k2.Matrix(tree, opts, device=dev)
         for mode, sr, direction, B in itertools.product(modes, semirings, ("right", "left"),
                                                         batches):
@@ -48,7 +51,7 @@ def run_all(k2, rows, cols, n_rows, n_cols, dev, semirings=ALL_SEMIRINGS, batche
             torch.cuda.synchronize()
             want = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
             check_parity(from_device(y, sr), want, sr,
-                         f"{label} tile={tile} {mode} {sr} {direction} B={B}")
+                         f"{label} tile={tile} {var} {mode} {sr} {direction} B={B}")
 
 
 def test_fig1(dev, fig1):

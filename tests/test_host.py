@@ -1,0 +1,200 @@
+"""Host logic of the library, checked on the CPU against the oracle.
+
+* k2_build: every level's packed signatures and the S = 256 directory equal
+  the oracle's, on several shapes and densities.
+* Tile plans (k2_plan_*): descent tiles and cached-level tiles cover the last
+  internal level exactly once, in order; no descent tile's subtree exceeds
+  tile_nodes; tile start codes are the Morton codes of their nodes; every
+  cell below a windowed tile lies inside its window.
+* k2_estimate_device_bytes: the parts add up and follow the sizes of the
+  levels, directories and cached codes.
+* Errors: out-of-range edges, bad options.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import tree_graph_spmv_amd as k2
+
+
+def rand_edges(seed, n_rows, n_cols, m):
+    rng = np.random.default_rng(seed)
+    return (rng.integers(0, n_rows, m).astype(np.uint32), rng.integers(0, n_cols, m).astype(np.uint32))
+
+
+def banded(seed, n, m, width):
+    rng = np.random.default_rng(seed)
+    r = rng.integers(0, n, m)
+    c = np.clip(r + rng.integers(-width, width + 1, m), 0, n - 1)
+    far = rng.random(m) < 0.1
+    c[far] = rng.integers(0, n, far.sum())
+    return r.astype(np.uint32), c.astype(np.uint32)
+
+
+CASES = {
+    "rmat12": lambda: (*synth.rmat(12, 32768, seed=12), 4096, 4096),
+    "rmat14": lambda: (*synth.rmat(14, 200000, seed=4), 2 ** 14, 2 ** 14),
+    "banded": lambda: (*banded(3, 50000, 300000, 300), 50000, 50000),
+    "rect": lambda: (*rand_edges(5, 3000, 700, 20000), 3000, 700),
+    "tiny": lambda: (np.array([0, 1, 2], np.uint32), np.array([2, 0, 1], np.uint32), 3, 3),
+    "dense64": lambda: (*[a.ravel().astype(np.uint32) for a in np.meshgrid(np.arange(64), np.arange(64),
+                                                                             indexing="ij")], 64, 64),
+}
+
+
+@pytest.fixture(scope="module", params=sorted(CASES))
+def case(request):
+    r, c, nr, nc = CASES[request.param]()
+    return request.param, r, c, nr, nc, k2.Tree(r, c, nr, nc), oracle.OracleTree(r, c, nr, nc)
+
+
+def test_build_matches_oracle(case):
+    name, r, c, nr, nc, t, o = case
+    assert t.levels == o.levels and t.nnz == o.nnz
+    assert t.level_nodes() == o.level_nodes()
+    for d in range(t.levels):
+        assert np.array_equal(t.level_words(d), o.level_words(d)), (name, d)
+    for d in range(t.levels - 1):
+        assert np.array_equal(t.directory(d).astype(np.uint64), o.directory(d, 256)), (name, d)
+
+
+def oracle_codes(o, upto):
+    """Morton codes of every level 0..upto, by expanding the oracle's tree."""
+    codes = [np.zeros(1, np.uint64)]
+    for d in range(upto):
+        sig = o.signatures(d)
+        nxt = []
+        for i, s in enumerate(sig.tolist()):
+            for b in range(4):
+                if s >> b & 1:
+                    nxt.append((int(codes[d][i]) << 2) | b)
+        codes.append(np.array(nxt, np.uint64))
+    return codes
+
+
+def check_plan(o, cells_r, cells_c, top, tiles, codes, ctiles, opts, all_codes):
+    L = o.levels
+    last = L - 2
+    nodes = o.level_nodes()
+    offs = [o.child_offsets(d) for d in range(L - 1)]
+
+    def down(d, i):
+        while d < last:
+            i = int(offs[d][i]) if i < nodes[d] else nodes[d + 1]
+            d += 1
+        return i
+
+    # cells of the last-internal-level range [a, b): leaves [off(a), off(b)),
+    # whose cells come consecutively in the oracle's enumeration
+    leaf_pop = np.array([bin(int(s)).count("1") for s in o.signatures(L - 1)], np.int64)
+    cell_start = np.concatenate([[0], np.cumsum(leaf_pop)])
+
+    def cells_of(a, b):
+        la = int(offs[last][a]) if a < nodes[last] else nodes[L - 1]
+        lb = int(offs[last][b]) if b < nodes[last] else nodes[L - 1]
+        return cells_r[cell_start[la]:cell_start[lb]], cells_c[cell_start[la]:cell_start[lb]]
+
+    def check_window(tl, a, b):
+        if tl[6] == 0xFFFFFFFF:
+            return
+        side = 1 << int(tl[6])
+        rr, cc = cells_of(a, b)
+        assert np.all((rr >= tl[4]) & (rr < tl[4] + side)), "cell row outside window"
+        assert np.all((cc >= tl[5]) & (cc < tl[5] + side)), "cell column outside window"
+        assert side * opts.window_batch <= max(opts.window_elems, 1)
+
+    pos = 0
+    for tl in tiles:
+        first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
+        assert top <= level <= last and count >= 1
+        a, b = down(level, first), down(level, first + count)
+        assert a == pos, "descent tiles must follow each other on the last internal level"
+        assert b - a <= opts.tile_nodes
+        pos = b
+        got = codes[int(tl[3]):int(tl[3]) + count]
+        assert np.array_equal(got, all_codes[level][first:first + count])
+        check_window(tl, a, b)
+    assert pos == nodes[last]
+    pos = 0
+    for tl in ctiles:
+        first, count = int(tl[0]), int(tl[1])
+        assert first == pos and count >= 1 and int(tl[2]) == last
+        pos = first + count
+        check_window(tl, first, first + count)
+    assert pos == nodes[last]
+
+
+@pytest.mark.parametrize("opt", [
+    dict(),
+    dict(tile_nodes=256, window_elems=1024, window_batch=1),
+    dict(tile_nodes=4096, window_elems=16384, window_batch=1),
+    dict(window_elems=0),
+    dict(host_top_max=4, window_elems=8192, window_batch=64),
+    dict(host_top_max=1 << 20, window_elems=2048, window_batch=2),
+])
+def test_plan_invariants(case, opt):
+    name, r, c, nr, nc, t, o = case
+    opts = k2.plan_defaults(**opt)
+    top, tiles, codes, ctiles = t.plan(opts)
+    if o.level_nodes()[o.levels - 2] == 0:
+        assert len(tiles) == 0 and len(ctiles) == 0
+        return
+    cr, cc = o.cells()
+    all_codes = oracle_codes(o, o.levels - 2)
+    check_plan(o, cr.astype(np.int64), cc.astype(np.int64), top, tiles, codes, ctiles, opts,
+               all_codes)
+
+
+def test_top_level(case):
+    name, r, c, nr, nc, t, o = case
+    nodes = o.level_nodes()
+    for cap in (1, 4, 100, 1 << 16):
+        top, *_ = t.plan(k2.plan_defaults(host_top_max=cap))
+        want = max(d for d in range(o.levels - 1) if nodes[d] <= cap)
+        assert top == want
+
+
+def test_estimate_parts(case):
+    name, r, c, nr, nc, t, o = case
+    nodes = o.level_nodes()
+    for cached in (0, 1):
+        opts = k2.plan_defaults(cache_last_level=cached)
+        est = t.estimate(opts, semiring="plus_times", batch=3)
+        top, tiles, codes, ctiles = t.plan(opts)
+        L = o.levels
+        assert est["tree"] == sum(8 * ((nodes[d] + 15) // 16) for d in range(top, L))
+        assert est["directory"] == sum(4 * ((nodes[d] + 255) // 256) for d in range(top, L - 1))
+        assert est["top_codes"] == 8 * len(codes)
+        assert est["tiles"] == 32 * len(tiles) + (32 * len(ctiles) if cached else 0)
+        assert est["cached_codes"] == (8 * nodes[L - 2] if cached else 0)
+        parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
+                                     "scratch", "alignment"))
+        assert est["arena"] == parts and est["arena"] % 256 == 0
+        assert est["vectors"] == (nr + nc) * 3 * 4
+        assert est["total"] == est["arena"] + est["vectors"]
+
+
+def test_errors():
+    with pytest.raises(k2.K2Error) as e:
+        k2.Tree([5], [0], 5, 5)
+    assert e.value.status == k2.K2_E_INDEX_RANGE
+    with pytest.raises(k2.K2Error) as e:
+        k2.Tree([0], [0], 0, 5)
+    assert e.value.status == k2.K2_E_INVALID_ARG
+    t = k2.Tree([0, 1], [1, 0], 2, 2)
+    for bad in (dict(tile_nodes=100), dict(tile_nodes=3000), dict(tile_nodes=8192),
+                dict(window_elems=1 << 15)):
+        with pytest.raises(k2.K2Error) as e:
+            t.estimate(k2.plan_defaults(**bad))
+        assert e.value.status == k2.K2_E_INVALID_ARG
+    with pytest.raises(k2.K2Error):
+        t.estimate(batch=0)
+
+
+def test_threads_do_not_change_the_tree():
+    r, c = synth.rmat(13, 60000, seed=8)
+    t1 = k2.Tree(r, c, 8192, 8192, n_threads=1)
+    t7 = k2.Tree(r, c, 8192, 8192, n_threads=7)
+    for d in range(t1.levels):
+        assert np.array_equal(t1.level_words(d), t7.level_words(d))

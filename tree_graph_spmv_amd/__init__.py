@@ -22,6 +22,7 @@ K2_OK, K2_E_INVALID_ARG, K2_E_INDEX_RANGE, K2_E_ARENA_TOO_SMALL, K2_E_HOST_OOM, 
 K2_PLUS_TIMES_F32, K2_BOOLEAN_F32, K2_BOOLEAN_U32X32, K2_TROPICAL_F32 = range(4)
 K2_RIGHT, K2_LEFT = 0, 1
 K2_MODE_AUTO, K2_MODE_TREE_ONLY, K2_MODE_CACHED = 0, 1, 2
+K2_SPMV_ACCUMULATE = 0x100
 
 SEMIRINGS = {"plus_times": K2_PLUS_TIMES_F32, "boolean": K2_BOOLEAN_F32,
              "boolean_u32": K2_BOOLEAN_U32X32, "tropical": K2_TROPICAL_F32}
@@ -31,7 +32,8 @@ MODES = {"auto": K2_MODE_AUTO, "tree": K2_MODE_TREE_ONLY, "cached": K2_MODE_CACH
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("tile_nodes", ctypes.c_uint32), ("host_top_max", ctypes.c_uint32),
-                ("cache_last_level", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("cache_last_level", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
+                ("window_elems", ctypes.c_uint32), ("window_batch", ctypes.c_uint32)]
 
 
 class MemBreakdown(ctypes.Structure):
@@ -75,9 +77,9 @@ _SIGS = {
     "k2_tree_directory": (ctypes.c_int, [_VP, ctypes.c_uint32, _U32P, ctypes.c_uint64]),
     "k2_estimate_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_int,
                                                 ctypes.c_uint32, ctypes.POINTER(MemBreakdown)]),
-    "k2_plan_info": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _U32P, _U64P, _U64P]),
-    "k2_plan_tiles": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _U32P, ctypes.c_uint64, _U64P,
-                                     ctypes.c_uint64]),
+    "k2_plan_info": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _U32P, _U64P, _U64P, _U64P]),
+    "k2_plan_tiles": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_int32, _U32P,
+                                     ctypes.c_uint64, _U64P, ctypes.c_uint64]),
     "k2_matrix_create": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _VP, ctypes.c_uint64, _VP,
                                         ctypes.POINTER(_VP)]),
     "k2_spmv": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int32,
@@ -86,6 +88,9 @@ _SIGS = {
     "k2_matrix_info": (ctypes.c_int, [_VP, _U32P, _U64P, ctypes.POINTER(ctypes.c_int32)]),
     "k2_matrix_level_words": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P, ctypes.c_uint64, _VP]),
     "k2_matrix_cached_codes": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
+    "k2_matrix_set_timing": (ctypes.c_int, [_VP, ctypes.c_int32]),
+    "k2_matrix_last_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_float),
+                                             ctypes.POINTER(ctypes.c_float)]),
     "k2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "k2_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -180,18 +185,22 @@ class Tree:
         return m.as_dict()
 
     def plan(self, opts=None):
-        """(top_level, tiles (n,4) uint32, codes uint64) of the tile plan."""
+        """(top_level, descent tiles (n,8) uint32, codes uint64, cached tiles (m,8))."""
         opts = opts or plan_defaults()
         top = ctypes.c_uint32()
         nt = ctypes.c_uint64()
+        nct = ctypes.c_uint64()
         nc = ctypes.c_uint64()
         _check(lib().k2_plan_info(self._h, ctypes.byref(opts), ctypes.byref(top), ctypes.byref(nt),
-                                  ctypes.byref(nc)), "k2_plan_info")
-        tiles = np.zeros((max(nt.value, 1), 4), np.uint32)
+                                  ctypes.byref(nct), ctypes.byref(nc)), "k2_plan_info")
+        tiles = np.zeros((max(nt.value, 1), 8), np.uint32)
         codes = np.zeros(max(nc.value, 1), np.uint64)
-        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), tiles.ctypes.data_as(_U32P),
+        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), 0, tiles.ctypes.data_as(_U32P),
                                    nt.value, codes.ctypes.data_as(_U64P), nc.value), "k2_plan_tiles")
-        return int(top.value), tiles[:nt.value], codes[:nc.value]
+        ctiles = np.zeros((max(nct.value, 1), 8), np.uint32)
+        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), 1, ctiles.ctypes.data_as(_U32P),
+                                   nct.value, None, 0), "k2_plan_tiles")
+        return int(top.value), tiles[:nt.value], codes[:nc.value], ctiles[:nct.value]
 
 
 def _stream_handle(stream):
@@ -234,9 +243,22 @@ class Matrix:
             _lib.k2_matrix_destroy(h)
             self._h = None
 
+    def set_timing(self, enable=True):
+        _check(lib().k2_matrix_set_timing(self._h, int(bool(enable))), "k2_matrix_set_timing")
+
+    def last_timing(self):
+        """(fill ms, main kernel ms) of the last product (waits for it)."""
+        a = ctypes.c_float()
+        b = ctypes.c_float()
+        _check(lib().k2_matrix_last_timing(self._h, ctypes.byref(a), ctypes.byref(b)),
+               "k2_matrix_last_timing")
+        return float(a.value), float(b.value)
+
     def spmv(self, x, y=None, direction="right", semiring="plus_times", batch=1, mode="auto",
-             stream=None):
-        """y = A x ('right') or x^T A ('left'); x, y torch device tensors."""
+             accumulate=False, stream=None):
+        """y = A x ('right') or x^T A ('left'); x, y torch device tensors.
+        accumulate=True: y is not filled first, the product is or-ed/added/
+        min-ed into it (y must then be given)."""
         import torch
         d = DIRECTIONS[direction]
         n_in = self.n_cols if d == K2_RIGHT else self.n_rows
@@ -247,10 +269,13 @@ class Matrix:
         if x.device != self.device:
             raise ValueError("x is on another device")
         if y is None:
+            if accumulate:
+                raise ValueError("accumulate needs y")
             y = torch.empty(n_out * batch, dtype=dtype, device=self.device)
         elif y.dtype != dtype or y.numel() != n_out * batch or not y.is_contiguous():
             raise ValueError(f"y must be a contiguous {dtype} tensor of {n_out * batch} elements")
-        _check(lib().k2_spmv(self._h, d, SEMIRINGS[semiring], int(batch), MODES[mode],
+        flags = MODES[mode] | (K2_SPMV_ACCUMULATE if accumulate else 0)
+        _check(lib().k2_spmv(self._h, d, SEMIRINGS[semiring], int(batch), flags,
                              _VP(x.data_ptr()), _VP(y.data_ptr()), _stream_handle(stream)),
                "k2_spmv")
         return y

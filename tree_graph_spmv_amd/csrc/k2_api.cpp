@@ -35,6 +35,7 @@ namespace {
 bool valid_opts(const k2_plan_opts &o) {
     if (o.tile_nodes < 256 || o.tile_nodes > 4096) return false;
     if (o.tile_nodes & (o.tile_nodes - 1)) return false;
+    if (o.window_elems > 16384) return false;
     return true;
 }
 
@@ -46,7 +47,8 @@ k2_status estimate(const HostTree &t, const k2_plan_opts &o, Plan *plan, Layout 
     k2_status st = make_plan(t, o, plan);
     if (st != K2_OK) return st;
     bool cached = o.cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
-    layout_for(t, plan->top_level, plan->codes.size(), plan->tiles.size(), cached, lay);
+    layout_for(t, plan->top_level, plan->codes.size(), plan->tiles.size(), plan->cached_tiles.size(),
+               cached, lay);
     return K2_OK;
 }
 
@@ -68,7 +70,9 @@ k2_status k2_plan_defaults(k2_plan_opts *opts) {
     opts->tile_nodes = 2048;
     opts->host_top_max = 1u << 16;
     opts->cache_last_level = 0;
-    opts->reserved = 0;
+    opts->xcd_remap = 0;
+    opts->window_elems = 0;
+    opts->window_batch = 8;
     return K2_OK;
 }
 
@@ -156,7 +160,7 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
 }
 
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *top_level,
-                       uint64_t *n_tiles, uint64_t *n_codes) {
+                       uint64_t *n_tiles, uint64_t *n_cached_tiles, uint64_t *n_codes) {
     if (!tree || !opts || !valid_opts(*opts)) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
@@ -168,13 +172,14 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *
     if (st != K2_OK) return st;
     if (top_level) *top_level = uint32_t(plan.top_level);
     if (n_tiles) *n_tiles = plan.tiles.size();
+    if (n_cached_tiles) *n_cached_tiles = plan.cached_tiles.size();
     if (n_codes) *n_codes = plan.codes.size();
     return K2_OK;
 }
 
-k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *tiles,
+k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which, uint32_t *tiles,
                         uint64_t n_tiles, uint64_t *codes, uint64_t n_codes) {
-    if (!tree || !opts || !valid_opts(*opts)) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || (which != 0 && which != 1)) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -183,15 +188,17 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, uint32_t 
         return K2_E_HOST_OOM;
     }
     if (st != K2_OK) return st;
-    if (n_tiles < plan.tiles.size() || n_codes < plan.codes.size()) return K2_E_INVALID_ARG;
-    if ((!tiles && !plan.tiles.empty()) || (!codes && !plan.codes.empty())) return K2_E_INVALID_ARG;
-    for (size_t k = 0; k < plan.tiles.size(); ++k) {
-        tiles[4 * k + 0] = plan.tiles[k].first;
-        tiles[4 * k + 1] = plan.tiles[k].count;
-        tiles[4 * k + 2] = plan.tiles[k].level;
-        tiles[4 * k + 3] = plan.tiles[k].code_off;
+    const std::vector<Tile> &list = which == 0 ? plan.tiles : plan.cached_tiles;
+    if (n_tiles < list.size() || (which == 0 && n_codes < plan.codes.size())) return K2_E_INVALID_ARG;
+    if ((!tiles && !list.empty()) || (which == 0 && !codes && !plan.codes.empty()))
+        return K2_E_INVALID_ARG;
+    for (size_t k = 0; k < list.size(); ++k) {
+        const Tile &tl = list[k];
+        const uint32_t v[8] = {tl.first, tl.count, tl.level, tl.code_off,
+                               tl.win_row, tl.win_col, tl.win_log2, 0u};
+        std::copy(v, v + 8, tiles + 8 * k);
     }
-    std::copy(plan.codes.begin(), plan.codes.end(), codes);
+    if (which == 0) std::copy(plan.codes.begin(), plan.codes.end(), codes);
     return K2_OK;
 }
 
@@ -224,6 +231,9 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     m.levels = t.levels;
     m.nodes = t.nodes;
     m.cached = opts->cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
+    m.xcd_remap = opts->xcd_remap != 0;
+    m.window_elems = m.plan.window_log2 >= 0 ? opts->window_elems : 0;
+    m.window_batch = opts->window_batch;
     std::memset(&m.dev, 0, sizeof(m.dev));
     m.dev.levels = t.levels;
     m.dev.top_level = m.plan.top_level;
@@ -276,6 +286,16 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
         }
     }
     if (m.cached) {
+        m.d_cached_tiles = reinterpret_cast<const Tile *>(m.arena + m.layout.cached_tiles_off);
+        if (!m.plan.cached_tiles.empty()) {
+            hipError_t e = hipMemcpyAsync(const_cast<Tile *>(m.d_cached_tiles), m.plan.cached_tiles.data(),
+                                          m.plan.cached_tiles.size() * sizeof(Tile),
+                                          hipMemcpyHostToDevice, st_h);
+            if (e != hipSuccess) {
+                set_hip_error(int(e), "upload cached tiles");
+                return fail(K2_E_HIP);
+            }
+        }
         m.d_cached = reinterpret_cast<uint64_t *>(m.arena + m.layout.cached_off);
         int e = launch_descent(m, K2_RIGHT, K2_BOOLEAN_U32X32, 1, nullptr, nullptr, m.d_cached, stream);
         if (e != hipSuccess) {
@@ -298,6 +318,8 @@ k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semirin
     if (int(direction) != K2_RIGHT && int(direction) != K2_LEFT) return K2_E_INVALID_ARG;
     if (int(semiring) < 0 || int(semiring) > 3) return K2_E_INVALID_ARG;
     Matrix &m = matrix->m;
+    const bool accumulate = (mode & K2_SPMV_ACCUMULATE) != 0;
+    mode &= ~int32_t(K2_SPMV_ACCUMULATE);
     if (mode == K2_MODE_AUTO) mode = m.cached ? K2_MODE_CACHED : K2_MODE_TREE_ONLY;
     if (mode != K2_MODE_TREE_ONLY && mode != K2_MODE_CACHED) return K2_E_INVALID_ARG;
     const bool empty = m.nodes[m.levels - 2] == 0;
@@ -309,25 +331,65 @@ k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semirin
         const uint64_t xl = n_in * batch * 4, yl = n_out * batch * 4;
         if (xb < yb + yl && yb < xb + xl) return K2_E_INVALID_ARG;
     }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (m.timing) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(m.ev[0]), st), "timing");
     const uint32_t zero = semiring == K2_TROPICAL_F32 ? 0x7F800000u : 0u;
-    int e = launch_fill(d_y, n_out * batch, zero, stream);
+    int e = accumulate ? int(hipSuccess) : launch_fill(d_y, n_out * batch, zero, stream);
     if (e != hipSuccess) {
         set_hip_error(e, "fill");
         return K2_E_HIP;
     }
-    if (empty) return K2_OK;
-    e = (mode == K2_MODE_CACHED)
-            ? launch_cached(m, direction, semiring, batch, d_x, d_y, stream)
-            : launch_descent(m, direction, semiring, batch, d_x, d_y, nullptr, stream);
+    if (m.timing) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(m.ev[1]), st), "timing");
+    if (!empty)
+        e = (mode == K2_MODE_CACHED)
+                ? launch_cached(m, direction, semiring, batch, d_x, d_y, stream)
+                : launch_descent(m, direction, semiring, batch, d_x, d_y, nullptr, stream);
     if (e != hipSuccess) {
         set_hip_error(e, "spmv");
         return K2_E_HIP;
     }
+    if (m.timing) {
+        HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(m.ev[2]), st), "timing");
+        m.timed_once = true;
+        m.last_accumulate = accumulate;
+    }
+    return K2_OK;
+}
+
+k2_status k2_matrix_set_timing(k2_matrix *matrix, int32_t enable) {
+    if (!matrix) return K2_E_INVALID_ARG;
+    Matrix &m = matrix->m;
+    if (enable && !m.ev[0]) {
+        for (int k = 0; k < 3; ++k) {
+            hipEvent_t ev;
+            HIP_TRY(hipEventCreate(&ev), "timing events");
+            m.ev[k] = ev;
+        }
+    }
+    m.timing = enable != 0;
+    m.timed_once = false;
+    return K2_OK;
+}
+
+k2_status k2_matrix_last_timing(k2_matrix *matrix, float *fill_ms, float *kernel_ms) {
+    if (!matrix) return K2_E_INVALID_ARG;
+    Matrix &m = matrix->m;
+    if (!m.timing || !m.timed_once) return K2_E_INVALID_ARG;
+    hipEvent_t e0 = static_cast<hipEvent_t>(m.ev[0]), e1 = static_cast<hipEvent_t>(m.ev[1]),
+               e2 = static_cast<hipEvent_t>(m.ev[2]);
+    HIP_TRY(hipEventSynchronize(e2), "timing");
+    float a = 0, b = 0;
+    HIP_TRY(hipEventElapsedTime(&a, e0, e1), "timing");
+    HIP_TRY(hipEventElapsedTime(&b, e1, e2), "timing");
+    if (fill_ms) *fill_ms = m.last_accumulate ? 0.0f : a;
+    if (kernel_ms) *kernel_ms = b;
     return K2_OK;
 }
 
 k2_status k2_matrix_destroy(k2_matrix *matrix) {
     if (!matrix) return K2_E_INVALID_ARG;
+    for (int k = 0; k < 3; ++k)
+        if (matrix->m.ev[k]) (void)hipEventDestroy(static_cast<hipEvent_t>(matrix->m.ev[k]));
     delete matrix;
     return K2_OK;
 }

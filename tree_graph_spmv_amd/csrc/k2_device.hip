@@ -46,10 +46,14 @@ struct PlusTimes {
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0.0f; }
     __device__ static bool contributes(T x) { return x != 0.0f; }
+    __device__ static bool contributes_out(T v) { return v != 0.0f; }
     __device__ static T contrib(T x) { return x; }
     __device__ static T combine(T a, T b) { return a + b; }
     __device__ static void atomic(T *p, T v) {
         __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ static void lds_atomic(T *p, T v) {
+        __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 };
 
@@ -58,11 +62,16 @@ struct BooleanF32 {
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0.0f; }
     __device__ static bool contributes(T x) { return (__float_as_uint(x) & 0x7FFFFFFFu) != 0u; }
+    __device__ static bool contributes_out(T v) { return __float_as_uint(v) != 0u; }
     __device__ static T contrib(T) { return 1.0f; }
     __device__ static T combine(T a, T b) { return a > b ? a : b; }
     __device__ static void atomic(T *p, T v) {
         __hip_atomic_fetch_max(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ static void lds_atomic(T *p, T v) {
+        __hip_atomic_fetch_max(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 };
 
@@ -71,10 +80,14 @@ struct BooleanU32 {
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0u; }
     __device__ static bool contributes(T x) { return x != 0u; }
+    __device__ static bool contributes_out(T v) { return v != 0u; }
     __device__ static T contrib(T x) { return x; }
     __device__ static T combine(T a, T b) { return a | b; }
     __device__ static void atomic(T *p, T v) {
         __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ static void lds_atomic(T *p, T v) {
+        __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 };
 
@@ -83,12 +96,17 @@ struct Tropical {
     static constexpr uint32_t kZeroBits = 0x7F800000u;   // +inf
     __device__ static T zero() { return __uint_as_float(kZeroBits); }
     __device__ static bool contributes(T x) { return x < __uint_as_float(kZeroBits); }
+    __device__ static bool contributes_out(T v) { return __float_as_uint(v) != kZeroBits; }
     __device__ static T contrib(T x) { return 1.0f + x; }
     __device__ static T combine(T a, T b) { return a < b ? a : b; }
     // non-negative floats order like their bit patterns
     __device__ static void atomic(T *p, T v) {
         __hip_atomic_fetch_min(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ static void lds_atomic(T *p, T v) {
+        __hip_atomic_fetch_min(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
     }
 };
 
@@ -112,14 +130,21 @@ __device__ __forceinline__ uint32_t compact_even(uint64_t x) {
     return uint32_t(x);
 }
 
-// Exclusive prefix sum over the workgroup of f in [0, 7] (fan-outs are 0..4).
-__device__ __forceinline__ uint32_t block_scan_small(uint32_t f, uint32_t *s_tot, uint32_t &total) {
+// Exclusive prefix sum over the workgroup of values f < 2^BITS: one ballot per
+// bit of f and the popcount of the lanes below give the wave's prefix; the
+// four wave totals meet in LDS.
+template <int BITS>
+__device__ __forceinline__ uint32_t block_scan(uint32_t f, uint32_t *s_tot, uint32_t &total) {
     const unsigned lane = __lane_id();
     const unsigned wave = threadIdx.x >> 6;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const uint64_t b0 = __ballot(f & 1u), b1 = __ballot(f & 2u), b2 = __ballot(f & 4u);
-    const uint32_t ex = __popcll(b0 & below) + 2u * __popcll(b1 & below) + 4u * __popcll(b2 & below);
-    const uint32_t wt = __popcll(b0) + 2u * __popcll(b1) + 4u * __popcll(b2);
+    uint32_t ex = 0, wt = 0;
+#pragma unroll
+    for (int k = 0; k < BITS; ++k) {
+        const uint64_t b = __ballot((f >> k) & 1u);
+        ex += uint32_t(__popcll(b & below)) << k;
+        wt += uint32_t(__popcll(b)) << k;
+    }
     if (lane == 0) s_tot[wave] = wt;
     __syncthreads();
     uint32_t before = 0, tot = 0;
@@ -163,61 +188,188 @@ __device__ __forceinline__ uint32_t block_child_offset(const DevTree &t, int d, 
     return r;
 }
 
-// The cells of one node of the last internal level: code F, signature s, first
-// leaf 'off'.  Folds the contributions per output index of the node's 4x4
-// block, then one atomic per touched output.  Vectors v = v0, v0+step, ...
-template <class SR, int DIR>
-__device__ __forceinline__ void leaf_node(uint64_t code, uint32_t s, uint32_t off,
-                                          const uint64_t *__restrict__ leaf_words,
-                                          const typename SR::T *__restrict__ x,
-                                          typename SR::T *__restrict__ y, uint32_t B, uint32_t v0,
-                                          uint32_t step) {
-    using T = typename SR::T;
-    if (s == 0) return;
-    const uint64_t R4 = compact_even(code >> 1), C4 = compact_even(code);   // 4x4 block
-    uint32_t lam[4];
-    uint32_t quad[4];
-    int nl = 0;
+// Exclusive prefix sum over the wave of values f < 2^BITS (no LDS): one
+// ballot per bit of f, popcounts of the lanes below.
+template <int BITS>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t f, uint32_t &total) {
+    const unsigned lane = __lane_id();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t ex = 0, tot = 0;
 #pragma unroll
-    for (uint32_t b = 0; b < 4; ++b)
-        if (s & (1u << b)) {
-            lam[nl] = nib(leaf_words, uint64_t(off) + uint64_t(nl));
-            quad[nl] = b;
-            ++nl;
-        }
-    const uint64_t in_base = (DIR == K2_RIGHT) ? 4 * C4 : 4 * R4;
-    const uint64_t out_base = (DIR == K2_RIGHT) ? 4 * R4 : 4 * C4;
-    for (uint32_t v = v0; v < B; v += step) {
-        T acc[4];
-        bool any[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc[k] = SR::zero();
-            any[k] = false;
-        }
-        for (int l = 0; l < nl; ++l) {
-            const uint32_t b = quad[l], lm = lam[l];
-#pragma unroll
-            for (uint32_t q = 0; q < 4; ++q) {
-                if (!(lm & (1u << q))) continue;
-                const uint32_t r = 2 * (b >> 1) + (q >> 1);   // row within the 4x4 block
-                const uint32_t c = 2 * (b & 1) + (q & 1);     // column within the block
-                const uint32_t in_l = (DIR == K2_RIGHT) ? c : r;
-                const uint32_t out_l = (DIR == K2_RIGHT) ? r : c;
-                const T xv = x[(in_base + in_l) * B + v];
-                if (SR::contributes(xv)) {
-                    acc[out_l] = SR::combine(acc[out_l], SR::contrib(xv));
-                    any[out_l] = true;
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (any[k]) SR::atomic(&y[(out_base + k) * B + v], acc[k]);
+    for (int k = 0; k < BITS; ++k) {
+        const uint64_t b = __ballot((f >> k) & 1u);
+        ex += uint32_t(__popcll(b & below)) << k;
+        tot += uint32_t(__popcll(b)) << k;
     }
+    total = tot;
+    return ex;
+}
+
+// Offset in level d+1 of the first child of node i of level d (i < nodes[d]),
+// computed by the calling wave alone: the directory sample of i's block plus
+// the popcounts of the words before i in the block (lanes 0..15, one word
+// each), summed across the wave.
+__device__ __forceinline__ uint32_t wave_child_offset(const DevTree &t, int d, uint32_t i) {
+    const unsigned lane = __lane_id();
+    const uint32_t blk = i >> 8;
+    const uint32_t wi = i >> 4;
+    const uint32_t w = blk * kWordsPerBlock + lane;
+    uint32_t c = 0;
+    if (lane < kWordsPerBlock && w <= wi) {
+        uint64_t v = t.words[d][w];
+        if (w == wi) {
+            const unsigned sh = (i & 15) * 4;
+            v = sh ? (v & ((1ull << sh) - 1)) : 0ull;
+        }
+        c = __popcll(v);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) c += __shfl_xor(c, o, 16);
+    return __shfl(c, 0) + t.dir[d][blk];
+}
+
+// Orders a wave's LDS writes before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Logical workgroup index.  Workgroups are dispatched round-robin over the 8
+// XCDs (workgroup b runs on XCD b % 8); with 'remap' set, XCD k instead gets
+// the k-th contiguous eighth of the logical order, so neighbouring Z-order
+// ranges, which share rows and columns, share one L2.  The grid is a
+// multiple of 8 whenever remap is set.
+__device__ __forceinline__ uint32_t logical_block(int remap) {
+    if (!remap) return blockIdx.x;
+    const uint32_t per = gridDim.x >> 3;
+    return (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
 }
 
 // ------------------------------------------------------------- kernels
+
+// LDS of one wave's leaf segment: the segment's nodes' 4x4-block
+// coordinates and the list of their cells, 2 bytes each: (node << 4) |
+// (4 * row + column) within the node's block.  A node has at most 4 leaves of
+// 4 cells.
+struct WaveCells {
+    uint32_t r4[64];
+    uint32_t c4[64];
+    uint16_t cell[16 * 64];
+};
+
+constexpr int kUnroll = 8;   // cells whose x loads are issued before their atomics
+
+// Output window of a tile: 'win' (LDS, or null) holds outputs [out0, out0 +
+// rows) x B; cells of the tile all land inside it.
+template <class T>
+struct Window {
+    T *win;
+    uint64_t out0;
+    uint32_t rows;
+};
+
+// Leaf work of one wave over a segment of up to 64 nodes of the last internal
+// level; lane l holds node l's code, signature s and first leaf 'off' (s = 0:
+// no node).  Phase A (a lane per node): read the node's leaf signatures and
+// list its cells in the wave's LDS at positions from a wave scan of the cell
+// counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
+// kUnroll cells, then apply the semiring's atomics, to the LDS window when
+// the tile has one, else to y.  No workgroup barrier.
+template <class SR, int DIR>
+__device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
+                                             const uint64_t *__restrict__ leaf_words,
+                                             const typename SR::T *__restrict__ x,
+                                             typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                             Window<typename SR::T> w, WaveCells *wc) {
+    using T = typename SR::T;
+    const uint32_t lane = __lane_id();
+    uint32_t lam[4] = {0u, 0u, 0u, 0u};   // leaf signature per quadrant b
+    uint32_t j = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b)
+        if (s & (1u << b)) lam[b] = nib(leaf_words, uint64_t(off) + j++);
+    const uint32_t ncell = __popc(lam[0]) + __popc(lam[1]) + __popc(lam[2]) + __popc(lam[3]);
+    uint32_t total;
+    uint32_t pos = wave_scan<5>(ncell, total);
+    wc->r4[lane] = compact_even(code >> 1);
+    wc->c4[lane] = compact_even(code);
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b) {
+#pragma unroll
+        for (uint32_t q = 0; q < 4; ++q)
+            if (lam[b] & (1u << q)) {
+                const uint32_t r = 2 * (b >> 1) + (q >> 1), c = 2 * (b & 1) + (q & 1);
+                wc->cell[pos++] = uint16_t((lane << 4) | (r << 2) | c);
+            }
+    }
+    wave_lds_sync();
+    const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
+    for (uint32_t k0 = g; k0 < total; k0 += G * kUnroll) {
+        uint32_t in_i[kUnroll], out_i[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t k = k0 + uint32_t(u) * G;
+            const uint32_t e = (k < total) ? uint32_t(wc->cell[k]) : 0u;
+            const uint32_t r = wc->r4[e >> 4] * 4 + ((e >> 2) & 3u);
+            const uint32_t c = wc->c4[e >> 4] * 4 + (e & 3u);
+            in_i[u] = (DIR == K2_RIGHT) ? c : r;
+            out_i[u] = (DIR == K2_RIGHT) ? r : c;
+        }
+        for (uint32_t v = lv; v < B; v += VL) {
+            T xv[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                xv[u] = (k0 + uint32_t(u) * G < total) ? x[uint64_t(in_i[u]) * B + v] : SR::zero();
+            if (w.win) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (k0 + uint32_t(u) * G < total && SR::contributes(xv[u]))
+                        SR::lds_atomic(&w.win[(uint64_t(out_i[u]) - w.out0) * B + v], SR::contrib(xv[u]));
+            } else {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (k0 + uint32_t(u) * G < total && SR::contributes(xv[u]))
+                        SR::atomic(&y[uint64_t(out_i[u]) * B + v], SR::contrib(xv[u]));
+            }
+        }
+    }
+    wave_lds_sync();
+}
+
+// The window of tile 'tl' for this product (no window: win = null), its LDS
+// set to the semiring zero.  'use' is false when the batch is too wide for
+// the planned window size.
+template <class SR, int DIR>
+__device__ __forceinline__ Window<typename SR::T> open_window(const Tile &tl, typename SR::T *lds,
+                                                              bool use, uint32_t B) {
+    Window<typename SR::T> w{nullptr, 0, 0};
+    if (!use || tl.win_log2 == kNoWindow) return w;
+    w.win = lds;
+    w.out0 = (DIR == K2_RIGHT) ? tl.win_row : tl.win_col;
+    w.rows = 1u << tl.win_log2;
+    const uint32_t n = w.rows * B;
+    for (uint32_t e = threadIdx.x; e < n; e += kThreads) lds[e] = SR::zero();
+    __syncthreads();
+    return w;
+}
+
+// Add a tile's window to y: one coalesced pass, skipping semiring zeros.
+template <class SR>
+__device__ __forceinline__ void close_window(const Window<typename SR::T> &w,
+                                             typename SR::T *__restrict__ y, uint64_t n_out,
+                                             uint32_t B) {
+    using T = typename SR::T;
+    if (!w.win) return;
+    __syncthreads();
+    const uint64_t rows = (w.out0 + w.rows <= n_out) ? w.rows : (n_out - w.out0);
+    const uint32_t n = uint32_t(rows) * B;
+    for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+        const T v = w.win[e];
+        if (SR::contributes_out(v)) SR::atomic(&y[w.out0 * B + e], v);
+    }
+    __syncthreads();
+}
 
 // y[0..n) = value; 16-byte stores when y is 16-byte aligned.
 __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y, uint64_t n,
@@ -231,61 +383,48 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y
     for (uint64_t k = n4 * 4 + i; k < n; k += stride) y[k] = value;
 }
 
-// Node data of one 256-node pass, for the batched leaf work.
-struct PassNodes {
-    uint64_t code[kThreads];
-    uint32_t off[kThreads];
-    uint8_t sig[kThreads];
-};
-
-// Leaf work of a pass of 256 nodes whose (code, s, off) each thread holds.
-template <class SR, int DIR, bool VL1>
-__device__ __forceinline__ void leaf_pass(uint64_t code, uint32_t s, uint32_t off,
-                                          const uint64_t *__restrict__ leaf_words,
-                                          const typename SR::T *__restrict__ x,
-                                          typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                          PassNodes *s_nodes) {
-    if (VL1) {
-        leaf_node<SR, DIR>(code, s, off, leaf_words, x, y, B, 0, 1);
-        return;
-    }
-    s_nodes->code[threadIdx.x] = code;
-    s_nodes->off[threadIdx.x] = off;
-    s_nodes->sig[threadIdx.x] = uint8_t(s);
-    __syncthreads();
-    const uint32_t groups = kThreads / VL;
-    const uint32_t g = threadIdx.x / VL, lv = threadIdx.x % VL;
-    for (uint32_t k = g; k < kThreads; k += groups)
-        leaf_node<SR, DIR>(s_nodes->code[k], s_nodes->sig[k], s_nodes->off[k], leaf_words, x, y, B,
-                           lv, VL);
-    __syncthreads();
-}
-
-// One product over the cached last internal level (Sec. 3.5): pass p covers
-// nodes [256p, 256p + 256) of level l-2, one directory block.
-template <class SR, int DIR, bool VL1>
-__global__ __launch_bounds__(kThreads) void cached_kernel(DevTree t,
-                                                          const uint64_t *__restrict__ codes,
-                                                          const typename SR::T *__restrict__ x,
-                                                          typename SR::T *__restrict__ y,
-                                                          uint32_t B, uint32_t VL) {
-    __shared__ uint32_t s_tot[kWaves];
-    __shared__ PassNodes s_nodes;
+// One product over the cached last internal level (Sec. 3.5): each workgroup
+// takes a tile, a range of that level's nodes; its waves take turns at
+// segments of 64 nodes, each finding the segment's first leaf from the
+// directory and the rest by a wave scan of the fan-outs.  The next segment's
+// codes and signatures are loaded before the current one is processed.
+template <class SR, int DIR>
+__global__ __launch_bounds__(kThreads) void cached_kernel(
+    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ codes,
+    const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+    uint64_t n_out, int use_window, int remap) {
+    using T = typename SR::T;
+    extern __shared__ uint64_t s_dyn[];   // the window
+    __shared__ WaveCells s_cells[kWaves];
     const int d = t.levels - 2;
-    const uint32_t N = t.nodes[d];
-    const uint32_t nblocks = (N + kThreads - 1) / kThreads;
+    const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
     const uint64_t *__restrict__ sig_words = t.words[d];
     const uint64_t *__restrict__ leaf_words = t.words[d + 1];
-    const uint32_t *__restrict__ dir = t.dir[d];
-    for (uint32_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
-        const uint32_t i = blk * kThreads + threadIdx.x;
-        const bool valid = i < N;
-        const uint32_t s = valid ? nib(sig_words, i) : 0u;
-        const uint64_t code = valid ? codes[i] : 0ull;
-        uint32_t total;
-        const uint32_t ex = block_scan_small(__popc(s), s_tot, total);
-        const uint32_t off = dir[blk] + ex;
-        leaf_pass<SR, DIR, VL1>(code, s, off, leaf_words, x, y, B, VL, &s_nodes);
+    WaveCells *wc = &s_cells[wave];
+    for (uint32_t ti = logical_block(remap); ti < n_tiles; ti += gridDim.x) {
+        const Tile tl = tiles[ti];
+        const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
+        uint32_t seg = wave * 64;
+        uint32_t i = tl.first + seg + lane;
+        bool valid = seg + lane < tl.count;
+        uint32_t s = valid ? nib(sig_words, i) : 0u;
+        uint64_t code = valid ? codes[i] : 0ull;
+        while (seg < tl.count) {
+            const uint32_t base = wave_child_offset(t, d, tl.first + seg);
+            // prefetch the wave's next segment
+            const uint32_t nseg = seg + kThreads;
+            const uint32_t ni = tl.first + nseg + lane;
+            const bool nvalid = nseg + lane < tl.count;
+            const uint32_t ns = nvalid ? nib(sig_words, ni) : 0u;
+            const uint64_t ncode = nvalid ? codes[ni] : 0ull;
+            uint32_t total;
+            const uint32_t ex = wave_scan<3>(__popc(s), total);
+            leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, wc);
+            seg = nseg;
+            s = ns;
+            code = ncode;
+        }
+        close_window<SR>(w, y, n_out, B);
     }
 }
 
@@ -293,21 +432,21 @@ __global__ __launch_bounds__(kThreads) void cached_kernel(DevTree t,
 // workgroup takes a tile and expands it level by level inside LDS, then visits
 // the leaves of its last-internal-level nodes in place.  With 'emit' set it
 // writes those nodes' codes instead (building the cached level, Sec. 3.5).
-template <class SR, int DIR, bool VL1, bool EMIT>
-__global__ __launch_bounds__(kThreads) void descent_kernel(DevTree t, const Tile *__restrict__ tiles,
-                                                           uint32_t n_tiles,
-                                                           const uint64_t *__restrict__ tile_codes,
-                                                           uint32_t cap,
-                                                           const typename SR::T *__restrict__ x,
-                                                           typename SR::T *__restrict__ y,
-                                                           uint32_t B, uint32_t VL,
-                                                           uint64_t *__restrict__ emit) {
-    extern __shared__ uint64_t s_front[];   // 2 * cap codes
+template <class SR, int DIR, bool EMIT>
+__global__ __launch_bounds__(kThreads) void descent_kernel(
+    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
+    const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
+    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
+    uint64_t *__restrict__ emit, int remap) {
+    using T = typename SR::T;
+    extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
     __shared__ uint32_t s_val;
-    __shared__ PassNodes s_nodes;
+    __shared__ WaveCells s_cells[kWaves];
     const int last = t.levels - 2;
-    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
+    const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
+    T *s_win = reinterpret_cast<T *>(s_front + 2 * size_t(cap));
+    for (uint32_t ti = logical_block(remap); ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         int d = int(tl.level);
         uint32_t lo = tl.first, cnt = tl.count;
@@ -316,14 +455,14 @@ __global__ __launch_bounds__(kThreads) void descent_kernel(DevTree t, const Tile
         __syncthreads();
         while (d < last) {
             const uint32_t base = block_child_offset(t, d, lo, &s_val);
-            const uint64_t *__restrict__ w = t.words[d];
+            const uint64_t *__restrict__ wd = t.words[d];
             uint32_t running = 0;
             for (uint32_t s0 = 0; s0 < cnt; s0 += kThreads) {
                 const uint32_t i = s0 + threadIdx.x;
                 const bool valid = i < cnt;
-                const uint32_t s = valid ? nib(w, uint64_t(lo) + i) : 0u;
+                const uint32_t s = valid ? nib(wd, uint64_t(lo) + i) : 0u;
                 uint32_t total;
-                const uint32_t ex = block_scan_small(__popc(s), s_tot, total);
+                const uint32_t ex = block_scan<3>(__popc(s), s_tot, total);
                 if (s) {
                     const uint64_t c2 = cur[i] << 2;
                     uint32_t p = running + ex;
@@ -344,21 +483,20 @@ __global__ __launch_bounds__(kThreads) void descent_kernel(DevTree t, const Tile
         if (EMIT) {
             for (uint32_t i = threadIdx.x; i < cnt; i += kThreads) emit[uint64_t(lo) + i] = cur[i];
         } else {
-            const uint32_t base = block_child_offset(t, last, lo, &s_val);
-            const uint64_t *__restrict__ w = t.words[last];
+            const Window<T> w = open_window<SR, DIR>(tl, s_win, use_window, B);
+            const uint64_t *__restrict__ wd = t.words[last];
             const uint64_t *__restrict__ leaf_words = t.words[last + 1];
-            uint32_t running = 0;
-            for (uint32_t s0 = 0; s0 < cnt; s0 += kThreads) {
-                const uint32_t i = s0 + threadIdx.x;
+            for (uint32_t seg = wave * 64; seg < cnt; seg += kThreads) {
+                const uint32_t i = seg + lane;
                 const bool valid = i < cnt;
-                const uint32_t s = valid ? nib(w, uint64_t(lo) + i) : 0u;
+                const uint32_t s = valid ? nib(wd, uint64_t(lo) + i) : 0u;
                 const uint64_t code = valid ? cur[i] : 0ull;
+                const uint32_t base = wave_child_offset(t, last, lo + seg);
                 uint32_t total;
-                const uint32_t ex = block_scan_small(__popc(s), s_tot, total);
-                leaf_pass<SR, DIR, VL1>(code, s, base + running + ex, leaf_words, x, y, B, VL,
-                                        &s_nodes);
-                running += total;
+                const uint32_t ex = wave_scan<3>(__popc(s), total);
+                leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, &s_cells[wave]);
             }
+            close_window<SR>(w, y, n_out, B);
         }
         __syncthreads();
     }
@@ -374,24 +512,42 @@ uint32_t lanes_per_node(uint32_t B) {
     return v;
 }
 
-uint32_t grid_for(uint64_t blocks) {
+uint32_t grid_for(uint64_t blocks, bool remap) {
     const uint64_t cap = 1u << 20;
-    return uint32_t(blocks < cap ? (blocks ? blocks : 1) : cap);
+    uint64_t g = blocks < cap ? (blocks ? blocks : 1) : cap;
+    if (remap) g = (g + 7) & ~uint64_t(7);   // whole rounds of the 8 XCDs
+    return uint32_t(g);
+}
+
+// Whether products with batch B use the planned windows, and their LDS bytes.
+size_t window_bytes(const Matrix &m, uint32_t B, int *use) {
+    *use = (m.window_elems > 0 && B <= m.window_batch) ? 1 : 0;
+    if (!*use) return 0;
+    return (size_t(1) << m.plan.window_log2) * B * 4;
+}
+
+int set_lds_limit(const void *k, size_t lds) {
+    if (lds <= 48 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
 }
 
 template <class SR, int DIR>
 int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t st) {
     using T = typename SR::T;
-    const uint32_t N = m.dev.nodes[m.levels - 2];
-    if (N == 0) return hipSuccess;
+    const uint32_t n_tiles = uint32_t(m.plan.cached_tiles.size());
+    if (n_tiles == 0) return hipSuccess;
     const uint32_t VL = lanes_per_node(B);
-    const uint32_t grid = grid_for((N + kThreads - 1) / kThreads);
-    if (VL == 1)
-        hipLaunchKernelGGL((cached_kernel<SR, DIR, true>), dim3(grid), dim3(kThreads), 0, st, m.dev,
-                           m.d_cached, static_cast<const T *>(x), static_cast<T *>(y), B, VL);
-    else
-        hipLaunchKernelGGL((cached_kernel<SR, DIR, false>), dim3(grid), dim3(kThreads), 0, st,
-                           m.dev, m.d_cached, static_cast<const T *>(x), static_cast<T *>(y), B, VL);
+    const int remap = m.xcd_remap ? 1 : 0;
+    const uint32_t grid = grid_for(n_tiles, remap);
+    int use = 0;
+    const size_t lds = window_bytes(m, B, &use);
+    const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
+    auto k = cached_kernel<SR, DIR>;
+    int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles, n_tiles,
+                       m.d_cached, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use,
+                       remap);
     return hipGetLastError();
 }
 
@@ -402,19 +558,19 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     const uint32_t n_tiles = uint32_t(m.plan.tiles.size());
     if (n_tiles == 0) return hipSuccess;
     const uint32_t cap = m.plan.tile_nodes;
-    const size_t lds = size_t(2) * cap * sizeof(uint64_t);
+    int use = 0;
+    const size_t win = EMIT ? 0 : window_bytes(m, B, &use);
+    const size_t lds = size_t(2) * cap * sizeof(uint64_t) + win;
     const uint32_t VL = lanes_per_node(B);
-    const uint32_t grid = grid_for(n_tiles);
-    auto kv1 = descent_kernel<SR, DIR, true, EMIT>;
-    auto kvn = descent_kernel<SR, DIR, false, EMIT>;
-    auto k = (VL == 1) ? kv1 : kvn;
-    if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(k),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-    }
+    const int remap = m.xcd_remap ? 1 : 0;
+    const uint32_t grid = grid_for(n_tiles, remap);
+    const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
+    auto k = descent_kernel<SR, DIR, EMIT>;
+    int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_tiles, n_tiles, m.d_codes,
-                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, emit);
+                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit,
+                       remap);
     return hipGetLastError();
 }
 

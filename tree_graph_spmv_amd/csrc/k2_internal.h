@@ -32,23 +32,32 @@ inline unsigned nibble(const std::vector<uint64_t> &w, uint64_t i) {
 // directory plus the popcounts of the words before i in its block.
 uint64_t child_offset(const HostTree &t, int d, uint64_t i);
 
-// One tile of the descent: 'count' consecutive nodes of level 'level'
-// starting at node 'first', whose codes are codes[code_off .. code_off+count).
+// One tile: 'count' consecutive nodes of level 'level' starting at node
+// 'first'; for descent tiles their codes are codes[code_off ..].  A tile with
+// a window (win_log2 != kNoWindow) lies inside the 2^win_log2 x 2^win_log2
+// quadrant at (win_row, win_col) and accumulates its outputs in LDS.
+constexpr uint32_t kNoWindow = 0xFFFFFFFFu;
 struct Tile {
     uint32_t first;
     uint32_t count;
     uint32_t level;
     uint32_t code_off;
+    uint32_t win_row;
+    uint32_t win_col;
+    uint32_t win_log2;
+    uint32_t pad;
 };
-static_assert(sizeof(Tile) == 16, "tile layout");
+static_assert(sizeof(Tile) == 32, "tile layout");
 
-// The plan of a matrix: host top level, tiles in depth-first order and the
-// codes their first level starts from.
+// The plan of a matrix: host top level, descent tiles in depth-first order and
+// the codes their first level starts from, and the tiles of the cached level.
 struct Plan {
     int top_level = 0;                 // d0
     uint32_t tile_nodes = 0;
+    int window_log2 = -1;              // quadrant side of the windows, -1: none
     std::vector<uint64_t> codes;       // tile start codes
-    std::vector<Tile> tiles;
+    std::vector<Tile> tiles;           // descent tiles
+    std::vector<Tile> cached_tiles;    // ranges of the last internal level
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -58,12 +67,12 @@ int top_level_for(const HostTree &t, uint32_t host_top_max);
 struct Layout {
     uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
-    uint64_t codes_off = 0, tiles_off = 0, cached_off = 0;
+    uint64_t codes_off = 0, tiles_off = 0, cached_tiles_off = 0, cached_off = 0;
     k2_mem_breakdown mem = {};
 };
 
-void layout_for(const HostTree &t, int top_level, uint64_t n_codes, uint64_t n_tiles, bool cached,
-                Layout *out);
+void layout_for(const HostTree &t, int top_level, uint64_t n_codes, uint64_t n_tiles,
+                uint64_t n_cached_tiles, bool cached, Layout *out);
 
 // ------------------------------------------------------------ device view
 
@@ -87,8 +96,14 @@ struct Matrix {
     char *arena = nullptr;
     const uint64_t *d_codes = nullptr;   // tile start codes
     const Tile *d_tiles = nullptr;
+    const Tile *d_cached_tiles = nullptr;
     uint64_t *d_cached = nullptr;        // last internal level codes or null
+    uint32_t window_elems = 0, window_batch = 0;
     bool cached = false;
+    bool xcd_remap = true;
+    // kernel timing (events created on first enable)
+    void *ev[3] = {nullptr, nullptr, nullptr};
+    bool timing = false, timed_once = false, last_accumulate = false;
 };
 
 // Kernel launchers (k2_device.hip).  Return hipError_t as int.
