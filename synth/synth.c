@@ -28,11 +28,17 @@ static inline double unit(uint64_t v) { return (double)(v >> 11) * (1.0 / 900719
 
 /* ------------------------------------------------------------------ R-MAT */
 
-static void rmat_edge(uint64_t seed, uint64_t k, int scale, double a, double ab, double abc,
+static inline uint64_t stream_key(uint64_t seed, uint64_t s) {
+    return mix64(seed ^ (s * 0xD1B54A32D192ED03ull));
+}
+/* draw k of a stream whose key is sk (same values as draw(seed, s, k)) */
+static inline uint64_t draw_k(uint64_t sk, uint64_t k) { return mix64(sk + k * 0x9E3779B97F4A7C15ull); }
+
+static void rmat_edge(uint64_t sk, uint64_t k, int scale, double a, double ab, double abc,
                       uint32_t *r, uint32_t *c) {
     uint32_t rr = 0, cc = 0;
     for (int lv = 0; lv < scale; lv++) {
-        double u = unit(draw(seed, 1, k * (uint64_t)scale + (uint64_t)lv));
+        double u = unit(draw_k(sk, k * (uint64_t)scale + (uint64_t)lv));
         uint32_t b1, b0;
         if (u < a) { b1 = 0; b0 = 0; }
         else if (u < ab) { b1 = 0; b0 = 1; }
@@ -44,40 +50,50 @@ static void rmat_edge(uint64_t seed, uint64_t k, int scale, double a, double ab,
     *r = rr; *c = cc;
 }
 
-/* Open-addressing set of 64-bit keys (key+1 stored, 0 = empty). */
-typedef struct { uint64_t *slot; uint64_t mask; uint64_t used; } kset;
-
-static int kset_init(kset *s, uint64_t want) {
-    uint64_t cap = 1024;
-    while (cap < 2 * want + 16) cap <<= 1;
-    s->slot = (uint64_t *)calloc(cap, sizeof(uint64_t));
-    s->mask = cap - 1; s->used = 0;
-    return s->slot ? 0 : -1;
-}
-static int kset_grow(kset *s) {
-    uint64_t cap = (s->mask + 1) * 2;
-    uint64_t *ns = (uint64_t *)calloc(cap, sizeof(uint64_t));
-    if (!ns) return -1;
-    for (uint64_t i = 0; i <= s->mask; i++) {
-        uint64_t v = s->slot[i];
-        if (!v) continue;
-        uint64_t h = mix64(v) & (cap - 1);
-        while (ns[h]) h = (h + 1) & (cap - 1);
-        ns[h] = v;
+/* Stable LSD radix sort of (key, idx) pairs on the low 'bits' bits of key. */
+static int sort_pairs(uint64_t *key, uint32_t *idx, uint64_t n, int bits, int threads) {
+    uint64_t *k2 = (uint64_t *)malloc((n ? n : 1) * sizeof(uint64_t));
+    uint32_t *i2 = (uint32_t *)malloc((n ? n : 1) * sizeof(uint32_t));
+    uint64_t *hist = (uint64_t *)calloc((size_t)threads * 256, sizeof(uint64_t));
+    if (!k2 || !i2 || !hist) { free(k2); free(i2); free(hist); return -1; }
+    uint64_t *ka = key, *kb = k2;
+    uint32_t *ia = idx, *ib = i2;
+    for (int sh = 0; sh < bits; sh += 8) {
+        memset(hist, 0, (size_t)threads * 256 * sizeof(uint64_t));
+        #pragma omp parallel num_threads(threads)
+        {
+            int t = omp_get_thread_num();
+            uint64_t lo = n * (uint64_t)t / (uint64_t)threads, hi = n * (uint64_t)(t + 1) / (uint64_t)threads;
+            uint64_t *h = hist + (size_t)t * 256;
+            for (uint64_t i = lo; i < hi; i++) h[(ka[i] >> sh) & 255]++;
+            #pragma omp barrier
+            #pragma omp single
+            {
+                uint64_t run = 0;
+                for (int d = 0; d < 256; d++)
+                    for (int q = 0; q < threads; q++) {
+                        uint64_t c = hist[(size_t)q * 256 + d];
+                        hist[(size_t)q * 256 + d] = run;
+                        run += c;
+                    }
+            }
+            for (uint64_t i = lo; i < hi; i++) {
+                uint64_t o = h[(ka[i] >> sh) & 255]++;
+                kb[o] = ka[i];
+                ib[o] = ia[i];
+            }
+        }
+        uint64_t *tk = ka; ka = kb; kb = tk;
+        uint32_t *ti = ia; ia = ib; ib = ti;
     }
-    free(s->slot); s->slot = ns; s->mask = cap - 1;
+    if (ka != key) {
+        memcpy(key, ka, n * sizeof(uint64_t));
+        memcpy(idx, ia, n * sizeof(uint32_t));
+    }
+    free(hist);
+    free(k2);
+    free(i2);
     return 0;
-}
-/* returns 1 if inserted (new), 0 if present */
-static int kset_insert(kset *s, uint64_t key) {
-    if (2 * (s->used + 1) > s->mask + 1) kset_grow(s);
-    uint64_t v = key + 1, h = mix64(v) & s->mask;
-    while (s->slot[h]) {
-        if (s->slot[h] == v) return 0;
-        h = (h + 1) & s->mask;
-    }
-    s->slot[h] = v; s->used++;
-    return 1;
 }
 
 /*
@@ -85,6 +101,9 @@ static int kset_insert(kset *s, uint64_t key) {
  * kept in generation order (first occurrence).  symmetric != 0: each drawn
  * pair (u, v), u != v, stands for the undirected edge and yields (u,v) and
  * (v,u); self-loops are skipped; n_edges must then be even.
+ * Candidates are drawn in one batch (25% spare); duplicates are found by a
+ * stable sort of the candidates' keys, which keeps each key's first draw; a
+ * batch that falls short is redrawn twice as long (same prefix of draws).
  * Returns 0, or -1 on bad arguments / out of memory.
  */
 int synth_rmat(int scale, uint64_t n_edges, double a, double b, double c, uint64_t seed,
@@ -96,68 +115,78 @@ int synth_rmat(int scale, uint64_t n_edges, double a, double b, double c, uint64
                                 : ldexp(1.0, 2 * scale);
     if ((double)target > 0.5 * maxpairs) return -1;
     if (threads < 1) threads = 1;
-    if (threads > 255) threads = 255;
-    int P = threads;
-    kset *sets = (kset *)calloc((size_t)P, sizeof(kset));
-    for (int p = 0; p < P; p++)
-        if (kset_init(&sets[p], target / (uint64_t)P + 1)) return -1;
-
-    uint64_t found = 0, next_k = 0;
-    uint64_t block = target + target / 4 + 1024;
-    uint64_t *cand = NULL;
-    uint8_t *fresh = NULL, *owner = NULL;
-    while (found < target) {
-        uint64_t nb = block;
-        cand = (uint64_t *)realloc(cand, nb * sizeof(uint64_t));
-        fresh = (uint8_t *)realloc(fresh, nb);
-        owner = (uint8_t *)realloc(owner, nb);
-        if (!cand || !fresh || !owner) return -1;
+    const uint64_t sk = stream_key(seed, 1);
+    const uint64_t invalid = 1ull << (2 * scale);
+    uint64_t nb = target + target / 4 + 1024;
+    for (;;) {
+        if (nb >= (1ull << 32)) return -1;
+        uint64_t *key = (uint64_t *)malloc(nb * sizeof(uint64_t));
+        uint32_t *idx = (uint32_t *)malloc(nb * sizeof(uint32_t));
+        uint8_t *fresh = (uint8_t *)calloc(nb, 1);
+        uint8_t *orient = (uint8_t *)malloc(nb);
+        if (!key || !idx || !fresh || !orient) { free(key); free(idx); free(fresh); free(orient); return -1; }
         #pragma omp parallel for num_threads(threads) schedule(static)
         for (int64_t i = 0; i < (int64_t)nb; i++) {
             uint32_t r, cc;
-            rmat_edge(seed, next_k + (uint64_t)i, scale, a, a + b, a + b + c, &r, &cc);
+            rmat_edge(sk, (uint64_t)i, scale, a, a + b, a + b + c, &r, &cc);
+            idx[i] = (uint32_t)i;
             if (symmetric) {
-                if (r == cc) { cand[i] = UINT64_MAX; continue; }
                 uint32_t lo = r < cc ? r : cc, hi = r < cc ? cc : r;
-                /* keep the drawn orientation in the low bit of a wider key */
-                cand[i] = ((uint64_t)lo << 32 | hi) ;
-                fresh[i] = (uint8_t)(r < cc);      /* 1: drawn as (lo,hi) */
+                key[i] = (r == cc) ? invalid : (((uint64_t)lo << scale) | hi);
+                orient[i] = (uint8_t)(r < cc);     /* 1: drawn as (lo, hi) */
             } else {
-                cand[i] = (uint64_t)r << 32 | cc;
+                key[i] = ((uint64_t)r << scale) | cc;
             }
-            owner[i] = (uint8_t)(mix64(cand[i] ^ 0x5bd1e995ull) % (uint64_t)P);
         }
-        /* each thread owns the keys that hash to it; marks first sightings */
-        #pragma omp parallel num_threads(P)
+        uint64_t *keys_by_idx = (uint64_t *)malloc(nb * sizeof(uint64_t));
+        if (!keys_by_idx) { free(key); free(idx); free(fresh); free(orient); return -1; }
+        memcpy(keys_by_idx, key, nb * sizeof(uint64_t));
+        if (sort_pairs(key, idx, nb, 2 * scale + 1, threads)) {
+            free(key); free(idx); free(fresh); free(orient); free(keys_by_idx); return -1;
+        }
+        /* the first of each run of equal keys is the earliest draw */
+        #pragma omp parallel for num_threads(threads) schedule(static)
+        for (int64_t i = 0; i < (int64_t)nb; i++)
+            if (key[i] != invalid && (i == 0 || key[i] != key[i - 1])) fresh[idx[i]] = 1;
+        free(key); free(idx);
+        /* keep the first 'target' fresh draws, in draw order */
+        uint64_t *cnt = (uint64_t *)calloc((size_t)threads + 1, sizeof(uint64_t));
+        #pragma omp parallel num_threads(threads)
         {
-            int p = omp_get_thread_num();
-            for (uint64_t i = 0; i < nb; i++) {
-                uint64_t key = cand[i];
-                if (key == UINT64_MAX || owner[i] != p) continue;
-                int isnew = kset_insert(&sets[p], key);
-                if (symmetric) fresh[i] = (uint8_t)(isnew ? (2 | fresh[i]) : 0);
-                else fresh[i] = (uint8_t)isnew;
+            int t = omp_get_thread_num();
+            uint64_t lo = nb * (uint64_t)t / (uint64_t)threads, hi = nb * (uint64_t)(t + 1) / (uint64_t)threads;
+            uint64_t k = 0;
+            for (uint64_t i = lo; i < hi; i++) k += fresh[i];
+            cnt[t + 1] = k;
+        }
+        for (int t = 0; t < threads; t++) cnt[t + 1] += cnt[t];
+        if (cnt[threads] < target) {
+            free(cnt); free(fresh); free(orient); free(keys_by_idx);
+            nb *= 2;
+            continue;
+        }
+        #pragma omp parallel num_threads(threads)
+        {
+            int t = omp_get_thread_num();
+            uint64_t lo = nb * (uint64_t)t / (uint64_t)threads, hi = nb * (uint64_t)(t + 1) / (uint64_t)threads;
+            uint64_t o = cnt[t];
+            for (uint64_t i = lo; i < hi && o < target; i++) {
+                if (!fresh[i]) continue;
+                uint64_t kk = keys_by_idx[i];
+                uint32_t k_hi = (uint32_t)(kk >> scale), k_lo = (uint32_t)(kk & ((1ull << scale) - 1));
+                if (symmetric) {
+                    uint32_t u = orient[i] ? k_hi : k_lo, v = orient[i] ? k_lo : k_hi;
+                    rows[2 * o] = u; cols[2 * o] = v;
+                    rows[2 * o + 1] = v; cols[2 * o + 1] = u;
+                } else {
+                    rows[o] = k_hi; cols[o] = k_lo;
+                }
+                o++;
             }
         }
-        for (uint64_t i = 0; i < nb && found < target; i++) {
-            uint64_t key = cand[i];
-            if (key == UINT64_MAX || !fresh[i]) continue;
-            uint32_t hi32 = (uint32_t)(key >> 32), lo32 = (uint32_t)key;
-            if (symmetric) {
-                uint32_t u = (fresh[i] & 1) ? hi32 : lo32, v = (fresh[i] & 1) ? lo32 : hi32;
-                rows[2 * found] = u; cols[2 * found] = v;
-                rows[2 * found + 1] = v; cols[2 * found + 1] = u;
-            } else {
-                rows[found] = hi32; cols[found] = lo32;
-            }
-            found++;
-        }
-        next_k += nb;
-        block = (target - found) * 2 + 1024;
+        free(cnt); free(fresh); free(orient); free(keys_by_idx);
+        return 0;
     }
-    for (int p = 0; p < P; p++) free(sets[p].slot);
-    free(sets); free(cand); free(fresh); free(owner);
-    return 0;
 }
 
 /* --------------------------------------------------------------- web-like */

@@ -1,0 +1,127 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark uses.
+
+The oracle computes sampled outputs one by one from the edge-list definition
+(oracle.spmv_sample); properties that hold at any size complete the check:
+left = right on a symmetric matrix, the all-ones product = out-degrees,
+tree-only = cached.  Also: the library allocates no device memory in
+k2_matrix_create and k2_spmv.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import ORC_DIR, ORC_SEMIRING, check_parity, from_device, to_device
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import tree_graph_spmv_amd  # noqa: F401
+    return torch.device("cuda:0")
+
+
+def sample_idx(n, k, seed):
+    rng = np.random.default_rng(seed)
+    s = rng.choice(n, size=min(k, n), replace=False)
+    # always include the first and last outputs and the R-MAT hubs near 0
+    return np.unique(np.concatenate([s, [0, 1, 2, n - 1]])).astype(np.uint32)
+
+
+def check_sampled(rows, cols, n, x, y, semiring, direction, batch, label, k=4000, seed=0):
+    idx = sample_idx(n, k, seed)
+    want = oracle.spmv_sample(rows, cols, n, n, x, ORC_SEMIRING[semiring], idx, ORC_DIR[direction],
+                              batch)
+    got = from_device(y, semiring).reshape(n, batch)[idx]
+    check_parity(got, want, semiring, label)
+
+
+def test_library_allocates_nothing(dev):
+    import tree_graph_spmv_amd as k2
+    rows, cols = synth.rmat(16, 300000, seed=2)
+    n = 2 ** 16
+    tree = k2.Tree(rows, cols, n, n)
+    for cached in (0, 1):
+        opts = k2.plan_defaults(cache_last_level=cached)
+        arena = k2.Matrix.arena_for(tree, opts, dev)
+        x = torch.rand(n * 8, device=dev)
+        y = torch.empty(n * 8, device=dev)
+        # load the code object first
+        k2.Matrix(k2.Tree([0], [0], 4, 4), device=dev).spmv(torch.zeros(4, device=dev))
+        torch.cuda.synchronize()
+        free0, _ = torch.cuda.mem_get_info()
+        m = k2.Matrix(tree, opts, device=dev, arena=arena)
+        for d in ("right", "left"):
+            m.spmv(x, y, direction=d, batch=8)
+        torch.cuda.synchronize()
+        free1, _ = torch.cuda.mem_get_info()
+        assert free0 - free1 == 0, f"library took {free0 - free1} bytes"
+        est = tree.estimate(opts, batch=8)
+        assert arena.numel() + x.numel() * 4 + y.numel() * 4 == est["total"]
+
+
+def test_rmat_s22_e64m_tropical(dev):
+    """R-MAT 2^22, 2^26 edges, min-plus with 10% finite x: right and left,
+    both traversals, bit-exact on sampled outputs."""
+    import tree_graph_spmv_amd as k2
+    rows, cols, n = synth.workload_edges("rmat_s22_e64m")
+    tree = k2.Tree(rows, cols, n, n)
+    assert tree.nnz == len(rows)
+    x = synth.workload_x("rmat_s22_e64m", n)
+    m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    xd = to_device(x, dev)
+    for direction in ("right", "left"):
+        ys = {}
+        for mode in ("tree", "cached"):
+            ys[mode] = m.spmv(xd, direction=direction, semiring="tropical", mode=mode)
+        torch.cuda.synchronize()
+        assert torch.equal(ys["tree"].view(torch.int32), ys["cached"].view(torch.int32))
+        check_sampled(rows, cols, n, x, ys["cached"], "tropical", direction, 1,
+                      f"rmat_s22 tropical {direction}", seed=1)
+
+
+def test_symrmat_s24_e256m_boolean(dev):
+    """Symmetric R-MAT 2^24, 2^28 directed edges, 32 Boolean vectors per word:
+    right product bit-exact on sampled outputs; left = right (symmetry)."""
+    import tree_graph_spmv_amd as k2
+    rows, cols, n = synth.workload_edges("symrmat_s24_e256m")
+    tree = k2.Tree(rows, cols, n, n)
+    assert tree.nnz == len(rows) == 2 ** 28
+    x = synth.workload_x("symrmat_s24_e256m", n)
+    m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    xd = to_device(x, dev)
+    yr = m.spmv(xd, direction="right", semiring="boolean_u32")
+    yl = m.spmv(xd, direction="left", semiring="boolean_u32")
+    yt = m.spmv(xd, direction="right", semiring="boolean_u32", mode="tree")
+    torch.cuda.synchronize()
+    assert torch.equal(yr, yl) and torch.equal(yr, yt)
+    check_sampled(rows, cols, n, x, yr, "boolean_u32", "right", 1, "symrmat_s24 right", seed=2)
+
+
+def test_web_n27_d9_batch8(dev):
+    """Web-like 2^27, ~1.2G edges, plus-times over 8 vectors, last internal
+    level cached (the benchmark's configuration): sampled outputs within the
+    fp32 tolerance, right and left; the all-ones product gives out-degrees."""
+    import tree_graph_spmv_amd as k2
+    rows, cols, n = synth.workload_edges("web_n27_d9")
+    tree = k2.Tree(rows, cols, n, n)
+    x = synth.workload_x("web_n27_d9", n)
+    m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    xd = to_device(x, dev)
+    for direction in ("right", "left"):
+        y = m.spmv(xd, direction=direction, batch=8)
+        torch.cuda.synchronize()
+        check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction}",
+                      k=3000, seed=3)
+        del y
+    ones = torch.ones(n, device=dev)
+    deg = m.spmv(ones, direction="right").cpu().numpy()
+    idx = sample_idx(n, 3000, 4)
+    want = oracle.spmv_sample(rows, cols, n, n, np.ones(n, np.float32), oracle.PLUS_TIMES, idx)
+    assert np.array_equal(deg[idx].astype(np.float64), want)
+    assert deg.astype(np.float64).sum() == tree.nnz

@@ -213,17 +213,27 @@ def _stream_handle(stream):
 class Matrix:
     """A tree resident in a device arena allocated through torch."""
 
-    def __init__(self, tree, opts=None, device="cuda", stream=None):
+    @staticmethod
+    def arena_for(tree, opts=None, device="cuda"):
+        """A torch uint8 device tensor of exactly the estimated arena size."""
         import torch
+        est = tree.estimate(opts or plan_defaults())
+        return torch.empty(max(est["arena"], 256), dtype=torch.uint8, device=device)
+
+    def __init__(self, tree, opts=None, device="cuda", stream=None, arena=None):
+        """Upload 'tree'.  'arena' (optional) is a caller-allocated uint8
+        device tensor of at least the estimated arena size, 256-byte aligned;
+        by default one is allocated here."""
         self.opts = opts or plan_defaults()
         est = tree.estimate(self.opts)
         self.arena_bytes = est["arena"]
-        # 256-byte aligned view of a torch allocation
-        raw = torch.empty(self.arena_bytes + 256, dtype=torch.uint8, device=device)
-        shift = (-raw.data_ptr()) % 256
-        self._raw = raw
-        self.arena_ptr = raw.data_ptr() + shift
-        self.device = raw.device
+        if arena is None:
+            arena = Matrix.arena_for(tree, self.opts, device)
+        if arena.numel() < self.arena_bytes or arena.data_ptr() % 256:
+            raise ValueError("arena too small or not 256-byte aligned")
+        self._raw = arena
+        self.arena_ptr = arena.data_ptr()
+        self.device = arena.device
         self.n_rows, self.n_cols, self.levels = tree.n_rows, tree.n_cols, tree.levels
         h = _VP()
         _check(lib().k2_matrix_create(tree.handle, ctypes.byref(self.opts), _VP(self.arena_ptr),
