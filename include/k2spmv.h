@@ -92,11 +92,13 @@ typedef struct {
        lines a Z-order region touches stay in one L2.  Default 0 (measured
        slower on the web-like 2^27 workload). */
     int32_t xcd_remap;
-    /* Output windows: a tile inside a dense Q x Q quadrant accumulates its
-       outputs in LDS and adds them to y once, where Q is the largest power
-       of 2 with Q * window_batch <= window_elems (at most 16384 elements of
-       4 bytes; 0 disables).  Products with more than window_batch vectors
-       use direct atomics everywhere.  Defaults 0 (off) and 8. */
+    /* Output windows for products over the cached level: Q is the largest
+       power of 2 with Q * window_batch <= window_elems (at most 16384
+       elements of 4 bytes; 0 disables).  A tile made of the dense Q x Q
+       quadrants of one row band (right products) or column band (left
+       products) accumulates its outputs in LDS and adds them to y once.
+       Products with more than window_batch vectors use direct atomics
+       everywhere.  Defaults 4096 and 8. */
     uint32_t window_elems;
     uint32_t window_batch;
 } k2_plan_opts;
@@ -171,20 +173,24 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
                                    k2_mem_breakdown *out);
 
 /* The tile plans a matrix created with 'opts' would use (host only, no HIP
-   call; Sec. 3.4): the host-top level d0, the number of descent tiles, of
-   cached-level tiles and of tile start codes.  Errors: K2_E_INVALID_ARG. */
-k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *top_level,
-                       uint64_t *n_tiles, uint64_t *n_cached_tiles, uint64_t *n_codes);
+   call; Sec. 3.4).  which = 0: the descent tiles and their start codes;
+   1 / 2: the cached-level tiles of right / left products and their node
+   ranges (empty unless opts->cache_last_level).  Reports the host-top level d0, the number of tiles and of codes
+   (which = 0) or ranges (1, 2).  Errors: K2_E_INVALID_ARG. */
+k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
+                       uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux);
 
-/* The tiles themselves, in depth-first order; which = 0: descent tiles (and
-   their start codes), 1: cached-level tiles ('codes' unused).
-   tiles[8k..8k+7] = (first node, node count, level, index of the first
-   node's code in 'codes', window row, window column, log2 of the window side
-   or 0xFFFFFFFF for no window, 0).  'codes' are Morton codes (row bit above
-   column bit per level, 2*level bits).  Host arrays of 8*n_tiles and n_codes
-   entries (from k2_plan_info).  Errors: K2_E_INVALID_ARG. */
+/* The tiles themselves, in the order the kernels take them.
+   tiles[8k..8k+7] = (first, count, level, code index, window row, window
+   column, log2 of the window side or 0xFFFFFFFF for no window, 0).
+   which = 0: 'count' nodes of 'level' from node 'first', whose Morton codes
+   (row bit above column bit per level, 2*level bits) are aux[code index ..].
+   which = 1 / 2: 'count' ranges of the last internal level from range
+   'first'; aux[r] = (first node << 32) | node count of range r.
+   Host arrays of 8*n_tiles and n_aux entries (sizes from k2_plan_info).
+   Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
-                        uint32_t *tiles, uint64_t n_tiles, uint64_t *codes, uint64_t n_codes);
+                        uint32_t *tiles, uint64_t n_tiles, uint64_t *aux, uint64_t n_aux);
 
 /* Upload a tree into the caller's device arena (d_arena, arena_bytes >=
    estimate's arena; 256-byte aligned) on 'stream' and return a matrix handle.

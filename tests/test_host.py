@@ -73,7 +73,8 @@ def oracle_codes(o, upto):
     return codes
 
 
-def check_plan(o, cells_r, cells_c, top, tiles, codes, ctiles, opts, all_codes):
+def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
+    """cached: {1: (tiles, ranges) of right products, 2: of left products}."""
     L = o.levels
     last = L - 2
     nodes = o.level_nodes()
@@ -95,14 +96,10 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, ctiles, opts, all_codes):
         lb = int(offs[last][b]) if b < nodes[last] else nodes[L - 1]
         return cells_r[cell_start[la]:cell_start[lb]], cells_c[cell_start[la]:cell_start[lb]]
 
-    def check_window(tl, a, b):
-        if tl[6] == 0xFFFFFFFF:
-            return
+    def side_of(tl):
         side = 1 << int(tl[6])
-        rr, cc = cells_of(a, b)
-        assert np.all((rr >= tl[4]) & (rr < tl[4] + side)), "cell row outside window"
-        assert np.all((cc >= tl[5]) & (cc < tl[5] + side)), "cell column outside window"
         assert side * opts.window_batch <= max(opts.window_elems, 1)
+        return side
 
     pos = 0
     for tl in tiles:
@@ -114,19 +111,41 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, ctiles, opts, all_codes):
         pos = b
         got = codes[int(tl[3]):int(tl[3]) + count]
         assert np.array_equal(got, all_codes[level][first:first + count])
-        check_window(tl, a, b)
+        if tl[6] != 0xFFFFFFFF:   # a descent window (kernels accept them) is the whole quadrant
+            side = side_of(tl)
+            rr, cc = cells_of(a, b)
+            assert np.all((rr >= tl[4]) & (rr < tl[4] + side)), "cell row outside window"
+            assert np.all((cc >= tl[5]) & (cc < tl[5] + side)), "cell column outside window"
     assert pos == nodes[last]
-    pos = 0
-    for tl in ctiles:
-        first, count = int(tl[0]), int(tl[1])
-        assert first == pos and count >= 1 and int(tl[2]) == last
-        pos = first + count
-        check_window(tl, first, first + count)
-    assert pos == nodes[last]
+    for which, (ctiles, ranges) in cached.items():
+        seen = []
+        for tl in ctiles:
+            first, count = int(tl[0]), int(tl[1])
+            assert count >= 1 and int(tl[2]) == last
+            total = 0
+            for r in ranges[first:first + count]:
+                lo, n = int(r) >> 32, int(r) & 0xFFFFFFFF
+                assert n >= 1
+                seen.append((lo, n))
+                total += n
+                if tl[6] != 0xFFFFFFFF:   # a band window covers the output coordinate
+                    side = side_of(tl)
+                    rr, cc = cells_of(lo, lo + n)
+                    out, base = (rr, tl[4]) if which == 1 else (cc, tl[5])
+                    assert np.all((out >= base) & (out < base + side)), "output outside band"
+            if tl[6] != 0xFFFFFFFF:
+                assert total <= 65536
+        seen.sort()
+        pos = 0
+        for lo, n in seen:
+            assert lo == pos, "cached ranges must cover the level exactly once"
+            pos = lo + n
+        assert pos == nodes[last]
 
 
 @pytest.mark.parametrize("opt", [
     dict(),
+    dict(window_elems=8192),
     dict(tile_nodes=256, window_elems=1024, window_batch=1),
     dict(tile_nodes=4096, window_elems=16384, window_batch=1),
     dict(window_elems=0),
@@ -135,14 +154,16 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, ctiles, opts, all_codes):
 ])
 def test_plan_invariants(case, opt):
     name, r, c, nr, nc, t, o = case
-    opts = k2.plan_defaults(**opt)
-    top, tiles, codes, ctiles = t.plan(opts)
+    opts = k2.plan_defaults(cache_last_level=1, **opt)
+    top, tiles, codes = t.plan(opts, 0)
+    cached = {w: t.plan(opts, w)[1:] for w in (1, 2)}
+    assert all(len(t.plan(k2.plan_defaults(cache_last_level=0, **opt), w)[1]) == 0 for w in (1, 2))
     if o.level_nodes()[o.levels - 2] == 0:
-        assert len(tiles) == 0 and len(ctiles) == 0
+        assert len(tiles) == 0 and all(len(v[0]) == 0 for v in cached.values())
         return
     cr, cc = o.cells()
     all_codes = oracle_codes(o, o.levels - 2)
-    check_plan(o, cr.astype(np.int64), cc.astype(np.int64), top, tiles, codes, ctiles, opts,
+    check_plan(o, cr.astype(np.int64), cc.astype(np.int64), top, tiles, codes, cached, opts,
                all_codes)
 
 
@@ -161,12 +182,13 @@ def test_estimate_parts(case):
     for cached in (0, 1):
         opts = k2.plan_defaults(cache_last_level=cached)
         est = t.estimate(opts, semiring="plus_times", batch=3)
-        top, tiles, codes, ctiles = t.plan(opts)
+        top, tiles, codes = t.plan(opts, 0)
+        extra = sum(32 * len(t.plan(opts, w)[1]) + 8 * len(t.plan(opts, w)[2]) for w in (1, 2))
         L = o.levels
         assert est["tree"] == sum(8 * ((nodes[d] + 15) // 16) for d in range(top, L))
         assert est["directory"] == sum(4 * ((nodes[d] + 255) // 256) for d in range(top, L - 1))
         assert est["top_codes"] == 8 * len(codes)
-        assert est["tiles"] == 32 * len(tiles) + (32 * len(ctiles) if cached else 0)
+        assert est["tiles"] == 32 * len(tiles) + (extra if cached else 0)
         assert est["cached_codes"] == (8 * nodes[L - 2] if cached else 0)
         parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
                                      "scratch", "alignment"))

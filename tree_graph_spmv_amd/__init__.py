@@ -77,7 +77,8 @@ _SIGS = {
     "k2_tree_directory": (ctypes.c_int, [_VP, ctypes.c_uint32, _U32P, ctypes.c_uint64]),
     "k2_estimate_device_bytes": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_int,
                                                 ctypes.c_uint32, ctypes.POINTER(MemBreakdown)]),
-    "k2_plan_info": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _U32P, _U64P, _U64P, _U64P]),
+    "k2_plan_info": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_int32, _U32P, _U64P,
+                                    _U64P]),
     "k2_plan_tiles": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_int32, _U32P,
                                      ctypes.c_uint64, _U64P, ctypes.c_uint64]),
     "k2_matrix_create": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), _VP, ctypes.c_uint64, _VP,
@@ -184,23 +185,22 @@ class Tree:
                "k2_estimate_device_bytes")
         return m.as_dict()
 
-    def plan(self, opts=None):
-        """(top_level, descent tiles (n,8) uint32, codes uint64, cached tiles (m,8))."""
+    def plan(self, opts=None, which=0):
+        """(top_level, tiles (n,8) uint32, aux uint64) of one tile plan:
+        which = 0 descent tiles (aux = start codes); 1 / 2 cached-level
+        tiles of right / left products (aux = (first node << 32) | count)."""
         opts = opts or plan_defaults()
         top = ctypes.c_uint32()
         nt = ctypes.c_uint64()
-        nct = ctypes.c_uint64()
-        nc = ctypes.c_uint64()
-        _check(lib().k2_plan_info(self._h, ctypes.byref(opts), ctypes.byref(top), ctypes.byref(nt),
-                                  ctypes.byref(nct), ctypes.byref(nc)), "k2_plan_info")
+        na = ctypes.c_uint64()
+        _check(lib().k2_plan_info(self._h, ctypes.byref(opts), int(which), ctypes.byref(top),
+                                  ctypes.byref(nt), ctypes.byref(na)), "k2_plan_info")
         tiles = np.zeros((max(nt.value, 1), 8), np.uint32)
-        codes = np.zeros(max(nc.value, 1), np.uint64)
-        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), 0, tiles.ctypes.data_as(_U32P),
-                                   nt.value, codes.ctypes.data_as(_U64P), nc.value), "k2_plan_tiles")
-        ctiles = np.zeros((max(nct.value, 1), 8), np.uint32)
-        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), 1, ctiles.ctypes.data_as(_U32P),
-                                   nct.value, None, 0), "k2_plan_tiles")
-        return int(top.value), tiles[:nt.value], codes[:nc.value], ctiles[:nct.value]
+        aux = np.zeros(max(na.value, 1), np.uint64)
+        _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), int(which),
+                                   tiles.ctypes.data_as(_U32P), nt.value, aux.ctypes.data_as(_U64P),
+                                   na.value), "k2_plan_tiles")
+        return int(top.value), tiles[:nt.value], aux[:na.value]
 
 
 def _stream_handle(stream):

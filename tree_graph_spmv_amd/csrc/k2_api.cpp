@@ -5,12 +5,18 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <mutex>
 #include <thread>
 
 #include "k2_internal.h"
 
 struct k2_tree {
     k2::HostTree t;
+    // the last plan computed, and the options it was made for
+    std::mutex plan_mu;
+    bool have_plan = false;
+    k2_plan_opts plan_opts{};
+    k2::Plan plan;
 };
 
 struct k2_matrix {
@@ -43,12 +49,33 @@ uint64_t vector_bytes(const HostTree &t, uint32_t batch) {
     return (uint64_t(t.n_rows) + uint64_t(t.n_cols)) * uint64_t(batch) * 4ull;
 }
 
-k2_status estimate(const HostTree &t, const k2_plan_opts &o, Plan *plan, Layout *lay) {
-    k2_status st = make_plan(t, o, plan);
+bool same_opts(const k2_plan_opts &a, const k2_plan_opts &b) {
+    return a.tile_nodes == b.tile_nodes && a.host_top_max == b.host_top_max &&
+           a.window_elems == b.window_elems && a.window_batch == b.window_batch &&
+           (a.cache_last_level != 0) == (b.cache_last_level != 0);
+}
+
+// The plan of 'tree' for 'o', computed once per option set.
+k2_status plan_of(const k2_tree *tree, const k2_plan_opts &o, Plan *out) {
+    k2_tree *t = const_cast<k2_tree *>(tree);
+    std::lock_guard<std::mutex> lock(t->plan_mu);
+    if (!t->have_plan || !same_opts(t->plan_opts, o)) {
+        t->have_plan = false;
+        k2_status st = make_plan(t->t, o, &t->plan);
+        if (st != K2_OK) return st;
+        t->plan_opts = o;
+        t->have_plan = true;
+    }
+    *out = t->plan;
+    return K2_OK;
+}
+
+k2_status estimate(const k2_tree *tree, const k2_plan_opts &o, Plan *plan, Layout *lay) {
+    const HostTree &t = tree->t;
+    k2_status st = plan_of(tree, o, plan);
     if (st != K2_OK) return st;
     bool cached = o.cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
-    layout_for(t, plan->top_level, plan->codes.size(), plan->tiles.size(), plan->cached_tiles.size(),
-               cached, lay);
+    layout_for(t, plan->top_level, *plan, cached, lay);
     return K2_OK;
 }
 
@@ -71,7 +98,7 @@ k2_status k2_plan_defaults(k2_plan_opts *opts) {
     opts->host_top_max = 1u << 16;
     opts->cache_last_level = 0;
     opts->xcd_remap = 0;
-    opts->window_elems = 0;
+    opts->window_elems = 4096;
     opts->window_batch = 8;
     return K2_OK;
 }
@@ -148,7 +175,7 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
     Layout lay;
     k2_status st;
     try {
-        st = estimate(tree->t, *opts, &plan, &lay);
+        st = estimate(tree, *opts, &plan, &lay);
     } catch (const std::bad_alloc &) {
         return K2_E_HOST_OOM;
     }
@@ -159,46 +186,50 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
     return K2_OK;
 }
 
-k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *top_level,
-                       uint64_t *n_tiles, uint64_t *n_cached_tiles, uint64_t *n_codes) {
-    if (!tree || !opts || !valid_opts(*opts)) return K2_E_INVALID_ARG;
+k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
+                       uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux) {
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 2) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
-        st = make_plan(tree->t, *opts, &plan);
+        st = plan_of(tree, *opts, &plan);
     } catch (const std::bad_alloc &) {
         return K2_E_HOST_OOM;
     }
     if (st != K2_OK) return st;
     if (top_level) *top_level = uint32_t(plan.top_level);
-    if (n_tiles) *n_tiles = plan.tiles.size();
-    if (n_cached_tiles) *n_cached_tiles = plan.cached_tiles.size();
-    if (n_codes) *n_codes = plan.codes.size();
+    if (n_tiles) *n_tiles = which == 0 ? plan.tiles.size() : plan.cached_tiles[which - 1].size();
+    if (n_aux) *n_aux = which == 0 ? plan.codes.size() : plan.cached_segs[which - 1].size();
     return K2_OK;
 }
 
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which, uint32_t *tiles,
-                        uint64_t n_tiles, uint64_t *codes, uint64_t n_codes) {
-    if (!tree || !opts || !valid_opts(*opts) || (which != 0 && which != 1)) return K2_E_INVALID_ARG;
+                        uint64_t n_tiles, uint64_t *aux, uint64_t n_aux) {
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 2) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
-        st = make_plan(tree->t, *opts, &plan);
+        st = plan_of(tree, *opts, &plan);
     } catch (const std::bad_alloc &) {
         return K2_E_HOST_OOM;
     }
     if (st != K2_OK) return st;
-    const std::vector<Tile> &list = which == 0 ? plan.tiles : plan.cached_tiles;
-    if (n_tiles < list.size() || (which == 0 && n_codes < plan.codes.size())) return K2_E_INVALID_ARG;
-    if ((!tiles && !list.empty()) || (which == 0 && !codes && !plan.codes.empty()))
-        return K2_E_INVALID_ARG;
+    const std::vector<Tile> &list = which == 0 ? plan.tiles : plan.cached_tiles[which - 1];
+    const uint64_t naux = which == 0 ? plan.codes.size() : plan.cached_segs[which - 1].size();
+    if (n_tiles < list.size() || n_aux < naux) return K2_E_INVALID_ARG;
+    if ((!tiles && !list.empty()) || (!aux && naux)) return K2_E_INVALID_ARG;
     for (size_t k = 0; k < list.size(); ++k) {
         const Tile &tl = list[k];
         const uint32_t v[8] = {tl.first, tl.count, tl.level, tl.code_off,
                                tl.win_row, tl.win_col, tl.win_log2, 0u};
         std::copy(v, v + 8, tiles + 8 * k);
     }
-    if (which == 0) std::copy(plan.codes.begin(), plan.codes.end(), codes);
+    if (which == 0) {
+        std::copy(plan.codes.begin(), plan.codes.end(), aux);
+    } else {
+        const std::vector<Seg> &sg = plan.cached_segs[which - 1];
+        for (size_t k = 0; k < sg.size(); ++k) aux[k] = (uint64_t(sg[k].lo) << 32) | sg[k].count;
+    }
     return K2_OK;
 }
 
@@ -213,7 +244,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     Matrix &m = mx->m;
     k2_status st;
     try {
-        st = estimate(t, *opts, &m.plan, &m.layout);
+        st = estimate(tree, *opts, &m.plan, &m.layout);
     } catch (const std::bad_alloc &) {
         st = K2_E_HOST_OOM;
     }
@@ -286,11 +317,18 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
         }
     }
     if (m.cached) {
-        m.d_cached_tiles = reinterpret_cast<const Tile *>(m.arena + m.layout.cached_tiles_off);
-        if (!m.plan.cached_tiles.empty()) {
-            hipError_t e = hipMemcpyAsync(const_cast<Tile *>(m.d_cached_tiles), m.plan.cached_tiles.data(),
-                                          m.plan.cached_tiles.size() * sizeof(Tile),
-                                          hipMemcpyHostToDevice, st_h);
+        for (int dir = 0; dir < 2; ++dir) {
+            m.d_cached_tiles[dir] = reinterpret_cast<const Tile *>(m.arena + m.layout.cached_tiles_off[dir]);
+            m.d_cached_segs[dir] = reinterpret_cast<const Seg *>(m.arena + m.layout.cached_segs_off[dir]);
+            const std::vector<Tile> &tl = m.plan.cached_tiles[dir];
+            const std::vector<Seg> &sg = m.plan.cached_segs[dir];
+            hipError_t e = hipSuccess;
+            if (!tl.empty())
+                e = hipMemcpyAsync(const_cast<Tile *>(m.d_cached_tiles[dir]), tl.data(), tl.size() * sizeof(Tile),
+                                   hipMemcpyHostToDevice, st_h);
+            if (e == hipSuccess && !sg.empty())
+                e = hipMemcpyAsync(const_cast<Seg *>(m.d_cached_segs[dir]), sg.data(), sg.size() * sizeof(Seg),
+                                   hipMemcpyHostToDevice, st_h);
             if (e != hipSuccess) {
                 set_hip_error(int(e), "upload cached tiles");
                 return fail(K2_E_HIP);

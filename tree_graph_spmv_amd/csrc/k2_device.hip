@@ -52,8 +52,17 @@ struct PlusTimes {
     __device__ static void atomic(T *p, T v) {
         __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // LDS fp32 add as an integer compare-and-swap: gfx950's ds_add_f32 takes
+    // about ten times the cycles of its integer LDS atomics.  The first try
+    // assumes the window's initial +0.0, so a first touch costs one atomic.
     __device__ static void lds_atomic(T *p, T v) {
-        __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        uint32_t *u = reinterpret_cast<uint32_t *>(p);
+        uint32_t expected = 0u;
+        while (!__hip_atomic_compare_exchange_strong(u, &expected,
+                                                     __float_as_uint(__uint_as_float(expected) + v),
+                                                     __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_WORKGROUP)) {
+        }
     }
 };
 
@@ -384,15 +393,16 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y
 }
 
 // One product over the cached last internal level (Sec. 3.5): each workgroup
-// takes a tile, a range of that level's nodes; its waves take turns at
-// segments of 64 nodes, each finding the segment's first leaf from the
+// takes a tile, a list of ranges of that level's nodes; its waves take turns
+// at segments of 64 nodes, each finding the segment's first leaf from the
 // directory and the rest by a wave scan of the fan-outs.  The next segment's
 // codes and signatures are loaded before the current one is processed.
 template <class SR, int DIR>
 __global__ __launch_bounds__(kThreads) void cached_kernel(
-    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ codes,
-    const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-    uint64_t n_out, int use_window, int remap) {
+    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
+    const uint64_t *__restrict__ codes, const typename SR::T *__restrict__ x,
+    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
+    int remap) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
     __shared__ WaveCells s_cells[kWaves];
@@ -404,25 +414,28 @@ __global__ __launch_bounds__(kThreads) void cached_kernel(
     for (uint32_t ti = logical_block(remap); ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
-        uint32_t seg = wave * 64;
-        uint32_t i = tl.first + seg + lane;
-        bool valid = seg + lane < tl.count;
-        uint32_t s = valid ? nib(sig_words, i) : 0u;
-        uint64_t code = valid ? codes[i] : 0ull;
-        while (seg < tl.count) {
-            const uint32_t base = wave_child_offset(t, d, tl.first + seg);
-            // prefetch the wave's next segment
-            const uint32_t nseg = seg + kThreads;
-            const uint32_t ni = tl.first + nseg + lane;
-            const bool nvalid = nseg + lane < tl.count;
-            const uint32_t ns = nvalid ? nib(sig_words, ni) : 0u;
-            const uint64_t ncode = nvalid ? codes[ni] : 0ull;
-            uint32_t total;
-            const uint32_t ex = wave_scan<3>(__popc(s), total);
-            leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, wc);
-            seg = nseg;
-            s = ns;
-            code = ncode;
+        for (uint32_t r = 0; r < tl.count; ++r) {
+            const Seg sg = segs[tl.first + r];
+            uint32_t seg = wave * 64;
+            uint32_t i = sg.lo + seg + lane;
+            bool valid = seg + lane < sg.count;
+            uint32_t s = valid ? nib(sig_words, i) : 0u;
+            uint64_t code = valid ? codes[i] : 0ull;
+            while (seg < sg.count) {
+                const uint32_t base = wave_child_offset(t, d, sg.lo + seg);
+                // prefetch the wave's next segment of this range
+                const uint32_t nseg = seg + kThreads;
+                const uint32_t ni = sg.lo + nseg + lane;
+                const bool nvalid = nseg + lane < sg.count;
+                const uint32_t ns = nvalid ? nib(sig_words, ni) : 0u;
+                const uint64_t ncode = nvalid ? codes[ni] : 0ull;
+                uint32_t total;
+                const uint32_t ex = wave_scan<3>(__popc(s), total);
+                leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, wc);
+                seg = nseg;
+                s = ns;
+                code = ncode;
+            }
         }
         close_window<SR>(w, y, n_out, B);
     }
@@ -534,7 +547,7 @@ int set_lds_limit(const void *k, size_t lds) {
 template <class SR, int DIR>
 int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t st) {
     using T = typename SR::T;
-    const uint32_t n_tiles = uint32_t(m.plan.cached_tiles.size());
+    const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
     if (n_tiles == 0) return hipSuccess;
     const uint32_t VL = lanes_per_node(B);
     const int remap = m.xcd_remap ? 1 : 0;
@@ -545,9 +558,9 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     auto k = cached_kernel<SR, DIR>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles, n_tiles,
-                       m.d_cached, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use,
-                       remap);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
+                       m.d_cached_segs[DIR], m.d_cached, static_cast<const T *>(x),
+                       static_cast<T *>(y), B, VL, n_out, use, remap);
     return hipGetLastError();
 }
 

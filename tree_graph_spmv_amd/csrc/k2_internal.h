@@ -49,15 +49,25 @@ struct Tile {
 };
 static_assert(sizeof(Tile) == 32, "tile layout");
 
+// A range of nodes of the last internal level.
+struct Seg {
+    uint32_t lo;
+    uint32_t count;
+};
+static_assert(sizeof(Seg) == 8, "segment layout");
+
 // The plan of a matrix: host top level, descent tiles in depth-first order and
-// the codes their first level starts from, and the tiles of the cached level.
+// the codes their first level starts from, and per product direction the
+// tiles of the cached level (a cached tile is 'count' ranges starting at
+// cached_segs[dir][first]).
 struct Plan {
     int top_level = 0;                 // d0
     uint32_t tile_nodes = 0;
     int window_log2 = -1;              // quadrant side of the windows, -1: none
     std::vector<uint64_t> codes;       // tile start codes
     std::vector<Tile> tiles;           // descent tiles
-    std::vector<Tile> cached_tiles;    // ranges of the last internal level
+    std::vector<Tile> cached_tiles[2];
+    std::vector<Seg> cached_segs[2];
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -67,12 +77,12 @@ int top_level_for(const HostTree &t, uint32_t host_top_max);
 struct Layout {
     uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
-    uint64_t codes_off = 0, tiles_off = 0, cached_tiles_off = 0, cached_off = 0;
+    uint64_t codes_off = 0, tiles_off = 0, cached_off = 0;
+    uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     k2_mem_breakdown mem = {};
 };
 
-void layout_for(const HostTree &t, int top_level, uint64_t n_codes, uint64_t n_tiles,
-                uint64_t n_cached_tiles, bool cached, Layout *out);
+void layout_for(const HostTree &t, int top_level, const Plan &plan, bool cached, Layout *out);
 
 // ------------------------------------------------------------ device view
 
@@ -96,7 +106,8 @@ struct Matrix {
     char *arena = nullptr;
     const uint64_t *d_codes = nullptr;   // tile start codes
     const Tile *d_tiles = nullptr;
-    const Tile *d_cached_tiles = nullptr;
+    const Tile *d_cached_tiles[2] = {nullptr, nullptr};
+    const Seg *d_cached_segs[2] = {nullptr, nullptr};
     uint64_t *d_cached = nullptr;        // last internal level codes or null
     uint32_t window_elems = 0, window_batch = 0;
     bool cached = false;

@@ -17,17 +17,23 @@
 // The tile start codes are the Morton codes of the first nodes, taken from the
 // host-top expansion or from a split parent.
 //
-// Cached tiles cover the last internal level in order, as ranges of at most
-// a few thousand nodes, for the kernel that reads the cached codes (Sec. 3.5).
+// Cached tiles (for the kernel that reads the cached codes of the last
+// internal level, Sec. 3.5) are lists of node ranges of that level, one list
+// per product direction.
 //
 // Windows.  Every node of a Q x Q quadrant (a node of level h = l - log2 Q)
-// has its rows and its columns inside the quadrant's Q.  When such a quadrant
-// holds many nodes, its tiles get a window: the workgroup accumulates its
+// has its rows and its columns inside the quadrant's Q.  A quadrant holding
+// many nodes is dense.  For the cached level the dense quadrants of one row
+// band (right product) or one column band (left product) are gathered into
+// one tile whose window is that band: the workgroup accumulates the band's
 // outputs in LDS (Q outputs x B vectors) and adds them to y once at the end,
-// so the y atomics of a dense region become LDS atomics plus one coalesced
-// pass.  Tiles never straddle a windowed quadrant; the sparse rest keeps one
-// y atomic per cell.
+// so each band's part of y costs one coalesced pass instead of one atomic
+// per cell.  The sparse rest keeps one y atomic per cell.  (The kernels also
+// accept windows on descent tiles; planning one per dense quadrant made many
+// small tiles and measured slower, so descent tiles carry none.)
 #include <algorithm>
+#include <atomic>
+#include <thread>
 
 #include "k2_internal.h"
 
@@ -57,7 +63,8 @@ struct Planner {
     uint64_t C;
     Plan &p;
     int last;           // last internal level
-    uint64_t cached_C;  // nodes per cached tile
+    uint64_t cached_C;  // nodes per cached tile without a window
+    static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
 
     // Descendant index on level 'to' of boundary 'i' of level d.
     uint64_t down(int d, uint64_t i, int to) const {
@@ -76,9 +83,17 @@ struct Planner {
 
     // Descent tiles over nodes [a, b) of level d (codes at
     // p.codes[code_base + i - a]), all with the window fields of 'win'.
-    void range(int d, uint64_t a, uint64_t b, uint64_t code_base, const Tile &win) {
-        std::vector<uint64_t> bound(b - a + 1);
-        for (uint64_t i = a; i <= b; ++i) bound[i - a] = down(d, i, last);
+    // bound[k] (optional) is node a + k's first descendant on the last
+    // internal level, for k = 0..b-a.
+    void range(int d, uint64_t a, uint64_t b, uint64_t code_base, const Tile &win,
+               const std::vector<uint64_t> *known = nullptr) {
+        std::vector<uint64_t> bound;
+        if (known) {
+            bound = *known;
+        } else {
+            bound.resize(b - a + 1);
+            for (uint64_t i = a; i <= b; ++i) bound[i - a] = down(d, i, last);
+        }
         uint64_t i = a;
         while (i < b) {
             if (bound[i + 1 - a] - bound[i - a] > C) {
@@ -98,16 +113,46 @@ struct Planner {
         }
     }
 
-    // Cached tiles over nodes [lo, hi) of the last internal level.
-    void cached(uint64_t lo, uint64_t hi, const Tile &win) {
+    // Cached tiles of direction dir over nodes [lo, hi) of the last internal
+    // level, no window: one range per tile.
+    void cached_run(int dir, uint64_t lo, uint64_t hi) {
         for (uint64_t i = lo; i < hi; i += cached_C) {
-            Tile tl = win;
-            tl.first = uint32_t(i);
-            tl.count = uint32_t(std::min(cached_C, hi - i));
+            Tile tl{};
+            tl.first = uint32_t(p.cached_segs[dir].size());
+            tl.count = 1;
             tl.level = uint32_t(last);
-            tl.code_off = 0;
-            p.cached_tiles.push_back(tl);
+            tl.win_log2 = kNoWindow;
+            p.cached_segs[dir].push_back({uint32_t(i), uint32_t(std::min(cached_C, hi - i))});
+            p.cached_tiles[dir].push_back(tl);
         }
+    }
+
+    // Cached tiles of direction dir over the ranges 'segs' of one band, all
+    // with the band's window; at most kBandCap nodes per tile.
+    void cached_band(int dir, const std::vector<Seg> &segs, const Tile &win) {
+        Tile tl = win;
+        tl.first = uint32_t(p.cached_segs[dir].size());
+        tl.count = 0;
+        tl.level = uint32_t(last);
+        uint64_t nodes = 0;
+        auto close = [&]() {
+            if (tl.count) p.cached_tiles[dir].push_back(tl);
+            tl.first = uint32_t(p.cached_segs[dir].size());
+            tl.count = 0;
+            nodes = 0;
+        };
+        for (Seg sg : segs) {
+            while (sg.count > 0) {
+                uint64_t take = std::min<uint64_t>(sg.count, kBandCap - nodes);
+                p.cached_segs[dir].push_back({sg.lo, uint32_t(take)});
+                ++tl.count;
+                nodes += take;
+                sg.lo += uint32_t(take);
+                sg.count -= uint32_t(take);
+                if (nodes == kBandCap) close();
+            }
+        }
+        close();
     }
 };
 
@@ -125,6 +170,21 @@ Tile window_of(uint64_t code, int h, int L) {
     w.win_log2 = uint32_t(sh);
     return w;
 }
+
+}  // namespace
+
+namespace {
+
+// A piece of the last internal level in depth-first order: the subtree(s) of
+// nodes [a, b) of level 'level' (codes in Units::codes from 'code_idx'),
+// covering nodes [lo2, hi2) of the last internal level; dense units are
+// single quadrants of the window level.
+struct Unit {
+    int level;
+    uint64_t a, b, code_idx, lo2, hi2;
+    bool dense;
+    uint64_t qcode;   // Morton code of the quadrant (dense units)
+};
 
 }  // namespace
 
@@ -164,109 +224,150 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         while (qlog >= 0 && (2ull << qlog) <= q) ++qlog;
     }
     p.window_log2 = -1;
+    // descent tiles: the plain depth-first cut (windowed descent tiles, one
+    // per dense quadrant, measured slower: many small tiles)
+    pl.range(d0, 0, t.nodes[d0], 0, no_window());
+    if (!o.cache_last_level) return K2_OK;
     if (qlog < 0) {
-        pl.range(d0, 0, t.nodes[d0], 0, no_window());
-        pl.cached(0, n2, no_window());
+        for (int dir = 0; dir < 2; ++dir) pl.cached_run(dir, 0, n2);
         return K2_OK;
     }
-    const int h = std::max(0, L - qlog);           // quadrant level
+    const int h = std::max(0, L - qlog);            // quadrant level
     p.window_log2 = L - h;
-    const uint64_t dense = std::max<uint64_t>(16, (1ull << (L - h)) / 8);   // nodes of level l-2
+    const uint64_t side = 1ull << (L - h);
+    const uint64_t dense = std::max<uint64_t>(16, side / 16);   // nodes of level l-2
 
+    // ---- units, in depth-first order
+    std::vector<Unit> units;
+    std::vector<uint64_t> ucodes;
     if (h <= d0) {
         // quadrants at or above the host top: each is a contiguous range of top nodes
-        uint64_t run_a = 0, run_lo2 = 0;
-        bool in_run = false;
         for (uint64_t q = 0; q < t.nodes[h]; ++q) {
             uint64_t a0 = pl.down(h, q, d0), b0 = pl.down(h, q + 1, d0);
-            uint64_t lo2 = pl.down(d0, a0, last), hi2 = pl.down(d0, b0, last);
-            if (hi2 - lo2 >= dense) {
-                if (in_run) {
-                    pl.range(d0, run_a, a0, run_a, no_window());
-                    pl.cached(run_lo2, lo2, no_window());
-                    in_run = false;
-                }
-                Tile w = window_of(codes[h][q], h, L);
-                pl.range(d0, a0, b0, a0, w);
-                pl.cached(lo2, hi2, w);
-            } else if (!in_run) {
-                in_run = true;
-                run_a = a0;
-                run_lo2 = lo2;
-            }
-        }
-        if (in_run) {
-            pl.range(d0, run_a, t.nodes[d0], run_a, no_window());
-            pl.cached(run_lo2, n2, no_window());
+            Unit u{d0, a0, b0, ucodes.size(), pl.down(d0, a0, last), pl.down(d0, b0, last), false,
+                   codes[h][q]};
+            u.dense = u.hi2 - u.lo2 >= dense;
+            ucodes.insert(ucodes.end(), codes[d0].begin() + int64_t(a0), codes[d0].begin() + int64_t(b0));
+            units.push_back(u);
         }
     } else {
         // Walk down from the host top.  A subtree with fewer than 'dense' nodes
-        // on the last internal level holds no dense quadrant and stays sparse;
-        // larger ones are split down to level h, whose dense nodes get windows.
-        // Consecutive sparse subtrees of one level, adjacent in it, form one run.
-        struct Run {
-            int level = -1;
-            uint64_t a = 0, b = 0, code_base = 0, lo2 = 0, hi2 = 0;
-        } run;
-        auto flush_run = [&]() {
-            if (run.level < 0) return;
-            pl.range(run.level, run.a, run.b, run.code_base, no_window());
-            pl.cached(run.lo2, run.hi2, no_window());
-            run.level = -1;
-        };
-        auto add_sparse = [&](int d, uint64_t node, uint64_t code, uint64_t lo2, uint64_t hi2) {
-            if (run.level == d && run.b == node) {
-                p.codes.push_back(code);
-                run.b = node + 1;
-                run.hi2 = hi2;
-                return;
-            }
-            flush_run();
-            run.level = d;
-            run.a = node;
-            run.b = node + 1;
-            run.code_base = p.codes.size();
-            p.codes.push_back(code);
-            run.lo2 = lo2;
-            run.hi2 = hi2;
-        };
-        // explicit stack of (level, node, code), children pushed in reverse
+        // on the last internal level holds no dense quadrant and stays whole;
+        // larger ones are split down to level h.  The top nodes are walked in
+        // parallel, in chunks whose units are concatenated in order.
         struct Item {
             int d;
-            uint64_t node, code;
+            uint64_t node, code, lo2, hi2;
         };
-        std::vector<Item> stack;
-        for (uint64_t i = t.nodes[d0]; i-- > 0;) stack.push_back({d0, i, codes[d0][i]});
-        while (!stack.empty()) {
-            Item it = stack.back();
-            stack.pop_back();
-            uint64_t lo2 = pl.down(it.d, it.node, last), hi2 = pl.down(it.d, it.node + 1, last);
-            uint64_t desc = hi2 - lo2;
-            if (it.d == h) {
-                if (desc >= dense) {
-                    flush_run();
-                    Tile w = window_of(it.code, h, L);
-                    uint64_t base = p.codes.size();
-                    p.codes.push_back(it.code);
-                    pl.range(h, it.node, it.node + 1, base, w);
-                    pl.cached(lo2, hi2, w);
-                } else {
-                    add_sparse(it.d, it.node, it.code, lo2, hi2);
+        const uint64_t ntop = t.nodes[d0];
+        const int nt = int(std::min<uint64_t>(uint64_t(std::max(1u, std::thread::hardware_concurrency())),
+                                              std::min<uint64_t>(64, ntop)));
+        std::atomic<uint64_t> next_chunk{0};
+        const uint64_t chunk = std::max<uint64_t>(1, ntop / (uint64_t(nt) * 16));
+        std::vector<std::vector<Unit>> chunk_units((ntop + chunk - 1) / chunk);
+        std::vector<std::vector<uint64_t>> chunk_codes(chunk_units.size());
+        auto worker = [&]() {
+            std::vector<Item> stack;
+            for (;;) {
+                const uint64_t c = next_chunk.fetch_add(1);
+                if (c >= chunk_units.size()) return;
+                std::vector<Unit> &us = chunk_units[c];
+                std::vector<uint64_t> &cs = chunk_codes[c];
+                const uint64_t i0 = c * chunk, i1 = std::min(ntop, i0 + chunk);
+                for (uint64_t i = i1; i-- > i0;)
+                    stack.push_back({d0, i, codes[d0][i], pl.down(d0, i, last), pl.down(d0, i + 1, last)});
+                while (!stack.empty()) {
+                    Item it = stack.back();
+                    stack.pop_back();
+                    const uint64_t desc = it.hi2 - it.lo2;
+                    if (it.d == h || desc < dense) {
+                        us.push_back({it.d, it.node, it.node + 1, cs.size(), it.lo2, it.hi2,
+                                      it.d == h && desc >= dense, it.code});
+                        cs.push_back(it.code);
+                        continue;
+                    }
+                    const uint64_t c0 = child_offset(t, it.d, it.node);
+                    const unsigned sg = nibble(t.words[it.d], it.node);
+                    Item ch[4];
+                    int nc = 0;
+                    for (unsigned b = 0; b < 4; ++b)
+                        if (sg & (1u << b)) {
+                            ch[nc].d = it.d + 1;
+                            ch[nc].node = c0 + uint64_t(nc);
+                            ch[nc].code = (it.code << 2) | b;
+                            ++nc;
+                        }
+                    // first and last boundaries are the parent's
+                    ch[0].lo2 = it.lo2;
+                    for (int k = 1; k < nc; ++k) ch[k].lo2 = ch[k - 1].hi2 = pl.down(it.d + 1, ch[k].node, last);
+                    ch[nc - 1].hi2 = it.hi2;
+                    for (int k = nc - 1; k >= 0; --k) stack.push_back(ch[k]);
                 }
-            } else if (desc < dense) {
-                add_sparse(it.d, it.node, it.code, lo2, hi2);
-            } else {
-                uint64_t c0 = child_offset(t, it.d, it.node);
-                unsigned s = nibble(t.words[it.d], it.node);
-                uint64_t ch[4];
-                int nc = 0;
-                for (unsigned b = 0; b < 4; ++b)
-                    if (s & (1u << b)) ch[nc++] = (it.code << 2) | b;
-                for (int k = nc - 1; k >= 0; --k)
-                    stack.push_back({it.d + 1, c0 + uint64_t(k), ch[k]});
             }
+        };
+        std::vector<std::thread> pool;
+        for (int k = 0; k < nt; ++k) pool.emplace_back(worker);
+        for (auto &th : pool) th.join();
+        for (size_t c = 0; c < chunk_units.size(); ++c) {
+            const uint64_t base = ucodes.size();
+            for (Unit u : chunk_units[c]) {
+                u.code_idx += base;
+                units.push_back(u);
+            }
+            ucodes.insert(ucodes.end(), chunk_codes[c].begin(), chunk_codes[c].end());
         }
-        flush_run();
+    }
+
+    // ---- cached tiles, per direction: windowed bands, then the sparse rest
+    const uint64_t band_min = std::max<uint64_t>(64, side * o.window_batch / 32);
+    for (int dir = 0; dir < 2; ++dir) {
+        // band of each dense unit: its row band (right) or column band (left)
+        std::vector<std::pair<uint64_t, uint32_t>> dense_units;   // (band, unit index)
+        for (size_t i = 0; i < units.size(); ++i)
+            if (units[i].dense) {
+                uint64_t code = units[i].qcode;
+                uint64_t band = dir == K2_RIGHT ? even_bits(code >> 1) : even_bits(code);
+                dense_units.push_back({band, uint32_t(i)});
+            }
+        std::stable_sort(dense_units.begin(), dense_units.end(),
+                         [](const auto &x, const auto &y) { return x.first < y.first; });
+        std::vector<char> windowed(units.size(), 0);
+        for (size_t i = 0; i < dense_units.size();) {
+            size_t j = i;
+            uint64_t total = 0;
+            while (j < dense_units.size() && dense_units[j].first == dense_units[i].first) {
+                const Unit &u = units[dense_units[j].second];
+                total += u.hi2 - u.lo2;
+                ++j;
+            }
+            if (total >= band_min) {
+                std::vector<Seg> segs;
+                for (size_t k = i; k < j; ++k) {
+                    const Unit &u = units[dense_units[k].second];
+                    windowed[dense_units[k].second] = 1;
+                    segs.push_back({uint32_t(u.lo2), uint32_t(u.hi2 - u.lo2)});
+                }
+                Tile w = window_of(units[dense_units[i].second].qcode, h, L);
+                pl.cached_band(dir, segs, w);
+            }
+            i = j;
+        }
+        // the sparse rest in depth-first order: contiguous runs of level l-2
+        uint64_t run_lo = 0, run_hi = 0;
+        bool in_run = false;
+        for (size_t i = 0; i < units.size(); ++i) {
+            if (windowed[i]) continue;
+            const Unit &u = units[i];
+            if (in_run && u.lo2 == run_hi) {
+                run_hi = u.hi2;
+                continue;
+            }
+            if (in_run) pl.cached_run(dir, run_lo, run_hi);
+            in_run = true;
+            run_lo = u.lo2;
+            run_hi = u.hi2;
+        }
+        if (in_run) pl.cached_run(dir, run_lo, run_hi);
     }
     if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
     return K2_OK;
@@ -274,8 +375,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
 
 static uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
 
-void layout_for(const HostTree &t, int top, uint64_t n_codes, uint64_t n_tiles, uint64_t n_cached_tiles,
-                bool cached, Layout *out) {
+void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layout *out) {
     Layout &l = *out;
     l = Layout();
     uint64_t off = 0, raw = 0;
@@ -290,9 +390,12 @@ void layout_for(const HostTree &t, int top, uint64_t n_codes, uint64_t n_tiles, 
         l.words_off[d] = take(8 * ((t.nodes[d] + 15) / 16), l.mem.tree);
     for (int d = top; d + 1 < t.levels; ++d)
         l.dir_off[d] = take(4 * ((t.nodes[d] + kDirBlock - 1) / kDirBlock), l.mem.directory);
-    l.codes_off = take(8 * n_codes, l.mem.top_codes);
-    l.tiles_off = take(sizeof(Tile) * n_tiles, l.mem.tiles);
-    l.cached_tiles_off = take(cached ? sizeof(Tile) * n_cached_tiles : 0, l.mem.tiles);
+    l.codes_off = take(8 * plan.codes.size(), l.mem.top_codes);
+    l.tiles_off = take(sizeof(Tile) * plan.tiles.size(), l.mem.tiles);
+    for (int dir = 0; dir < 2; ++dir) {
+        l.cached_tiles_off[dir] = take(cached ? sizeof(Tile) * plan.cached_tiles[dir].size() : 0, l.mem.tiles);
+        l.cached_segs_off[dir] = take(cached ? sizeof(Seg) * plan.cached_segs[dir].size() : 0, l.mem.tiles);
+    }
     l.cached_off = take(cached ? 8 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
     l.mem.scratch = 0;
     l.mem.alignment = off - raw;
