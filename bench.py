@@ -32,7 +32,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="web_n27_d9")
     p.add_argument("--mode", default=None, help="tree or cached (default: the workload's)")
-    p.add_argument("--tile-nodes", type=int, default=2048)
+    p.add_argument("--tile-nodes", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-stride", type=int, default=32,
                    help="oracle sample: the edges whose source is a multiple of this")

@@ -78,7 +78,7 @@ typedef struct {
     /* Tiled descent (Sec. 3.4): a tile is a contiguous node range whose
        subtree holds at most tile_nodes nodes on every level; one workgroup
        descends a tile with its frontier in LDS.  256..4096, power of 2.
-       Default 2048. */
+       Default 1024. */
     uint32_t tile_nodes;
     /* Host-side top (Sec. 3.4): the device starts from the deepest level with
        at most host_top_max nodes (never below the last internal level).

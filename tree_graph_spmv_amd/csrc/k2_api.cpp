@@ -94,7 +94,7 @@ extern "C" {
 
 k2_status k2_plan_defaults(k2_plan_opts *opts) {
     if (!opts) return K2_E_INVALID_ARG;
-    opts->tile_nodes = 2048;
+    opts->tile_nodes = 1024;
     opts->host_top_max = 1u << 16;
     opts->cache_last_level = 0;
     opts->xcd_remap = 0;

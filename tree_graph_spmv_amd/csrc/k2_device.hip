@@ -123,6 +123,10 @@ struct Tropical {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
+// Workgroups per CU the product kernels are compiled for: 8 x 4 waves fills
+// the 8 wave slots of each SIMD (64 VGPRs); the leaf phase is latency-bound,
+// so resident waves matter more than registers.
+constexpr int kOccupancy = 8;
 
 __device__ __forceinline__ uint32_t nib(const uint64_t *__restrict__ w, uint64_t i) {
     return uint32_t(w[i >> 4] >> ((i & 15) * 4)) & 0xFu;
@@ -258,16 +262,18 @@ __device__ __forceinline__ uint32_t logical_block(int remap) {
 // ------------------------------------------------------------- kernels
 
 // LDS of one wave's leaf segment: the segment's nodes' 4x4-block
-// coordinates and the list of their cells, 2 bytes each: (node << 4) |
-// (4 * row + column) within the node's block.  A node has at most 4 leaves of
-// 4 cells.
+// coordinates and a round of the list of their cells, 2 bytes each:
+// (node << 4) | (4 * row + column) within the node's block.  A node has at
+// most 4 leaves of 4 cells, so a segment has at most 1024 cells; they go
+// through the buffer kCellRound at a time (one round in the common case).
+constexpr uint32_t kCellRound = 256;
 struct WaveCells {
     uint32_t r4[64];
     uint32_t c4[64];
-    uint16_t cell[16 * 64];
+    uint16_t cell[kCellRound];
 };
 
-constexpr int kUnroll = 8;   // cells whose x loads are issued before their atomics
+constexpr int kUnroll = 4;   // cells whose x loads are issued before their atomics
 
 // Output window of a tile: 'win' (LDS, or null) holds outputs [out0, out0 +
 // rows) x B; cells of the tile all land inside it.
@@ -300,50 +306,58 @@ __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t
         if (s & (1u << b)) lam[b] = nib(leaf_words, uint64_t(off) + j++);
     const uint32_t ncell = __popc(lam[0]) + __popc(lam[1]) + __popc(lam[2]) + __popc(lam[3]);
     uint32_t total;
-    uint32_t pos = wave_scan<5>(ncell, total);
+    const uint32_t pos0 = wave_scan<5>(ncell, total);
     wc->r4[lane] = compact_even(code >> 1);
     wc->c4[lane] = compact_even(code);
-#pragma unroll
-    for (uint32_t b = 0; b < 4; ++b) {
-#pragma unroll
-        for (uint32_t q = 0; q < 4; ++q)
-            if (lam[b] & (1u << q)) {
-                const uint32_t r = 2 * (b >> 1) + (q >> 1), c = 2 * (b & 1) + (q & 1);
-                wc->cell[pos++] = uint16_t((lane << 4) | (r << 2) | c);
-            }
-    }
-    wave_lds_sync();
     const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
-    for (uint32_t k0 = g; k0 < total; k0 += G * kUnroll) {
-        uint32_t in_i[kUnroll], out_i[kUnroll];
+    for (uint32_t round = 0; round < total; round += kCellRound) {
+        // this lane's cells with list positions in [round, round + kCellRound)
+        uint32_t pos = pos0;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t k = k0 + uint32_t(u) * G;
-            const uint32_t e = (k < total) ? uint32_t(wc->cell[k]) : 0u;
-            const uint32_t r = wc->r4[e >> 4] * 4 + ((e >> 2) & 3u);
-            const uint32_t c = wc->c4[e >> 4] * 4 + (e & 3u);
-            in_i[u] = (DIR == K2_RIGHT) ? c : r;
-            out_i[u] = (DIR == K2_RIGHT) ? r : c;
+        for (uint32_t b = 0; b < 4; ++b) {
+#pragma unroll
+            for (uint32_t q = 0; q < 4; ++q)
+                if (lam[b] & (1u << q)) {
+                    if (pos - round < kCellRound) {   // unsigned: false below 'round'
+                        const uint32_t r = 2 * (b >> 1) + (q >> 1), c = 2 * (b & 1) + (q & 1);
+                        wc->cell[pos - round] = uint16_t((lane << 4) | (r << 2) | c);
+                    }
+                    ++pos;
+                }
         }
-        for (uint32_t v = lv; v < B; v += VL) {
-            T xv[kUnroll];
+        wave_lds_sync();
+        const uint32_t n = (total - round < kCellRound) ? total - round : kCellRound;
+        for (uint32_t k0 = g; k0 < n; k0 += G * kUnroll) {
+            uint32_t in_i[kUnroll], out_i[kUnroll];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
-                xv[u] = (k0 + uint32_t(u) * G < total) ? x[uint64_t(in_i[u]) * B + v] : SR::zero();
-            if (w.win) {
+            for (int u = 0; u < kUnroll; ++u) {
+                const uint32_t k = k0 + uint32_t(u) * G;
+                const uint32_t e = (k < n) ? uint32_t(wc->cell[k]) : 0u;
+                const uint32_t r = wc->r4[e >> 4] * 4 + ((e >> 2) & 3u);
+                const uint32_t c = wc->c4[e >> 4] * 4 + (e & 3u);
+                in_i[u] = (DIR == K2_RIGHT) ? c : r;
+                out_i[u] = (DIR == K2_RIGHT) ? r : c;
+            }
+            for (uint32_t v = lv; v < B; v += VL) {
+                T xv[kUnroll];
 #pragma unroll
                 for (int u = 0; u < kUnroll; ++u)
-                    if (k0 + uint32_t(u) * G < total && SR::contributes(xv[u]))
-                        SR::lds_atomic(&w.win[(uint64_t(out_i[u]) - w.out0) * B + v], SR::contrib(xv[u]));
-            } else {
+                    xv[u] = (k0 + uint32_t(u) * G < n) ? x[uint64_t(in_i[u]) * B + v] : SR::zero();
+                if (w.win) {
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
-                    if (k0 + uint32_t(u) * G < total && SR::contributes(xv[u]))
-                        SR::atomic(&y[uint64_t(out_i[u]) * B + v], SR::contrib(xv[u]));
+                    for (int u = 0; u < kUnroll; ++u)
+                        if (k0 + uint32_t(u) * G < n && SR::contributes(xv[u]))
+                            SR::lds_atomic(&w.win[(uint64_t(out_i[u]) - w.out0) * B + v], SR::contrib(xv[u]));
+                } else {
+#pragma unroll
+                    for (int u = 0; u < kUnroll; ++u)
+                        if (k0 + uint32_t(u) * G < n && SR::contributes(xv[u]))
+                            SR::atomic(&y[uint64_t(out_i[u]) * B + v], SR::contrib(xv[u]));
+                }
             }
         }
+        wave_lds_sync();
     }
-    wave_lds_sync();
 }
 
 // The window of tile 'tl' for this product (no window: win = null), its LDS
@@ -398,7 +412,7 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y
 // directory and the rest by a wave scan of the fan-outs.  The next segment's
 // codes and signatures are loaded before the current one is processed.
 template <class SR, int DIR>
-__global__ __launch_bounds__(kThreads) void cached_kernel(
+__global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
     const uint64_t *__restrict__ codes, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
@@ -414,25 +428,32 @@ __global__ __launch_bounds__(kThreads) void cached_kernel(
     for (uint32_t ti = logical_block(remap); ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
+        // The tile's ranges are cut into 64-node segments, numbered across
+        // the ranges; wave w takes segments w, w + 4, ... so short ranges
+        // still keep every wave busy.
+        uint32_t seg_base = 0;   // segments in the ranges before this one
         for (uint32_t r = 0; r < tl.count; ++r) {
             const Seg sg = segs[tl.first + r];
-            uint32_t seg = wave * 64;
-            uint32_t i = sg.lo + seg + lane;
-            bool valid = seg + lane < sg.count;
+            const uint32_t nseg = (sg.count + 63) / 64;
+            uint32_t k = (wave + kWaves - (seg_base % kWaves)) % kWaves;   // first of this wave
+            seg_base += nseg;
+            if (k >= nseg) continue;
+            uint32_t i = sg.lo + k * 64 + lane;
+            bool valid = k * 64 + lane < sg.count;
             uint32_t s = valid ? nib(sig_words, i) : 0u;
             uint64_t code = valid ? codes[i] : 0ull;
-            while (seg < sg.count) {
-                const uint32_t base = wave_child_offset(t, d, sg.lo + seg);
+            while (k < nseg) {
+                const uint32_t base = wave_child_offset(t, d, sg.lo + k * 64);
                 // prefetch the wave's next segment of this range
-                const uint32_t nseg = seg + kThreads;
-                const uint32_t ni = sg.lo + nseg + lane;
-                const bool nvalid = nseg + lane < sg.count;
+                const uint32_t nk = k + kWaves;
+                const uint32_t ni = sg.lo + nk * 64 + lane;
+                const bool nvalid = nk * 64 + lane < sg.count;
                 const uint32_t ns = nvalid ? nib(sig_words, ni) : 0u;
                 const uint64_t ncode = nvalid ? codes[ni] : 0ull;
                 uint32_t total;
                 const uint32_t ex = wave_scan<3>(__popc(s), total);
                 leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, wc);
-                seg = nseg;
+                k = nk;
                 s = ns;
                 code = ncode;
             }
@@ -446,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void cached_kernel(
 // the leaves of its last-internal-level nodes in place.  With 'emit' set it
 // writes those nodes' codes instead (building the cached level, Sec. 3.5).
 template <class SR, int DIR, bool EMIT>
-__global__ __launch_bounds__(kThreads) void descent_kernel(
+__global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
     const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
@@ -571,9 +592,9 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     const uint32_t n_tiles = uint32_t(m.plan.tiles.size());
     if (n_tiles == 0) return hipSuccess;
     const uint32_t cap = m.plan.tile_nodes;
-    int use = 0;
-    const size_t win = EMIT ? 0 : window_bytes(m, B, &use);
-    const size_t lds = size_t(2) * cap * sizeof(uint64_t) + win;
+    // descent tiles are planned without windows: reserve no window LDS
+    const int use = 0;
+    const size_t lds = size_t(2) * cap * sizeof(uint64_t);
     const uint32_t VL = lanes_per_node(B);
     const int remap = m.xcd_remap ? 1 : 0;
     const uint32_t grid = grid_for(n_tiles, remap);
