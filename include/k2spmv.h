@@ -87,10 +87,12 @@ typedef struct {
     /* Keep the Morton codes of the last internal level on the device, 8 bytes
        per node (Sec. 3.5, "k2+F").  Default 0. */
     int32_t cache_last_level;
-    /* Workgroup order: 1 gives each of the MI355X's 8 XCDs (own L2 each)
-       contiguous node ranges instead of round-robin neighbours, so the y
-       lines a Z-order region touches stay in one L2.  Default 0 (measured
-       slower on the web-like 2^27 workload). */
+    /* Tile order for the MI355X's 8 XCDs (each with its own L2; workgroup b
+       runs on XCD b % 8): 1 gives each XCD a contiguous run of the Z order,
+       of about equal work, by placing run k's tiles at positions k, k + 8,
+       ...; 0 keeps the Z order, which spreads neighbouring tiles over all
+       XCDs.  Padding tiles (count 0) make the lists equal in length.
+       Default 0. */
     int32_t xcd_remap;
     /* Output windows for products over the cached level: Q is the largest
        power of 2 with Q * window_batch <= window_elems (at most 16384
@@ -176,7 +178,7 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
    call; Sec. 3.4).  which = 0: the descent tiles and their start codes;
    1 / 2: the cached-level tiles of right / left products and their node
    ranges (empty unless opts->cache_last_level).  Reports the host-top level d0, the number of tiles and of codes
-   (which = 0) or ranges (1, 2).  Errors: K2_E_INVALID_ARG. */
+   (which = 0) or twice the number of segments (1, 2).  Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux);
 
@@ -185,8 +187,9 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
    column, log2 of the window side or 0xFFFFFFFF for no window, 0).
    which = 0: 'count' nodes of 'level' from node 'first', whose Morton codes
    (row bit above column bit per level, 2*level bits) are aux[code index ..].
-   which = 1 / 2: 'count' ranges of the last internal level from range
-   'first'; aux[r] = (first node << 32) | node count of range r.
+   which = 1 / 2: 'count' segments of the last internal level from segment
+   'first'; segment r is aux[2r] = (first node << 32) | node count (1..64)
+   and aux[2r + 1] = the leaf-level index of its first node's first child.
    Host arrays of 8*n_tiles and n_aux entries (sizes from k2_plan_info).
    Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,

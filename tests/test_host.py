@@ -73,6 +73,26 @@ def oracle_codes(o, upto):
     return codes
 
 
+def check_xcd_order(ordered, plain, band_count):
+    """An XCD-ordered tile list is the plain list's tiles, regrouped: the tiles
+    at positions k, k + 8, ... (XCD k) are a contiguous run of each group of
+    the plain list (bands, then the sparse rest), and the runs of XCD 0..7
+    follow each other; every other entry is padding (count 0)."""
+    assert len(ordered) % 8 == 0
+    lists = [[tuple(int(v) for v in tl) for tl in ordered[k::8] if int(tl[1])] for k in range(8)]
+    plain = [tuple(int(v) for v in tl) for tl in plain]
+    assert sum(len(x) for x in lists) == len(plain)
+    groups = [plain[:band_count], plain[band_count:]]
+    first_group = set(groups[0])
+    rebuilt = [[], []]
+    for lst in lists:
+        nb = sum(1 for tl in lst if tl in first_group)
+        assert all(tl in first_group for tl in lst[:nb]), "a run of the first group comes first"
+        rebuilt[0] += lst[:nb]
+        rebuilt[1] += lst[nb:]
+    assert rebuilt[0] == groups[0] and rebuilt[1] == groups[1]
+
+
 def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
     """cached: {1: (tiles, ranges) of right products, 2: of left products}."""
     L = o.levels
@@ -89,6 +109,9 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
     # cells of the last-internal-level range [a, b): leaves [off(a), off(b)),
     # whose cells come consecutively in the oracle's enumeration
     leaf_pop = np.array([bin(int(s)).count("1") for s in o.signatures(L - 1)], np.int64)
+
+    def leaf_of(i):   # first child of node i of the last internal level
+        return int(offs[last][i]) if i < nodes[last] else nodes[L - 1]
     cell_start = np.concatenate([[0], np.cumsum(leaf_pop)])
 
     def cells_of(a, b):
@@ -101,14 +124,16 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
         assert side * opts.window_batch <= max(opts.window_elems, 1)
         return side
 
-    pos = 0
+    spans = []
     for tl in tiles:
         first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
-        assert top <= level <= last and count >= 1
+        if count == 0:   # padding of an XCD-ordered list
+            assert opts.xcd_remap and level == last
+            continue
+        assert top <= level <= last
         a, b = down(level, first), down(level, first + count)
-        assert a == pos, "descent tiles must follow each other on the last internal level"
         assert b - a <= opts.tile_nodes
-        pos = b
+        spans.append((a, b))
         got = codes[int(tl[3]):int(tl[3]) + count]
         assert np.array_equal(got, all_codes[level][first:first + count])
         if tl[6] != 0xFFFFFFFF:   # a descent window (kernels accept them) is the whole quadrant
@@ -116,16 +141,26 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
             rr, cc = cells_of(a, b)
             assert np.all((rr >= tl[4]) & (rr < tl[4] + side)), "cell row outside window"
             assert np.all((cc >= tl[5]) & (cc < tl[5] + side)), "cell column outside window"
+    if not opts.xcd_remap:
+        assert spans == sorted(spans), "descent tiles must follow each other in Z order"
+    pos = 0
+    for a, b in sorted(spans):
+        assert a == pos, "descent tiles must cover the last internal level exactly once"
+        pos = b
     assert pos == nodes[last]
     for which, (ctiles, ranges) in cached.items():
         seen = []
         for tl in ctiles:
             first, count = int(tl[0]), int(tl[1])
-            assert count >= 1 and int(tl[2]) == last
+            assert int(tl[2]) == last
+            if count == 0:
+                assert opts.xcd_remap and tl[6] == 0xFFFFFFFF
+                continue
             total = 0
-            for r in ranges[first:first + count]:
+            for r, leaf in ranges[first:first + count]:
                 lo, n = int(r) >> 32, int(r) & 0xFFFFFFFF
-                assert n >= 1
+                assert 1 <= n <= 64
+                assert int(leaf) == leaf_of(lo), "first leaf of a segment"
                 seen.append((lo, n))
                 total += n
                 if tl[6] != 0xFFFFFFFF:   # a band window covers the output coordinate
@@ -145,6 +180,8 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
 
 @pytest.mark.parametrize("opt", [
     dict(),
+    dict(xcd_remap=1),
+    dict(xcd_remap=1, window_elems=0),
     dict(window_elems=8192),
     dict(tile_nodes=256, window_elems=1024, window_batch=1),
     dict(tile_nodes=4096, window_elems=16384, window_batch=1),
@@ -165,6 +202,14 @@ def test_plan_invariants(case, opt):
     all_codes = oracle_codes(o, o.levels - 2)
     check_plan(o, cr.astype(np.int64), cc.astype(np.int64), top, tiles, codes, cached, opts,
                all_codes)
+    if opts.xcd_remap:
+        plain = k2.plan_defaults(cache_last_level=1, **dict(opt, xcd_remap=0))
+        check_xcd_order(tiles, t.plan(plain, 0)[1], len(t.plan(plain, 0)[1]))
+        for w in (1, 2):
+            ptiles = t.plan(plain, w)[1]
+            n_band = sum(1 for tl in ptiles if tl[6] != 0xFFFFFFFF)
+            assert all(tl[6] != 0xFFFFFFFF for tl in ptiles[:n_band]), "bands come first"
+            check_xcd_order(cached[w][0], ptiles, n_band)
 
 
 def test_top_level(case):
@@ -183,7 +228,7 @@ def test_estimate_parts(case):
         opts = k2.plan_defaults(cache_last_level=cached)
         est = t.estimate(opts, semiring="plus_times", batch=3)
         top, tiles, codes = t.plan(opts, 0)
-        extra = sum(32 * len(t.plan(opts, w)[1]) + 8 * len(t.plan(opts, w)[2]) for w in (1, 2))
+        extra = sum(32 * len(t.plan(opts, w)[1]) + 16 * len(t.plan(opts, w)[2]) for w in (1, 2))
         L = o.levels
         assert est["tree"] == sum(8 * ((nodes[d] + 15) // 16) for d in range(top, L))
         assert est["directory"] == sum(4 * ((nodes[d] + 255) // 256) for d in range(top, L - 1))

@@ -188,7 +188,8 @@ class Tree:
     def plan(self, opts=None, which=0):
         """(top_level, tiles (n,8) uint32, aux uint64) of one tile plan:
         which = 0 descent tiles (aux = start codes); 1 / 2 cached-level
-        tiles of right / left products (aux = (first node << 32) | count)."""
+        tiles of right / left products (aux = (n_segments, 2): (first node
+        << 32) | count, and the first node's first leaf)."""
         opts = opts or plan_defaults()
         top = ctypes.c_uint32()
         nt = ctypes.c_uint64()
@@ -200,7 +201,8 @@ class Tree:
         _check(lib().k2_plan_tiles(self._h, ctypes.byref(opts), int(which),
                                    tiles.ctypes.data_as(_U32P), nt.value, aux.ctypes.data_as(_U64P),
                                    na.value), "k2_plan_tiles")
-        return int(top.value), tiles[:nt.value], aux[:na.value]
+        aux = aux[:na.value]
+        return int(top.value), tiles[:nt.value], aux if which == 0 else aux.reshape(-1, 2)
 
 
 def _stream_handle(stream):

@@ -52,7 +52,8 @@ uint64_t vector_bytes(const HostTree &t, uint32_t batch) {
 bool same_opts(const k2_plan_opts &a, const k2_plan_opts &b) {
     return a.tile_nodes == b.tile_nodes && a.host_top_max == b.host_top_max &&
            a.window_elems == b.window_elems && a.window_batch == b.window_batch &&
-           (a.cache_last_level != 0) == (b.cache_last_level != 0);
+           (a.cache_last_level != 0) == (b.cache_last_level != 0) &&
+           (a.xcd_remap != 0) == (b.xcd_remap != 0);
 }
 
 // The plan of 'tree' for 'o', computed once per option set.
@@ -199,7 +200,7 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
     if (st != K2_OK) return st;
     if (top_level) *top_level = uint32_t(plan.top_level);
     if (n_tiles) *n_tiles = which == 0 ? plan.tiles.size() : plan.cached_tiles[which - 1].size();
-    if (n_aux) *n_aux = which == 0 ? plan.codes.size() : plan.cached_segs[which - 1].size();
+    if (n_aux) *n_aux = which == 0 ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
     return K2_OK;
 }
 
@@ -215,7 +216,7 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
     }
     if (st != K2_OK) return st;
     const std::vector<Tile> &list = which == 0 ? plan.tiles : plan.cached_tiles[which - 1];
-    const uint64_t naux = which == 0 ? plan.codes.size() : plan.cached_segs[which - 1].size();
+    const uint64_t naux = which == 0 ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
     if (n_tiles < list.size() || n_aux < naux) return K2_E_INVALID_ARG;
     if ((!tiles && !list.empty()) || (!aux && naux)) return K2_E_INVALID_ARG;
     for (size_t k = 0; k < list.size(); ++k) {
@@ -228,7 +229,10 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
         std::copy(plan.codes.begin(), plan.codes.end(), aux);
     } else {
         const std::vector<Seg> &sg = plan.cached_segs[which - 1];
-        for (size_t k = 0; k < sg.size(); ++k) aux[k] = (uint64_t(sg[k].lo) << 32) | sg[k].count;
+        for (size_t k = 0; k < sg.size(); ++k) {
+            aux[2 * k] = (uint64_t(sg[k].lo) << 32) | sg[k].count;
+            aux[2 * k + 1] = sg[k].leaf;
+        }
     }
     return K2_OK;
 }
@@ -262,7 +266,6 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     m.levels = t.levels;
     m.nodes = t.nodes;
     m.cached = opts->cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
-    m.xcd_remap = opts->xcd_remap != 0;
     m.window_elems = m.plan.window_log2 >= 0 ? opts->window_elems : 0;
     m.window_batch = opts->window_batch;
     std::memset(&m.dev, 0, sizeof(m.dev));

@@ -248,17 +248,6 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Logical workgroup index.  Workgroups are dispatched round-robin over the 8
-// XCDs (workgroup b runs on XCD b % 8); with 'remap' set, XCD k instead gets
-// the k-th contiguous eighth of the logical order, so neighbouring Z-order
-// ranges, which share rows and columns, share one L2.  The grid is a
-// multiple of 8 whenever remap is set.
-__device__ __forceinline__ uint32_t logical_block(int remap) {
-    if (!remap) return blockIdx.x;
-    const uint32_t per = gridDim.x >> 3;
-    return (blockIdx.x & 7u) * per + (blockIdx.x >> 3);
-}
-
 // ------------------------------------------------------------- kernels
 
 // LDS of one wave's leaf segment: the segment's nodes' 4x4-block
@@ -285,25 +274,20 @@ struct Window {
 };
 
 // Leaf work of one wave over a segment of up to 64 nodes of the last internal
-// level; lane l holds node l's code, signature s and first leaf 'off' (s = 0:
-// no node).  Phase A (a lane per node): read the node's leaf signatures and
-// list its cells in the wave's LDS at positions from a wave scan of the cell
-// counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
-// kUnroll cells, then apply the semiring's atomics, to the LDS window when
-// the tile has one, else to y.  No workgroup barrier.
+// level; lane l holds node l's code, signature s (0: no node) and the leaf
+// signatures lam[b] of its children b (0 where s lacks bit b).  Phase A (a
+// lane per node): list the segment's cells in the wave's LDS at positions
+// from a wave scan of the cell counts.  Phase B (VL adjacent lanes per cell,
+// one per vector): gather x for kUnroll cells, then apply the semiring's
+// atomics, to the LDS window when the tile has one, else to y.  No workgroup
+// barrier.
 template <class SR, int DIR>
-__device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
-                                             const uint64_t *__restrict__ leaf_words,
-                                             const typename SR::T *__restrict__ x,
-                                             typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                             Window<typename SR::T> w, WaveCells *wc) {
+__device__ __forceinline__ void leaf_cells(uint64_t code, const uint32_t (&lam)[4],
+                                           const typename SR::T *__restrict__ x,
+                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                           Window<typename SR::T> w, WaveCells *wc) {
     using T = typename SR::T;
     const uint32_t lane = __lane_id();
-    uint32_t lam[4] = {0u, 0u, 0u, 0u};   // leaf signature per quadrant b
-    uint32_t j = 0;
-#pragma unroll
-    for (uint32_t b = 0; b < 4; ++b)
-        if (s & (1u << b)) lam[b] = nib(leaf_words, uint64_t(off) + j++);
     const uint32_t ncell = __popc(lam[0]) + __popc(lam[1]) + __popc(lam[2]) + __popc(lam[3]);
     uint32_t total;
     const uint32_t pos0 = wave_scan<5>(ncell, total);
@@ -360,6 +344,21 @@ __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t
     }
 }
 
+// leaf_cells for a lane whose node's first leaf is leaf-level node 'off'.
+template <class SR, int DIR>
+__device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
+                                             const uint64_t *__restrict__ leaf_words,
+                                             const typename SR::T *__restrict__ x,
+                                             typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                             Window<typename SR::T> w, WaveCells *wc) {
+    uint32_t lam[4] = {0u, 0u, 0u, 0u};
+    uint32_t j = 0;
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b)
+        if (s & (1u << b)) lam[b] = nib(leaf_words, uint64_t(off) + j++);
+    leaf_cells<SR, DIR>(code, lam, x, y, B, VL, w, wc);
+}
+
 // The window of tile 'tl' for this product (no window: win = null), its LDS
 // set to the semiring zero.  'use' is false when the batch is too wide for
 // the planned window size.
@@ -406,57 +405,94 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y
     for (uint64_t k = n4 * 4 + i; k < n; k += stride) y[k] = value;
 }
 
+// Pipeline state of one segment of a cached tile.  Stage 1, issued two
+// segments ahead: the descriptor (uniform) and each lane's node signature.
+struct SegSig {
+    uint32_t lo, count, leaf;   // uniform; count = 0 past the wave's last segment
+    uint32_t s;                 // the lane's node signature, 0 outside the segment
+};
+// Stage 2, issued one segment ahead: the lane's code, and its signature s
+// and first-leaf nibble position p packed as s | p << 6, and the two
+// leaf-level dwords that hold its leaf signatures (from nibble p of lo32).
+struct SegLeaves {
+    uint64_t code;
+    uint32_t ssh, lo32, hi32;
+};
+
+__device__ __forceinline__ SegSig stage_sig(const Seg *__restrict__ segs, uint32_t first,
+                                            uint32_t k, uint32_t nseg,
+                                            const uint64_t *__restrict__ sig_words) {
+    SegSig a{0u, 0u, 0u, 0u};
+    if (k < nseg) {
+        const Seg sg = segs[first + k];
+        a.lo = sg.lo;
+        a.count = sg.count;
+        a.leaf = sg.leaf;
+        if (__lane_id() < sg.count) a.s = nib(sig_words, uint64_t(sg.lo) + __lane_id());
+    }
+    return a;
+}
+
+// The lane's first leaf is the segment's first leaf plus the fan-outs of the
+// lanes before it (a wave scan).  A node's at most 4 leaf nibbles start at
+// nibble off % 8 of dword off / 8 and reach into the next dword only if
+// off % 8 + fan-out > 8, which is the only case that reads it.
+__device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_t *__restrict__ codes,
+                                                  const uint32_t *__restrict__ leaf_dw) {
+    SegLeaves b{0ull, a.s, 0u, 0u};
+    uint32_t total;
+    const uint32_t ex = wave_scan<3>(__popc(a.s), total);
+    if (__lane_id() < a.count) b.code = codes[a.lo + __lane_id()];
+    if (a.s) {
+        const uint32_t off = a.leaf + ex;
+        b.ssh = a.s | ((off & 7u) << 6);
+        b.lo32 = leaf_dw[off >> 3];
+        if ((off & 7u) + __popc(a.s) > 8u) b.hi32 = leaf_dw[(off >> 3) + 1u];
+    }
+    return b;
+}
+
 // One product over the cached last internal level (Sec. 3.5): each workgroup
-// takes a tile, a list of ranges of that level's nodes; its waves take turns
-// at segments of 64 nodes, each finding the segment's first leaf from the
-// directory and the rest by a wave scan of the fan-outs.  The next segment's
-// codes and signatures are loaded before the current one is processed.
+// takes a tile, a list of segments of up to 64 nodes of that level, each
+// with its first leaf's index; wave w takes segments w, w + 4, ...  A wave
+// works on three of its segments at once: while it visits the leaves of one,
+// the codes and leaf signatures of the next and the signatures of the one
+// after are in flight.
 template <class SR, int DIR>
 __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
     const uint64_t *__restrict__ codes, const typename SR::T *__restrict__ x,
-    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    int remap) {
+    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
     __shared__ WaveCells s_cells[kWaves];
     const int d = t.levels - 2;
-    const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
+    const uint32_t wave = threadIdx.x >> 6;
     const uint64_t *__restrict__ sig_words = t.words[d];
-    const uint64_t *__restrict__ leaf_words = t.words[d + 1];
+    const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[d + 1]);
     WaveCells *wc = &s_cells[wave];
-    for (uint32_t ti = logical_block(remap); ti < n_tiles; ti += gridDim.x) {
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
-        // The tile's ranges are cut into 64-node segments, numbered across
-        // the ranges; wave w takes segments w, w + 4, ... so short ranges
-        // still keep every wave busy.
-        uint32_t seg_base = 0;   // segments in the ranges before this one
-        for (uint32_t r = 0; r < tl.count; ++r) {
-            const Seg sg = segs[tl.first + r];
-            const uint32_t nseg = (sg.count + 63) / 64;
-            uint32_t k = (wave + kWaves - (seg_base % kWaves)) % kWaves;   // first of this wave
-            seg_base += nseg;
-            if (k >= nseg) continue;
-            uint32_t i = sg.lo + k * 64 + lane;
-            bool valid = k * 64 + lane < sg.count;
-            uint32_t s = valid ? nib(sig_words, i) : 0u;
-            uint64_t code = valid ? codes[i] : 0ull;
-            while (k < nseg) {
-                const uint32_t base = wave_child_offset(t, d, sg.lo + k * 64);
-                // prefetch the wave's next segment of this range
-                const uint32_t nk = k + kWaves;
-                const uint32_t ni = sg.lo + nk * 64 + lane;
-                const bool nvalid = nk * 64 + lane < sg.count;
-                const uint32_t ns = nvalid ? nib(sig_words, ni) : 0u;
-                const uint64_t ncode = nvalid ? codes[ni] : 0ull;
-                uint32_t total;
-                const uint32_t ex = wave_scan<3>(__popc(s), total);
-                leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, wc);
-                k = nk;
-                s = ns;
-                code = ncode;
+        const uint32_t nseg = tl.count;
+        uint32_t k = wave;
+        SegSig a1 = stage_sig(segs, tl.first, k + kWaves, nseg, sig_words);
+        SegLeaves b0 = stage_leaves(stage_sig(segs, tl.first, k, nseg, sig_words), codes, leaf_dw);
+        for (; k < nseg; k += kWaves) {
+            const SegSig a2 = stage_sig(segs, tl.first, k + 2 * kWaves, nseg, sig_words);
+            const SegLeaves b1 = stage_leaves(a1, codes, leaf_dw);
+            const uint32_t s0 = b0.ssh & 15u;
+            const uint64_t bits = ((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u);
+            uint32_t lam[4];
+            uint32_t j = 0;
+#pragma unroll
+            for (uint32_t b = 0; b < 4; ++b) {
+                lam[b] = (s0 & (1u << b)) ? uint32_t(bits >> (4 * j)) & 15u : 0u;
+                j += (s0 >> b) & 1u;
             }
+            leaf_cells<SR, DIR>(b0.code, lam, x, y, B, VL, w, wc);
+            b0 = b1;
+            a1 = a2;
         }
         close_window<SR>(w, y, n_out, B);
     }
@@ -471,7 +507,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
     const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    uint64_t *__restrict__ emit, int remap) {
+    uint64_t *__restrict__ emit) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
@@ -480,7 +516,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     const int last = t.levels - 2;
     const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
     T *s_win = reinterpret_cast<T *>(s_front + 2 * size_t(cap));
-    for (uint32_t ti = logical_block(remap); ti < n_tiles; ti += gridDim.x) {
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         int d = int(tl.level);
         uint32_t lo = tl.first, cnt = tl.count;
@@ -546,11 +582,12 @@ uint32_t lanes_per_node(uint32_t B) {
     return v;
 }
 
-uint32_t grid_for(uint64_t blocks, bool remap) {
+// One workgroup per tile up to 2^20 workgroups, then a grid-stride loop; the
+// cap is a multiple of 8, so a tile runs on the XCD its position names (tile
+// lists ordered for the XCDs rely on it).
+uint32_t grid_for(uint64_t blocks) {
     const uint64_t cap = 1u << 20;
-    uint64_t g = blocks < cap ? (blocks ? blocks : 1) : cap;
-    if (remap) g = (g + 7) & ~uint64_t(7);   // whole rounds of the 8 XCDs
-    return uint32_t(g);
+    return uint32_t(blocks < cap ? (blocks ? blocks : 1) : cap);
 }
 
 // Whether products with batch B use the planned windows, and their LDS bytes.
@@ -571,8 +608,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
     if (n_tiles == 0) return hipSuccess;
     const uint32_t VL = lanes_per_node(B);
-    const int remap = m.xcd_remap ? 1 : 0;
-    const uint32_t grid = grid_for(n_tiles, remap);
+    const uint32_t grid = grid_for(n_tiles);
     int use = 0;
     const size_t lds = window_bytes(m, B, &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
@@ -581,7 +617,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
                        m.d_cached_segs[DIR], m.d_cached, static_cast<const T *>(x),
-                       static_cast<T *>(y), B, VL, n_out, use, remap);
+                       static_cast<T *>(y), B, VL, n_out, use);
     return hipGetLastError();
 }
 
@@ -596,15 +632,13 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     const int use = 0;
     const size_t lds = size_t(2) * cap * sizeof(uint64_t);
     const uint32_t VL = lanes_per_node(B);
-    const int remap = m.xcd_remap ? 1 : 0;
-    const uint32_t grid = grid_for(n_tiles, remap);
+    const uint32_t grid = grid_for(n_tiles);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     auto k = descent_kernel<SR, DIR, EMIT>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_tiles, n_tiles, m.d_codes,
-                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit,
-                       remap);
+                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit);
     return hipGetLastError();
 }
 

@@ -49,16 +49,21 @@ struct Tile {
 };
 static_assert(sizeof(Tile) == 32, "tile layout");
 
-// A range of nodes of the last internal level.
+// A segment of a cached tile: up to kSegNodes consecutive nodes of the last
+// internal level, one wave's job, with the level-order index of the first
+// node's first child (its first leaf), so the kernel needs no rank query.
+constexpr uint32_t kSegNodes = 64;
 struct Seg {
     uint32_t lo;
     uint32_t count;
+    uint32_t leaf;
+    uint32_t pad;
 };
-static_assert(sizeof(Seg) == 8, "segment layout");
+static_assert(sizeof(Seg) == 16, "segment layout");
 
 // The plan of a matrix: host top level, descent tiles in depth-first order and
 // the codes their first level starts from, and per product direction the
-// tiles of the cached level (a cached tile is 'count' ranges starting at
+// tiles of the cached level (a cached tile is 'count' segments starting at
 // cached_segs[dir][first]).
 struct Plan {
     int top_level = 0;                 // d0
@@ -111,7 +116,6 @@ struct Matrix {
     uint64_t *d_cached = nullptr;        // last internal level codes or null
     uint32_t window_elems = 0, window_batch = 0;
     bool cached = false;
-    bool xcd_remap = true;
     // kernel timing (events created on first enable)
     void *ev[3] = {nullptr, nullptr, nullptr};
     bool timing = false, timed_once = false, last_accumulate = false;

@@ -19,7 +19,9 @@
 //
 // Cached tiles (for the kernel that reads the cached codes of the last
 // internal level, Sec. 3.5) are lists of node ranges of that level, one list
-// per product direction.
+// per product direction, cut into segments of at most 64 nodes (a wave's
+// job) that carry their first leaf's index, which the planner finds with the
+// same directory query the descent uses.
 //
 // Windows.  Every node of a Q x Q quadrant (a node of level h = l - log2 Q)
 // has its rows and its columns inside the quadrant's Q.  A quadrant holding
@@ -65,6 +67,7 @@ struct Planner {
     int last;           // last internal level
     uint64_t cached_C;  // nodes per cached tile without a window
     static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
+    std::vector<uint64_t> tile_weight;            // last-internal-level nodes per descent tile
 
     // Descendant index on level 'to' of boundary 'i' of level d.
     uint64_t down(int d, uint64_t i, int to) const {
@@ -109,43 +112,49 @@ struct Planner {
             tl.level = uint32_t(d);
             tl.code_off = uint32_t(code_base + (i - a));
             p.tiles.push_back(tl);
+            tile_weight.push_back(bound[j - a] - bound[i - a]);
             i = j;
         }
     }
 
+    // Appends the segments of nodes [lo, lo + count) of the last internal level.
+    void push_segs(int dir, uint64_t lo, uint64_t count) {
+        for (uint64_t i = 0; i < count; i += kSegNodes)
+            p.cached_segs[dir].push_back(
+                {uint32_t(lo + i), uint32_t(std::min<uint64_t>(kSegNodes, count - i)), 0u, 0u});
+    }
+
     // Cached tiles of direction dir over nodes [lo, hi) of the last internal
-    // level, no window: one range per tile.
+    // level, no window: cached_C nodes per tile.
     void cached_run(int dir, uint64_t lo, uint64_t hi) {
         for (uint64_t i = lo; i < hi; i += cached_C) {
             Tile tl{};
             tl.first = uint32_t(p.cached_segs[dir].size());
-            tl.count = 1;
             tl.level = uint32_t(last);
             tl.win_log2 = kNoWindow;
-            p.cached_segs[dir].push_back({uint32_t(i), uint32_t(std::min(cached_C, hi - i))});
+            push_segs(dir, i, std::min(cached_C, hi - i));
+            tl.count = uint32_t(p.cached_segs[dir].size() - tl.first);
             p.cached_tiles[dir].push_back(tl);
         }
     }
 
-    // Cached tiles of direction dir over the ranges 'segs' of one band, all
-    // with the band's window; at most kBandCap nodes per tile.
-    void cached_band(int dir, const std::vector<Seg> &segs, const Tile &win) {
+    // Cached tiles of direction dir over the node ranges 'ranges' of one
+    // band, all with the band's window; at most kBandCap nodes per tile.
+    void cached_band(int dir, const std::vector<Seg> &ranges, const Tile &win) {
         Tile tl = win;
         tl.first = uint32_t(p.cached_segs[dir].size());
-        tl.count = 0;
         tl.level = uint32_t(last);
         uint64_t nodes = 0;
         auto close = [&]() {
+            tl.count = uint32_t(p.cached_segs[dir].size() - tl.first);
             if (tl.count) p.cached_tiles[dir].push_back(tl);
             tl.first = uint32_t(p.cached_segs[dir].size());
-            tl.count = 0;
             nodes = 0;
         };
-        for (Seg sg : segs) {
+        for (Seg sg : ranges) {
             while (sg.count > 0) {
                 uint64_t take = std::min<uint64_t>(sg.count, kBandCap - nodes);
-                p.cached_segs[dir].push_back({sg.lo, uint32_t(take)});
-                ++tl.count;
+                push_segs(dir, sg.lo, take);
                 nodes += take;
                 sg.lo += uint32_t(take);
                 sg.count -= uint32_t(take);
@@ -153,6 +162,20 @@ struct Planner {
             }
         }
         close();
+    }
+
+    // First leaf of every segment's first node, in parallel.
+    void set_leaves(int dir) {
+        std::vector<Seg> &sg = p.cached_segs[dir];
+        const size_t n = sg.size();
+        const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+        std::vector<std::thread> pool;
+        for (unsigned k = 0; k < nt; ++k)
+            pool.emplace_back([&, k]() {
+                for (size_t i = n * k / nt; i < n * (k + 1) / nt; ++i)
+                    sg[i].leaf = uint32_t(child_offset(t, last, sg[i].lo));
+            });
+        for (auto &th : pool) th.join();
     }
 };
 
@@ -185,6 +208,41 @@ struct Unit {
     bool dense;
     uint64_t qcode;   // Morton code of the quadrant (dense units)
 };
+
+// Workgroup b of a launch runs on XCD b % 8, and each of the 8 XCDs has its
+// own L2.  Neighbouring tiles in Z order share rows and columns (a row band's
+// tiles gather x from overlapping column windows), so they should run on one
+// XCD.  The tiles of each group [group[g], group[g+1]) are cut into 8 runs of
+// about equal weight; XCD k's list is its run of every group in turn, and
+// list k's j-th tile goes to position 8 j + k.  Shorter lists are padded with
+// empty tiles (count 0), so the length is a multiple of 8.
+void xcd_order(std::vector<Tile> &tiles, const std::vector<uint64_t> &weight,
+               const std::vector<size_t> &group, uint32_t pad_level) {
+    constexpr int kXcds = 8;
+    std::vector<Tile> list[kXcds];
+    for (size_t g = 0; g + 1 < group.size(); ++g) {
+        const size_t a = group[g], b = group[g + 1];
+        uint64_t total = 0;
+        for (size_t i = a; i < b; ++i) total += weight[i];
+        uint64_t acc = 0;
+        for (size_t i = a; i < b; ++i) {
+            // the run whose share of the group's weight holds this tile's middle
+            const uint64_t mid = acc + weight[i] / 2;
+            const int k = total ? int(std::min<uint64_t>(kXcds - 1, mid * kXcds / total)) : 0;
+            list[k].push_back(tiles[i]);
+            acc += weight[i];
+        }
+    }
+    size_t len = 0;
+    for (auto &l : list) len = std::max(len, l.size());
+    Tile pad{};
+    pad.level = pad_level;
+    pad.win_log2 = kNoWindow;
+    std::vector<Tile> out(len * kXcds, pad);
+    for (int k = 0; k < kXcds; ++k)
+        for (size_t j = 0; j < list[k].size(); ++j) out[j * kXcds + size_t(k)] = list[k][j];
+    tiles.swap(out);
+}
 
 }  // namespace
 
@@ -227,9 +285,25 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles: the plain depth-first cut (windowed descent tiles, one
     // per dense quadrant, measured slower: many small tiles)
     pl.range(d0, 0, t.nodes[d0], 0, no_window());
+    if (o.xcd_remap) xcd_order(p.tiles, pl.tile_weight, {0, p.tiles.size()}, uint32_t(last));
+    auto order_cached = [&](int dir, size_t n_band) {
+        pl.set_leaves(dir);
+        if (!o.xcd_remap) return;
+        std::vector<uint64_t> w;
+        for (const Tile &tl : p.cached_tiles[dir]) {
+            uint64_t nodes = 64;   // a tile's fixed cost, in nodes
+            for (uint32_t r = 0; r < tl.count; ++r) nodes += p.cached_segs[dir][tl.first + r].count;
+            nodes += 8 * tl.count;   // a segment's fixed cost
+            w.push_back(nodes);
+        }
+        xcd_order(p.cached_tiles[dir], w, {0, n_band, p.cached_tiles[dir].size()}, uint32_t(last));
+    };
     if (!o.cache_last_level) return K2_OK;
     if (qlog < 0) {
-        for (int dir = 0; dir < 2; ++dir) pl.cached_run(dir, 0, n2);
+        for (int dir = 0; dir < 2; ++dir) {
+            pl.cached_run(dir, 0, n2);
+            order_cached(dir, 0);
+        }
         return K2_OK;
     }
     const int h = std::max(0, L - qlog);            // quadrant level
@@ -341,18 +415,19 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                 ++j;
             }
             if (total >= band_min) {
-                std::vector<Seg> segs;
+                std::vector<Seg> ranges;
                 for (size_t k = i; k < j; ++k) {
                     const Unit &u = units[dense_units[k].second];
                     windowed[dense_units[k].second] = 1;
-                    segs.push_back({uint32_t(u.lo2), uint32_t(u.hi2 - u.lo2)});
+                    ranges.push_back({uint32_t(u.lo2), uint32_t(u.hi2 - u.lo2), 0u, 0u});
                 }
                 Tile w = window_of(units[dense_units[i].second].qcode, h, L);
-                pl.cached_band(dir, segs, w);
+                pl.cached_band(dir, ranges, w);
             }
             i = j;
         }
         // the sparse rest in depth-first order: contiguous runs of level l-2
+        const size_t n_band = p.cached_tiles[dir].size();
         uint64_t run_lo = 0, run_hi = 0;
         bool in_run = false;
         for (size_t i = 0; i < units.size(); ++i) {
@@ -368,6 +443,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
             run_hi = u.hi2;
         }
         if (in_run) pl.cached_run(dir, run_lo, run_hi);
+        order_cached(dir, n_band);
     }
     if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
     return K2_OK;
