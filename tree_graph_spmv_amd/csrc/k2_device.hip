@@ -54,10 +54,11 @@ struct PlusTimes {
     }
     // LDS fp32 add as an integer compare-and-swap: gfx950's ds_add_f32 takes
     // about ten times the cycles of its integer LDS atomics.  The first try
-    // assumes the window's initial +0.0, so a first touch costs one atomic.
+    // uses the value read just before, so it fails only when another lane
+    // changed the word in between.
     __device__ static void lds_atomic(T *p, T v) {
         uint32_t *u = reinterpret_cast<uint32_t *>(p);
-        uint32_t expected = 0u;
+        uint32_t expected = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         while (!__hip_atomic_compare_exchange_strong(u, &expected,
                                                      __float_as_uint(__uint_as_float(expected) + v),
                                                      __ATOMIC_RELAXED, __ATOMIC_RELAXED,
@@ -250,16 +251,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 
 // ------------------------------------------------------------- kernels
 
-// LDS of one wave's leaf segment: the segment's nodes' 4x4-block
-// coordinates and a round of the list of their cells, 2 bytes each:
-// (node << 4) | (4 * row + column) within the node's block.  A node has at
+// LDS of one wave's leaf segment: a round of the list of its cells, each as
+// the element offsets of its input in x (input index * B) and of its output
+// (output index * B in y, or relative to the tile's window).  A node has at
 // most 4 leaves of 4 cells, so a segment has at most 1024 cells; they go
-// through the buffer kCellRound at a time (one round in the common case).
-constexpr uint32_t kCellRound = 256;
+// through the buffer kRound at a time (one round in the common case).  Off is
+// uint32_t when every offset fits, else uint64_t (half as many per round).
+template <class Off>
 struct WaveCells {
-    uint32_t r4[64];
-    uint32_t c4[64];
-    uint16_t cell[kCellRound];
+    static constexpr uint32_t kRound = 512 / sizeof(Off);
+    Off xo[kRound];
+    Off yo[kRound];
 };
 
 constexpr int kUnroll = 4;   // cells whose x loads are issued before their atomics
@@ -274,69 +276,69 @@ struct Window {
 };
 
 // Leaf work of one wave over a segment of up to 64 nodes of the last internal
-// level; lane l holds node l's code, signature s (0: no node) and the leaf
-// signatures lam[b] of its children b (0 where s lacks bit b).  Phase A (a
-// lane per node): list the segment's cells in the wave's LDS at positions
-// from a wave scan of the cell counts.  Phase B (VL adjacent lanes per cell,
-// one per vector): gather x for kUnroll cells, then apply the semiring's
-// atomics, to the LDS window when the tile has one, else to y.  No workgroup
-// barrier.
-template <class SR, int DIR>
-__device__ __forceinline__ void leaf_cells(uint64_t code, const uint32_t (&lam)[4],
+// level; lane l holds node l's Morton code and the cells of its 4x4 block as
+// a 16-bit mask (bit 4 b + q: cell q of the leaf for child b; 0: no node).
+// Phase A (a lane per node): list the segment's cells in the wave's LDS, each
+// as its x and output offsets, at positions from a wave scan of the cell
+// counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
+// kUnroll cells, then apply the semiring's atomics, to the LDS window when
+// the tile has one, else to y.  No workgroup barrier.
+template <class SR, int DIR, class Off>
+__device__ __forceinline__ void leaf_cells(uint64_t code, uint32_t cells,
                                            const typename SR::T *__restrict__ x,
                                            typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                           Window<typename SR::T> w, WaveCells *wc) {
+                                           Window<typename SR::T> w, WaveCells<Off> *wc) {
     using T = typename SR::T;
+    constexpr uint32_t R = WaveCells<Off>::kRound;
     const uint32_t lane = __lane_id();
-    const uint32_t ncell = __popc(lam[0]) + __popc(lam[1]) + __popc(lam[2]) + __popc(lam[3]);
     uint32_t total;
-    const uint32_t pos0 = wave_scan<5>(ncell, total);
-    wc->r4[lane] = compact_even(code >> 1);
-    wc->c4[lane] = compact_even(code);
+    const uint32_t pos0 = wave_scan<5>(__popc(cells), total);
+    const uint32_t row4 = compact_even(code >> 1) * 4u, col4 = compact_even(code) * 4u;
+    const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
     const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
-    for (uint32_t round = 0; round < total; round += kCellRound) {
-        // this lane's cells with list positions in [round, round + kCellRound)
-        uint32_t pos = pos0;
-#pragma unroll
-        for (uint32_t b = 0; b < 4; ++b) {
-#pragma unroll
-            for (uint32_t q = 0; q < 4; ++q)
-                if (lam[b] & (1u << q)) {
-                    if (pos - round < kCellRound) {   // unsigned: false below 'round'
-                        const uint32_t r = 2 * (b >> 1) + (q >> 1), c = 2 * (b & 1) + (q & 1);
-                        wc->cell[pos - round] = uint16_t((lane << 4) | (r << 2) | c);
-                    }
-                    ++pos;
-                }
+    for (uint32_t round = 0; round < total; round += R) {
+        // this lane's cells with list positions in [round, round + R)
+        uint32_t m = cells, pos = pos0;
+        while (m && pos < round + R) {
+            const uint32_t bit = __builtin_ctz(m);
+            m &= m - 1u;
+            if (pos >= round) {
+                const uint32_t b = bit >> 2, q = bit & 3u;
+                const uint32_t r = row4 + 2u * (b >> 1) + (q >> 1);
+                const uint32_t c = col4 + 2u * (b & 1u) + (q & 1u);
+                const uint32_t in = (DIR == K2_RIGHT) ? c : r, out = (DIR == K2_RIGHT) ? r : c;
+                wc->xo[pos - round] = Off(in) * B;
+                wc->yo[pos - round] = Off(out - obase) * B;
+            }
+            ++pos;
         }
         wave_lds_sync();
-        const uint32_t n = (total - round < kCellRound) ? total - round : kCellRound;
+        const uint32_t n = (total - round < R) ? total - round : R;
         for (uint32_t k0 = g; k0 < n; k0 += G * kUnroll) {
-            uint32_t in_i[kUnroll], out_i[kUnroll];
+            // cells past n repeat cell k0 for the loads and skip the atomics
+            Off xo[kUnroll], yo[kUnroll];
+            bool ok[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const uint32_t k = k0 + uint32_t(u) * G;
-                const uint32_t e = (k < n) ? uint32_t(wc->cell[k]) : 0u;
-                const uint32_t r = wc->r4[e >> 4] * 4 + ((e >> 2) & 3u);
-                const uint32_t c = wc->c4[e >> 4] * 4 + (e & 3u);
-                in_i[u] = (DIR == K2_RIGHT) ? c : r;
-                out_i[u] = (DIR == K2_RIGHT) ? r : c;
+                ok[u] = k < n;
+                const uint32_t kk = ok[u] ? k : k0;
+                xo[u] = wc->xo[kk];
+                yo[u] = wc->yo[kk];
             }
             for (uint32_t v = lv; v < B; v += VL) {
                 T xv[kUnroll];
 #pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
-                    xv[u] = (k0 + uint32_t(u) * G < n) ? x[uint64_t(in_i[u]) * B + v] : SR::zero();
+                for (int u = 0; u < kUnroll; ++u) xv[u] = x[xo[u] + v];
                 if (w.win) {
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u)
-                        if (k0 + uint32_t(u) * G < n && SR::contributes(xv[u]))
-                            SR::lds_atomic(&w.win[(uint64_t(out_i[u]) - w.out0) * B + v], SR::contrib(xv[u]));
+                        if (ok[u] && SR::contributes(xv[u]))
+                            SR::lds_atomic(&w.win[yo[u] + v], SR::contrib(xv[u]));
                 } else {
 #pragma unroll
                     for (int u = 0; u < kUnroll; ++u)
-                        if (k0 + uint32_t(u) * G < n && SR::contributes(xv[u]))
-                            SR::atomic(&y[uint64_t(out_i[u]) * B + v], SR::contrib(xv[u]));
+                        if (ok[u] && SR::contributes(xv[u])) SR::atomic(&y[yo[u] + v], SR::contrib(xv[u]));
                 }
             }
         }
@@ -344,19 +346,18 @@ __device__ __forceinline__ void leaf_cells(uint64_t code, const uint32_t (&lam)[
     }
 }
 
-// leaf_cells for a lane whose node's first leaf is leaf-level node 'off'.
-template <class SR, int DIR>
+// leaf_cells for a lane whose node has signature s and first leaf 'off'.
+template <class SR, int DIR, class Off>
 __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
                                              const uint64_t *__restrict__ leaf_words,
                                              const typename SR::T *__restrict__ x,
                                              typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                             Window<typename SR::T> w, WaveCells *wc) {
-    uint32_t lam[4] = {0u, 0u, 0u, 0u};
-    uint32_t j = 0;
+                                             Window<typename SR::T> w, WaveCells<Off> *wc) {
+    uint32_t cells = 0u, j = 0u;
 #pragma unroll
     for (uint32_t b = 0; b < 4; ++b)
-        if (s & (1u << b)) lam[b] = nib(leaf_words, uint64_t(off) + j++);
-    leaf_cells<SR, DIR>(code, lam, x, y, B, VL, w, wc);
+        if (s & (1u << b)) cells |= nib(leaf_words, uint64_t(off) + j++) << (4 * b);
+    leaf_cells<SR, DIR, Off>(code, cells, x, y, B, VL, w, wc);
 }
 
 // The window of tile 'tl' for this product (no window: win = null), its LDS
@@ -458,19 +459,19 @@ __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_
 // works on three of its segments at once: while it visits the leaves of one,
 // the codes and leaf signatures of the next and the signatures of the one
 // after are in flight.
-template <class SR, int DIR>
+template <class SR, int DIR, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
     const uint64_t *__restrict__ codes, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
-    __shared__ WaveCells s_cells[kWaves];
+    __shared__ WaveCells<Off> s_cells[kWaves];
     const int d = t.levels - 2;
     const uint32_t wave = threadIdx.x >> 6;
     const uint64_t *__restrict__ sig_words = t.words[d];
     const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[d + 1]);
-    WaveCells *wc = &s_cells[wave];
+    WaveCells<Off> *wc = &s_cells[wave];
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
@@ -482,15 +483,15 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             const SegSig a2 = stage_sig(segs, tl.first, k + 2 * kWaves, nseg, sig_words);
             const SegLeaves b1 = stage_leaves(a1, codes, leaf_dw);
             const uint32_t s0 = b0.ssh & 15u;
-            const uint64_t bits = ((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u);
-            uint32_t lam[4];
-            uint32_t j = 0;
+            uint64_t bits = ((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u);
+            uint32_t cells = 0u;
 #pragma unroll
-            for (uint32_t b = 0; b < 4; ++b) {
-                lam[b] = (s0 & (1u << b)) ? uint32_t(bits >> (4 * j)) & 15u : 0u;
-                j += (s0 >> b) & 1u;
-            }
-            leaf_cells<SR, DIR>(b0.code, lam, x, y, B, VL, w, wc);
+            for (uint32_t b = 0; b < 4; ++b)
+                if (s0 & (1u << b)) {
+                    cells |= (uint32_t(bits) & 15u) << (4 * b);
+                    bits >>= 4;
+                }
+            leaf_cells<SR, DIR, Off>(b0.code, cells, x, y, B, VL, w, wc);
             b0 = b1;
             a1 = a2;
         }
@@ -502,7 +503,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
 // workgroup takes a tile and expands it level by level inside LDS, then visits
 // the leaves of its last-internal-level nodes in place.  With 'emit' set it
 // writes those nodes' codes instead (building the cached level, Sec. 3.5).
-template <class SR, int DIR, bool EMIT>
+template <class SR, int DIR, bool EMIT, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
     const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
@@ -512,7 +513,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
     __shared__ uint32_t s_val;
-    __shared__ WaveCells s_cells[kWaves];
+    __shared__ WaveCells<Off> s_cells[kWaves];
     const int last = t.levels - 2;
     const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
     T *s_win = reinterpret_cast<T *>(s_front + 2 * size_t(cap));
@@ -564,7 +565,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 const uint32_t base = wave_child_offset(t, last, lo + seg);
                 uint32_t total;
                 const uint32_t ex = wave_scan<3>(__popc(s), total);
-                leaf_segment<SR, DIR>(code, s, base + ex, leaf_words, x, y, B, VL, w, &s_cells[wave]);
+                leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_words, x, y, B, VL, w, &s_cells[wave]);
             }
             close_window<SR>(w, y, n_out, B);
         }
@@ -602,7 +603,12 @@ int set_lds_limit(const void *k, size_t lds) {
     return hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
 }
 
-template <class SR, int DIR>
+// Cell offsets (index * B + vector) fit 32 bits when every index times B does.
+bool narrow_offsets(const Matrix &m, uint32_t B) {
+    return uint64_t(m.n_rows > m.n_cols ? m.n_rows : m.n_cols) * B <= 0xFFFFFFFFull;
+}
+
+template <class SR, int DIR, class Off>
 int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t st) {
     using T = typename SR::T;
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
@@ -612,7 +618,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     int use = 0;
     const size_t lds = window_bytes(m, B, &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
-    auto k = cached_kernel<SR, DIR>;
+    auto k = cached_kernel<SR, DIR, Off>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
@@ -621,7 +627,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     return hipGetLastError();
 }
 
-template <class SR, int DIR, bool EMIT>
+template <class SR, int DIR, bool EMIT, class Off = uint32_t>
 int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *emit,
                 hipStream_t st) {
     using T = typename SR::T;
@@ -634,7 +640,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     const uint32_t VL = lanes_per_node(B);
     const uint32_t grid = grid_for(n_tiles);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
-    auto k = descent_kernel<SR, DIR, EMIT>;
+    auto k = descent_kernel<SR, DIR, EMIT, Off>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_tiles, n_tiles, m.d_codes,
@@ -646,10 +652,14 @@ template <int DIR>
 int dispatch_cached(const Matrix &m, int semiring, uint32_t B, const void *x, void *y,
                     hipStream_t st) {
     switch (semiring) {
-    case K2_PLUS_TIMES_F32: return run_cached<PlusTimes, DIR>(m, B, x, y, st);
-    case K2_BOOLEAN_F32: return run_cached<BooleanF32, DIR>(m, B, x, y, st);
-    case K2_BOOLEAN_U32X32: return run_cached<BooleanU32, DIR>(m, B, x, y, st);
-    case K2_TROPICAL_F32: return run_cached<Tropical, DIR>(m, B, x, y, st);
+    case K2_PLUS_TIMES_F32: return narrow_offsets(m, B) ? run_cached<PlusTimes, DIR, uint32_t>(m, B, x, y, st)
+                                                         : run_cached<PlusTimes, DIR, uint64_t>(m, B, x, y, st);
+    case K2_BOOLEAN_F32: return narrow_offsets(m, B) ? run_cached<BooleanF32, DIR, uint32_t>(m, B, x, y, st)
+                                                         : run_cached<BooleanF32, DIR, uint64_t>(m, B, x, y, st);
+    case K2_BOOLEAN_U32X32: return narrow_offsets(m, B) ? run_cached<BooleanU32, DIR, uint32_t>(m, B, x, y, st)
+                                                         : run_cached<BooleanU32, DIR, uint64_t>(m, B, x, y, st);
+    case K2_TROPICAL_F32: return narrow_offsets(m, B) ? run_cached<Tropical, DIR, uint32_t>(m, B, x, y, st)
+                                                         : run_cached<Tropical, DIR, uint64_t>(m, B, x, y, st);
     }
     return hipErrorInvalidValue;
 }
@@ -658,10 +668,18 @@ template <int DIR>
 int dispatch_descent(const Matrix &m, int semiring, uint32_t B, const void *x, void *y,
                      hipStream_t st) {
     switch (semiring) {
-    case K2_PLUS_TIMES_F32: return run_descent<PlusTimes, DIR, false>(m, B, x, y, nullptr, st);
-    case K2_BOOLEAN_F32: return run_descent<BooleanF32, DIR, false>(m, B, x, y, nullptr, st);
-    case K2_BOOLEAN_U32X32: return run_descent<BooleanU32, DIR, false>(m, B, x, y, nullptr, st);
-    case K2_TROPICAL_F32: return run_descent<Tropical, DIR, false>(m, B, x, y, nullptr, st);
+    case K2_PLUS_TIMES_F32: return narrow_offsets(m, B)
+                   ? run_descent<PlusTimes, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
+                   : run_descent<PlusTimes, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+    case K2_BOOLEAN_F32: return narrow_offsets(m, B)
+                   ? run_descent<BooleanF32, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
+                   : run_descent<BooleanF32, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+    case K2_BOOLEAN_U32X32: return narrow_offsets(m, B)
+                   ? run_descent<BooleanU32, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
+                   : run_descent<BooleanU32, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+    case K2_TROPICAL_F32: return narrow_offsets(m, B)
+                   ? run_descent<Tropical, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
+                   : run_descent<Tropical, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
     }
     return hipErrorInvalidValue;
 }
