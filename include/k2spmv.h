@@ -84,8 +84,9 @@ typedef struct {
        at most host_top_max nodes (never below the last internal level).
        Default 65536. */
     uint32_t host_top_max;
-    /* Keep the Morton codes of the last internal level on the device, 8 bytes
-       per node (Sec. 3.5, "k2+F").  Default 0. */
+    /* Keep the last internal level's nodes on the device, 8 bytes per node
+       (Sec. 3.5, "k2+F"; stored as the block coordinates their Morton codes
+       encode).  Default 0. */
     int32_t cache_last_level;
     /* Tile order for the MI355X's 8 XCDs (each with its own L2; workgroup b
        runs on XCD b % 8): 1 gives each XCD a contiguous run of the Z order,
@@ -238,11 +239,13 @@ k2_status k2_matrix_info(const k2_matrix *matrix, uint32_t *top_level, uint64_t 
 k2_status k2_matrix_level_words(const k2_matrix *matrix, uint32_t level, uint64_t *words,
                                 uint64_t n_words, void *stream);
 
-/* Copy the cached last-internal-level codes back to the host (synchronous),
-   codes[i] = Morton code of node i of level l-2 (row bit above column bit
-   at every level).  Errors: K2_E_INVALID_ARG if not cached. */
-k2_status k2_matrix_cached_codes(const k2_matrix *matrix, uint64_t *codes, uint64_t n_codes,
-                                 void *stream);
+/* Copy the cached last internal level back to the host (synchronous):
+   blocks[i] = (first row << 32) | first column of the 4x4 block of node i of
+   level l-2, the coordinates its Morton code encodes (Sec. 3.5 keeps that
+   level's codes; the device keeps them decoded, 8 bytes either way).
+   Errors: K2_E_INVALID_ARG if not cached or n_blocks is too small. */
+k2_status k2_matrix_cached_blocks(const k2_matrix *matrix, uint64_t *blocks, uint64_t n_blocks,
+                                  void *stream);
 
 const char *k2_status_string(k2_status status);
 

@@ -96,9 +96,10 @@ def test_rmat_s12_e32k(dev):
             label="rmat_s12_e32k")
 
 
-def test_device_tree_and_cached_codes(dev):
+def test_device_tree_and_cached_blocks(dev):
     """The device copy of every level equals the canonical export, and the
-    cached codes of the last internal level are the nodes' Morton codes."""
+    cached last internal level holds each node's block origin, decoded from
+    the Morton code the oracle's signatures give it."""
     import tree_graph_spmv_amd as k2
     rows, cols = synth.rmat(14, 100000, seed=9)
     n = 2 ** 14
@@ -118,8 +119,13 @@ def test_device_tree_and_cached_codes(dev):
                 if s >> b & 1:
                     nxt.append((int(codes[i]) << 2) | b)
         codes = np.array(nxt, np.uint64)
-    got = m.cached_codes(nodes[tree.levels - 2])
-    assert np.array_equal(got, codes)
+    got = m.cached_blocks(nodes[tree.levels - 2])
+    row = np.zeros(codes.size, np.uint64)
+    col = np.zeros(codes.size, np.uint64)
+    for k in range(tree.levels - 2):   # bit 2k + 1 of a code is a row bit, 2k a column bit
+        row |= ((codes >> np.uint64(2 * k + 1)) & np.uint64(1)) << np.uint64(k)
+        col |= ((codes >> np.uint64(2 * k)) & np.uint64(1)) << np.uint64(k)
+    assert np.array_equal(got, ((row * np.uint64(4)) << np.uint64(32)) | (col * np.uint64(4)))
 
 
 def test_web_n20_d16(dev):

@@ -88,7 +88,7 @@ _SIGS = {
     "k2_matrix_destroy": (ctypes.c_int, [_VP]),
     "k2_matrix_info": (ctypes.c_int, [_VP, _U32P, _U64P, ctypes.POINTER(ctypes.c_int32)]),
     "k2_matrix_level_words": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P, ctypes.c_uint64, _VP]),
-    "k2_matrix_cached_codes": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
+    "k2_matrix_cached_blocks": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
     "k2_matrix_set_timing": (ctypes.c_int, [_VP, ctypes.c_int32]),
     "k2_matrix_last_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_float),
                                              ctypes.POINTER(ctypes.c_float)]),
@@ -298,8 +298,9 @@ class Matrix:
                                            _stream_handle(stream)), "k2_matrix_level_words")
         return out
 
-    def cached_codes(self, n_nodes, stream=None):
+    def cached_blocks(self, n_nodes, stream=None):
+        """(first row << 32) | first column of each cached node's 4x4 block."""
         out = np.zeros(max(n_nodes, 1), np.uint64)
-        _check(lib().k2_matrix_cached_codes(self._h, out.ctypes.data_as(_U64P), n_nodes,
-                                            _stream_handle(stream)), "k2_matrix_cached_codes")
+        _check(lib().k2_matrix_cached_blocks(self._h, out.ctypes.data_as(_U64P), n_nodes,
+                                             _stream_handle(stream)), "k2_matrix_cached_blocks")
         return out[:n_nodes]

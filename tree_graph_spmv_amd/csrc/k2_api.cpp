@@ -459,16 +459,16 @@ k2_status k2_matrix_level_words(const k2_matrix *matrix, uint32_t level, uint64_
     return K2_OK;
 }
 
-k2_status k2_matrix_cached_codes(const k2_matrix *matrix, uint64_t *codes, uint64_t n_codes,
-                                 void *stream) {
-    if (!matrix || !codes) return K2_E_INVALID_ARG;
+k2_status k2_matrix_cached_blocks(const k2_matrix *matrix, uint64_t *blocks, uint64_t n_blocks,
+                                  void *stream) {
+    if (!matrix || !blocks) return K2_E_INVALID_ARG;
     const Matrix &m = matrix->m;
     if (!m.cached) return K2_E_INVALID_ARG;
     const uint64_t n = m.nodes[m.levels - 2];
-    if (n_codes < n) return K2_E_INVALID_ARG;
+    if (n_blocks < n) return K2_E_INVALID_ARG;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    HIP_TRY(hipMemcpyAsync(codes, m.d_cached, n * 8, hipMemcpyDeviceToHost, st), "read codes");
-    HIP_TRY(hipStreamSynchronize(st), "read codes");
+    HIP_TRY(hipMemcpyAsync(blocks, m.d_cached, n * 8, hipMemcpyDeviceToHost, st), "read blocks");
+    HIP_TRY(hipStreamSynchronize(st), "read blocks");
     return K2_OK;
 }
 

@@ -144,22 +144,34 @@ __device__ __forceinline__ uint32_t compact_even(uint64_t x) {
     return uint32_t(x);
 }
 
-// Exclusive prefix sum over the workgroup of values f < 2^BITS: one ballot per
-// bit of f and the popcount of the lanes below give the wave's prefix; the
-// four wave totals meet in LDS.
-template <int BITS>
+// Inclusive prefix sum over the 64 lanes of a wave: four shifts within each
+// row of 16 lanes (lanes shifted in from outside the row add 0), then row
+// 0's total is added to row 1 and row 2's to row 3 (broadcast of lane 15),
+// then lane 31's sum of rows 0-1 to rows 2 and 3 (broadcast of lane 31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x111, 0xf, 0xf, true));    // row_shr:1
+    v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x112, 0xf, 0xf, true));    // row_shr:2
+    v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x114, 0xf, 0xf, true));    // row_shr:4
+    v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x118, 0xf, 0xf, true));    // row_shr:8
+    v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x142, 0xa, 0xf, false));   // row_bcast:15
+    v += uint32_t(__builtin_amdgcn_update_dpp(0, int(v), 0x143, 0xc, 0xf, false));   // row_bcast:31
+    return v;
+}
+
+// Exclusive prefix sum of f over the wave, and the wave's total.
+__device__ __forceinline__ uint32_t wave_scan(uint32_t f, uint32_t &total) {
+    const uint32_t incl = wave_incl_scan(f);
+    total = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+    return incl - f;
+}
+
+// Exclusive prefix sum of f over the workgroup: wave scans, then the four
+// wave totals meet in LDS.
 __device__ __forceinline__ uint32_t block_scan(uint32_t f, uint32_t *s_tot, uint32_t &total) {
-    const unsigned lane = __lane_id();
     const unsigned wave = threadIdx.x >> 6;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint32_t ex = 0, wt = 0;
-#pragma unroll
-    for (int k = 0; k < BITS; ++k) {
-        const uint64_t b = __ballot((f >> k) & 1u);
-        ex += uint32_t(__popcll(b & below)) << k;
-        wt += uint32_t(__popcll(b)) << k;
-    }
-    if (lane == 0) s_tot[wave] = wt;
+    uint32_t wt;
+    const uint32_t ex = wave_scan(f, wt);
+    if (__lane_id() == 0) s_tot[wave] = wt;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
@@ -200,23 +212,6 @@ __device__ __forceinline__ uint32_t block_child_offset(const DevTree &t, int d, 
     const uint32_t r = *s_val;
     __syncthreads();
     return r;
-}
-
-// Exclusive prefix sum over the wave of values f < 2^BITS (no LDS): one
-// ballot per bit of f, popcounts of the lanes below.
-template <int BITS>
-__device__ __forceinline__ uint32_t wave_scan(uint32_t f, uint32_t &total) {
-    const unsigned lane = __lane_id();
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    uint32_t ex = 0, tot = 0;
-#pragma unroll
-    for (int k = 0; k < BITS; ++k) {
-        const uint64_t b = __ballot((f >> k) & 1u);
-        ex += uint32_t(__popcll(b & below)) << k;
-        tot += uint32_t(__popcll(b)) << k;
-    }
-    total = tot;
-    return ex;
 }
 
 // Offset in level d+1 of the first child of node i of level d (i < nodes[d]),
@@ -275,16 +270,32 @@ struct Window {
     uint32_t rows;
 };
 
+// Row and column offsets within a node's 4x4 block of cell q of the leaf for
+// child b, at bits 2 (4 b + q) of these words: b = 2 b1 + b0 and q = 2 q1 +
+// q0 give row 2 b1 + q1 and column 2 b0 + q0.
+constexpr uint32_t cell_offset_table(bool row) {
+    uint32_t t = 0;
+    for (uint32_t bit = 0; bit < 16; ++bit) {
+        const uint32_t b = bit >> 2, q = bit & 3u;
+        const uint32_t v = row ? 2u * (b >> 1) + (q >> 1) : 2u * (b & 1u) + (q & 1u);
+        t |= v << (2 * bit);
+    }
+    return t;
+}
+constexpr uint32_t kCellRowTable = cell_offset_table(true);
+constexpr uint32_t kCellColTable = cell_offset_table(false);
+
 // Leaf work of one wave over a segment of up to 64 nodes of the last internal
-// level; lane l holds node l's Morton code and the cells of its 4x4 block as
-// a 16-bit mask (bit 4 b + q: cell q of the leaf for child b; 0: no node).
+// level; lane l holds the first row and column of node l's 4x4 block and its
+// cells as a 16-bit mask (bit 4 b + q: cell q of the leaf for child b; 0: no
+// node).
 // Phase A (a lane per node): list the segment's cells in the wave's LDS, each
 // as its x and output offsets, at positions from a wave scan of the cell
 // counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
 // kUnroll cells, then apply the semiring's atomics, to the LDS window when
 // the tile has one, else to y.  No workgroup barrier.
 template <class SR, int DIR, class Off>
-__device__ __forceinline__ void leaf_cells(uint64_t code, uint32_t cells,
+__device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_t cells,
                                            const typename SR::T *__restrict__ x,
                                            typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
                                            Window<typename SR::T> w, WaveCells<Off> *wc) {
@@ -292,23 +303,23 @@ __device__ __forceinline__ void leaf_cells(uint64_t code, uint32_t cells,
     constexpr uint32_t R = WaveCells<Off>::kRound;
     const uint32_t lane = __lane_id();
     uint32_t total;
-    const uint32_t pos0 = wave_scan<5>(__popc(cells), total);
-    const uint32_t row4 = compact_even(code >> 1) * 4u, col4 = compact_even(code) * 4u;
+    const uint32_t pos0 = wave_scan(__popc(cells), total);
     const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
+    // offsets of the block's first cell; a cell adds its in-block offset * B
+    const Off xb = Off((DIR == K2_RIGHT) ? col0 : row0) * B;
+    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * B;
+    constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
+    constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
     const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
     for (uint32_t round = 0; round < total; round += R) {
         // this lane's cells with list positions in [round, round + R)
         uint32_t m = cells, pos = pos0;
         while (m && pos < round + R) {
-            const uint32_t bit = __builtin_ctz(m);
+            const uint32_t sh = 2u * uint32_t(__builtin_ctz(m));
             m &= m - 1u;
             if (pos >= round) {
-                const uint32_t b = bit >> 2, q = bit & 3u;
-                const uint32_t r = row4 + 2u * (b >> 1) + (q >> 1);
-                const uint32_t c = col4 + 2u * (b & 1u) + (q & 1u);
-                const uint32_t in = (DIR == K2_RIGHT) ? c : r, out = (DIR == K2_RIGHT) ? r : c;
-                wc->xo[pos - round] = Off(in) * B;
-                wc->yo[pos - round] = Off(out - obase) * B;
+                wc->xo[pos - round] = xb + __umul24((kInTable >> sh) & 3u, B);
+                wc->yo[pos - round] = yb + __umul24((kOutTable >> sh) & 3u, B);
             }
             ++pos;
         }
@@ -346,7 +357,8 @@ __device__ __forceinline__ void leaf_cells(uint64_t code, uint32_t cells,
     }
 }
 
-// leaf_cells for a lane whose node has signature s and first leaf 'off'.
+// leaf_cells for a lane whose node has Morton code 'code', signature s and
+// first leaf 'off'.
 template <class SR, int DIR, class Off>
 __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
                                              const uint64_t *__restrict__ leaf_words,
@@ -357,7 +369,8 @@ __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t
 #pragma unroll
     for (uint32_t b = 0; b < 4; ++b)
         if (s & (1u << b)) cells |= nib(leaf_words, uint64_t(off) + j++) << (4 * b);
-    leaf_cells<SR, DIR, Off>(code, cells, x, y, B, VL, w, wc);
+    leaf_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u, cells, x, y, B,
+                             VL, w, wc);
 }
 
 // The window of tile 'tl' for this product (no window: win = null), its LDS
@@ -412,11 +425,12 @@ struct SegSig {
     uint32_t lo, count, leaf;   // uniform; count = 0 past the wave's last segment
     uint32_t s;                 // the lane's node signature, 0 outside the segment
 };
-// Stage 2, issued one segment ahead: the lane's code, and its signature s
-// and first-leaf nibble position p packed as s | p << 6, and the two
-// leaf-level dwords that hold its leaf signatures (from nibble p of lo32).
+// Stage 2, issued one segment ahead: the lane's node's block origin (first
+// row << 32 | first column), its signature s and first-leaf nibble position
+// p packed as s | p << 6, and the two leaf-level dwords that hold its leaf
+// signatures (from nibble p of lo32).
 struct SegLeaves {
-    uint64_t code;
+    uint64_t blk;
     uint32_t ssh, lo32, hi32;
 };
 
@@ -438,12 +452,12 @@ __device__ __forceinline__ SegSig stage_sig(const Seg *__restrict__ segs, uint32
 // lanes before it (a wave scan).  A node's at most 4 leaf nibbles start at
 // nibble off % 8 of dword off / 8 and reach into the next dword only if
 // off % 8 + fan-out > 8, which is the only case that reads it.
-__device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_t *__restrict__ codes,
+__device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_t *__restrict__ blocks,
                                                   const uint32_t *__restrict__ leaf_dw) {
     SegLeaves b{0ull, a.s, 0u, 0u};
     uint32_t total;
-    const uint32_t ex = wave_scan<3>(__popc(a.s), total);
-    if (__lane_id() < a.count) b.code = codes[a.lo + __lane_id()];
+    const uint32_t ex = wave_scan(__popc(a.s), total);
+    if (__lane_id() < a.count) b.blk = blocks[a.lo + __lane_id()];
     if (a.s) {
         const uint32_t off = a.leaf + ex;
         b.ssh = a.s | ((off & 7u) << 6);
@@ -462,7 +476,7 @@ __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_
 template <class SR, int DIR, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
-    const uint64_t *__restrict__ codes, const typename SR::T *__restrict__ x,
+    const uint64_t *__restrict__ blocks, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
@@ -478,20 +492,21 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
         const uint32_t nseg = tl.count;
         uint32_t k = wave;
         SegSig a1 = stage_sig(segs, tl.first, k + kWaves, nseg, sig_words);
-        SegLeaves b0 = stage_leaves(stage_sig(segs, tl.first, k, nseg, sig_words), codes, leaf_dw);
+        SegLeaves b0 = stage_leaves(stage_sig(segs, tl.first, k, nseg, sig_words), blocks, leaf_dw);
         for (; k < nseg; k += kWaves) {
             const SegSig a2 = stage_sig(segs, tl.first, k + 2 * kWaves, nseg, sig_words);
-            const SegLeaves b1 = stage_leaves(a1, codes, leaf_dw);
+            const SegLeaves b1 = stage_leaves(a1, blocks, leaf_dw);
+            // the node's leaf nibbles are the low 4 * fan-out bits of 'bits'
             const uint32_t s0 = b0.ssh & 15u;
-            uint64_t bits = ((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u);
+            uint32_t bits = uint32_t(((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u));
             uint32_t cells = 0u;
 #pragma unroll
             for (uint32_t b = 0; b < 4; ++b)
                 if (s0 & (1u << b)) {
-                    cells |= (uint32_t(bits) & 15u) << (4 * b);
+                    cells |= (bits & 15u) << (4 * b);
                     bits >>= 4;
                 }
-            leaf_cells<SR, DIR, Off>(b0.code, cells, x, y, B, VL, w, wc);
+            leaf_cells<SR, DIR, Off>(uint32_t(b0.blk >> 32), uint32_t(b0.blk), cells, x, y, B, VL, w, wc);
             b0 = b1;
             a1 = a2;
         }
@@ -502,7 +517,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
 // One product by tiled descent (Algorithm 1 with the tiles of Sec. 3.4): each
 // workgroup takes a tile and expands it level by level inside LDS, then visits
 // the leaves of its last-internal-level nodes in place.  With 'emit' set it
-// writes those nodes' codes instead (building the cached level, Sec. 3.5).
+// writes those nodes' block origins instead (building the cached level,
+// Sec. 3.5).
 template <class SR, int DIR, bool EMIT, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
@@ -533,7 +549,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 const bool valid = i < cnt;
                 const uint32_t s = valid ? nib(wd, uint64_t(lo) + i) : 0u;
                 uint32_t total;
-                const uint32_t ex = block_scan<3>(__popc(s), s_tot, total);
+                const uint32_t ex = block_scan(__popc(s), s_tot, total);
                 if (s) {
                     const uint64_t c2 = cur[i] << 2;
                     uint32_t p = running + ex;
@@ -552,7 +568,9 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
             ++d;
         }
         if (EMIT) {
-            for (uint32_t i = threadIdx.x; i < cnt; i += kThreads) emit[uint64_t(lo) + i] = cur[i];
+            for (uint32_t i = threadIdx.x; i < cnt; i += kThreads)
+                emit[uint64_t(lo) + i] = (uint64_t(compact_even(cur[i] >> 1) * 4u) << 32) |
+                                         (compact_even(cur[i]) * 4u);
         } else {
             const Window<T> w = open_window<SR, DIR>(tl, s_win, use_window, B);
             const uint64_t *__restrict__ wd = t.words[last];
@@ -564,7 +582,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 const uint64_t code = valid ? cur[i] : 0ull;
                 const uint32_t base = wave_child_offset(t, last, lo + seg);
                 uint32_t total;
-                const uint32_t ex = wave_scan<3>(__popc(s), total);
+                const uint32_t ex = wave_scan(__popc(s), total);
                 leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_words, x, y, B, VL, w, &s_cells[wave]);
             }
             close_window<SR>(w, y, n_out, B);
