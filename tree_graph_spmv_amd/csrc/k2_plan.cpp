@@ -67,6 +67,7 @@ struct Planner {
     int last;           // last internal level
     uint64_t cached_C;  // nodes per cached tile without a window
     static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
+    static constexpr uint64_t kSparseTile = 2048; // nodes per sparse cached tile beside bands
     std::vector<uint64_t> tile_weight;            // last-internal-level nodes per descent tile
 
     // Descendant index on level 'to' of boundary 'i' of level d.
@@ -125,14 +126,15 @@ struct Planner {
     }
 
     // Cached tiles of direction dir over nodes [lo, hi) of the last internal
-    // level, no window: cached_C nodes per tile.
-    void cached_run(int dir, uint64_t lo, uint64_t hi) {
-        for (uint64_t i = lo; i < hi; i += cached_C) {
+    // level, no window: 'per' nodes per tile (cached_C if 0).
+    void cached_run(int dir, uint64_t lo, uint64_t hi, uint64_t per = 0) {
+        if (!per) per = cached_C;
+        for (uint64_t i = lo; i < hi; i += per) {
             Tile tl{};
             tl.first = uint32_t(p.cached_segs[dir].size());
             tl.level = uint32_t(last);
             tl.win_log2 = kNoWindow;
-            push_segs(dir, i, std::min(cached_C, hi - i));
+            push_segs(dir, i, std::min(per, hi - i));
             tl.count = uint32_t(p.cached_segs[dir].size() - tl.first);
             p.cached_tiles[dir].push_back(tl);
         }
@@ -392,9 +394,20 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         }
     }
 
-    // ---- cached tiles, per direction: windowed bands, then the sparse rest
+    // ---- cached tiles, per direction: windowed bands and the sparse rest,
+    // merged in order of output blocks of 2^kb rows (right products) or
+    // columns (left), about 32 MB of y each at window_batch vectors.  The
+    // tiles in flight then update one narrow slice of y, whose lines the
+    // chip's last-level cache can hold while their atomics arrive.
     const uint64_t band_min = std::max<uint64_t>(64, side * o.window_batch / 32);
+    int kb = L - h;
+    while (kb < 30 && (2ull << kb) * o.window_batch * 4 <= (32ull << 20)) ++kb;
     for (int dir = 0; dir < 2; ++dir) {
+        // output coordinate of a quadrant's first cell
+        auto out_of = [&](uint64_t code, int level) -> uint64_t {
+            const uint64_t c = dir == K2_RIGHT ? even_bits(code >> 1) : even_bits(code);
+            return c << (L - level);
+        };
         // band of each dense unit: its row band (right) or column band (left)
         std::vector<std::pair<uint64_t, uint32_t>> dense_units;   // (band, unit index)
         for (size_t i = 0; i < units.size(); ++i)
@@ -406,6 +419,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         std::stable_sort(dense_units.begin(), dense_units.end(),
                          [](const auto &x, const auto &y) { return x.first < y.first; });
         std::vector<char> windowed(units.size(), 0);
+        std::vector<std::pair<uint64_t, Tile>> keyed;   // (output block, tile)
         for (size_t i = 0; i < dense_units.size();) {
             size_t j = i;
             uint64_t total = 0;
@@ -422,28 +436,43 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                     ranges.push_back({uint32_t(u.lo2), uint32_t(u.hi2 - u.lo2), 0u, 0u});
                 }
                 Tile w = window_of(units[dense_units[i].second].qcode, h, L);
+                const size_t t0 = p.cached_tiles[dir].size();
                 pl.cached_band(dir, ranges, w);
+                const uint64_t key = (dense_units[i].first << (L - h)) >> kb;
+                for (size_t t = t0; t < p.cached_tiles[dir].size(); ++t) keyed.push_back({key, p.cached_tiles[dir][t]});
+                p.cached_tiles[dir].resize(t0);
             }
             i = j;
         }
         // the sparse rest in depth-first order: contiguous runs of level l-2
-        const size_t n_band = p.cached_tiles[dir].size();
-        uint64_t run_lo = 0, run_hi = 0;
+        // within one output block
+        uint64_t run_lo = 0, run_hi = 0, run_key = 0;
         bool in_run = false;
+        auto flush = [&]() {
+            const size_t t0 = p.cached_tiles[dir].size();
+            pl.cached_run(dir, run_lo, run_hi, Planner::kSparseTile);
+            for (size_t t = t0; t < p.cached_tiles[dir].size(); ++t) keyed.push_back({run_key, p.cached_tiles[dir][t]});
+            p.cached_tiles[dir].resize(t0);
+        };
         for (size_t i = 0; i < units.size(); ++i) {
             if (windowed[i]) continue;
             const Unit &u = units[i];
-            if (in_run && u.lo2 == run_hi) {
+            const uint64_t key = out_of(ucodes[u.code_idx], u.level) >> kb;
+            if (in_run && u.lo2 == run_hi && key == run_key) {
                 run_hi = u.hi2;
                 continue;
             }
-            if (in_run) pl.cached_run(dir, run_lo, run_hi);
+            if (in_run) flush();
             in_run = true;
             run_lo = u.lo2;
             run_hi = u.hi2;
+            run_key = key;
         }
-        if (in_run) pl.cached_run(dir, run_lo, run_hi);
-        order_cached(dir, n_band);
+        if (in_run) flush();
+        std::stable_sort(keyed.begin(), keyed.end(),
+                         [](const auto &x, const auto &y) { return x.first < y.first; });
+        for (const auto &kt : keyed) p.cached_tiles[dir].push_back(kt.second);
+        order_cached(dir, p.cached_tiles[dir].size());
     }
     if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
     return K2_OK;
