@@ -67,7 +67,7 @@ struct Planner {
     int last;           // last internal level
     uint64_t cached_C;  // nodes per cached tile without a window
     static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
-    static constexpr uint64_t kSparseTile = 2048; // nodes per sparse cached tile beside bands
+    static constexpr uint64_t kSparseTile = 8192; // nodes per sparse cached tile beside bands
     std::vector<uint64_t> tile_weight;            // last-internal-level nodes per descent tile
 
     // Descendant index on level 'to' of boundary 'i' of level d.
@@ -396,12 +396,12 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
 
     // ---- cached tiles, per direction: windowed bands and the sparse rest,
     // merged in order of output blocks of 2^kb rows (right products) or
-    // columns (left), about 32 MB of y each at window_batch vectors.  The
+    // columns (left), about 16 MB of y each at window_batch vectors.  The
     // tiles in flight then update one narrow slice of y, whose lines the
     // chip's last-level cache can hold while their atomics arrive.
     const uint64_t band_min = std::max<uint64_t>(64, side * o.window_batch / 32);
     int kb = L - h;
-    while (kb < 30 && (2ull << kb) * o.window_batch * 4 <= (32ull << 20)) ++kb;
+    while (kb < 30 && (2ull << kb) * o.window_batch * 4 <= (16ull << 20)) ++kb;
     for (int dir = 0; dir < 2; ++dir) {
         // output coordinate of a quadrant's first cell
         auto out_of = [&](uint64_t code, int level) -> uint64_t {
