@@ -46,9 +46,13 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """Hash of the sources that decide the main kernel's memory traffic: the
+    device code and the tile planner (tile order changes what the caches
+    catch)."""
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "tree_graph_spmv_amd", "csrc", "k2_device.hip"), "rb") as f:
-        h.update(f.read())
+    for name in ("k2_device.hip", "k2_plan.cpp"):
+        with open(os.path.join(ROOT, "tree_graph_spmv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
