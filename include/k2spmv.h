@@ -88,12 +88,15 @@ typedef struct {
        (Sec. 3.5, "k2+F"; stored as the block coordinates their Morton codes
        encode).  Default 0. */
     int32_t cache_last_level;
-    /* Tile order for the MI355X's 8 XCDs (each with its own L2; workgroup b
-       runs on XCD b % 8): 1 gives each XCD a contiguous run of the Z order,
-       of about equal work, by placing run k's tiles at positions k, k + 8,
-       ...; 0 keeps the Z order, which spreads neighbouring tiles over all
-       XCDs.  Padding tiles (count 0) make the lists equal in length.
-       Default 0. */
+    /* Order of the cached-level tiles for the MI355X's 8 XCDs (each with
+       its own L2; workgroup b runs on XCD b % 8).  The tiles are kept in
+       order of output blocks (about 16 MB of y each); with 1, the band tiles
+       of a block and its sparse tiles are each cut into 8 runs of about
+       equal work and run k goes to positions k, k + 8, ..., so each XCD
+       takes neighbouring bands (their shared x columns in its own L2) while
+       all XCDs stay in one block of y.  Padding tiles (count 0) even out
+       the lists.  0 keeps the block order.  Descent tiles keep their Z
+       order either way.  Default 1. */
     int32_t xcd_remap;
     /* Output windows for products over the cached level: Q is the largest
        power of 2 with Q * window_batch <= window_elems (at most 16384

@@ -73,24 +73,19 @@ def oracle_codes(o, upto):
     return codes
 
 
-def check_xcd_order(ordered, plain, band_count):
-    """An XCD-ordered tile list is the plain list's tiles, regrouped: the tiles
-    at positions k, k + 8, ... (XCD k) are a contiguous run of each group of
-    the plain list (the first band_count tiles, then the rest), and the runs
-    of XCD 0..7 follow each other; every other entry is padding (count 0)."""
+def check_xcd_order(ordered, plain):
+    """An XCD-ordered tile list holds the plain list's tiles once each; the
+    tiles at positions k, k + 8, ... (XCD k) keep the plain order; every
+    other entry is padding (count 0)."""
     assert len(ordered) % 8 == 0
-    lists = [[tuple(int(v) for v in tl) for tl in ordered[k::8] if int(tl[1])] for k in range(8)]
-    plain = [tuple(int(v) for v in tl) for tl in plain]
-    assert sum(len(x) for x in lists) == len(plain)
-    groups = [plain[:band_count], plain[band_count:]]
-    first_group = set(groups[0])
-    rebuilt = [[], []]
-    for lst in lists:
-        nb = sum(1 for tl in lst if tl in first_group)
-        assert all(tl in first_group for tl in lst[:nb]), "a run of the first group comes first"
-        rebuilt[0] += lst[:nb]
-        rebuilt[1] += lst[nb:]
-    assert rebuilt[0] == groups[0] and rebuilt[1] == groups[1]
+    index = {tuple(int(v) for v in tl): i for i, tl in enumerate(plain)}
+    assert len(index) == len(plain)
+    seen = []
+    for k in range(8):
+        pos = [index[tuple(int(v) for v in tl)] for tl in ordered[k::8] if int(tl[1])]
+        assert pos == sorted(pos), "an XCD's tiles keep the plain order"
+        seen += pos
+    assert sorted(seen) == list(range(len(plain)))
 
 
 def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
@@ -127,9 +122,7 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
     spans = []
     for tl in tiles:
         first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
-        if count == 0:   # padding of an XCD-ordered list
-            assert opts.xcd_remap and level == last
-            continue
+        assert count >= 1, "descent tiles are never padded"
         assert top <= level <= last
         a, b = down(level, first), down(level, first + count)
         assert b - a <= opts.tile_nodes
@@ -141,8 +134,7 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
             rr, cc = cells_of(a, b)
             assert np.all((rr >= tl[4]) & (rr < tl[4] + side)), "cell row outside window"
             assert np.all((cc >= tl[5]) & (cc < tl[5] + side)), "cell column outside window"
-    if not opts.xcd_remap:
-        assert spans == sorted(spans), "descent tiles must follow each other in Z order"
+    assert spans == sorted(spans), "descent tiles must follow each other in Z order"
     pos = 0
     for a, b in sorted(spans):
         assert a == pos, "descent tiles must cover the last internal level exactly once"
@@ -180,7 +172,7 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
 
 @pytest.mark.parametrize("opt", [
     dict(),
-    dict(xcd_remap=1),
+    dict(xcd_remap=0),
     dict(xcd_remap=1, window_elems=0),
     dict(window_elems=8192),
     dict(tile_nodes=256, window_elems=1024, window_batch=1),
@@ -204,10 +196,10 @@ def test_plan_invariants(case, opt):
                all_codes)
     if opts.xcd_remap:
         plain = k2.plan_defaults(cache_last_level=1, **dict(opt, xcd_remap=0))
-        check_xcd_order(tiles, t.plan(plain, 0)[1], len(t.plan(plain, 0)[1]))
+        assert np.array_equal(tiles, t.plan(plain, 0)[1]), "XCD order leaves descent tiles alone"
         for w in (1, 2):
             ptiles = t.plan(plain, w)[1]
-            check_xcd_order(cached[w][0], ptiles, len(ptiles))
+            check_xcd_order(cached[w][0], ptiles)
 
 
 def test_top_level(case):

@@ -98,7 +98,7 @@ k2_status k2_plan_defaults(k2_plan_opts *opts) {
     opts->tile_nodes = 1024;
     opts->host_top_max = 1u << 16;
     opts->cache_last_level = 0;
-    opts->xcd_remap = 0;
+    opts->xcd_remap = 1;
     opts->window_elems = 4096;
     opts->window_batch = 8;
     return K2_OK;

@@ -287,8 +287,8 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles: the plain depth-first cut (windowed descent tiles, one
     // per dense quadrant, measured slower: many small tiles)
     pl.range(d0, 0, t.nodes[d0], 0, no_window());
-    if (o.xcd_remap) xcd_order(p.tiles, pl.tile_weight, {0, p.tiles.size()}, uint32_t(last));
-    auto order_cached = [&](int dir, size_t n_band) {
+    // group boundaries: tile indexes where a new group starts (and the end)
+    auto order_cached = [&](int dir, std::vector<size_t> groups) {
         pl.set_leaves(dir);
         if (!o.xcd_remap) return;
         std::vector<uint64_t> w;
@@ -298,13 +298,13 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
             nodes += 8 * tl.count;   // a segment's fixed cost
             w.push_back(nodes);
         }
-        xcd_order(p.cached_tiles[dir], w, {0, n_band, p.cached_tiles[dir].size()}, uint32_t(last));
+        xcd_order(p.cached_tiles[dir], w, groups, uint32_t(last));
     };
     if (!o.cache_last_level) return K2_OK;
     if (qlog < 0) {
         for (int dir = 0; dir < 2; ++dir) {
             pl.cached_run(dir, 0, n2);
-            order_cached(dir, 0);
+            order_cached(dir, {0, p.cached_tiles[dir].size()});
         }
         return K2_OK;
     }
@@ -471,8 +471,19 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         if (in_run) flush();
         std::stable_sort(keyed.begin(), keyed.end(),
                          [](const auto &x, const auto &y) { return x.first < y.first; });
-        for (const auto &kt : keyed) p.cached_tiles[dir].push_back(kt.second);
-        order_cached(dir, p.cached_tiles[dir].size());
+        // with XCD order, the bands of an output block are one group and its
+        // sparse tiles another: all XCDs stay in the block (y in the
+        // last-level cache) and each takes a run of neighbouring bands (their
+        // shared x columns in its own L2) and an eighth of the sparse tiles
+        std::vector<size_t> groups{0};
+        for (size_t i = 0; i < keyed.size(); ++i) {
+            if (i && (keyed[i].first != keyed[i - 1].first ||
+                      (keyed[i].second.win_log2 == kNoWindow) != (keyed[i - 1].second.win_log2 == kNoWindow)))
+                groups.push_back(i);
+            p.cached_tiles[dir].push_back(keyed[i].second);
+        }
+        groups.push_back(keyed.size());
+        order_cached(dir, groups);
     }
     if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
     return K2_OK;
