@@ -125,3 +125,44 @@ def test_web_n27_d9_batch8(dev):
     want = oracle.spmv_sample(rows, cols, n, n, np.ones(n, np.float32), oracle.PLUS_TIMES, idx)
     assert np.array_equal(deg[idx].astype(np.float64), want)
     assert deg.astype(np.float64).sum() == tree.nnz
+
+
+def test_wide_offsets(dev):
+    """Dimensions 2^31 x 2^31 with 4 vectors: index * batch passes 2^32, so
+    the kernels keep 64-bit cell offsets.  x and y (32 GB each) live on the
+    device.  The oracle computes the sampled outputs from the edges that
+    reach them, over a compact copy of the x entries those edges read
+    (fetched from the device), with the input indices renumbered to it."""
+    import tree_graph_spmv_amd as k2
+    n, B = 2 ** 31, 4
+    rng = np.random.default_rng(31)
+    m = 200000
+    rows = rng.integers(0, n, m, dtype=np.int64)
+    cols = rng.integers(0, n, m, dtype=np.int64)
+    rows[:4] = [n - 1, n - 1, 0, n - 2]                  # the far corners
+    cols[:4] = [n - 1, 0, n - 1, n - 1]
+    rows[4:2000] = n - 1 - rng.integers(0, 64, 1996)     # a dense strip at the end
+    rows, cols = rows.astype(np.uint32), cols.astype(np.uint32)
+    tree = k2.Tree(rows, cols, n, n)
+    x = torch.rand(n * B, device=dev)
+    mat = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    for direction in ("right", "left"):
+        out_of, in_of = (rows, cols) if direction == "right" else (cols, rows)
+        sample = np.unique(np.concatenate([out_of[:3000], rng.integers(0, n, 1000), [0, n - 1]])
+                           ).astype(np.uint32)
+        hit = np.isin(out_of, sample)
+        need, local = np.unique(in_of[hit], return_inverse=True)
+        xc = x.view(n, B)[torch.from_numpy(need.astype(np.int64)).to(dev)].cpu().numpy()
+        if direction == "right":
+            want = oracle.spmv_sample(out_of[hit], local.astype(np.uint32), n, need.size, xc,
+                                      oracle.PLUS_TIMES, sample, oracle.RIGHT, B)
+        else:
+            want = oracle.spmv_sample(local.astype(np.uint32), out_of[hit], need.size, n, xc,
+                                      oracle.PLUS_TIMES, sample, oracle.LEFT, B)
+        for mode in ("tree", "cached"):
+            y = mat.spmv(x, direction=direction, batch=B, mode=mode)
+            torch.cuda.synchronize()
+            got = y.view(n, B)[torch.from_numpy(sample.astype(np.int64)).to(dev)].cpu().numpy()
+            check_parity(got, want, "plus_times", f"wide {direction} {mode}")
+            del y
+    del x

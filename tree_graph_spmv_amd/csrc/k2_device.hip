@@ -259,7 +259,10 @@ struct WaveCells {
     Off yo[kRound];
 };
 
-constexpr int kUnroll = 4;   // cells whose x loads are issued before their atomics
+// cells whose x loads a lane issues before their atomics: as many as 64
+// registers hold (64-bit offsets take twice the registers)
+template <class Off>
+constexpr int unroll_for() { return sizeof(Off) == 4 ? 8 : 4; }
 
 // Output window of a tile: 'win' (LDS, or null) holds outputs [out0, out0 +
 // rows) x B; cells of the tile all land inside it.
@@ -311,6 +314,7 @@ __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_
     constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
     constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
     const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
+    constexpr int kUnroll = unroll_for<Off>();
     for (uint32_t round = 0; round < total; round += R) {
         // this lane's cells with list positions in [round, round + R)
         uint32_t m = cells, pos = pos0;
