@@ -34,7 +34,7 @@ def parse():
     p.add_argument("--mode", default=None, help="tree or cached (default: the workload's)")
     p.add_argument("--tile-nodes", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-stride", type=int, default=32,
+    p.add_argument("--cpu-sample-stride", type=int, default=8,
                    help="oracle sample: the edges whose source is a multiple of this")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a 1 GiB device copy (counter calibration) and exit")
