@@ -107,14 +107,31 @@ typedef struct {
        everywhere.  Defaults 4096 and 8. */
     uint32_t window_elems;
     uint32_t window_batch;
+    /* Where the kernels get child offsets (Sec. 3.2, "ChildOffset"; the
+       ablation of Sec. 5.5 compares the two):
+       K2_OFFSETS_DIRECTORY: on the device, from the directory (one sample per
+         256 nodes of each internal level) plus the popcounts of at most 16
+         signature words: per descent tile and level, and per 64-node segment
+         of the cached level.
+       K2_OFFSETS_SCAN: from exclusive prefix sums of the fan-outs: the host
+         plan holds each descent tile's first child offset on every level it
+         spans and each cached segment's first leaf; the kernels scan the
+         fan-outs inside tiles and segments.  No directory is uploaded.
+       K2_OFFSETS_AUTO: K2_OFFSETS_SCAN (measured at least as fast on gfx950
+         for every workload here, single and batched).  Default AUTO. */
+    int32_t offsets;
 } k2_plan_opts;
+
+enum { K2_OFFSETS_AUTO = 0, K2_OFFSETS_DIRECTORY = 1, K2_OFFSETS_SCAN = 2 };
 
 /* Device bytes of a matrix and of one product, by part; 'arena' is what
    k2_matrix_create needs, 'vectors' the caller's x and y for the semiring
    and batch asked about, 'total' = arena + vectors. */
 typedef struct {
     uint64_t tree;        /* signatures of the levels the device reads */
-    uint64_t directory;   /* one uint32 per 256 nodes of each internal level */
+    uint64_t directory;   /* offset source: one uint32 per 256 nodes of each
+                             internal level (directory), or the planned first
+                             child offsets of the descent tiles (scan) */
     uint64_t top_codes;   /* Morton codes of the tile starts (host top + splits) */
     uint64_t tiles;       /* the tile plan */
     uint64_t cached_codes;/* 8 bytes per node of the last internal level, or 0 */
@@ -188,7 +205,10 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
 
 /* The tiles themselves, in the order the kernels take them.
    tiles[8k..8k+7] = (first, count, level, code index, window row, window
-   column, log2 of the window side or 0xFFFFFFFF for no window, 0).
+   column, log2 of the window side or 0xFFFFFFFF for no window, base index).
+   With scan offsets a descent tile's first child offsets on levels level ..
+   l-2 (the last its first leaf) are entries base index .. of the plan's
+   offsets (k2_plan_offsets); otherwise the base index is 0.
    which = 0: 'count' nodes of 'level' from node 'first', whose Morton codes
    (row bit above column bit per level, 2*level bits) are aux[code index ..].
    which = 1 / 2: 'count' segments of the last internal level from segment
@@ -198,6 +218,16 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
    Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                         uint32_t *tiles, uint64_t n_tiles, uint64_t *aux, uint64_t n_aux);
+
+/* The scan offsets of the descent tiles (host only): with
+   K2_OFFSETS_SCAN (or AUTO), tile k's first child offsets on levels
+   tiles[k].level .. l-2 are bases[base index of tile k ..] (Sec. 3.2: the
+   exclusive prefix sums of the fan-outs, sampled at the tile starts); empty
+   with K2_OFFSETS_DIRECTORY.  *n_total receives the count; bases may be
+   null to ask only for it, else it must hold n_bases >= that many entries.
+   Errors: K2_E_INVALID_ARG. */
+k2_status k2_plan_offsets(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *bases,
+                          uint64_t n_bases, uint64_t *n_total);
 
 /* Upload a tree into the caller's device arena (d_arena, arena_bytes >=
    estimate's arena; 256-byte aligned) on 'stream' and return a matrix handle.

@@ -202,6 +202,33 @@ def test_plan_invariants(case, opt):
             check_xcd_order(cached[w][0], ptiles)
 
 
+def test_scan_offsets(case):
+    """With scan offsets each descent tile carries its first node's first
+    child on every level it spans; they equal the oracle's child offsets
+    followed down from the tile's first node."""
+    name, r, c, nr, nc, t, o = case
+    L = o.levels
+    nodes = o.level_nodes()
+    offs = [o.child_offsets(d) for d in range(L - 1)]
+    for tile_nodes in (256, 4096):
+        opts = k2.plan_defaults(tile_nodes=tile_nodes, offsets="scan")
+        top, tiles, codes = t.plan(opts, 0)
+        bases = t.plan_offsets(opts)
+        total = 0
+        for tl in tiles:
+            level, first, at = int(tl[2]), int(tl[0]), int(tl[7])
+            assert at == total
+            node = first
+            for d in range(level, L - 1):
+                node = int(offs[d][node]) if node < nodes[d] else nodes[d + 1]
+                assert int(bases[at + d - level]) == node, (name, d)
+            total += L - 1 - level
+        assert total == bases.size
+        dir_opts = k2.plan_defaults(tile_nodes=tile_nodes, offsets="directory")
+        assert np.array_equal(t.plan(dir_opts, 0)[1][:, :7], tiles[:, :7])
+        assert np.all(t.plan(dir_opts, 0)[1][:, 7] == 0)
+
+
 def test_top_level(case):
     name, r, c, nr, nc, t, o = case
     nodes = o.level_nodes()
@@ -214,14 +241,18 @@ def test_top_level(case):
 def test_estimate_parts(case):
     name, r, c, nr, nc, t, o = case
     nodes = o.level_nodes()
-    for cached in (0, 1):
-        opts = k2.plan_defaults(cache_last_level=cached)
+    for cached, offsets in ((0, "scan"), (1, "scan"), (0, "directory"), (1, "directory")):
+        opts = k2.plan_defaults(cache_last_level=cached, offsets=offsets)
         est = t.estimate(opts, semiring="plus_times", batch=3)
         top, tiles, codes = t.plan(opts, 0)
         extra = sum(32 * len(t.plan(opts, w)[1]) + 16 * len(t.plan(opts, w)[2]) for w in (1, 2))
         L = o.levels
         assert est["tree"] == sum(8 * ((nodes[d] + 15) // 16) for d in range(top, L))
-        assert est["directory"] == sum(4 * ((nodes[d] + 255) // 256) for d in range(top, L - 1))
+        if offsets == "directory":
+            assert est["directory"] == sum(4 * ((nodes[d] + 255) // 256) for d in range(top, L - 1))
+            assert t.plan_offsets(opts).size == 0
+        else:
+            assert est["directory"] == 4 * t.plan_offsets(opts).size
         assert est["top_codes"] == 8 * len(codes)
         assert est["tiles"] == 32 * len(tiles) + (extra if cached else 0)
         assert est["cached_codes"] == (8 * nodes[L - 2] if cached else 0)

@@ -23,6 +23,8 @@ K2_PLUS_TIMES_F32, K2_BOOLEAN_F32, K2_BOOLEAN_U32X32, K2_TROPICAL_F32 = range(4)
 K2_RIGHT, K2_LEFT = 0, 1
 K2_MODE_AUTO, K2_MODE_TREE_ONLY, K2_MODE_CACHED = 0, 1, 2
 K2_SPMV_ACCUMULATE = 0x100
+K2_OFFSETS_AUTO, K2_OFFSETS_DIRECTORY, K2_OFFSETS_SCAN = 0, 1, 2
+OFFSETS = {"auto": K2_OFFSETS_AUTO, "directory": K2_OFFSETS_DIRECTORY, "scan": K2_OFFSETS_SCAN}
 
 SEMIRINGS = {"plus_times": K2_PLUS_TIMES_F32, "boolean": K2_BOOLEAN_F32,
              "boolean_u32": K2_BOOLEAN_U32X32, "tropical": K2_TROPICAL_F32}
@@ -33,7 +35,8 @@ MODES = {"auto": K2_MODE_AUTO, "tree": K2_MODE_TREE_ONLY, "cached": K2_MODE_CACH
 class PlanOpts(ctypes.Structure):
     _fields_ = [("tile_nodes", ctypes.c_uint32), ("host_top_max", ctypes.c_uint32),
                 ("cache_last_level", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
-                ("window_elems", ctypes.c_uint32), ("window_batch", ctypes.c_uint32)]
+                ("window_elems", ctypes.c_uint32), ("window_batch", ctypes.c_uint32),
+                ("offsets", ctypes.c_int32)]
 
 
 class MemBreakdown(ctypes.Structure):
@@ -88,6 +91,7 @@ _SIGS = {
     "k2_matrix_destroy": (ctypes.c_int, [_VP]),
     "k2_matrix_info": (ctypes.c_int, [_VP, _U32P, _U64P, ctypes.POINTER(ctypes.c_int32)]),
     "k2_matrix_level_words": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P, ctypes.c_uint64, _VP]),
+    "k2_plan_offsets": (ctypes.c_int, [_VP, _VP, _U32P, ctypes.c_uint64, _U64P]),
     "k2_matrix_cached_blocks": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
     "k2_matrix_set_timing": (ctypes.c_int, [_VP, ctypes.c_int32]),
     "k2_matrix_last_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_float),
@@ -127,6 +131,8 @@ def plan_defaults(**kw):
     o = PlanOpts()
     _check(lib().k2_plan_defaults(ctypes.byref(o)), "k2_plan_defaults")
     for k, v in kw.items():
+        if k == "offsets" and isinstance(v, str):
+            v = OFFSETS[v]
         setattr(o, k, int(v))
     return o
 
@@ -184,6 +190,17 @@ class Tree:
                                               int(batch), ctypes.byref(m)),
                "k2_estimate_device_bytes")
         return m.as_dict()
+
+    def plan_offsets(self, opts=None):
+        """The descent tiles' scan offsets (k2_plan_offsets), uint32."""
+        opts = opts or plan_defaults()
+        n = ctypes.c_uint64()
+        _check(lib().k2_plan_offsets(self._h, ctypes.byref(opts), None, 0, ctypes.byref(n)),
+               "k2_plan_offsets")
+        out = np.zeros(max(n.value, 1), np.uint32)
+        _check(lib().k2_plan_offsets(self._h, ctypes.byref(opts), out.ctypes.data_as(_U32P), n.value,
+                                     ctypes.byref(n)), "k2_plan_offsets")
+        return out[:n.value]
 
     def plan(self, opts=None, which=0):
         """(top_level, tiles (n,8) uint32, aux uint64) of one tile plan:

@@ -42,6 +42,7 @@ bool valid_opts(const k2_plan_opts &o) {
     if (o.tile_nodes < 256 || o.tile_nodes > 4096) return false;
     if (o.tile_nodes & (o.tile_nodes - 1)) return false;
     if (o.window_elems > 16384) return false;
+    if (o.offsets < K2_OFFSETS_AUTO || o.offsets > K2_OFFSETS_SCAN) return false;
     return true;
 }
 
@@ -53,7 +54,8 @@ bool same_opts(const k2_plan_opts &a, const k2_plan_opts &b) {
     return a.tile_nodes == b.tile_nodes && a.host_top_max == b.host_top_max &&
            a.window_elems == b.window_elems && a.window_batch == b.window_batch &&
            (a.cache_last_level != 0) == (b.cache_last_level != 0) &&
-           (a.xcd_remap != 0) == (b.xcd_remap != 0);
+           (a.xcd_remap != 0) == (b.xcd_remap != 0) &&
+           (a.offsets == K2_OFFSETS_DIRECTORY) == (b.offsets == K2_OFFSETS_DIRECTORY);
 }
 
 // The plan of 'tree' for 'o', computed once per option set.
@@ -101,6 +103,7 @@ k2_status k2_plan_defaults(k2_plan_opts *opts) {
     opts->xcd_remap = 1;
     opts->window_elems = 4096;
     opts->window_batch = 8;
+    opts->offsets = K2_OFFSETS_AUTO;
     return K2_OK;
 }
 
@@ -222,7 +225,7 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
     for (size_t k = 0; k < list.size(); ++k) {
         const Tile &tl = list[k];
         const uint32_t v[8] = {tl.first, tl.count, tl.level, tl.code_off,
-                               tl.win_row, tl.win_col, tl.win_log2, 0u};
+                               tl.win_row, tl.win_col, tl.win_log2, tl.base_off};
         std::copy(v, v + 8, tiles + 8 * k);
     }
     if (which == 0) {
@@ -234,6 +237,24 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
             aux[2 * k + 1] = sg[k].leaf;
         }
     }
+    return K2_OK;
+}
+
+k2_status k2_plan_offsets(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *bases,
+                          uint64_t n_bases, uint64_t *n_total) {
+    if (!tree || !opts || !valid_opts(*opts)) return K2_E_INVALID_ARG;
+    Plan plan;
+    k2_status st;
+    try {
+        st = plan_of(tree, *opts, &plan);
+    } catch (const std::bad_alloc &) {
+        return K2_E_HOST_OOM;
+    }
+    if (st != K2_OK) return st;
+    if (n_total) *n_total = plan.tile_bases.size();
+    if (!bases) return K2_OK;
+    if (n_bases < plan.tile_bases.size()) return K2_E_INVALID_ARG;
+    std::copy(plan.tile_bases.begin(), plan.tile_bases.end(), bases);
     return K2_OK;
 }
 
@@ -289,7 +310,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             }
         }
     }
-    for (int d = m.plan.top_level; d + 1 < t.levels; ++d) {
+    for (int d = m.plan.top_level; d + 1 < t.levels && m.plan.use_directory; ++d) {
         char *p = m.arena + m.layout.dir_off[d];
         m.dev.dir[d] = reinterpret_cast<const uint32_t *>(p);
         if (!t.dir[d].empty()) {
@@ -308,6 +329,15 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
                                       m.plan.codes.size() * 8, hipMemcpyHostToDevice, st_h);
         if (e != hipSuccess) {
             set_hip_error(int(e), "upload tile codes");
+            return fail(K2_E_HIP);
+        }
+    }
+    if (!m.plan.tile_bases.empty()) {
+        m.d_bases = reinterpret_cast<const uint32_t *>(m.arena + m.layout.bases_off);
+        hipError_t e = hipMemcpyAsync(const_cast<uint32_t *>(m.d_bases), m.plan.tile_bases.data(),
+                                      m.plan.tile_bases.size() * 4, hipMemcpyHostToDevice, st_h);
+        if (e != hipSuccess) {
+            set_hip_error(int(e), "upload tile offsets");
             return fail(K2_E_HIP);
         }
     }

@@ -438,15 +438,17 @@ struct SegLeaves {
     uint32_t ssh, lo32, hi32;
 };
 
-__device__ __forceinline__ SegSig stage_sig(const Seg *__restrict__ segs, uint32_t first,
-                                            uint32_t k, uint32_t nseg,
-                                            const uint64_t *__restrict__ sig_words) {
+// With use_dir the segment's first leaf comes from the directory on the
+// device, else from the plan.
+__device__ __forceinline__ SegSig stage_sig(const DevTree &t, int d, const Seg *__restrict__ segs,
+                                            uint32_t first, uint32_t k, uint32_t nseg,
+                                            const uint64_t *__restrict__ sig_words, int use_dir) {
     SegSig a{0u, 0u, 0u, 0u};
     if (k < nseg) {
         const Seg sg = segs[first + k];
         a.lo = sg.lo;
         a.count = sg.count;
-        a.leaf = sg.leaf;
+        a.leaf = use_dir ? wave_child_offset(t, d, sg.lo) : sg.leaf;
         if (__lane_id() < sg.count) a.s = nib(sig_words, uint64_t(sg.lo) + __lane_id());
     }
     return a;
@@ -481,7 +483,8 @@ template <class SR, int DIR, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
     const uint64_t *__restrict__ blocks, const typename SR::T *__restrict__ x,
-    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window) {
+    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
+    int use_dir) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
     __shared__ WaveCells<Off> s_cells[kWaves];
@@ -495,10 +498,11 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
         const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
         const uint32_t nseg = tl.count;
         uint32_t k = wave;
-        SegSig a1 = stage_sig(segs, tl.first, k + kWaves, nseg, sig_words);
-        SegLeaves b0 = stage_leaves(stage_sig(segs, tl.first, k, nseg, sig_words), blocks, leaf_dw);
+        SegSig a1 = stage_sig(t, d, segs, tl.first, k + kWaves, nseg, sig_words, use_dir);
+        SegLeaves b0 = stage_leaves(stage_sig(t, d, segs, tl.first, k, nseg, sig_words, use_dir), blocks,
+                                    leaf_dw);
         for (; k < nseg; k += kWaves) {
-            const SegSig a2 = stage_sig(segs, tl.first, k + 2 * kWaves, nseg, sig_words);
+            const SegSig a2 = stage_sig(t, d, segs, tl.first, k + 2 * kWaves, nseg, sig_words, use_dir);
             const SegLeaves b1 = stage_leaves(a1, blocks, leaf_dw);
             // the node's leaf nibbles are the low 4 * fan-out bits of 'bits'
             const uint32_t s0 = b0.ssh & 15u;
@@ -528,10 +532,11 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
     const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    uint64_t *__restrict__ emit) {
+    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
+    __shared__ uint32_t s_segtot[4096 / 64];   // scan offsets: fan-out per leaf segment
     __shared__ uint32_t s_val;
     __shared__ WaveCells<Off> s_cells[kWaves];
     const int last = t.levels - 2;
@@ -545,7 +550,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
         for (uint32_t i = threadIdx.x; i < cnt; i += kThreads) cur[i] = tile_codes[tl.code_off + i];
         __syncthreads();
         while (d < last) {
-            const uint32_t base = block_child_offset(t, d, lo, &s_val);
+            const uint32_t base = bases ? bases[tl.base_off + uint32_t(d - int(tl.level))]
+                                        : block_child_offset(t, d, lo, &s_val);
             const uint64_t *__restrict__ wd = t.words[d];
             uint32_t running = 0;
             for (uint32_t s0 = 0; s0 < cnt; s0 += kThreads) {
@@ -579,12 +585,31 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
             const Window<T> w = open_window<SR, DIR>(tl, s_win, use_window, B);
             const uint64_t *__restrict__ wd = t.words[last];
             const uint64_t *__restrict__ leaf_words = t.words[last + 1];
+            uint32_t leaf0 = 0;
+            if (bases) {
+                // scan offsets: the tile's first leaf, plus the fan-outs of the
+                // 64-node segments before each segment
+                leaf0 = bases[tl.base_off + uint32_t(last - int(tl.level))];
+                for (uint32_t seg = wave * 64; seg < cnt; seg += kThreads) {
+                    const uint32_t i = seg + lane;
+                    const uint32_t s = i < cnt ? nib(wd, uint64_t(lo) + i) : 0u;
+                    uint32_t total;
+                    wave_scan(__popc(s), total);
+                    if (lane == 0) s_segtot[seg >> 6] = total;
+                }
+                __syncthreads();
+            }
             for (uint32_t seg = wave * 64; seg < cnt; seg += kThreads) {
                 const uint32_t i = seg + lane;
                 const bool valid = i < cnt;
                 const uint32_t s = valid ? nib(wd, uint64_t(lo) + i) : 0u;
                 const uint64_t code = valid ? cur[i] : 0ull;
-                const uint32_t base = wave_child_offset(t, last, lo + seg);
+                uint32_t base = leaf0;
+                if (bases) {
+                    for (uint32_t k = 0; k < (seg >> 6); ++k) base += s_segtot[k];
+                } else {
+                    base = wave_child_offset(t, last, lo + seg);
+                }
                 uint32_t total;
                 const uint32_t ex = wave_scan(__popc(s), total);
                 leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_words, x, y, B, VL, w, &s_cells[wave]);
@@ -645,7 +670,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
                        m.d_cached_segs[DIR], m.d_cached, static_cast<const T *>(x),
-                       static_cast<T *>(y), B, VL, n_out, use);
+                       static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -666,7 +691,8 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_tiles, n_tiles, m.d_codes,
-                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit);
+                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit,
+                       m.d_bases);
     return hipGetLastError();
 }
 

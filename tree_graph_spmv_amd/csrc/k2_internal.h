@@ -45,7 +45,7 @@ struct Tile {
     uint32_t win_row;
     uint32_t win_col;
     uint32_t win_log2;
-    uint32_t pad;
+    uint32_t base_off;   // descent tiles with scan offsets: index into tile_bases
 };
 static_assert(sizeof(Tile) == 32, "tile layout");
 
@@ -73,6 +73,13 @@ struct Plan {
     std::vector<Tile> tiles;           // descent tiles
     std::vector<Tile> cached_tiles[2];
     std::vector<Seg> cached_segs[2];
+    // offset source: true = the directory on the device; false = planned
+    // prefix sums (tile_bases, and the segments' first leaves)
+    bool use_directory = false;
+    // scan offsets: descent tile k's first child offset on each level it
+    // spans, tile_bases[tiles[k].base_off + (d - tiles[k].level)] for d = level ..
+    // last internal level (the last entry is its first leaf)
+    std::vector<uint32_t> tile_bases;
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -82,7 +89,7 @@ int top_level_for(const HostTree &t, uint32_t host_top_max);
 struct Layout {
     uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
-    uint64_t codes_off = 0, tiles_off = 0, cached_off = 0;
+    uint64_t codes_off = 0, tiles_off = 0, cached_off = 0, bases_off = 0;
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     k2_mem_breakdown mem = {};
 };
@@ -111,6 +118,7 @@ struct Matrix {
     char *arena = nullptr;
     const uint64_t *d_codes = nullptr;   // tile start codes
     const Tile *d_tiles = nullptr;
+    const uint32_t *d_bases = nullptr;   // scan offsets of the descent tiles, or null
     const Tile *d_cached_tiles[2] = {nullptr, nullptr};
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
     uint64_t *d_cached = nullptr;        // last internal level codes or null

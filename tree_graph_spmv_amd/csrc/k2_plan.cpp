@@ -287,6 +287,33 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles: the plain depth-first cut (windowed descent tiles, one
     // per dense quadrant, measured slower: many small tiles)
     pl.range(d0, 0, t.nodes[d0], 0, no_window());
+    p.use_directory = o.offsets == K2_OFFSETS_DIRECTORY;
+    if (!p.use_directory) {
+        // scan offsets: each descent tile's first child on every level it
+        // spans, by following its first node down (the host's rank query)
+        uint64_t total = 0;
+        for (Tile &tl : p.tiles) {
+            tl.base_off = uint32_t(total);
+            total += uint64_t(last - int(tl.level) + 1);
+        }
+        if (total >= (1ull << 32)) return K2_E_UNSUPPORTED;
+        p.tile_bases.resize(total);
+        const size_t nt = p.tiles.size();
+        const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+        std::vector<std::thread> pool;
+        for (unsigned k = 0; k < nth; ++k)
+            pool.emplace_back([&, k]() {
+                for (size_t i = nt * k / nth; i < nt * (k + 1) / nth; ++i) {
+                    const Tile &tl = p.tiles[i];
+                    uint64_t node = tl.first;
+                    for (int d = int(tl.level); d <= last; ++d) {
+                        node = child_offset(t, d, node);
+                        p.tile_bases[tl.base_off + uint32_t(d - int(tl.level))] = uint32_t(node);
+                    }
+                }
+            });
+        for (auto &th : pool) th.join();
+    }
     // group boundaries: tile indexes where a new group starts (and the end)
     auto order_cached = [&](int dir, std::vector<size_t> groups) {
         pl.set_leaves(dir);
@@ -505,7 +532,9 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
     for (int d = top; d < t.levels; ++d)
         l.words_off[d] = take(8 * ((t.nodes[d] + 15) / 16), l.mem.tree);
     for (int d = top; d + 1 < t.levels; ++d)
-        l.dir_off[d] = take(4 * ((t.nodes[d] + kDirBlock - 1) / kDirBlock), l.mem.directory);
+        l.dir_off[d] = take(plan.use_directory ? 4 * ((t.nodes[d] + kDirBlock - 1) / kDirBlock) : 0,
+                            l.mem.directory);
+    l.bases_off = take(4 * plan.tile_bases.size(), l.mem.directory);
     l.codes_off = take(8 * plan.codes.size(), l.mem.top_codes);
     l.tiles_off = take(sizeof(Tile) * plan.tiles.size(), l.mem.tiles);
     for (int dir = 0; dir < 2; ++dir) {
