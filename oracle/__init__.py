@@ -75,6 +75,9 @@ def _load():
                                     ctypes.c_int, ctypes.c_int, ctypes.c_uint32, vp, u32p,
                                     ctypes.c_uint64, vp]
     lib.orc_spmv_sample.restype = ctypes.c_int
+    lib.orc_bfs.argtypes = [u32p, u32p, ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int, u32p,
+                            ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    lib.orc_bfs.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -210,3 +213,16 @@ def spmv_sample(rows, cols, n_rows, n_cols, x, semiring, sample, direction=RIGHT
     _check(lib.orc_spmv_sample(rp, cp, r.size, n_rows, n_cols, direction, semiring, batch,
                                x.ctypes.data, sp, s.size, y.ctypes.data))
     return y if batch == 1 else y.reshape(s.size, batch)
+
+
+def bfs(rows, cols, n, sources, direction=RIGHT, max_levels=2 ** 31 - 1):
+    """Hop distances (n, len(sources)) int32 from each source of the square
+    n x n matrix, -1 where unreached within max_levels (Sec. 5.8).  A RIGHT
+    step reaches row r from column c for a cell (r, c); LEFT the reverse."""
+    lib = _load()
+    r, rp = _u32(rows)
+    c, cp = _u32(cols)
+    s, sp = _u32(sources)
+    dist = np.empty((n, s.size), np.int32)
+    _check(lib.orc_bfs(rp, cp, r.size, n, direction, sp, s.size, max_levels, dist.ctypes.data))
+    return dist

@@ -30,6 +30,9 @@
  *              q = 2*dr + dc is the cell (r0+dr, c0+dc).
  *   edges   -- the same product straight from the definition over the
  *              deduplicated edge list (no tree at all).
+ *   bfs     -- Sec. 5.8's multi-source search (hop distances from several
+ *              sources, one level per product) as a plain queue search per
+ *              source over adjacency lists of the edge list.
  *
  * Readings where the pages are silent (shared with the library's contract):
  *   - l = max(2, ceil(log2(max(n_rows, n_cols)))), so a last internal level
@@ -438,4 +441,70 @@ int orc_spmv_sample(const uint32_t *rows, const uint32_t *cols, uint64_t m,
     }
     free(sel); free(slot);
     return ORC_OK;
+}
+
+/* ---- multi-source search (Sec. 5.8) ----------------------------------
+ * Hop distances from several sources of a square n x n matrix, one level
+ * per step, as the paper's search computes them by iterating the batched
+ * Boolean product to its fixed point.  A step in direction RIGHT reaches row
+ * r from column c for every cell (r, c) (the right product's y[r] gathers
+ * x[c]); LEFT reaches column c from row r.  dist[v * n_src + j] is the hop
+ * count from sources[j] to v, 0 at the source, -1 when v is not reached
+ * within max_levels steps.  Written as a plain queue search per source over
+ * adjacency lists built from the edge list; duplicated edges are harmless. */
+int orc_bfs(const uint32_t *rows, const uint32_t *cols, uint64_t m, uint32_t n, int dir,
+            const uint32_t *sources, uint32_t n_src, uint32_t max_levels, int32_t *dist) {
+    if ((m && (!rows || !cols)) || (n_src && (!sources || !dist)) || n == 0) return ORC_E_ARG;
+    if (dir != ORC_RIGHT && dir != ORC_LEFT) return ORC_E_ARG;
+    for (uint32_t j = 0; j < n_src; j++)
+        if (sources[j] >= n) return ORC_E_RANGE;
+    uint64_t *start = (uint64_t *)calloc((size_t)n + 1, sizeof(uint64_t));
+    uint32_t *adj = (uint32_t *)malloc((size_t)(m ? m : 1) * sizeof(uint32_t));
+    if (!start || !adj) { free(start); free(adj); return ORC_E_OOM; }
+    for (uint64_t e = 0; e < m; e++) {
+        if (rows[e] >= n || cols[e] >= n) { free(start); free(adj); return ORC_E_RANGE; }
+        uint32_t from = (dir == ORC_RIGHT) ? cols[e] : rows[e];
+        start[from + 1]++;
+    }
+    for (uint64_t v = 0; v < n; v++) start[v + 1] += start[v];
+    uint64_t *fillp = (uint64_t *)malloc((size_t)n * sizeof(uint64_t));
+    if (!fillp) { free(start); free(adj); return ORC_E_OOM; }
+    memcpy(fillp, start, (size_t)n * sizeof(uint64_t));
+    for (uint64_t e = 0; e < m; e++) {
+        uint32_t from = (dir == ORC_RIGHT) ? cols[e] : rows[e];
+        uint32_t to = (dir == ORC_RIGHT) ? rows[e] : cols[e];
+        adj[fillp[from]++] = to;
+    }
+    free(fillp);
+    for (uint64_t k = 0; k < (uint64_t)n * n_src; k++) dist[k] = -1;
+    int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t j = 0; j < (int64_t)n_src; j++) {
+        uint32_t *queue = (uint32_t *)malloc((size_t)n * sizeof(uint32_t));
+        if (!queue) {
+#pragma omp critical
+            err = ORC_E_OOM;
+            continue;
+        }
+        uint64_t head = 0, tail = 0;
+        uint32_t s = sources[j];
+        dist[(uint64_t)s * n_src + (uint64_t)j] = 0;
+        queue[tail++] = s;
+        while (head < tail) {
+            uint32_t u = queue[head++];
+            int32_t du = dist[(uint64_t)u * n_src + (uint64_t)j];
+            if ((uint32_t)du >= max_levels) continue;
+            for (uint64_t a = start[u]; a < start[u + 1]; a++) {
+                uint32_t v = adj[a];
+                int32_t *dv = &dist[(uint64_t)v * n_src + (uint64_t)j];
+                if (*dv < 0) {
+                    *dv = du + 1;
+                    queue[tail++] = v;
+                }
+            }
+        }
+        free(queue);
+    }
+    free(start); free(adj);
+    return err;
 }

@@ -436,3 +436,71 @@ def test_boolean_packed_is_32_boolean_products(mid_tree):
         xb = ((words >> bit) & 1).astype(np.float32)
         yb = t.spmv(xb, BOOLEAN_F32, RIGHT)
         assert np.array_equal(((y >> bit) & 1).astype(np.float32), yb)
+
+
+# ---- multi-source search (Sec. 5.8) -----------------------------------
+
+def test_bfs_path_graph_closed_form():
+    """Edges i -> i+1 (cells (i, i+1)): a LEFT step moves from row to column,
+    so from s the distance to v >= s is v - s; a RIGHT step moves the other
+    way, v <= s at s - v.  max_levels cuts both."""
+    n = 40
+    r = np.arange(n - 1, dtype=np.uint32)
+    c = r + 1
+    src = np.array([0, 7, 39], np.uint32)
+    v = np.arange(n)[:, None]
+    s = src[None, :].astype(np.int64)
+    left = oracle.bfs(r, c, n, src, oracle.LEFT)
+    right = oracle.bfs(r, c, n, src, oracle.RIGHT)
+    assert np.array_equal(left, np.where(v >= s, v - s, -1))
+    assert np.array_equal(right, np.where(v <= s, s - v, -1))
+    cut = oracle.bfs(r, c, n, src, oracle.LEFT, max_levels=5)
+    want = np.where((v >= s) & (v - s <= 5), v - s, -1)
+    assert np.array_equal(cut, want)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_bfs_against_scipy(seed):
+    """Unweighted shortest paths of scipy.sparse.csgraph on random directed
+    graphs (a cell (r, c) is the arc r -> c for LEFT steps, c -> r for
+    RIGHT steps)."""
+    from scipy.sparse import coo_matrix
+    from scipy.sparse.csgraph import shortest_path
+    rng = np.random.default_rng(50 + seed)
+    n = int(rng.integers(2, 300))
+    m = int(rng.integers(0, 4 * n))
+    r = rng.integers(0, n, m).astype(np.uint32)
+    c = rng.integers(0, n, m).astype(np.uint32)
+    src = rng.integers(0, n, 7).astype(np.uint32)
+    g = coo_matrix((np.ones(m), (r, c)), shape=(n, n)).tocsr()
+    for direction, graph in ((oracle.LEFT, g), (oracle.RIGHT, g.T.tocsr())):
+        d = shortest_path(graph, method="D", directed=True, unweighted=True, indices=src)
+        want = np.where(np.isinf(d), -1, d).astype(np.int64).T
+        assert np.array_equal(oracle.bfs(r, c, n, src, direction), want)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_bfs_is_iterated_min_plus(seed):
+    """The paper derives the search from Bellman-Ford on unit lengths: from
+    x = 0 at the source and +inf elsewhere, x <- min(x, A (min,+) x) (the
+    tree's tropical product, 1 + x_j per cell) converges to the hop
+    distances, in either direction."""
+    rng = np.random.default_rng(70 + seed)
+    n = int(rng.integers(2, 200))
+    m = int(rng.integers(0, 3 * n))
+    r = rng.integers(0, n, m).astype(np.uint32)
+    c = rng.integers(0, n, m).astype(np.uint32)
+    t = oracle.OracleTree(r, c, n, n)
+    src = rng.integers(0, n, 3).astype(np.uint32)
+    for direction in (oracle.RIGHT, oracle.LEFT):
+        want = oracle.bfs(r, c, n, src, direction)
+        for j, s in enumerate(src):
+            x = np.full(n, np.inf, np.float32)
+            x[s] = 0
+            while True:
+                y = np.minimum(x, t.spmv(x, oracle.TROPICAL, direction, 1).astype(np.float32))
+                if np.array_equal(y, x):
+                    break
+                x = y
+            got = np.where(np.isinf(x), -1, x).astype(np.int64)
+            assert np.array_equal(got, want[:, j])
