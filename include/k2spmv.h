@@ -280,6 +280,34 @@ k2_status k2_matrix_level_words(const k2_matrix *matrix, uint32_t level, uint64_
 k2_status k2_matrix_cached_blocks(const k2_matrix *matrix, uint64_t *blocks, uint64_t n_blocks,
                                   void *stream);
 
+/* Multi-source search to the fixed point (Sec. 5.8, Table 6): hop distances
+   from n_sources sources of a square matrix at once, one level per batched
+   Boolean product.  A level's product runs in 'direction' (K2_RIGHT: row r
+   is reached from column c for a cell (r, c); K2_LEFT: column c from row r)
+   over the packed frontier of the previous level (32 sources per uint32,
+   K2_BOOLEAN_U32X32 with batch ceil(n_sources / 32)), with the matrix's
+   cached level when it has one; a marking kernel keeps the entries not
+   reached before as the next frontier and writes their distance.  The search
+   stops after a level that reaches nothing new, or after max_levels levels.
+     sources            host array of n_sources vertex ids (< n; repeats are
+                        independent searches)
+     d_dist             device n x n_sources int32, row-major: d_dist[v *
+                        n_sources + j] = hops from sources[j] to v, -1 if not
+                        reached (overwritten)
+     d_workspace        device, 256-byte aligned, k2_bfs_workspace_bytes bytes
+                        (caller-owned; the library allocates nothing)
+     levels             out: the last level that reached a new entry
+     reached_per_level  optional host array of max_levels entries: entries
+                        reached at each level run (the last run level's is 0
+                        when the search converged)
+   Synchronous per level (the host reads one count).  Errors:
+   K2_E_INVALID_ARG (null, non-square matrix, no sources, small or unaligned
+   workspace), K2_E_INDEX_RANGE (a source >= n), K2_E_HIP. */
+k2_status k2_bfs_workspace_bytes(const k2_matrix *matrix, uint32_t n_sources, uint64_t *bytes);
+k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
+                 uint32_t max_levels, int32_t *d_dist, void *d_workspace, uint64_t workspace_bytes,
+                 void *stream, uint32_t *levels, uint64_t *reached_per_level);
+
 const char *k2_status_string(k2_status status);
 
 /* Text of the last HIP error this thread saw (empty string if none). */

@@ -92,6 +92,9 @@ _SIGS = {
     "k2_matrix_info": (ctypes.c_int, [_VP, _U32P, _U64P, ctypes.POINTER(ctypes.c_int32)]),
     "k2_matrix_level_words": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P, ctypes.c_uint64, _VP]),
     "k2_plan_offsets": (ctypes.c_int, [_VP, _VP, _U32P, ctypes.c_uint64, _U64P]),
+    "k2_bfs_workspace_bytes": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P]),
+    "k2_bfs": (ctypes.c_int, [_VP, ctypes.c_int, _U32P, ctypes.c_uint32, ctypes.c_uint32, _VP, _VP,
+                              ctypes.c_uint64, _VP, _U32P, _U64P]),
     "k2_matrix_cached_blocks": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
     "k2_matrix_set_timing": (ctypes.c_int, [_VP, ctypes.c_int32]),
     "k2_matrix_last_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_float),
@@ -308,6 +311,35 @@ class Matrix:
                              _VP(x.data_ptr()), _VP(y.data_ptr()), _stream_handle(stream)),
                "k2_spmv")
         return y
+
+    def bfs(self, sources, direction="right", max_levels=2 ** 31 - 1, dist=None, workspace=None,
+            stream=None):
+        """Multi-source search to the fixed point (k2_bfs): returns (dist, levels,
+        reached) with dist an (n, len(sources)) int32 device tensor of hop
+        counts (-1 unreached), levels the last level that reached something
+        new, reached the entries each level run reached."""
+        import torch
+        src, sp = _u32(sources)
+        n = self.n_rows
+        nb = ctypes.c_uint64()
+        _check(lib().k2_bfs_workspace_bytes(self._h, src.size, ctypes.byref(nb)), "k2_bfs_workspace_bytes")
+        if dist is None:
+            dist = torch.empty((n, src.size), dtype=torch.int32, device=self.device)
+        if workspace is None:
+            workspace = torch.empty(nb.value, dtype=torch.uint8, device=self.device)
+        if dist.numel() != n * src.size or dist.dtype != torch.int32 or not dist.is_contiguous():
+            raise ValueError("dist must be a contiguous int32 tensor of n x len(sources)")
+        levels = ctypes.c_uint32()
+        max_levels = int(min(max_levels, 2 ** 31 - 1))
+        # per-level counts are kept for searches of at most 2^16 levels
+        reached = np.zeros(max(max_levels, 1), np.uint64) if max_levels <= (1 << 16) else None
+        _check(lib().k2_bfs(self._h, DIRECTIONS[direction], sp, src.size, max_levels, _VP(dist.data_ptr()),
+                            _VP(workspace.data_ptr()), workspace.numel(), _stream_handle(stream),
+                            ctypes.byref(levels),
+                            reached.ctypes.data_as(_U64P) if reached is not None else None), "k2_bfs")
+        if reached is not None:
+            reached = reached[:min(levels.value + 1, max_levels)]
+        return dist, levels.value, reached
 
     def device_level_words(self, level, n_nodes, stream=None):
         out = np.zeros((n_nodes + 15) // 16, np.uint64)

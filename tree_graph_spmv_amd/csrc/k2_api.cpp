@@ -502,6 +502,88 @@ k2_status k2_matrix_cached_blocks(const k2_matrix *matrix, uint64_t *blocks, uin
     return K2_OK;
 }
 
+namespace {
+
+// Workspace of a search: frontier, reached set and product output (n W
+// words each), the per-level count, the sources.
+struct BfsSpace {
+    uint64_t words_off[3], count_off, src_off, bytes;
+};
+
+BfsSpace bfs_space(uint64_t n, uint32_t S) {
+    const uint64_t W = (uint64_t(S) + 31) / 32;
+    auto a256 = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    BfsSpace b{};
+    uint64_t off = 0;
+    for (int k = 0; k < 3; ++k) {
+        b.words_off[k] = off;
+        off += n * W * 4;   // contiguous: the init kernel clears all three at once
+    }
+    off = a256(off);
+    b.count_off = off;
+    off = a256(off + 8);
+    b.src_off = off;
+    b.bytes = a256(off + uint64_t(S) * 4);
+    return b;
+}
+
+}  // namespace
+
+k2_status k2_bfs_workspace_bytes(const k2_matrix *matrix, uint32_t n_sources, uint64_t *bytes) {
+    if (!matrix || !bytes || n_sources == 0) return K2_E_INVALID_ARG;
+    *bytes = bfs_space(matrix->m.n_rows, n_sources).bytes;
+    return K2_OK;
+}
+
+k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
+                 uint32_t max_levels, int32_t *d_dist, void *d_workspace, uint64_t workspace_bytes,
+                 void *stream, uint32_t *levels, uint64_t *reached_per_level) {
+    if (!matrix || !sources || n_sources == 0 || !d_dist || !d_workspace || !levels) return K2_E_INVALID_ARG;
+    if (int(direction) != K2_RIGHT && int(direction) != K2_LEFT) return K2_E_INVALID_ARG;
+    Matrix &m = matrix->m;
+    if (m.n_rows != m.n_cols) return K2_E_INVALID_ARG;
+    const uint64_t n = m.n_rows;
+    for (uint32_t j = 0; j < n_sources; ++j)
+        if (sources[j] >= n) return K2_E_INDEX_RANGE;
+    const BfsSpace sp = bfs_space(n, n_sources);
+    if (workspace_bytes < sp.bytes || (reinterpret_cast<uintptr_t>(d_workspace) & 255)) return K2_E_INVALID_ARG;
+    const uint32_t W = (n_sources + 31) / 32;
+    char *ws = static_cast<char *>(d_workspace);
+    uint32_t *F = reinterpret_cast<uint32_t *>(ws + sp.words_off[0]);
+    uint32_t *V = reinterpret_cast<uint32_t *>(ws + sp.words_off[1]);
+    uint32_t *Y = reinterpret_cast<uint32_t *>(ws + sp.words_off[2]);
+    auto *count = reinterpret_cast<unsigned long long *>(ws + sp.count_off);
+    uint32_t *src = reinterpret_cast<uint32_t *>(ws + sp.src_off);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool empty = m.nodes[m.levels - 2] == 0;
+    HIP_TRY(hipMemcpyAsync(src, sources, uint64_t(n_sources) * 4, hipMemcpyHostToDevice, st), "search sources");
+    int e = launch_bfs_init(d_dist, n * n_sources, F, 3 * n * W, stream);
+    if (e == hipSuccess) e = launch_bfs_seed(src, n_sources, W, d_dist, F, V, stream);
+    if (e != hipSuccess) {
+        set_hip_error(e, "search init");
+        return K2_E_HIP;
+    }
+    *levels = 0;
+    for (uint32_t level = 1; level <= max_levels && level < 0x7FFFFFFFu; ++level) {
+        HIP_TRY(hipMemsetAsync(count, 0, 8, st), "search count");
+        if (!empty)
+            e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, stream)
+                         : launch_descent(m, direction, K2_BOOLEAN_U32X32, W, F, Y, nullptr, stream);
+        if (e == hipSuccess) e = launch_bfs_mark(Y, V, F, d_dist, n * W, W, n_sources, int32_t(level), count, stream);
+        if (e != hipSuccess) {
+            set_hip_error(e, "search level");
+            return K2_E_HIP;
+        }
+        unsigned long long found = 0;
+        HIP_TRY(hipMemcpyAsync(&found, count, 8, hipMemcpyDeviceToHost, st), "search count");
+        HIP_TRY(hipStreamSynchronize(st), "search level");
+        if (reached_per_level) reached_per_level[level - 1] = found;
+        if (found == 0) break;
+        *levels = level;
+    }
+    return K2_OK;
+}
+
 const char *k2_status_string(k2_status status) {
     switch (status) {
     case K2_OK: return "ok";

@@ -620,6 +620,70 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     }
 }
 
+// ------------------------------------------------------------- search
+
+// Multi-source search (Sec. 5.8): dense tables of n vertices x S sources.
+// The frontier F, the reached set V and the product output y hold W = S/32
+// (rounded up) words per vertex, bit j % 32 of word j / 32 for source j;
+// dist is n x S int32.
+
+// dist = -1 everywhere; F, V and y (3 n W contiguous words) = 0.
+__global__ __launch_bounds__(kThreads) void bfs_init_kernel(int32_t *__restrict__ dist, uint64_t n_dist,
+                                                            uint32_t *__restrict__ words,
+                                                            uint64_t n_words) {
+    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    for (uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x; i < n_dist; i += stride) dist[i] = -1;
+    for (uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x; i < n_words; i += stride) words[i] = 0u;
+}
+
+// Source j starts at distance 0 in the frontier and the reached set.
+__global__ __launch_bounds__(kThreads) void bfs_seed_kernel(const uint32_t *__restrict__ src, uint32_t S,
+                                                            uint32_t W, int32_t *__restrict__ dist,
+                                                            uint32_t *__restrict__ F,
+                                                            uint32_t *__restrict__ V) {
+    const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
+    if (j >= S) return;
+    const uint64_t v = src[j];
+    dist[v * S + j] = 0;
+    const uint32_t bit = 1u << (j & 31u);
+    atomicOr(&F[v * W + (j >> 5)], bit);
+    atomicOr(&V[v * W + (j >> 5)], bit);
+}
+
+// After the level's product y = A (or, and) F: the newly reached bits are
+// y & ~V; they become the next frontier, join V and get distance 'level'.
+// y is left zero for the next product, which accumulates into it.  The
+// number of newly reached (vertex, source) pairs is added to *count.
+__global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict__ y,
+                                                            uint32_t *__restrict__ V,
+                                                            uint32_t *__restrict__ F,
+                                                            int32_t *__restrict__ dist, uint64_t n_words,
+                                                            uint32_t W, uint32_t S, int32_t level,
+                                                            unsigned long long *__restrict__ count) {
+    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    uint32_t found = 0;
+    for (uint64_t e = uint64_t(blockIdx.x) * kThreads + threadIdx.x; e < n_words; e += stride) {
+        const uint32_t yw = y[e];
+        uint32_t fresh = 0u;
+        if (yw) {
+            y[e] = 0u;
+            const uint32_t seen = V[e];
+            fresh = yw & ~seen;
+            if (fresh) {
+                V[e] = seen | fresh;
+                const uint64_t v = e / W;
+                const uint32_t j0 = uint32_t(e % W) * 32u;
+                for (uint32_t m = fresh; m; m &= m - 1u) dist[v * S + j0 + uint32_t(__builtin_ctz(m))] = level;
+                found += uint32_t(__popc(fresh));
+            }
+        }
+        F[e] = fresh;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) found += __shfl_xor(found, o);
+    if (__lane_id() == 0 && found) atomicAdd(count, (unsigned long long)found);
+}
+
 // ------------------------------------------------------------- launchers
 
 namespace {
@@ -760,5 +824,34 @@ int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const
 }
 
 const char *hip_error_text(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+}  // namespace k2
+
+namespace k2 {
+
+static uint32_t small_grid(uint64_t items) {
+    const uint64_t b = (items + kThreads - 1) / kThreads;
+    return uint32_t(b < 8192 ? (b ? b : 1) : 8192);
+}
+
+int launch_bfs_init(int32_t *dist, uint64_t n_dist, uint32_t *words, uint64_t n_words, void *stream) {
+    hipLaunchKernelGGL(bfs_init_kernel, dim3(small_grid(n_dist > n_words ? n_dist : n_words)), dim3(kThreads),
+                       0, static_cast<hipStream_t>(stream), dist, n_dist, words, n_words);
+    return hipGetLastError();
+}
+
+int launch_bfs_seed(const uint32_t *src, uint32_t S, uint32_t W, int32_t *dist, uint32_t *F, uint32_t *V,
+                    void *stream) {
+    hipLaunchKernelGGL(bfs_seed_kernel, dim3((S + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), src, S, W, dist, F, V);
+    return hipGetLastError();
+}
+
+int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, int32_t *dist, uint64_t n_words, uint32_t W,
+                    uint32_t S, int32_t level, unsigned long long *count, void *stream) {
+    hipLaunchKernelGGL(bfs_mark_kernel, dim3(small_grid(n_words)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), y, V, F, dist, n_words, W, S, level, count);
+    return hipGetLastError();
+}
 
 }  // namespace k2

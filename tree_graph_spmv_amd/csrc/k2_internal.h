@@ -131,6 +131,11 @@ struct Matrix {
 
 // Kernel launchers (k2_device.hip).  Return hipError_t as int.
 int launch_fill(void *y, uint64_t n_words32, uint32_t value, void *stream);
+int launch_bfs_init(int32_t *dist, uint64_t n_dist, uint32_t *words, uint64_t n_words, void *stream);
+int launch_bfs_seed(const uint32_t *src, uint32_t S, uint32_t W, int32_t *dist, uint32_t *F, uint32_t *V,
+                    void *stream);
+int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, int32_t *dist, uint64_t n_words, uint32_t W,
+                    uint32_t S, int32_t level, unsigned long long *count, void *stream);
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
                    uint64_t *emit_codes, void *stream);
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
