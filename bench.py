@@ -33,6 +33,12 @@ def parse():
     p.add_argument("--workload", default="web_n27_d9")
     p.add_argument("--mode", default=None, help="tree or cached (default: the workload's)")
     p.add_argument("--tile-nodes", type=int, default=1024)
+    p.add_argument("--batch", type=int, default=None, help="vectors per product (default: the workload's)")
+    p.add_argument("--window-elems", type=int, default=None, help="plan option (default: the library's)")
+    p.add_argument("--window-batch", type=int, default=None, help="plan option (default: the library's)")
+    p.add_argument("--offsets", default=None, choices=("auto", "directory", "scan"),
+                   help="plan option (default: the library's)")
+    p.add_argument("--xcd-remap", type=int, default=None, help="plan option (default: the library's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-stride", type=int, default=8,
                    help="oracle sample: the edges whose source is a multiple of this")
@@ -134,7 +140,7 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     mode = args.mode or ("cached" if w["cached"] else "tree")
-    batch = w["batch"]
+    batch = args.batch or w["batch"]
     semiring = w["semiring"]
     directions = list(w["directions"])
     dev = torch.device("cuda:0")
@@ -149,7 +155,9 @@ def main():
     nodes = tree.level_nodes()
     log(f"built: nnz={tree.nnz} nodes={tree.nodes} levels={tree.levels} in {build_s:.1f}s")
 
-    opts = k2.plan_defaults(tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"))
+    extra = {k: v for k, v in (("window_elems", args.window_elems), ("window_batch", args.window_batch),
+                               ("offsets", args.offsets), ("xcd_remap", args.xcd_remap)) if v is not None}
+    opts = k2.plan_defaults(tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"), **extra)
     est = tree.estimate(opts, semiring=semiring, batch=batch)
     # load the kernels' code object first (a tiny product), so that the
     # memory measured below is the matrix's and the vectors' alone
@@ -161,7 +169,7 @@ def main():
         tm.spmv(tx, direction=d, semiring=semiring, batch=batch)
     torch.cuda.synchronize()
     del tm, tx
-    xh = synth.workload_x(args.workload, n)   # one x and one y serve both directions
+    xh = synth.workload_x(args.workload, n, batch=batch)   # one x and one y serve both directions
     x = torch.from_numpy(xh.view(np.int32) if xh.dtype == np.uint32 else xh).to(dev)
     y = torch.empty(n * batch, dtype=x.dtype, device=dev)
     del xh
@@ -248,7 +256,7 @@ def main():
         "config": {"workload": args.workload, "vertices": n, "edges": tree.nnz,
                    "tree_nodes": tree.nodes, "levels": tree.levels, "batch": batch,
                    "semiring": semiring, "mode": mode, "directions": directions,
-                   "tile_nodes": args.tile_nodes},
+                   "tile_nodes": args.tile_nodes, **extra},
         "roofline": {"kernel": f"{'cached_kernel' if mode == 'cached' else 'descent_kernel'} "
                                f"({dom} product)",
                      "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",

@@ -103,8 +103,9 @@ typedef struct {
        elements of 4 bytes; 0 disables).  A tile made of the dense Q x Q
        quadrants of one row band (right products) or column band (left
        products) accumulates its outputs in LDS and adds them to y once.
-       Products with more than window_batch vectors use direct atomics
-       everywhere.  Defaults 4096 and 8. */
+       Products with more than window_batch vectors use the same windows
+       while Q x batch elements fit one workgroup's LDS (fewer workgroups per
+       CU), else direct atomics everywhere.  Defaults 4096 and 8. */
     uint32_t window_elems;
     uint32_t window_batch;
     /* Where the kernels get child offsets (Sec. 3.2, "ChildOffset"; the

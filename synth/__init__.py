@@ -171,11 +171,12 @@ def workload_edges(name, threads=None):
     return r, c, w["n"]
 
 
-def workload_x(name, n, seed_offset=0, threads=None):
-    """The input vector(s) of a named workload, row-major (n, batch) flattened."""
+def workload_x(name, n, seed_offset=0, threads=None, batch=None):
+    """The input vector(s) of a named workload, row-major (n, batch) flattened
+    (batch: the workload's unless given)."""
     w = WORKLOADS[name]
     seed = 1000 + w["seed"] + seed_offset
-    count = n * w["batch"]
+    count = n * (w["batch"] if batch is None else batch)
     if w["semiring"] == "tropical":
         return tropical(count, seed, threads=threads)
     if w["semiring"] == "boolean_u32":

@@ -289,6 +289,17 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     m.cached = opts->cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
     m.window_elems = m.plan.window_log2 >= 0 ? opts->window_elems : 0;
     m.window_batch = opts->window_batch;
+    {   // the window shares a workgroup's LDS with the cell lists (a few KB)
+        int dev = 0, lds = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (e != hipSuccess) {
+            set_hip_error(int(e), "LDS size");
+            delete mx;
+            return K2_E_HIP;
+        }
+        m.max_window_lds = lds > 16384 ? size_t(lds) - 8192 : 0;
+    }
     std::memset(&m.dev, 0, sizeof(m.dev));
     m.dev.levels = t.levels;
     m.dev.top_level = m.plan.top_level;

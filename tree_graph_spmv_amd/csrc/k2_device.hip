@@ -688,8 +688,12 @@ __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict
 
 namespace {
 
-uint32_t lanes_per_node(uint32_t B) {
-    uint32_t v = 1;
+// Lanes per cell: B rounded up to a power of 2 (at most 64).  Right products
+// take at least 4: neighbouring cells of a list (Z order) often share a row,
+// and with 64 cells per instruction their LDS compare-and-swaps keep
+// colliding (B = 1: 35 ms against 14 ms for the left product at 2^27).
+uint32_t lanes_per_node(uint32_t B, int dir) {
+    uint32_t v = dir == K2_RIGHT ? 4u : 1u;
     while (v < B && v < 64) v <<= 1;
     return v;
 }
@@ -702,11 +706,13 @@ uint32_t grid_for(uint64_t blocks) {
     return uint32_t(blocks < cap ? (blocks ? blocks : 1) : cap);
 }
 
-// Whether products with batch B use the planned windows, and their LDS bytes.
+// Whether products with batch B use the planned windows, and their LDS bytes:
+// whenever the window (Q outputs x B) fits one workgroup's LDS; beyond
+// window_batch vectors fewer workgroups share a CU.
 size_t window_bytes(const Matrix &m, uint32_t B, int *use) {
-    *use = (m.window_elems > 0 && B <= m.window_batch) ? 1 : 0;
-    if (!*use) return 0;
-    return (size_t(1) << m.plan.window_log2) * B * 4;
+    const size_t bytes = m.plan.window_log2 >= 0 ? (size_t(1) << m.plan.window_log2) * B * 4 : 0;
+    *use = (m.window_elems > 0 && bytes <= m.max_window_lds) ? 1 : 0;
+    return *use ? bytes : 0;
 }
 
 int set_lds_limit(const void *k, size_t lds) {
@@ -724,7 +730,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     using T = typename SR::T;
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
     if (n_tiles == 0) return hipSuccess;
-    const uint32_t VL = lanes_per_node(B);
+    const uint32_t VL = lanes_per_node(B, DIR);
     const uint32_t grid = grid_for(n_tiles);
     int use = 0;
     const size_t lds = window_bytes(m, B, &use);
@@ -748,7 +754,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     // descent tiles are planned without windows: reserve no window LDS
     const int use = 0;
     const size_t lds = size_t(2) * cap * sizeof(uint64_t);
-    const uint32_t VL = lanes_per_node(B);
+    const uint32_t VL = lanes_per_node(B, DIR);
     const uint32_t grid = grid_for(n_tiles);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     auto k = descent_kernel<SR, DIR, EMIT, Off>;

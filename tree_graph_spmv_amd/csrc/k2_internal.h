@@ -123,6 +123,7 @@ struct Matrix {
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
     uint64_t *d_cached = nullptr;        // last internal level codes or null
     uint32_t window_elems = 0, window_batch = 0;
+    size_t max_window_lds = 0;   // LDS bytes a product's window may take per workgroup
     bool cached = false;
     // kernel timing (events created on first enable)
     void *ev[3] = {nullptr, nullptr, nullptr};
