@@ -229,6 +229,36 @@ def test_scan_offsets(case):
         assert np.all(t.plan(dir_opts, 0)[1][:, 7] == 0)
 
 
+def test_descent_order(case):
+    """Right / left products take the descent tiles in order of the output
+    block (row / column >> k, 2^k * window_batch * 4 the largest power of 2
+    <= 16 MB) of each tile's first node, depth first within a block."""
+    name, r, c, nr, nc, t, o = case
+    opts = k2.plan_defaults(window_batch=8)
+    kb = 19
+    top, tiles, codes = t.plan(opts, 0)
+    L = o.levels
+    for which, odd in ((3, 1), (4, 0)):
+        _, ordered, codes2 = t.plan(opts, which)
+        assert np.array_equal(codes2, codes)
+        assert sorted(map(tuple, ordered.tolist())) == sorted(map(tuple, tiles.tolist()))
+        keys = []
+        for tl in ordered:
+            code = int(codes[int(tl[3])])
+            coord = 0
+            for k in range(int(tl[2])):   # odd bits are rows, even bits columns
+                coord |= ((code >> (2 * k + odd)) & 1) << k
+            keys.append((coord << (L - int(tl[2]))) >> kb)
+        assert keys == sorted(keys), name
+        # depth first within a block: the tiles' first descendants on the
+        # last internal level increase within each block
+        pos = {tuple(tl.tolist()): i for i, tl in enumerate(tiles)}
+        idx = [pos[tuple(tl.tolist())] for tl in ordered]
+        for a in range(1, len(idx)):
+            if keys[a] == keys[a - 1]:
+                assert idx[a] > idx[a - 1]
+
+
 def test_top_level(case):
     name, r, c, nr, nc, t, o = case
     nodes = o.level_nodes()
@@ -254,7 +284,8 @@ def test_estimate_parts(case):
         else:
             assert est["directory"] == 4 * t.plan_offsets(opts).size
         assert est["top_codes"] == 8 * len(codes)
-        assert est["tiles"] == 32 * len(tiles) + (extra if cached else 0)
+        # descent tiles, their two direction orders, the cached tiles
+        assert est["tiles"] == (32 + 2 * 4) * len(tiles) + (extra if cached else 0)
         assert est["cached_codes"] == (8 * nodes[L - 2] if cached else 0)
         parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
                                      "scratch", "alignment"))

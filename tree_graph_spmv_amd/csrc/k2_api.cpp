@@ -192,7 +192,7 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
 
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux) {
-    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 2) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 4) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -202,14 +202,15 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
     }
     if (st != K2_OK) return st;
     if (top_level) *top_level = uint32_t(plan.top_level);
-    if (n_tiles) *n_tiles = which == 0 ? plan.tiles.size() : plan.cached_tiles[which - 1].size();
-    if (n_aux) *n_aux = which == 0 ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
+    const bool descent = which == 0 || which >= 3;
+    if (n_tiles) *n_tiles = descent ? plan.tiles.size() : plan.cached_tiles[which - 1].size();
+    if (n_aux) *n_aux = descent ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
     return K2_OK;
 }
 
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which, uint32_t *tiles,
                         uint64_t n_tiles, uint64_t *aux, uint64_t n_aux) {
-    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 2) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 4) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -218,8 +219,14 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
         return K2_E_HOST_OOM;
     }
     if (st != K2_OK) return st;
-    const std::vector<Tile> &list = which == 0 ? plan.tiles : plan.cached_tiles[which - 1];
-    const uint64_t naux = which == 0 ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
+    // which 3 / 4: the descent tiles in the order right / left products take them
+    std::vector<Tile> ordered;
+    if (which >= 3)
+        for (uint32_t i : plan.tile_order[which - 3]) ordered.push_back(plan.tiles[i]);
+    const std::vector<Tile> &list =
+        which == 0 ? plan.tiles : which >= 3 ? ordered : plan.cached_tiles[which - 1];
+    const bool codes_aux = which == 0 || which >= 3;
+    const uint64_t naux = codes_aux ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
     if (n_tiles < list.size() || n_aux < naux) return K2_E_INVALID_ARG;
     if ((!tiles && !list.empty()) || (!aux && naux)) return K2_E_INVALID_ARG;
     for (size_t k = 0; k < list.size(); ++k) {
@@ -228,7 +235,7 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
                                tl.win_row, tl.win_col, tl.win_log2, tl.base_off};
         std::copy(v, v + 8, tiles + 8 * k);
     }
-    if (which == 0) {
+    if (codes_aux) {
         std::copy(plan.codes.begin(), plan.codes.end(), aux);
     } else {
         const std::vector<Seg> &sg = plan.cached_segs[which - 1];
@@ -349,6 +356,17 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
                                       m.plan.tile_bases.size() * 4, hipMemcpyHostToDevice, st_h);
         if (e != hipSuccess) {
             set_hip_error(int(e), "upload tile offsets");
+            return fail(K2_E_HIP);
+        }
+    }
+    for (int dir = 0; dir < 2; ++dir) {
+        const std::vector<uint32_t> &ord = m.plan.tile_order[dir];
+        if (ord.empty()) continue;
+        m.d_tile_order[dir] = reinterpret_cast<const uint32_t *>(m.arena + m.layout.order_off[dir]);
+        hipError_t e = hipMemcpyAsync(const_cast<uint32_t *>(m.d_tile_order[dir]), ord.data(), ord.size() * 4,
+                                      hipMemcpyHostToDevice, st_h);
+        if (e != hipSuccess) {
+            set_hip_error(int(e), "upload tile order");
             return fail(K2_E_HIP);
         }
     }

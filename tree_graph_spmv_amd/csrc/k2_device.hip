@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
     const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases) {
+    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, const uint32_t *__restrict__ order) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
     T *s_win = reinterpret_cast<T *>(s_front + 2 * size_t(cap));
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
-        const Tile tl = tiles[ti];
+        const Tile tl = tiles[order ? order[ti] : ti];
         int d = int(tl.level);
         uint32_t lo = tl.first, cnt = tl.count;
         uint64_t *cur = s_front, *nxt = s_front + cap;
@@ -762,7 +762,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_tiles, n_tiles, m.d_codes,
                        cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit,
-                       m.d_bases);
+                       m.d_bases, EMIT ? nullptr : m.d_tile_order[DIR]);
     return hipGetLastError();
 }
 

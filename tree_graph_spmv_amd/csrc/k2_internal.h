@@ -80,6 +80,9 @@ struct Plan {
     // spans, tile_bases[tiles[k].base_off + (d - tiles[k].level)] for d = level ..
     // last internal level (the last entry is its first leaf)
     std::vector<uint32_t> tile_bases;
+    // per direction, the order the descent kernel takes the descent tiles in
+    // (by output block, then depth first)
+    std::vector<uint32_t> tile_order[2];
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -90,6 +93,7 @@ struct Layout {
     uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
     uint64_t codes_off = 0, tiles_off = 0, cached_off = 0, bases_off = 0;
+    uint64_t order_off[2] = {0, 0};
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     k2_mem_breakdown mem = {};
 };
@@ -119,6 +123,7 @@ struct Matrix {
     const uint64_t *d_codes = nullptr;   // tile start codes
     const Tile *d_tiles = nullptr;
     const uint32_t *d_bases = nullptr;   // scan offsets of the descent tiles, or null
+    const uint32_t *d_tile_order[2] = {nullptr, nullptr};
     const Tile *d_cached_tiles[2] = {nullptr, nullptr};
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
     uint64_t *d_cached = nullptr;        // last internal level codes or null

@@ -187,6 +187,15 @@ Tile no_window() {
     return w;
 }
 
+// log2 of the rows (right products) or columns (left) of an output block:
+// about 16 MB of y at window_batch vectors, at least 2^min_log2.
+int block_log2(const k2_plan_opts &o, int min_log2) {
+    int kb = min_log2;
+    const uint64_t wb = o.window_batch ? o.window_batch : 1;
+    while (kb < 30 && (2ull << kb) * wb * 4 <= (16ull << 20)) ++kb;
+    return kb;
+}
+
 Tile window_of(uint64_t code, int h, int L) {
     Tile w{};
     const int sh = L - h;                       // log2 of the quadrant side
@@ -287,6 +296,24 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles: the plain depth-first cut (windowed descent tiles, one
     // per dense quadrant, measured slower: many small tiles)
     pl.range(d0, 0, t.nodes[d0], 0, no_window());
+    {   // descent order per direction: by output block of the tile's first
+        // node, then depth first, so the tiles in flight update one slice of
+        // y (its lines stay in the last-level cache while the atomics land)
+        const int kb = block_log2(o, 0);
+        for (int dir = 0; dir < 2; ++dir) {
+            std::vector<std::pair<uint64_t, uint32_t>> key(p.tiles.size());
+            for (size_t i = 0; i < p.tiles.size(); ++i) {
+                const Tile &tl = p.tiles[i];
+                const uint64_t code = p.codes[tl.code_off];
+                const uint64_t c = dir == K2_RIGHT ? even_bits(code >> 1) : even_bits(code);
+                key[i] = {(c << (L - int(tl.level))) >> kb, uint32_t(i)};
+            }
+            std::stable_sort(key.begin(), key.end(),
+                             [](const auto &x, const auto &y) { return x.first < y.first; });
+            p.tile_order[dir].resize(key.size());
+            for (size_t i = 0; i < key.size(); ++i) p.tile_order[dir][i] = key[i].second;
+        }
+    }
     p.use_directory = o.offsets == K2_OFFSETS_DIRECTORY;
     if (!p.use_directory) {
         // scan offsets: each descent tile's first child on every level it
@@ -427,8 +454,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // tiles in flight then update one narrow slice of y, whose lines the
     // chip's last-level cache can hold while their atomics arrive.
     const uint64_t band_min = std::max<uint64_t>(64, side * o.window_batch / 32);
-    int kb = L - h;
-    while (kb < 30 && (2ull << kb) * o.window_batch * 4 <= (16ull << 20)) ++kb;
+    const int kb = block_log2(o, L - h);
     for (int dir = 0; dir < 2; ++dir) {
         // output coordinate of a quadrant's first cell
         auto out_of = [&](uint64_t code, int level) -> uint64_t {
@@ -537,6 +563,7 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
     l.bases_off = take(4 * plan.tile_bases.size(), l.mem.directory);
     l.codes_off = take(8 * plan.codes.size(), l.mem.top_codes);
     l.tiles_off = take(sizeof(Tile) * plan.tiles.size(), l.mem.tiles);
+    for (int dir = 0; dir < 2; ++dir) l.order_off[dir] = take(4 * plan.tile_order[dir].size(), l.mem.tiles);
     for (int dir = 0; dir < 2; ++dir) {
         l.cached_tiles_off[dir] = take(cached ? sizeof(Tile) * plan.cached_tiles[dir].size() : 0, l.mem.tiles);
         l.cached_segs_off[dir] = take(cached ? sizeof(Seg) * plan.cached_segs[dir].size() : 0, l.mem.tiles);
