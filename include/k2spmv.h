@@ -197,12 +197,13 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
                                    k2_mem_breakdown *out);
 
 /* The tile plans a matrix created with 'opts' would use (host only, no HIP
-   call; Sec. 3.4).  which = 0: the descent tiles and their start codes;
-   1 / 2: the cached-level tiles of right / left products and their
-   segments (empty unless opts->cache_last_level); 3 / 4: the descent tiles
-   in the order right / left products take them.  Reports the host-top
-   level d0, the number of tiles and of codes (which = 0, 3, 4) or twice the
-   number of segments (1, 2).  Errors: K2_E_INVALID_ARG. */
+   call; Sec. 3.4).  which = 0: the descent tiles (depth first) and their
+   start codes (all codes of the plan); 1 / 2: the cached-level tiles of
+   right / left products and their segments (empty unless
+   opts->cache_last_level); for tree-only right / left products, 3 / 4: the
+   rest tiles and their skip ranges, 5 / 6: the band groups, 7 / 8: the
+   band groups' tiles.  Reports the host-top level d0, the number of tiles
+   and of aux entries (see k2_plan_tiles).  Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux);
 
@@ -214,10 +215,17 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
    offsets (k2_plan_offsets); otherwise the base index is 0.
    which = 0: 'count' nodes of 'level' from node 'first', whose Morton codes
    (row bit above column bit per level, 2*level bits) are aux[code index ..].
-   which = 3 / 4: the descent tiles (as for 0) in the order right / left
-   products take them: by output block (2^k rows / columns with 2^k *
-   window_batch * 4 the largest power of 2 <= 16 MB; the block of a tile's
-   first node), then depth first (stable).
+   Tree-only right / left products take, when windows are planned and the
+   batch fits them, first the band groups (which = 5 / 6), each a workgroup's
+   job: 'count' tiles from tile 'first' of list 7 / 8 (descent tiles as for
+   0, over the dense quadrants of one row / column band), sharing the
+   group's window (fields 4-6); then the rest tiles (which = 3 / 4): descent
+   tiles as for 0, in order of output block (2^k rows / columns, 2^k *
+   window_batch * 4 the largest power of 2 <= 16 MB; a tile's block is its
+   first node's), that skip the last-internal-level nodes band groups cover:
+   'window column' ranges from aux index 'window row', each aux[r] = (first
+   node << 32) | end node.  Without planned windows the rest tiles are every
+   descent tile, skipping nothing.
    which = 1 / 2: 'count' segments of the last internal level from segment
    'first'; segment r is aux[2r] = (first node << 32) | node count (1..64)
    and aux[2r + 1] = the leaf-level index of its first node's first child.

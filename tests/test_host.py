@@ -215,48 +215,104 @@ def test_scan_offsets(case):
         top, tiles, codes = t.plan(opts, 0)
         bases = t.plan_offsets(opts)
         total = 0
-        for tl in tiles:
-            level, first, at = int(tl[2]), int(tl[0]), int(tl[7])
-            assert at == total
-            node = first
-            for d in range(level, L - 1):
-                node = int(offs[d][node]) if node < nodes[d] else nodes[d + 1]
-                assert int(bases[at + d - level]) == node, (name, d)
-            total += L - 1 - level
+        lists = [tiles] + [t.plan(opts, w)[1] for w in (7, 8)]   # descent tiles, band tiles
+        for lst in lists:
+            for tl in lst:
+                level, first, at = int(tl[2]), int(tl[0]), int(tl[7])
+                node = first
+                for d in range(level, L - 1):
+                    node = int(offs[d][node]) if node < nodes[d] else nodes[d + 1]
+                    assert int(bases[at + d - level]) == node, (name, d)
+                total += L - 1 - level
         assert total == bases.size
         dir_opts = k2.plan_defaults(tile_nodes=tile_nodes, offsets="directory")
         assert np.array_equal(t.plan(dir_opts, 0)[1][:, :7], tiles[:, :7])
         assert np.all(t.plan(dir_opts, 0)[1][:, 7] == 0)
 
 
-def test_descent_order(case):
-    """Right / left products take the descent tiles in order of the output
-    block (row / column >> k, 2^k * window_batch * 4 the largest power of 2
-    <= 16 MB) of each tile's first node, depth first within a block."""
+@pytest.mark.parametrize("opt", [dict(), dict(window_elems=0), dict(window_elems=1024, window_batch=1),
+                                 dict(tile_nodes=256), dict(host_top_max=4)])
+def test_tree_only_plan(case, opt):
+    """Tree-only products, per direction: the band groups' tiles (with their
+    band window) and the rest tiles minus their skip ranges cover the last
+    internal level exactly once; a band tile's outputs lie in its window and
+    its subtree holds at most min(tile_nodes, 512) nodes per level; rest
+    tiles come in output-block order (2^k * window_batch * 4 the largest
+    power of 2 <= 16 MB)."""
     name, r, c, nr, nc, t, o = case
-    opts = k2.plan_defaults(window_batch=8)
-    kb = 19
-    top, tiles, codes = t.plan(opts, 0)
+    opts = k2.plan_defaults(**opt)
     L = o.levels
-    for which, odd in ((3, 1), (4, 0)):
-        _, ordered, codes2 = t.plan(opts, which)
-        assert np.array_equal(codes2, codes)
-        assert sorted(map(tuple, ordered.tolist())) == sorted(map(tuple, tiles.tolist()))
+    last = L - 2
+    nodes = o.level_nodes()
+    if nodes[last] == 0:
+        return
+    offs = [o.child_offsets(d) for d in range(L - 1)]
+
+    def down(d, i):
+        while d < last:
+            i = int(offs[d][i]) if i < nodes[d] else nodes[d + 1]
+            d += 1
+        return i
+    cr, cc = o.cells()
+    leaf_pop = np.array([bin(int(s)).count("1") for s in o.signatures(L - 1)], np.int64)
+    cell_start = np.concatenate([[0], np.cumsum(leaf_pop)])
+
+    def cells_of(a, b):
+        la = int(offs[last][a]) if a < nodes[last] else nodes[L - 1]
+        lb = int(offs[last][b]) if b < nodes[last] else nodes[L - 1]
+        return cr[cell_start[la]:cell_start[lb]], cc[cell_start[la]:cell_start[lb]]
+    all_codes = oracle_codes(o, last)
+    _, _, codes = t.plan(opts, 0)
+    cap = min(opts.tile_nodes, 512)
+    wb = max(opts.window_batch, 1)
+    kb = 0
+    while kb < 30 and (2 << kb) * wb * 4 <= (16 << 20):
+        kb += 1
+    for w, out_is_row in ((0, True), (1, False)):
+        covered = []
+        groups = t.plan(opts, 5 + w)[1]
+        sub = t.plan(opts, 7 + w)[1]
+        assert sum(int(g[1]) for g in groups) == len(sub)
+        for g in groups:
+            side = 1 << int(g[6])
+            base = int(g[4]) if out_is_row else int(g[5])
+            for tl in sub[int(g[0]):int(g[0]) + int(g[1])]:
+                first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
+                assert np.array_equal(codes[int(tl[3]):int(tl[3]) + count], all_codes[level][first:first + count])
+                a, b = down(level, first), down(level, first + count)
+                assert b - a <= cap
+                rr, ccc = cells_of(a, b)
+                out = rr if out_is_row else ccc
+                assert np.all((out >= base) & (out < base + side)), "band output outside its window"
+                covered.append((a, b))
+        _, rest, skips = t.plan(opts, 3 + w)
         keys = []
-        for tl in ordered:
+        for tl in rest:
+            first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
+            a, b = down(level, first), down(level, first + count)
             code = int(codes[int(tl[3])])
             coord = 0
-            for k in range(int(tl[2])):   # odd bits are rows, even bits columns
-                coord |= ((code >> (2 * k + odd)) & 1) << k
-            keys.append((coord << (L - int(tl[2]))) >> kb)
-        assert keys == sorted(keys), name
-        # depth first within a block: the tiles' first descendants on the
-        # last internal level increase within each block
-        pos = {tuple(tl.tolist()): i for i, tl in enumerate(tiles)}
-        idx = [pos[tuple(tl.tolist())] for tl in ordered]
-        for a in range(1, len(idx)):
-            if keys[a] == keys[a - 1]:
-                assert idx[a] > idx[a - 1]
+            for k in range(level):
+                coord |= ((code >> (2 * k + (1 if out_is_row else 0))) & 1) << k
+            keys.append((coord << (L - level)) >> kb)
+            pos = a
+            for sk in skips[int(tl[4]):int(tl[4]) + int(tl[5])]:
+                lo, hi = int(sk) >> 32, int(sk) & 0xFFFFFFFF
+                assert a <= lo < hi <= b and lo >= pos
+                if lo > pos:
+                    covered.append((pos, lo))
+                pos = hi
+            if pos < b:
+                covered.append((pos, b))
+            assert int(tl[5]) == 0 or (b - a) > sum((int(x) & 0xFFFFFFFF) - (int(x) >> 32)
+                                                    for x in skips[int(tl[4]):int(tl[4]) + int(tl[5])])
+        assert keys == sorted(keys)
+        covered.sort()
+        pos = 0
+        for a, b in covered:
+            assert a == pos, (name, w, "tree-only items must cover the level exactly once")
+            pos = b
+        assert pos == nodes[last]
 
 
 def test_top_level(case):
@@ -284,8 +340,10 @@ def test_estimate_parts(case):
         else:
             assert est["directory"] == 4 * t.plan_offsets(opts).size
         assert est["top_codes"] == 8 * len(codes)
-        # descent tiles, their two direction orders, the cached tiles
-        assert est["tiles"] == (32 + 2 * 4) * len(tiles) + (extra if cached else 0)
+        # descent tiles, the tree-only lists of both directions, the cached tiles
+        tree_only = sum(32 * (len(t.plan(opts, 3 + w)[1]) + len(t.plan(opts, 5 + w)[1]) +
+                              len(t.plan(opts, 7 + w)[1])) + 8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
+        assert est["tiles"] == 32 * len(tiles) + tree_only + (extra if cached else 0)
         assert est["cached_codes"] == (8 * nodes[L - 2] if cached else 0)
         parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
                                      "scratch", "alignment"))

@@ -222,7 +222,7 @@ class Tree:
                                    tiles.ctypes.data_as(_U32P), nt.value, aux.ctypes.data_as(_U64P),
                                    na.value), "k2_plan_tiles")
         aux = aux[:na.value]
-        return int(top.value), tiles[:nt.value], aux if which in (0, 3, 4) else aux.reshape(-1, 2)
+        return int(top.value), tiles[:nt.value], aux.reshape(-1, 2) if which in (1, 2) else aux
 
 
 def _stream_handle(stream):

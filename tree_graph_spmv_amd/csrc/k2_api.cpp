@@ -190,9 +190,28 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
     return K2_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The tile list and aux entry count k2_plan_tiles exports for 'which'.
+void plan_list(const Plan &p, int which, const std::vector<Tile> **list, uint64_t *naux) {
+    switch (which) {
+    case 0: *list = &p.tiles; *naux = p.codes.size(); break;
+    case 1: case 2: *list = &p.cached_tiles[which - 1]; *naux = 2 * p.cached_segs[which - 1].size(); break;
+    case 3: case 4: *list = &p.rest_tiles[which - 3]; *naux = p.skip[which - 3].size(); break;
+    case 5: case 6: *list = &p.band_groups[which - 5]; *naux = 0; break;
+    default: *list = &p.band_sub[which - 7]; *naux = 0; break;
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux) {
-    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 4) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 8) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -202,15 +221,17 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
     }
     if (st != K2_OK) return st;
     if (top_level) *top_level = uint32_t(plan.top_level);
-    const bool descent = which == 0 || which >= 3;
-    if (n_tiles) *n_tiles = descent ? plan.tiles.size() : plan.cached_tiles[which - 1].size();
-    if (n_aux) *n_aux = descent ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
+    const std::vector<Tile> *list = nullptr;
+    uint64_t naux = 0;
+    plan_list(plan, which, &list, &naux);
+    if (n_tiles) *n_tiles = list->size();
+    if (n_aux) *n_aux = naux;
     return K2_OK;
 }
 
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which, uint32_t *tiles,
                         uint64_t n_tiles, uint64_t *aux, uint64_t n_aux) {
-    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 4) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 8) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -219,14 +240,10 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
         return K2_E_HOST_OOM;
     }
     if (st != K2_OK) return st;
-    // which 3 / 4: the descent tiles in the order right / left products take them
-    std::vector<Tile> ordered;
-    if (which >= 3)
-        for (uint32_t i : plan.tile_order[which - 3]) ordered.push_back(plan.tiles[i]);
-    const std::vector<Tile> &list =
-        which == 0 ? plan.tiles : which >= 3 ? ordered : plan.cached_tiles[which - 1];
-    const bool codes_aux = which == 0 || which >= 3;
-    const uint64_t naux = codes_aux ? plan.codes.size() : 2 * plan.cached_segs[which - 1].size();
+    const std::vector<Tile> *lp = nullptr;
+    uint64_t naux = 0;
+    plan_list(plan, which, &lp, &naux);
+    const std::vector<Tile> &list = *lp;
     if (n_tiles < list.size() || n_aux < naux) return K2_E_INVALID_ARG;
     if ((!tiles && !list.empty()) || (!aux && naux)) return K2_E_INVALID_ARG;
     for (size_t k = 0; k < list.size(); ++k) {
@@ -235,9 +252,11 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
                                tl.win_row, tl.win_col, tl.win_log2, tl.base_off};
         std::copy(v, v + 8, tiles + 8 * k);
     }
-    if (codes_aux) {
+    if (which == 0) {
         std::copy(plan.codes.begin(), plan.codes.end(), aux);
-    } else {
+    } else if (which == 3 || which == 4) {
+        std::copy(plan.skip[which - 3].begin(), plan.skip[which - 3].end(), aux);
+    } else if (which == 1 || which == 2) {
         const std::vector<Seg> &sg = plan.cached_segs[which - 1];
         for (size_t k = 0; k < sg.size(); ++k) {
             aux[2 * k] = (uint64_t(sg[k].lo) << 32) | sg[k].count;
@@ -360,15 +379,27 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
         }
     }
     for (int dir = 0; dir < 2; ++dir) {
-        const std::vector<uint32_t> &ord = m.plan.tile_order[dir];
-        if (ord.empty()) continue;
-        m.d_tile_order[dir] = reinterpret_cast<const uint32_t *>(m.arena + m.layout.order_off[dir]);
-        hipError_t e = hipMemcpyAsync(const_cast<uint32_t *>(m.d_tile_order[dir]), ord.data(), ord.size() * 4,
-                                      hipMemcpyHostToDevice, st_h);
-        if (e != hipSuccess) {
-            set_hip_error(int(e), "upload tile order");
-            return fail(K2_E_HIP);
-        }
+        auto up = [&](uint64_t off, const void *src, uint64_t bytes) -> const char * {
+            if (!bytes) return nullptr;
+            char *dst = m.arena + off;
+            hipError_t e = hipMemcpyAsync(dst, src, bytes, hipMemcpyHostToDevice, st_h);
+            if (e != hipSuccess) {
+                set_hip_error(int(e), "upload tree-only plan");
+                return reinterpret_cast<const char *>(1);
+            }
+            return dst;
+        };
+        const Plan &pn = m.plan;
+        const char *g = up(m.layout.groups_off[dir], pn.band_groups[dir].data(), pn.band_groups[dir].size() * sizeof(Tile));
+        const char *sb = up(m.layout.sub_off[dir], pn.band_sub[dir].data(), pn.band_sub[dir].size() * sizeof(Tile));
+        const char *r = up(m.layout.rest_off[dir], pn.rest_tiles[dir].data(), pn.rest_tiles[dir].size() * sizeof(Tile));
+        const char *k = up(m.layout.skip_off[dir], pn.skip[dir].data(), pn.skip[dir].size() * 8);
+        const char *bad = reinterpret_cast<const char *>(1);
+        if (g == bad || sb == bad || r == bad || k == bad) return fail(K2_E_HIP);
+        m.d_band_groups[dir] = reinterpret_cast<const Tile *>(g);
+        m.d_band_sub[dir] = reinterpret_cast<const Tile *>(sb);
+        m.d_rest[dir] = reinterpret_cast<const Tile *>(r);
+        m.d_skip[dir] = reinterpret_cast<const uint64_t *>(k);
     }
     if (!m.plan.tiles.empty()) {
         hipError_t e = hipMemcpyAsync(const_cast<Tile *>(m.d_tiles), m.plan.tiles.data(),

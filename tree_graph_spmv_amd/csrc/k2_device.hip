@@ -43,6 +43,9 @@ namespace k2 {
 
 struct PlusTimes {
     using T = float;
+    // tree-only products use the band groups: every cell's contribution is an
+    // atomic add that the windows absorb
+    static constexpr bool kTreeBands = true;
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0.0f; }
     __device__ static bool contributes(T x) { return x != 0.0f; }
@@ -69,6 +72,8 @@ struct PlusTimes {
 
 struct BooleanF32 {
     using T = float;
+    // tree-only products take the depth-first tiles (see PlusTimes)
+    static constexpr bool kTreeBands = false;
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0.0f; }
     __device__ static bool contributes(T x) { return (__float_as_uint(x) & 0x7FFFFFFFu) != 0u; }
@@ -87,6 +92,8 @@ struct BooleanF32 {
 
 struct BooleanU32 {
     using T = uint32_t;
+    // tree-only products take the depth-first tiles (see PlusTimes)
+    static constexpr bool kTreeBands = false;
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0u; }
     __device__ static bool contributes(T x) { return x != 0u; }
@@ -103,6 +110,9 @@ struct BooleanU32 {
 
 struct Tropical {
     using T = float;
+    // tree-only products take the depth-first tiles: contributions equal
+    // to the zero (x = +inf) issue no atomic, and relaxation steps skip most
+    static constexpr bool kTreeBands = false;
     static constexpr uint32_t kZeroBits = 0x7F800000u;   // +inf
     __device__ static T zero() { return __uint_as_float(kZeroBits); }
     __device__ static bool contributes(T x) { return x < __uint_as_float(kZeroBits); }
@@ -522,17 +532,33 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     }
 }
 
+// Whether v lies in one of the n sorted disjoint ranges r[k] = (lo << 32) | hi.
+__device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32_t n, uint32_t v) {
+    uint32_t a = 0, b = n;
+    while (a < b) {   // the first range ending after v
+        const uint32_t mid = (a + b) >> 1;
+        if (uint32_t(r[mid]) <= v) a = mid + 1;
+        else b = mid;
+    }
+    return a < n && uint32_t(r[a] >> 32) <= v;
+}
+
 // One product by tiled descent (Algorithm 1 with the tiles of Sec. 3.4): each
-// workgroup takes a tile and expands it level by level inside LDS, then visits
-// the leaves of its last-internal-level nodes in place.  With 'emit' set it
-// writes those nodes' block origins instead (building the cached level,
+// workgroup takes an item and, for each of its tiles, expands the tile level
+// by level inside LDS, then visits the leaves of its last-internal-level nodes
+// in place.  An item is a group (groups non-null: 'count' tiles from tiles +
+// 'first', sharing the group's LDS window) or a single tile.  A tile with
+// skips (win_col ranges from skips + win_row) leaves the listed
+// last-internal-level nodes to other items.  With 'emit' set the kernel
+// writes the last level's block origins instead (building the cached level,
 // Sec. 3.5).
 template <class SR, int DIR, bool EMIT, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
-    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles,
-    const uint64_t *__restrict__ tile_codes, uint32_t cap, const typename SR::T *__restrict__ x,
+    DevTree t, const Tile *__restrict__ groups, const Tile *__restrict__ tiles, uint32_t n_items,
+    const uint64_t *__restrict__ skips, const uint64_t *__restrict__ tile_codes, uint32_t cap,
+    const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, const uint32_t *__restrict__ order) {
+    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
@@ -542,8 +568,19 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     const int last = t.levels - 2;
     const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
     T *s_win = reinterpret_cast<T *>(s_front + 2 * size_t(cap));
-    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
-        const Tile tl = tiles[order ? order[ti] : ti];
+    for (uint32_t gi = blockIdx.x; gi < n_items; gi += gridDim.x) {
+      Tile gr;
+      if (groups) {
+          gr = groups[gi];
+      } else {
+          gr.first = gi;
+          gr.count = 1;
+          gr.win_log2 = kNoWindow;
+      }
+      const Window<T> w = EMIT ? Window<T>{nullptr, 0, 0} : open_window<SR, DIR>(gr, s_win, use_window, B);
+      for (uint32_t si = 0; si < gr.count; ++si) {
+        const Tile tl = tiles[gr.first + si];
+        const uint32_t nskip = skips ? tl.win_col : 0u;
         int d = int(tl.level);
         uint32_t lo = tl.first, cnt = tl.count;
         uint64_t *cur = s_front, *nxt = s_front + cap;
@@ -582,7 +619,6 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 emit[uint64_t(lo) + i] = (uint64_t(compact_even(cur[i] >> 1) * 4u) << 32) |
                                          (compact_even(cur[i]) * 4u);
         } else {
-            const Window<T> w = open_window<SR, DIR>(tl, s_win, use_window, B);
             const uint64_t *__restrict__ wd = t.words[last];
             const uint64_t *__restrict__ leaf_words = t.words[last + 1];
             uint32_t leaf0 = 0;
@@ -611,12 +647,15 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                     base = wave_child_offset(t, last, lo + seg);
                 }
                 uint32_t total;
-                const uint32_t ex = wave_scan(__popc(s), total);
-                leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_words, x, y, B, VL, w, &s_cells[wave]);
+                const uint32_t ex = wave_scan(__popc(s), total);   // the true fan-outs give the offsets
+                const bool skip = valid && nskip && in_ranges(skips + tl.win_row, nskip, lo + i);
+                leaf_segment<SR, DIR, Off>(code, skip ? 0u : s, base + ex, leaf_words, x, y, B, VL, w,
+                                           &s_cells[wave]);
             }
-            close_window<SR>(w, y, n_out, B);
         }
         __syncthreads();
+      }
+      if (!EMIT) close_window<SR>(w, y, n_out, B);
     }
 }
 
@@ -748,22 +787,37 @@ template <class SR, int DIR, bool EMIT, class Off = uint32_t>
 int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *emit,
                 hipStream_t st) {
     using T = typename SR::T;
-    const uint32_t n_tiles = uint32_t(m.plan.tiles.size());
-    if (n_tiles == 0) return hipSuccess;
-    const uint32_t cap = m.plan.tile_nodes;
-    // descent tiles are planned without windows: reserve no window LDS
-    const int use = 0;
-    const size_t lds = size_t(2) * cap * sizeof(uint64_t);
     const uint32_t VL = lanes_per_node(B, DIR);
-    const uint32_t grid = grid_for(n_tiles);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     auto k = descent_kernel<SR, DIR, EMIT, Off>;
-    int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_tiles, n_tiles, m.d_codes,
-                       cap, static_cast<const T *>(x), static_cast<T *>(y), B, VL, n_out, use, emit,
-                       m.d_bases, EMIT ? nullptr : m.d_tile_order[DIR]);
-    return hipGetLastError();
+    // one launch over items (groups of tiles, or tiles); LDS: the frontier's
+    // two levels of 'cap' codes, then the window
+    auto launch = [&](const Tile *groups, const Tile *tiles, size_t n_items, const uint64_t *skips,
+                      uint32_t cap, int use, size_t win_bytes) -> int {
+        if (n_items == 0) return hipSuccess;
+        const size_t lds = size_t(2) * cap * sizeof(uint64_t) + win_bytes;
+        int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(k, dim3(grid_for(n_items)), dim3(kThreads), lds, st, m.dev, groups, tiles,
+                           uint32_t(n_items), skips, m.d_codes, cap, static_cast<const T *>(x),
+                           static_cast<T *>(y), B, VL, n_out, use, emit, m.d_bases);
+        return hipGetLastError();
+    };
+    const Plan &p = m.plan;
+    if (EMIT) return launch(nullptr, m.d_tiles, p.tiles.size(), nullptr, p.tile_nodes, 0, 0);
+    int use = 0;
+    const size_t wb = SR::kTreeBands ? window_bytes(m, B, &use) : 0;
+    if (use) {
+        // the bands' dense quadrants into their windows, then the rest
+        int e = launch(m.d_band_groups[DIR], m.d_band_sub[DIR], p.band_groups[DIR].size(), nullptr,
+                       p.band_cap, 1, wb);
+        if (e != hipSuccess) return e;
+        return launch(nullptr, m.d_rest[DIR], p.rest_tiles[DIR].size(), m.d_skip[DIR], p.tile_nodes, 0, 0);
+    }
+    if (p.window_log2 < 0 && SR::kTreeBands)   // no windows planned: every tile, in block order
+        return launch(nullptr, m.d_rest[DIR], p.rest_tiles[DIR].size(), nullptr, p.tile_nodes, 0, 0);
+    // every tile, depth first
+    return launch(nullptr, m.d_tiles, p.tiles.size(), nullptr, p.tile_nodes, 0, 0);
 }
 
 template <int DIR>

@@ -80,9 +80,20 @@ struct Plan {
     // spans, tile_bases[tiles[k].base_off + (d - tiles[k].level)] for d = level ..
     // last internal level (the last entry is its first leaf)
     std::vector<uint32_t> tile_bases;
-    // per direction, the order the descent kernel takes the descent tiles in
+    // per direction, the order the descent tiles are taken in for products
     // (by output block, then depth first)
     std::vector<uint32_t> tile_order[2];
+    // Tree-only products, per direction.  Band groups (when windows are
+    // planned): a group (first, count = its sub-tiles in band_sub[dir], window
+    // fields) descends the dense quadrants of one row / column band into one
+    // LDS window, with frontiers of at most band_cap nodes.  The rest: the
+    // descent tiles in tile_order[dir] that are not wholly inside windowed
+    // quadrants, each skipping the last-internal-level nodes listed for it in
+    // skip[dir] (ranges (lo << 32) | hi, sorted): rest_tiles[dir] holds them
+    // as tiles with win_row = first skip range, win_col = skip count.
+    uint32_t band_cap = 0;
+    std::vector<Tile> band_groups[2], band_sub[2], rest_tiles[2];
+    std::vector<uint64_t> skip[2];
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -93,7 +104,7 @@ struct Layout {
     uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
     uint64_t codes_off = 0, tiles_off = 0, cached_off = 0, bases_off = 0;
-    uint64_t order_off[2] = {0, 0};
+    uint64_t groups_off[2] = {0, 0}, sub_off[2] = {0, 0}, rest_off[2] = {0, 0}, skip_off[2] = {0, 0};
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     k2_mem_breakdown mem = {};
 };
@@ -123,7 +134,9 @@ struct Matrix {
     const uint64_t *d_codes = nullptr;   // tile start codes
     const Tile *d_tiles = nullptr;
     const uint32_t *d_bases = nullptr;   // scan offsets of the descent tiles, or null
-    const uint32_t *d_tile_order[2] = {nullptr, nullptr};
+    const Tile *d_band_groups[2] = {nullptr, nullptr}, *d_band_sub[2] = {nullptr, nullptr};
+    const Tile *d_rest[2] = {nullptr, nullptr};
+    const uint64_t *d_skip[2] = {nullptr, nullptr};
     const Tile *d_cached_tiles[2] = {nullptr, nullptr};
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
     uint64_t *d_cached = nullptr;        // last internal level codes or null

@@ -69,6 +69,10 @@ struct Planner {
     static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
     static constexpr uint64_t kSparseTile = 8192; // nodes per sparse cached tile beside bands
     std::vector<uint64_t> tile_weight;            // last-internal-level nodes per descent tile
+    std::vector<uint64_t> tile_lo2;               // first last-internal-level node per descent tile
+    std::vector<Tile> *sink = nullptr;            // where range() puts tiles (p.tiles if null)
+    std::vector<uint64_t> sink_weight;            // last-internal-level nodes of the sink's tiles
+    static constexpr uint64_t kGroupCap = 4096;   // last-internal-level nodes per band group
 
     // Descendant index on level 'to' of boundary 'i' of level d.
     uint64_t down(int d, uint64_t i, int to) const {
@@ -112,8 +116,14 @@ struct Planner {
             tl.count = uint32_t(j - i);
             tl.level = uint32_t(d);
             tl.code_off = uint32_t(code_base + (i - a));
-            p.tiles.push_back(tl);
-            tile_weight.push_back(bound[j - a] - bound[i - a]);
+            if (sink) {
+                sink->push_back(tl);
+                sink_weight.push_back(bound[j - a] - bound[i - a]);
+            } else {
+                p.tiles.push_back(tl);
+                tile_weight.push_back(bound[j - a] - bound[i - a]);
+                tile_lo2.push_back(bound[i - a]);
+            }
             i = j;
         }
     }
@@ -354,13 +364,58 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         }
         xcd_order(p.cached_tiles[dir], w, groups, uint32_t(last));
     };
-    if (!o.cache_last_level) return K2_OK;
-    if (qlog < 0) {
-        for (int dir = 0; dir < 2; ++dir) {
-            pl.cached_run(dir, 0, n2);
-            order_cached(dir, {0, p.cached_tiles[dir].size()});
+    const bool cache = o.cache_last_level != 0;
+    p.band_cap = std::min<uint32_t>(o.tile_nodes, 512);
+    // Tree-only products: the descent tiles in block order, minus the
+    // last-internal-level ranges 'wr' (sorted) that band groups cover.
+    auto rest_plain = [&](int dir, const std::vector<std::pair<uint64_t, uint64_t>> &wr) {
+        for (uint32_t idx : p.tile_order[dir]) {
+            const uint64_t a = pl.tile_lo2[idx], b = a + pl.tile_weight[idx];
+            auto it = std::lower_bound(wr.begin(), wr.end(), a,
+                                       [](const std::pair<uint64_t, uint64_t> &r, uint64_t v) { return r.second <= v; });
+            Tile r = p.tiles[idx];
+            r.win_row = uint32_t(p.skip[dir].size());
+            r.win_col = 0;
+            uint64_t covered = 0;
+            for (; it != wr.end() && it->first < b; ++it) {
+                const uint64_t lo = std::max(a, it->first), hi = std::min(b, it->second);
+                p.skip[dir].push_back((lo << 32) | hi);
+                covered += hi - lo;
+                ++r.win_col;
+            }
+            if (covered == b - a && b > a) {   // wholly inside band groups
+                p.skip[dir].resize(r.win_row);
+                continue;
+            }
+            p.rest_tiles[dir].push_back(r);
         }
+    };
+    // Scan offsets of the band groups' sub-tiles (the rest tiles are copies of
+    // descent tiles and share their offsets).
+    auto finish = [&]() -> k2_status {
+        if (!p.use_directory) {
+            for (int dir = 0; dir < 2; ++dir)
+                for (Tile &tl : p.band_sub[dir]) {
+                    tl.base_off = uint32_t(p.tile_bases.size());
+                    uint64_t node = tl.first;
+                    for (int d = int(tl.level); d <= last; ++d) {
+                        node = child_offset(t, d, node);
+                        p.tile_bases.push_back(uint32_t(node));
+                    }
+                }
+            if (p.tile_bases.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
+        }
+        if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
         return K2_OK;
+    };
+    if (qlog < 0) {
+        for (int dir = 0; dir < 2; ++dir) rest_plain(dir, {});
+        if (cache)
+            for (int dir = 0; dir < 2; ++dir) {
+                pl.cached_run(dir, 0, n2);
+                order_cached(dir, {0, p.cached_tiles[dir].size()});
+            }
+        return finish();
     }
     const int h = std::max(0, L - qlog);            // quadrant level
     p.window_log2 = L - h;
@@ -472,7 +527,8 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         std::stable_sort(dense_units.begin(), dense_units.end(),
                          [](const auto &x, const auto &y) { return x.first < y.first; });
         std::vector<char> windowed(units.size(), 0);
-        std::vector<std::pair<uint64_t, Tile>> keyed;   // (output block, tile)
+        std::vector<std::pair<uint64_t, Tile>> keyed;    // (output block, cached tile)
+        std::vector<std::pair<uint64_t, Tile>> dkeyed;   // (output block, band group)
         for (size_t i = 0; i < dense_units.size();) {
             size_t j = i;
             uint64_t total = 0;
@@ -489,14 +545,71 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                     ranges.push_back({uint32_t(u.lo2), uint32_t(u.hi2 - u.lo2), 0u, 0u});
                 }
                 Tile w = window_of(units[dense_units[i].second].qcode, h, L);
-                const size_t t0 = p.cached_tiles[dir].size();
-                pl.cached_band(dir, ranges, w);
                 const uint64_t key = (dense_units[i].first << (L - h)) >> kb;
-                for (size_t t = t0; t < p.cached_tiles[dir].size(); ++t) keyed.push_back({key, p.cached_tiles[dir][t]});
-                p.cached_tiles[dir].resize(t0);
+                if (cache) {
+                    const size_t t0 = p.cached_tiles[dir].size();
+                    pl.cached_band(dir, ranges, w);
+                    for (size_t t = t0; t < p.cached_tiles[dir].size(); ++t) keyed.push_back({key, p.cached_tiles[dir][t]});
+                    p.cached_tiles[dir].resize(t0);
+                }
+                // the band's groups for tree-only products: its quadrants'
+                // subtrees cut into sub-tiles of at most band_cap nodes, and
+                // those into groups of at most kGroupCap nodes (one window
+                // flush each), so dense bands still spread over the GPU
+                const size_t s0 = p.band_sub[dir].size();
+                const uint64_t C0 = pl.C;
+                pl.C = p.band_cap;
+                pl.sink = &p.band_sub[dir];
+                pl.sink_weight.clear();
+                for (size_t k = i; k < j; ++k) {
+                    const Unit &u = units[dense_units[k].second];
+                    const uint64_t cb = p.codes.size();
+                    p.codes.insert(p.codes.end(), ucodes.begin() + int64_t(u.code_idx),
+                                   ucodes.begin() + int64_t(u.code_idx + (u.b - u.a)));
+                    pl.range(u.level, u.a, u.b, cb, no_window());
+                }
+                pl.sink = nullptr;
+                pl.C = C0;
+                Tile g = w;
+                g.level = uint32_t(last);
+                g.first = uint32_t(s0);
+                uint64_t acc = 0;
+                for (size_t q = 0; q < pl.sink_weight.size(); ++q) {
+                    if (acc > 0 && acc + pl.sink_weight[q] > Planner::kGroupCap) {
+                        g.count = uint32_t(s0 + q - g.first);
+                        dkeyed.push_back({key, g});
+                        g.first = uint32_t(s0 + q);
+                        acc = 0;
+                    }
+                    acc += pl.sink_weight[q];
+                }
+                g.count = uint32_t(p.band_sub[dir].size() - g.first);
+                if (g.count) dkeyed.push_back({key, g});
             }
             i = j;
         }
+        // tree-only products: band groups in block order, then the rest.
+        // Groups pay for their sequential descents only when the windows
+        // cover most of the level (measured: web-like 2^27, 84% covered, 30%
+        // faster; R-MAT, mostly sparse, 2-3x slower), so below half the
+        // level every tile stays a rest tile.
+        std::vector<std::pair<uint64_t, uint64_t>> wr;
+        uint64_t in_bands = 0;
+        for (size_t i = 0; i < units.size(); ++i)
+            if (windowed[i]) {
+                wr.push_back({units[i].lo2, units[i].hi2});
+                in_bands += units[i].hi2 - units[i].lo2;
+            }
+        if (2 * in_bands >= n2) {
+            std::stable_sort(dkeyed.begin(), dkeyed.end(),
+                             [](const auto &x, const auto &y) { return x.first < y.first; });
+            for (const auto &kg : dkeyed) p.band_groups[dir].push_back(kg.second);
+        } else {
+            wr.clear();
+            p.band_sub[dir].clear();
+        }
+        rest_plain(dir, wr);
+        if (!cache) continue;
         // the sparse rest in depth-first order: contiguous runs of level l-2
         // within one output block
         uint64_t run_lo = 0, run_hi = 0, run_key = 0;
@@ -538,8 +651,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         groups.push_back(keyed.size());
         order_cached(dir, groups);
     }
-    if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
-    return K2_OK;
+    return finish();
 }
 
 static uint64_t align256(uint64_t v) { return (v + 255) & ~uint64_t(255); }
@@ -563,7 +675,12 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
     l.bases_off = take(4 * plan.tile_bases.size(), l.mem.directory);
     l.codes_off = take(8 * plan.codes.size(), l.mem.top_codes);
     l.tiles_off = take(sizeof(Tile) * plan.tiles.size(), l.mem.tiles);
-    for (int dir = 0; dir < 2; ++dir) l.order_off[dir] = take(4 * plan.tile_order[dir].size(), l.mem.tiles);
+    for (int dir = 0; dir < 2; ++dir) {
+        l.groups_off[dir] = take(sizeof(Tile) * plan.band_groups[dir].size(), l.mem.tiles);
+        l.sub_off[dir] = take(sizeof(Tile) * plan.band_sub[dir].size(), l.mem.tiles);
+        l.rest_off[dir] = take(sizeof(Tile) * plan.rest_tiles[dir].size(), l.mem.tiles);
+        l.skip_off[dir] = take(8 * plan.skip[dir].size(), l.mem.tiles);
+    }
     for (int dir = 0; dir < 2; ++dir) {
         l.cached_tiles_off[dir] = take(cached ? sizeof(Tile) * plan.cached_tiles[dir].size() : 0, l.mem.tiles);
         l.cached_segs_off[dir] = take(cached ? sizeof(Seg) * plan.cached_segs[dir].size() : 0, l.mem.tiles);
