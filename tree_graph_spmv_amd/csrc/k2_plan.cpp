@@ -394,16 +394,31 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles and share their offsets).
     auto finish = [&]() -> k2_status {
         if (!p.use_directory) {
+            uint64_t total = p.tile_bases.size();
             for (int dir = 0; dir < 2; ++dir)
                 for (Tile &tl : p.band_sub[dir]) {
-                    tl.base_off = uint32_t(p.tile_bases.size());
-                    uint64_t node = tl.first;
-                    for (int d = int(tl.level); d <= last; ++d) {
-                        node = child_offset(t, d, node);
-                        p.tile_bases.push_back(uint32_t(node));
-                    }
+                    tl.base_off = uint32_t(total);
+                    total += uint64_t(last - int(tl.level) + 1);
                 }
-            if (p.tile_bases.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
+            if (total >= (1ull << 32)) return K2_E_UNSUPPORTED;
+            p.tile_bases.resize(total);
+            const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+            for (int dir = 0; dir < 2; ++dir) {
+                const std::vector<Tile> &bs = p.band_sub[dir];
+                const size_t nt = bs.size();
+                std::vector<std::thread> pool;
+                for (unsigned k = 0; k < nth; ++k)
+                    pool.emplace_back([&, k]() {
+                        for (size_t i = nt * k / nth; i < nt * (k + 1) / nth; ++i) {
+                            uint64_t node = bs[i].first;
+                            for (int d = int(bs[i].level); d <= last; ++d) {
+                                node = child_offset(t, d, node);
+                                p.tile_bases[bs[i].base_off + uint32_t(d - int(bs[i].level))] = uint32_t(node);
+                            }
+                        }
+                    });
+                for (auto &th : pool) th.join();
+            }
         }
         if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
         return K2_OK;
