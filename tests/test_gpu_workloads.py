@@ -105,8 +105,9 @@ def test_symrmat_s24_e256m_boolean(dev):
 
 def test_web_n27_d9_batch8(dev):
     """Web-like 2^27, ~1.2G edges, plus-times over 8 vectors, last internal
-    level cached (the benchmark's configuration): sampled outputs within the
-    fp32 tolerance, right and left; the all-ones product gives out-degrees."""
+    level cached (the benchmark's configuration) and tree-only: sampled
+    outputs within the fp32 tolerance, right and left; the all-ones product
+    gives out-degrees."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("web_n27_d9")
     tree = k2.Tree(rows, cols, n, n)
@@ -114,11 +115,12 @@ def test_web_n27_d9_batch8(dev):
     m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
     xd = to_device(x, dev)
     for direction in ("right", "left"):
-        y = m.spmv(xd, direction=direction, batch=8)
-        torch.cuda.synchronize()
-        check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction}",
-                      k=3000, seed=3)
-        del y
+        for mode in ("cached", "tree"):   # tree-only: band groups, then the rest tiles
+            y = m.spmv(xd, direction=direction, batch=8, mode=mode)
+            torch.cuda.synchronize()
+            check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction} {mode}",
+                          k=3000, seed=3)
+            del y
     ones = torch.ones(n, device=dev)
     deg = m.spmv(ones, direction="right").cpu().numpy()
     idx = sample_idx(n, 3000, 4)
