@@ -371,6 +371,106 @@ __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_
     }
 }
 
+// One pass over 'count' cells of a wave's ring from position 'head' (R
+// slots, R a power of 2): VL lanes per cell, kUnroll cells per lane, their
+// gathers issued before their atomics.
+template <class SR, class Off>
+__device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
+                                          const typename SR::T *__restrict__ x,
+                                          typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                          const Window<typename SR::T> &w) {
+    using T = typename SR::T;
+    constexpr uint32_t R = WaveCells<Off>::kRound;
+    constexpr int kUnroll = unroll_for<Off>();
+    const uint32_t lane = __lane_id();
+    const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
+    for (uint32_t k0 = g; k0 < count; k0 += G * kUnroll) {
+        // slots past count repeat cell k0 for the loads and skip the atomics
+        Off xo[kUnroll], yo[kUnroll];
+        bool ok[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const uint32_t k = k0 + uint32_t(u) * G;
+            ok[u] = k < count;
+            const uint32_t at = (head + (ok[u] ? k : k0)) & (R - 1u);
+            xo[u] = wc->xo[at];
+            yo[u] = wc->yo[at];
+        }
+        for (uint32_t v = lv; v < B; v += VL) {
+            T xv[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) xv[u] = x[xo[u] + v];
+            if (w.win) {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (ok[u] && SR::contributes(xv[u])) SR::lds_atomic(&w.win[yo[u] + v], SR::contrib(xv[u]));
+            } else {
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (ok[u] && SR::contributes(xv[u])) SR::atomic(&y[yo[u] + v], SR::contrib(xv[u]));
+            }
+        }
+    }
+}
+
+// The cells of one segment (as for leaf_cells) queued in the wave's ring
+// behind the 'fill' cells already there from 'head': whenever a full pass
+// (G x kUnroll cells, at most the ring) is queued it runs, so a segment's
+// last few cells wait for the next segment instead of taking a pass of
+// their own.  ring_drain runs what is left at the end of a tile.
+template <class SR, int DIR, class Off>
+__device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_t cells,
+                                           const typename SR::T *__restrict__ x,
+                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                           const Window<typename SR::T> &w, WaveCells<Off> *wc,
+                                           uint32_t &head, uint32_t &fill) {
+    constexpr uint32_t R = WaveCells<Off>::kRound;
+    constexpr int kUnroll = unroll_for<Off>();
+    uint32_t total;
+    const uint32_t pos0 = wave_scan(__popc(cells), total);
+    const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
+    const Off xb = Off((DIR == K2_RIGHT) ? col0 : row0) * B;
+    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * B;
+    constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
+    constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
+    const uint32_t G = 64 / VL;
+    const uint32_t P = (G * uint32_t(kUnroll) < R) ? G * uint32_t(kUnroll) : R;
+    for (uint32_t done = 0; done < total;) {
+        const uint32_t now = (total - done < R - fill) ? total - done : R - fill;
+        // this lane's cells with segment positions in [done, done + now)
+        uint32_t m = cells, pos = pos0;
+        while (m && pos < done + now) {
+            const uint32_t sh = 2u * uint32_t(__builtin_ctz(m));
+            m &= m - 1u;
+            if (pos >= done) {
+                const uint32_t at = (head + fill + (pos - done)) & (R - 1u);
+                wc->xo[at] = xb + __umul24((kInTable >> sh) & 3u, B);
+                wc->yo[at] = yb + __umul24((kOutTable >> sh) & 3u, B);
+            }
+            ++pos;
+        }
+        fill += now;
+        done += now;
+        wave_lds_sync();
+        while (fill >= P) {
+            ring_pass<SR, Off>(wc, head, P, x, y, B, VL, w);
+            head = (head + P) & (R - 1u);
+            fill -= P;
+        }
+        wave_lds_sync();
+    }
+}
+
+template <class SR, class Off>
+__device__ __forceinline__ void ring_drain(const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y,
+                                           uint32_t B, uint32_t VL, const Window<typename SR::T> &w,
+                                           WaveCells<Off> *wc, uint32_t &head, uint32_t &fill) {
+    if (fill) ring_pass<SR, Off>(wc, head, fill, x, y, B, VL, w);
+    wave_lds_sync();
+    head = 0;
+    fill = 0;
+}
+
 // leaf_cells for a lane whose node has Morton code 'code', signature s and
 // first leaf 'off'.
 template <class SR, int DIR, class Off>
@@ -507,6 +607,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
         const Tile tl = tiles[ti];
         const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
         const uint32_t nseg = tl.count;
+        uint32_t ring_head = 0, ring_fill = 0;   // the wave's queued cells
         uint32_t k = wave;
         SegSig a1 = stage_sig(t, d, segs, tl.first, k + kWaves, nseg, sig_words, use_dir);
         SegLeaves b0 = stage_leaves(stage_sig(t, d, segs, tl.first, k, nseg, sig_words, use_dir), blocks,
@@ -524,10 +625,12 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
                     cells |= (bits & 15u) << (4 * b);
                     bits >>= 4;
                 }
-            leaf_cells<SR, DIR, Off>(uint32_t(b0.blk >> 32), uint32_t(b0.blk), cells, x, y, B, VL, w, wc);
+            ring_cells<SR, DIR, Off>(uint32_t(b0.blk >> 32), uint32_t(b0.blk), cells, x, y, B, VL, w, wc,
+                                     ring_head, ring_fill);
             b0 = b1;
             a1 = a2;
         }
+        ring_drain<SR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
         close_window<SR>(w, y, n_out, B);
     }
 }
