@@ -298,79 +298,6 @@ constexpr uint32_t cell_offset_table(bool row) {
 constexpr uint32_t kCellRowTable = cell_offset_table(true);
 constexpr uint32_t kCellColTable = cell_offset_table(false);
 
-// Leaf work of one wave over a segment of up to 64 nodes of the last internal
-// level; lane l holds the first row and column of node l's 4x4 block and its
-// cells as a 16-bit mask (bit 4 b + q: cell q of the leaf for child b; 0: no
-// node).
-// Phase A (a lane per node): list the segment's cells in the wave's LDS, each
-// as its x and output offsets, at positions from a wave scan of the cell
-// counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
-// kUnroll cells, then apply the semiring's atomics, to the LDS window when
-// the tile has one, else to y.  No workgroup barrier.
-template <class SR, int DIR, class Off>
-__device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_t cells,
-                                           const typename SR::T *__restrict__ x,
-                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                           Window<typename SR::T> w, WaveCells<Off> *wc) {
-    using T = typename SR::T;
-    constexpr uint32_t R = WaveCells<Off>::kRound;
-    const uint32_t lane = __lane_id();
-    uint32_t total;
-    const uint32_t pos0 = wave_scan(__popc(cells), total);
-    const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
-    // offsets of the block's first cell; a cell adds its in-block offset * B
-    const Off xb = Off((DIR == K2_RIGHT) ? col0 : row0) * B;
-    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * B;
-    constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
-    constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
-    const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
-    constexpr int kUnroll = unroll_for<Off>();
-    for (uint32_t round = 0; round < total; round += R) {
-        // this lane's cells with list positions in [round, round + R)
-        uint32_t m = cells, pos = pos0;
-        while (m && pos < round + R) {
-            const uint32_t sh = 2u * uint32_t(__builtin_ctz(m));
-            m &= m - 1u;
-            if (pos >= round) {
-                wc->xo[pos - round] = xb + __umul24((kInTable >> sh) & 3u, B);
-                wc->yo[pos - round] = yb + __umul24((kOutTable >> sh) & 3u, B);
-            }
-            ++pos;
-        }
-        wave_lds_sync();
-        const uint32_t n = (total - round < R) ? total - round : R;
-        for (uint32_t k0 = g; k0 < n; k0 += G * kUnroll) {
-            // cells past n repeat cell k0 for the loads and skip the atomics
-            Off xo[kUnroll], yo[kUnroll];
-            bool ok[kUnroll];
-#pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const uint32_t k = k0 + uint32_t(u) * G;
-                ok[u] = k < n;
-                const uint32_t kk = ok[u] ? k : k0;
-                xo[u] = wc->xo[kk];
-                yo[u] = wc->yo[kk];
-            }
-            for (uint32_t v = lv; v < B; v += VL) {
-                T xv[kUnroll];
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u) xv[u] = x[xo[u] + v];
-                if (w.win) {
-#pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
-                        if (ok[u] && SR::contributes(xv[u]))
-                            SR::lds_atomic(&w.win[yo[u] + v], SR::contrib(xv[u]));
-                } else {
-#pragma unroll
-                    for (int u = 0; u < kUnroll; ++u)
-                        if (ok[u] && SR::contributes(xv[u])) SR::atomic(&y[yo[u] + v], SR::contrib(xv[u]));
-                }
-            }
-        }
-        wave_lds_sync();
-    }
-}
-
 // One pass over 'count' cells of a wave's ring from position 'head' (R
 // slots, R a power of 2): VL lanes per cell, kUnroll cells per lane, their
 // gathers issued before their atomics.
@@ -410,6 +337,48 @@ __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t hea
                     if (ok[u] && SR::contributes(xv[u])) SR::atomic(&y[yo[u] + v], SR::contrib(xv[u]));
             }
         }
+    }
+}
+
+// Leaf work of one wave over a segment of up to 64 nodes of the last internal
+// level; lane l holds the first row and column of node l's 4x4 block and its
+// cells as a 16-bit mask (bit 4 b + q: cell q of the leaf for child b; 0: no
+// node).
+// Phase A (a lane per node): list the segment's cells in the wave's LDS, each
+// as its x and output offsets, at positions from a wave scan of the cell
+// counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
+// kUnroll cells, then apply the semiring's atomics, to the LDS window when
+// the tile has one, else to y.  No workgroup barrier.
+template <class SR, int DIR, class Off>
+__device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_t cells,
+                                           const typename SR::T *__restrict__ x,
+                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                           Window<typename SR::T> w, WaveCells<Off> *wc) {
+    constexpr uint32_t R = WaveCells<Off>::kRound;
+    uint32_t total;
+    const uint32_t pos0 = wave_scan(__popc(cells), total);
+    const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
+    // offsets of the block's first cell; a cell adds its in-block offset * B
+    const Off xb = Off((DIR == K2_RIGHT) ? col0 : row0) * B;
+    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * B;
+    constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
+    constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
+    for (uint32_t round = 0; round < total; round += R) {
+        // this lane's cells with list positions in [round, round + R)
+        uint32_t m = cells, pos = pos0;
+        while (m && pos < round + R) {
+            const uint32_t sh = 2u * uint32_t(__builtin_ctz(m));
+            m &= m - 1u;
+            if (pos >= round) {
+                wc->xo[pos - round] = xb + __umul24((kInTable >> sh) & 3u, B);
+                wc->yo[pos - round] = yb + __umul24((kOutTable >> sh) & 3u, B);
+            }
+            ++pos;
+        }
+        wave_lds_sync();
+        const uint32_t n = (total - round < R) ? total - round : R;
+        ring_pass<SR, Off>(wc, 0u, n, x, y, B, VL, w);
+        wave_lds_sync();
     }
 }
 
@@ -533,62 +502,74 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y
     for (uint64_t k = n4 * 4 + i; k < n; k += stride) y[k] = value;
 }
 
-// Pipeline state of one segment of a cached tile.  Stage 1, issued two
-// segments ahead: the descriptor (uniform) and each lane's node signature.
+// Pipeline state of one segment of a cached tile, in three stages: its
+// descriptor (uniform: a scalar load), issued three segments ahead; the
+// 64-bit signature word holding each lane's node, two segments ahead; and
+// (SegLeaves) one segment ahead: the lane's node's block origin (first row
+// << 32 | first column), its signature s and first-leaf nibble position p
+// packed as s | p << 6, and the two leaf-level dwords that hold its leaf
+// signatures (from nibble p of lo32).
+// Every lane issues every load of a stage, at an index clamped into its
+// array, and no load sits under a branch: the compiler then knows how many
+// loads are still in flight at each use and waits only for the ones the use
+// needs, so a stage's loads stay in flight while the wave works on the
+// segment before.
 struct SegSig {
     uint32_t lo, count, leaf;   // uniform; count = 0 past the wave's last segment
-    uint32_t s;                 // the lane's node signature, 0 outside the segment
+    uint64_t word;              // signature word of node lo + lane (node lo past count)
 };
-// Stage 2, issued one segment ahead: the lane's node's block origin (first
-// row << 32 | first column), its signature s and first-leaf nibble position
-// p packed as s | p << 6, and the two leaf-level dwords that hold its leaf
-// signatures (from nibble p of lo32).
 struct SegLeaves {
     uint64_t blk;
     uint32_t ssh, lo32, hi32;
 };
 
+__device__ __forceinline__ Seg stage_seg(const Seg *__restrict__ segs, uint32_t first, uint32_t k,
+                                         uint32_t nseg) {
+    Seg g{0u, 0u, 0u, 0u};
+    if (k < nseg) g = segs[first + k];
+    return g;
+}
+
 // With use_dir the segment's first leaf comes from the directory on the
 // device, else from the plan.
-__device__ __forceinline__ SegSig stage_sig(const DevTree &t, int d, const Seg *__restrict__ segs,
-                                            uint32_t first, uint32_t k, uint32_t nseg,
+__device__ __forceinline__ SegSig stage_sig(const DevTree &t, int d, const Seg &g,
                                             const uint64_t *__restrict__ sig_words, int use_dir) {
-    SegSig a{0u, 0u, 0u, 0u};
-    if (k < nseg) {
-        const Seg sg = segs[first + k];
-        a.lo = sg.lo;
-        a.count = sg.count;
-        a.leaf = use_dir ? wave_child_offset(t, d, sg.lo) : sg.leaf;
-        if (__lane_id() < sg.count) a.s = nib(sig_words, uint64_t(sg.lo) + __lane_id());
-    }
+    SegSig a;
+    a.lo = g.lo;
+    a.count = g.count;
+    a.leaf = (use_dir && g.count) ? wave_child_offset(t, d, g.lo) : g.leaf;
+    const uint32_t lane = __lane_id();
+    a.word = sig_words[(g.lo + (lane < g.count ? lane : 0u)) >> 4];
     return a;
 }
 
 // The lane's first leaf is the segment's first leaf plus the fan-outs of the
 // lanes before it (a wave scan).  A node's at most 4 leaf nibbles start at
-// nibble off % 8 of dword off / 8 and reach into the next dword only if
-// off % 8 + fan-out > 8, which is the only case that reads it.
+// nibble off % 8 of dword off / 8 and may reach into the next dword;
+// last_dw is the leaf level's last dword.
 __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_t *__restrict__ blocks,
-                                                  const uint32_t *__restrict__ leaf_dw) {
-    SegLeaves b{0ull, a.s, 0u, 0u};
+                                                  const uint32_t *__restrict__ leaf_dw, uint32_t last_dw) {
+    const uint32_t lane = __lane_id();
+    const bool in = lane < a.count;
+    const uint32_t s = in ? uint32_t(a.word >> (((a.lo + lane) & 15u) * 4u)) & 15u : 0u;
     uint32_t total;
-    const uint32_t ex = wave_scan(__popc(a.s), total);
-    if (__lane_id() < a.count) b.blk = blocks[a.lo + __lane_id()];
-    if (a.s) {
-        const uint32_t off = a.leaf + ex;
-        b.ssh = a.s | ((off & 7u) << 6);
-        b.lo32 = leaf_dw[off >> 3];
-        if ((off & 7u) + __popc(a.s) > 8u) b.hi32 = leaf_dw[(off >> 3) + 1u];
-    }
+    const uint32_t ex = wave_scan(__popc(s), total);
+    const uint32_t off = a.leaf + ex;
+    const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
+    SegLeaves b;
+    b.blk = blocks[a.lo + (in ? lane : 0u)];
+    b.ssh = s | ((off & 7u) << 6);
+    b.lo32 = leaf_dw[dw];
+    b.hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
     return b;
 }
 
 // One product over the cached last internal level (Sec. 3.5): each workgroup
 // takes a tile, a list of segments of up to 64 nodes of that level, each
 // with its first leaf's index; wave w takes segments w, w + 4, ...  A wave
-// works on three of its segments at once: while it visits the leaves of one,
-// the codes and leaf signatures of the next and the signatures of the one
-// after are in flight.
+// works on four of its segments at once: while it visits the leaves of one,
+// the block origins and leaf signatures of the next, the signatures of the
+// one after and the descriptor of the third are in flight.
 template <class SR, int DIR, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
@@ -599,9 +580,11 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     extern __shared__ uint64_t s_dyn[];   // the window
     __shared__ WaveCells<Off> s_cells[kWaves];
     const int d = t.levels - 2;
-    const uint32_t wave = threadIdx.x >> 6;
+    // uniform, so that segment descriptors are scalar loads
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t *__restrict__ sig_words = t.words[d];
     const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[d + 1]);
+    const uint32_t last_dw = uint32_t((uint64_t(t.nodes[d + 1]) + 15u) / 16u * 2u - 1u);
     WaveCells<Off> *wc = &s_cells[wave];
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
@@ -609,12 +592,14 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
         const uint32_t nseg = tl.count;
         uint32_t ring_head = 0, ring_fill = 0;   // the wave's queued cells
         uint32_t k = wave;
-        SegSig a1 = stage_sig(t, d, segs, tl.first, k + kWaves, nseg, sig_words, use_dir);
-        SegLeaves b0 = stage_leaves(stage_sig(t, d, segs, tl.first, k, nseg, sig_words, use_dir), blocks,
-                                    leaf_dw);
+        Seg g2 = stage_seg(segs, tl.first, k + 2 * kWaves, nseg);
+        SegSig a1 = stage_sig(t, d, stage_seg(segs, tl.first, k + kWaves, nseg), sig_words, use_dir);
+        SegLeaves b0 = stage_leaves(stage_sig(t, d, stage_seg(segs, tl.first, k, nseg), sig_words, use_dir),
+                                    blocks, leaf_dw, last_dw);
         for (; k < nseg; k += kWaves) {
-            const SegSig a2 = stage_sig(t, d, segs, tl.first, k + 2 * kWaves, nseg, sig_words, use_dir);
-            const SegLeaves b1 = stage_leaves(a1, blocks, leaf_dw);
+            const Seg g3 = stage_seg(segs, tl.first, k + 3 * kWaves, nseg);
+            const SegSig a2 = stage_sig(t, d, g2, sig_words, use_dir);
+            const SegLeaves b1 = stage_leaves(a1, blocks, leaf_dw, last_dw);
             // the node's leaf nibbles are the low 4 * fan-out bits of 'bits'
             const uint32_t s0 = b0.ssh & 15u;
             uint32_t bits = uint32_t(((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u));
@@ -629,6 +614,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
                                      ring_head, ring_fill);
             b0 = b1;
             a1 = a2;
+            g2 = g3;
         }
         ring_drain<SR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
         close_window<SR>(w, y, n_out, B);
