@@ -298,10 +298,51 @@ constexpr uint32_t cell_offset_table(bool row) {
 constexpr uint32_t kCellRowTable = cell_offset_table(true);
 constexpr uint32_t kCellColTable = cell_offset_table(false);
 
+// The atomics of a lane's kUnroll cells (contributions xv, outputs yo + v of
+// 'out': the LDS window when kWin, else y).  kRuns: the cells are
+// consecutive in the list (ok[] a prefix), and runs of one output are
+// combined into one atomic.
+template <class SR, class Off, int kUnroll, bool kRuns, bool kWin>
+__device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll], const Off (&yo)[kUnroll],
+                                            const bool (&ok)[kUnroll], typename SR::T *__restrict__ out,
+                                            uint32_t v) {
+    using T = typename SR::T;
+    auto apply = [&](Off o, T c) {
+        if constexpr (kWin) SR::lds_atomic(&out[o + v], c);
+        else SR::atomic(&out[o + v], c);
+    };
+    if constexpr (kRuns) {
+        T acc = SR::zero();
+        Off cur = yo[0];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (ok[u]) {
+                if (yo[u] != cur) {
+                    if (SR::contributes_out(acc)) apply(cur, acc);
+                    acc = SR::zero();
+                    cur = yo[u];
+                }
+                if (SR::contributes(xv[u])) acc = SR::combine(acc, SR::contrib(xv[u]));
+            }
+        if (SR::contributes_out(acc)) apply(cur, acc);
+    } else {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u)
+            if (ok[u] && SR::contributes(xv[u])) apply(yo[u], SR::contrib(xv[u]));
+    }
+}
+
 // One pass over 'count' cells of a wave's ring from position 'head' (R
 // slots, R a power of 2): VL lanes per cell, kUnroll cells per lane, their
-// gathers issued before their atomics.
-template <class SR, class Off>
+// gathers issued before their atomics.  Without kRuns an instruction takes
+// kUnroll-strided cells, G neighbours of the list at a time, whose x rows
+// often share cache lines.  With kRuns each lane group takes kUnroll
+// neighbours of the list and combines runs of equal outputs before their
+// atomic: in a right product the cells of one row of a 4x4 block, and of
+// horizontally adjacent blocks, are neighbours in Z order, so a row of many
+// non-zeros would otherwise send several lanes of one instruction to the same
+// word (serialised, and a failed compare-and-swap each).
+template <class SR, class Off, bool kRuns>
 __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
                                           const typename SR::T *__restrict__ x,
                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
@@ -311,15 +352,18 @@ __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t hea
     constexpr int kUnroll = unroll_for<Off>();
     const uint32_t lane = __lane_id();
     const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
-    for (uint32_t k0 = g; k0 < count; k0 += G * kUnroll) {
-        // slots past count repeat cell k0 for the loads and skip the atomics
+    // cell u of this lane is k0 + u * step
+    const uint32_t step = kRuns ? 1u : G;
+    for (uint32_t base = 0; base < count; base += G * kUnroll) {
+        const uint32_t k0 = base + (kRuns ? g * uint32_t(kUnroll) : g);
+        // slots past count repeat cell 'base' for the loads and skip the atomics
         Off xo[kUnroll], yo[kUnroll];
         bool ok[kUnroll];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t k = k0 + uint32_t(u) * G;
+            const uint32_t k = k0 + uint32_t(u) * step;
             ok[u] = k < count;
-            const uint32_t at = (head + (ok[u] ? k : k0)) & (R - 1u);
+            const uint32_t at = (head + (ok[u] ? k : base)) & (R - 1u);
             xo[u] = wc->xo[at];
             yo[u] = wc->yo[at];
         }
@@ -327,15 +371,8 @@ __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t hea
             T xv[kUnroll];
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) xv[u] = x[xo[u] + v];
-            if (w.win) {
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
-                    if (ok[u] && SR::contributes(xv[u])) SR::lds_atomic(&w.win[yo[u] + v], SR::contrib(xv[u]));
-            } else {
-#pragma unroll
-                for (int u = 0; u < kUnroll; ++u)
-                    if (ok[u] && SR::contributes(xv[u])) SR::atomic(&y[yo[u] + v], SR::contrib(xv[u]));
-            }
+            if (w.win) apply_cells<SR, Off, kUnroll, kRuns, true>(xv, yo, ok, w.win, v);
+            else apply_cells<SR, Off, kUnroll, kRuns, false>(xv, yo, ok, y, v);
         }
     }
 }
@@ -377,7 +414,7 @@ __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_
         }
         wave_lds_sync();
         const uint32_t n = (total - round < R) ? total - round : R;
-        ring_pass<SR, Off>(wc, 0u, n, x, y, B, VL, w);
+        ring_pass<SR, Off, DIR == K2_RIGHT>(wc, 0u, n, x, y, B, VL, w);
         wave_lds_sync();
     }
 }
@@ -422,7 +459,7 @@ __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_
         done += now;
         wave_lds_sync();
         while (fill >= P) {
-            ring_pass<SR, Off>(wc, head, P, x, y, B, VL, w);
+            ring_pass<SR, Off, DIR == K2_RIGHT>(wc, head, P, x, y, B, VL, w);
             head = (head + P) & (R - 1u);
             fill -= P;
         }
@@ -430,11 +467,11 @@ __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_
     }
 }
 
-template <class SR, class Off>
+template <class SR, int DIR, class Off>
 __device__ __forceinline__ void ring_drain(const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y,
                                            uint32_t B, uint32_t VL, const Window<typename SR::T> &w,
                                            WaveCells<Off> *wc, uint32_t &head, uint32_t &fill) {
-    if (fill) ring_pass<SR, Off>(wc, head, fill, x, y, B, VL, w);
+    if (fill) ring_pass<SR, Off, DIR == K2_RIGHT>(wc, head, fill, x, y, B, VL, w);
     wave_lds_sync();
     head = 0;
     fill = 0;
@@ -616,7 +653,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             a1 = a2;
             g2 = g3;
         }
-        ring_drain<SR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
+        ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
         close_window<SR>(w, y, n_out, B);
     }
 }
