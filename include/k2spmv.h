@@ -121,6 +121,14 @@ typedef struct {
        K2_OFFSETS_AUTO: K2_OFFSETS_SCAN (measured at least as fast on gfx950
          for every workload here, single and batched).  Default AUTO. */
     int32_t offsets;
+    /* With windows and a cached level: 1 gives every row band (right
+       products) or column band (left) that holds nodes outside the dense
+       quadrants a windowed tile, and those nodes are added to their band's
+       window too (strays), instead of one y atomic per cell from separate
+       sparse tiles.  k2_matrix_create groups the strays by band on the
+       device (16 bytes per stray node and direction: its block origin,
+       first leaf and signature).  0: sparse tiles.  Default 1. */
+    int32_t band_strays;
 } k2_plan_opts;
 
 enum { K2_OFFSETS_AUTO = 0, K2_OFFSETS_DIRECTORY = 1, K2_OFFSETS_SCAN = 2 };
@@ -135,7 +143,8 @@ typedef struct {
                              child offsets of the descent tiles (scan) */
     uint64_t top_codes;   /* Morton codes of the tile starts (host top + splits) */
     uint64_t tiles;       /* the tile plan */
-    uint64_t cached_codes;/* 8 bytes per node of the last internal level, or 0 */
+    uint64_t cached_codes;/* 8 bytes per node of the last internal level, plus
+                             16 per stray node and direction (band_strays), or 0 */
     uint64_t scratch;     /* transient product memory (0: frontiers live in LDS) */
     uint64_t alignment;   /* padding between parts */
     uint64_t arena;       /* sum of the above */
@@ -202,7 +211,7 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
    right / left products and their segments (empty unless
    opts->cache_last_level); for tree-only right / left products, 3 / 4: the
    rest tiles and their skip ranges, 5 / 6: the band groups, 7 / 8: the
-   band groups' tiles.  Reports the host-top level d0, the number of tiles
+   band groups' tiles, 9 / 10: the stray segments of right / left products.  Reports the host-top level d0, the number of tiles
    and of aux entries (see k2_plan_tiles).  Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux);
@@ -229,6 +238,10 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
    which = 1 / 2: 'count' segments of the last internal level from segment
    'first'; segment r is aux[2r] = (first node << 32) | node count (1..64)
    and aux[2r + 1] = the leaf-level index of its first node's first child.
+   With band_strays, a tile of 1 / 2 with code index 1 owns its band (row
+   band for 1, column band for 2, from the window fields) and also adds the
+   band's strays: the nodes of the segments of which = 9 / 10 (no tiles; aux
+   as for 1 / 2) whose block's first row (9) or column (10) lies in it.
    Host arrays of 8*n_tiles and n_aux entries (sizes from k2_plan_info).
    Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,

@@ -30,7 +30,8 @@ def dev():
 
 
 PLAN_VARIANTS = (dict(), dict(window_elems=0), dict(host_top_max=4, window_elems=4096, window_batch=4),
-                 dict(xcd_remap=0, host_top_max=16), dict(offsets="directory", host_top_max=16))
+                 dict(xcd_remap=0, host_top_max=16), dict(offsets="directory", host_top_max=16),
+                 dict(band_strays=0, window_elems=1024, window_batch=1))
 
 
 def run_all(k2, rows, cols, n_rows, n_cols, dev, semirings=ALL_SEMIRINGS, batches=(1, 3),

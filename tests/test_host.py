@@ -76,20 +76,21 @@ def oracle_codes(o, upto):
 def check_xcd_order(ordered, plain):
     """An XCD-ordered tile list holds the plain list's tiles once each; the
     tiles at positions k, k + 8, ... (XCD k) keep the plain order; every
-    other entry is padding (count 0)."""
+    other entry is padding (count 0, not a band's owner)."""
     assert len(ordered) % 8 == 0
     index = {tuple(int(v) for v in tl): i for i, tl in enumerate(plain)}
     assert len(index) == len(plain)
     seen = []
     for k in range(8):
-        pos = [index[tuple(int(v) for v in tl)] for tl in ordered[k::8] if int(tl[1])]
+        pos = [index[tuple(int(v) for v in tl)] for tl in ordered[k::8] if int(tl[1]) or int(tl[3])]
         assert pos == sorted(pos), "an XCD's tiles keep the plain order"
         seen += pos
     assert sorted(seen) == list(range(len(plain)))
 
 
-def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
-    """cached: {1: (tiles, ranges) of right products, 2: of left products}."""
+def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes, strays=None):
+    """cached: {1: (tiles, ranges) of right products, 2: of left products};
+    strays: {1: stray segments of right products, 2: of left products}."""
     L = o.levels
     last = L - 2
     nodes = o.level_nodes()
@@ -142,11 +143,18 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
     assert pos == nodes[last]
     for which, (ctiles, ranges) in cached.items():
         seen = []
+        owners = set()
+        for tl in ctiles:
+            if int(tl[3]):   # a band's owner tile: windowed, one per band
+                assert int(tl[3]) == 1 and tl[6] != 0xFFFFFFFF
+                band = (int(tl[4]) if which == 1 else int(tl[5])) >> int(tl[6])
+                assert band not in owners, "one owner tile per band"
+                owners.add(band)
         for tl in ctiles:
             first, count = int(tl[0]), int(tl[1])
             assert int(tl[2]) == last
             if count == 0:
-                assert opts.xcd_remap and tl[6] == 0xFFFFFFFF
+                assert (opts.xcd_remap and tl[6] == 0xFFFFFFFF) or int(tl[3]) == 1
                 continue
             total = 0
             for r, leaf in ranges[first:first + count]:
@@ -162,6 +170,18 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
                     assert np.all((out >= base) & (out < base + side)), "output outside band"
             if tl[6] != 0xFFFFFFFF:
                 assert total <= 65536
+        stray = strays[which] if strays else np.zeros((0, 2), np.uint64)
+        if len(stray):
+            log2 = int(next(tl[6] for tl in ctiles if int(tl[3])))
+        for r, leaf in stray:   # each stray's band has an owner tile
+            lo, n = int(r) >> 32, int(r) & 0xFFFFFFFF
+            assert 1 <= n <= 64
+            assert int(leaf) == leaf_of(lo), "first leaf of a stray segment"
+            seen.append((lo, n))
+            for i in range(lo, lo + n):
+                rr, cc = cells_of(i, i + 1)
+                out = (rr if which == 1 else cc) >> log2
+                assert len(out) and np.all(out == out[0]) and int(out[0]) in owners, "stray without owner"
         seen.sort()
         pos = 0
         for lo, n in seen:
@@ -180,20 +200,24 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes):
     dict(window_elems=0),
     dict(host_top_max=4, window_elems=8192, window_batch=64),
     dict(host_top_max=1 << 20, window_elems=2048, window_batch=2),
+    dict(band_strays=0),
+    dict(band_strays=0, window_elems=1024, window_batch=1),
 ])
 def test_plan_invariants(case, opt):
     name, r, c, nr, nc, t, o = case
     opts = k2.plan_defaults(cache_last_level=1, **opt)
     top, tiles, codes = t.plan(opts, 0)
     cached = {w: t.plan(opts, w)[1:] for w in (1, 2)}
+    strays = {w: t.plan(opts, w + 8)[2] for w in (1, 2)}
     assert all(len(t.plan(k2.plan_defaults(cache_last_level=0, **opt), w)[1]) == 0 for w in (1, 2))
+    assert all(len(t.plan(k2.plan_defaults(cache_last_level=0, **opt), w)[2]) == 0 for w in (9, 10))
     if o.level_nodes()[o.levels - 2] == 0:
         assert len(tiles) == 0 and all(len(v[0]) == 0 for v in cached.values())
         return
     cr, cc = o.cells()
     all_codes = oracle_codes(o, o.levels - 2)
     check_plan(o, cr.astype(np.int64), cc.astype(np.int64), top, tiles, codes, cached, opts,
-               all_codes)
+               all_codes, strays)
     if opts.xcd_remap:
         plain = k2.plan_defaults(cache_last_level=1, **dict(opt, xcd_remap=0))
         assert np.array_equal(tiles, t.plan(plain, 0)[1]), "XCD order leaves descent tiles alone"
@@ -332,6 +356,17 @@ def test_estimate_parts(case):
         est = t.estimate(opts, semiring="plus_times", batch=3)
         top, tiles, codes = t.plan(opts, 0)
         extra = sum(32 * len(t.plan(opts, w)[1]) + 16 * len(t.plan(opts, w)[2]) for w in (1, 2))
+        stray_tiles = stray_records = 0
+        for w in (1, 2):   # strays: segments, band offsets and cursors; 16-byte records
+            owners = [tl for tl in t.plan(opts, w)[1] if int(tl[3])]
+            segs = t.plan(opts, w + 8)[2]
+            if owners:
+                log2 = int(owners[0][6])
+                nb = ((nr if w == 1 else nc) + (1 << log2) - 1) >> log2
+                stray_tiles += 16 * len(segs) + 4 * (nb + 1) + 4 * nb
+                stray_records += 16 * sum(int(r) & 0xFFFFFFFF for r, _ in segs)
+            else:
+                assert len(segs) == 0
         L = o.levels
         assert est["tree"] == sum(8 * ((nodes[d] + 15) // 16) for d in range(top, L))
         if offsets == "directory":
@@ -343,8 +378,8 @@ def test_estimate_parts(case):
         # descent tiles, the tree-only lists of both directions, the cached tiles
         tree_only = sum(32 * (len(t.plan(opts, 3 + w)[1]) + len(t.plan(opts, 5 + w)[1]) +
                               len(t.plan(opts, 7 + w)[1])) + 8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
-        assert est["tiles"] == 32 * len(tiles) + tree_only + (extra if cached else 0)
-        assert est["cached_codes"] == (8 * nodes[L - 2] if cached else 0)
+        assert est["tiles"] == 32 * len(tiles) + tree_only + (extra + stray_tiles if cached else 0)
+        assert est["cached_codes"] == (8 * nodes[L - 2] + stray_records if cached else 0)
         parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
                                      "scratch", "alignment"))
         assert est["arena"] == parts and est["arena"] % 256 == 0

@@ -36,7 +36,7 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("tile_nodes", ctypes.c_uint32), ("host_top_max", ctypes.c_uint32),
                 ("cache_last_level", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("window_elems", ctypes.c_uint32), ("window_batch", ctypes.c_uint32),
-                ("offsets", ctypes.c_int32)]
+                ("offsets", ctypes.c_int32), ("band_strays", ctypes.c_int32)]
 
 
 class MemBreakdown(ctypes.Structure):
@@ -209,7 +209,9 @@ class Tree:
         """(top_level, tiles (n,8) uint32, aux uint64) of one tile plan:
         which = 0 descent tiles (aux = start codes); 1 / 2 cached-level
         tiles of right / left products (aux = (n_segments, 2): (first node
-        << 32) | count, and the first node's first leaf)."""
+        << 32) | count, and the first node's first leaf); 3-8 the tree-only
+        lists; 9 / 10 the stray segments of right / left products (no tiles,
+        aux as for 1 / 2)."""
         opts = opts or plan_defaults()
         top = ctypes.c_uint32()
         nt = ctypes.c_uint64()
@@ -222,7 +224,7 @@ class Tree:
                                    tiles.ctypes.data_as(_U32P), nt.value, aux.ctypes.data_as(_U64P),
                                    na.value), "k2_plan_tiles")
         aux = aux[:na.value]
-        return int(top.value), tiles[:nt.value], aux.reshape(-1, 2) if which in (1, 2) else aux
+        return int(top.value), tiles[:nt.value], aux.reshape(-1, 2) if which in (1, 2, 9, 10) else aux
 
 
 def _stream_handle(stream):

@@ -55,7 +55,8 @@ bool same_opts(const k2_plan_opts &a, const k2_plan_opts &b) {
            a.window_elems == b.window_elems && a.window_batch == b.window_batch &&
            (a.cache_last_level != 0) == (b.cache_last_level != 0) &&
            (a.xcd_remap != 0) == (b.xcd_remap != 0) &&
-           (a.offsets == K2_OFFSETS_DIRECTORY) == (b.offsets == K2_OFFSETS_DIRECTORY);
+           (a.offsets == K2_OFFSETS_DIRECTORY) == (b.offsets == K2_OFFSETS_DIRECTORY) &&
+           (a.band_strays != 0) == (b.band_strays != 0);
 }
 
 // The plan of 'tree' for 'o', computed once per option set.
@@ -104,6 +105,7 @@ k2_status k2_plan_defaults(k2_plan_opts *opts) {
     opts->window_elems = 4096;
     opts->window_batch = 8;
     opts->offsets = K2_OFFSETS_AUTO;
+    opts->band_strays = 1;
     return K2_OK;
 }
 
@@ -201,7 +203,12 @@ void plan_list(const Plan &p, int which, const std::vector<Tile> **list, uint64_
     case 1: case 2: *list = &p.cached_tiles[which - 1]; *naux = 2 * p.cached_segs[which - 1].size(); break;
     case 3: case 4: *list = &p.rest_tiles[which - 3]; *naux = p.skip[which - 3].size(); break;
     case 5: case 6: *list = &p.band_groups[which - 5]; *naux = 0; break;
-    default: *list = &p.band_sub[which - 7]; *naux = 0; break;
+    case 7: case 8: *list = &p.band_sub[which - 7]; *naux = 0; break;
+    default: {
+        static const std::vector<Tile> none;
+        *list = &none;
+        *naux = 2 * p.stray_segs[which - 9].size();
+    }
     }
 }
 
@@ -211,7 +218,7 @@ extern "C" {
 
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux) {
-    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 8) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 10) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -231,7 +238,7 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
 
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which, uint32_t *tiles,
                         uint64_t n_tiles, uint64_t *aux, uint64_t n_aux) {
-    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 8) return K2_E_INVALID_ARG;
+    if (!tree || !opts || !valid_opts(*opts) || which < 0 || which > 10) return K2_E_INVALID_ARG;
     Plan plan;
     k2_status st;
     try {
@@ -256,8 +263,8 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
         std::copy(plan.codes.begin(), plan.codes.end(), aux);
     } else if (which == 3 || which == 4) {
         std::copy(plan.skip[which - 3].begin(), plan.skip[which - 3].end(), aux);
-    } else if (which == 1 || which == 2) {
-        const std::vector<Seg> &sg = plan.cached_segs[which - 1];
+    } else if (which == 1 || which == 2 || which == 9 || which == 10) {
+        const std::vector<Seg> &sg = which <= 2 ? plan.cached_segs[which - 1] : plan.stray_segs[which - 9];
         for (size_t k = 0; k < sg.size(); ++k) {
             aux[2 * k] = (uint64_t(sg[k].lo) << 32) | sg[k].count;
             aux[2 * k + 1] = sg[k].leaf;
@@ -283,6 +290,62 @@ k2_status k2_plan_offsets(const k2_tree *tree, const k2_plan_opts *opts, uint32_
     std::copy(plan.tile_bases.begin(), plan.tile_bases.end(), bases);
     return K2_OK;
 }
+
+namespace {
+
+// Strays of direction dir grouped by band, once the block origins are on the
+// device: count per band, prefix sums on the host, then each stray's record
+// at its band's cursor.  Every band with strays must have an owner tile.
+k2_status group_strays(Matrix &m, int dir, hipStream_t st) {
+    const Plan &pn = m.plan;
+    const uint32_t nb = pn.n_bands[dir];
+    if (nb == 0) return K2_OK;
+    const std::vector<Seg> &sg = pn.stray_segs[dir];
+    Seg *d_segs = reinterpret_cast<Seg *>(m.arena + m.layout.stray_segs_off[dir]);
+    uint32_t *d_off = reinterpret_cast<uint32_t *>(m.arena + m.layout.stray_off_off[dir]);
+    uint32_t *d_cur = reinterpret_cast<uint32_t *>(m.arena + m.layout.stray_cur_off[dir]);
+    StrayRec *d_rec = reinterpret_cast<StrayRec *>(m.arena + m.layout.strays_off[dir]);
+    if (pn.stray_nodes[dir] >= (1ull << 32) || sg.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
+    std::vector<uint32_t> cnt(nb), off(size_t(nb) + 1);
+    hipError_t e = hipSuccess;
+    if (!sg.empty()) e = hipMemcpyAsync(d_segs, sg.data(), sg.size() * sizeof(Seg), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemsetAsync(d_cur, 0, size_t(nb) * 4, st);
+    if (e == hipSuccess) e = hipError_t(launch_stray_count(m, dir, d_segs, uint32_t(sg.size()), d_cur, st));
+    if (e == hipSuccess) e = hipMemcpyAsync(cnt.data(), d_cur, size_t(nb) * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+        set_hip_error(int(e), "count strays");
+        return K2_E_HIP;
+    }
+    std::vector<char> owner(nb, 0);
+    for (const Tile &tl : pn.cached_tiles[dir])
+        if (tl.code_off && tl.win_log2 != kNoWindow) {
+            const uint64_t b = uint64_t(dir == K2_RIGHT ? tl.win_row : tl.win_col) >> tl.win_log2;
+            if (b < nb) owner[b] = 1;
+        }
+    uint64_t total = 0;
+    for (uint32_t b = 0; b < nb; ++b) {
+        if (cnt[b] && !owner[b]) return K2_E_UNSUPPORTED;   // planner invariant
+        off[b] = uint32_t(total);
+        total += cnt[b];
+    }
+    off[nb] = uint32_t(total);
+    if (total != pn.stray_nodes[dir]) return K2_E_UNSUPPORTED;
+    e = hipMemcpyAsync(d_off, off.data(), off.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(d_cur, off.data(), size_t(nb) * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = hipError_t(launch_stray_scatter(m, dir, d_segs, uint32_t(sg.size()), d_cur, d_rec, st));
+    if (e == hipSuccess) e = hipStreamSynchronize(st);   // before off goes away
+    if (e != hipSuccess) {
+        set_hip_error(int(e), "group strays");
+        return K2_E_HIP;
+    }
+    m.d_strays[dir] = d_rec;
+    m.d_stray_off[dir] = d_off;
+    return K2_OK;
+}
+
+}  // namespace
 
 k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *d_arena,
                            uint64_t arena_bytes, void *stream, k2_matrix **out) {
@@ -432,6 +495,10 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
         if (e != hipSuccess) {
             set_hip_error(e, "cache last internal level");
             return fail(K2_E_HIP);
+        }
+        for (int dir = 0; dir < 2; ++dir) {
+            const k2_status s = group_strays(m, dir, st_h);
+            if (s != K2_OK) return fail(s);
         }
     }
     hipError_t e = hipStreamSynchronize(st_h);

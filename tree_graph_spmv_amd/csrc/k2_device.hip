@@ -601,16 +601,37 @@ __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_
     return b;
 }
 
+// A node's cells as a 16-bit mask (bit 4 b + q: cell q of the leaf for
+// child b) from ssh = s | p << 6 (signature s, first leaf nibble p of lo32)
+// and the two leaf-level dwords holding its leaf nibbles: they are the low
+// 4 * fan-out bits of (hi32:lo32) >> 4 p, in child order.
+__device__ __forceinline__ uint32_t node_cells(uint32_t ssh, uint32_t lo32, uint32_t hi32) {
+    const uint32_t s = ssh & 15u;
+    uint32_t bits = uint32_t(((uint64_t(hi32) << 32) | lo32) >> ((ssh >> 4) & 28u));
+    uint32_t cells = 0u;
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b)
+        if (s & (1u << b)) {
+            cells |= (bits & 15u) << (4 * b);
+            bits >>= 4;
+        }
+    return cells;
+}
+
 // One product over the cached last internal level (Sec. 3.5): each workgroup
 // takes a tile, a list of segments of up to 64 nodes of that level, each
 // with its first leaf's index; wave w takes segments w, w + 4, ...  A wave
 // works on four of its segments at once: while it visits the leaves of one,
 // the block origins and leaf signatures of the next, the signatures of the
-// one after and the descriptor of the third are in flight.
+// one after and the descriptor of the third are in flight.  A band's owner
+// tile (code_off = 1) then adds the band's strays (strays[stray_off[band]
+// .. stray_off[band + 1]), each with its block origin, first leaf and
+// signature) to the same window.
 template <class SR, int DIR, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
-    const uint64_t *__restrict__ blocks, const typename SR::T *__restrict__ x,
+    const uint64_t *__restrict__ blocks, const StrayRec *__restrict__ strays,
+    const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
     int use_dir) {
     using T = typename SR::T;
@@ -637,21 +658,28 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             const Seg g3 = stage_seg(segs, tl.first, k + 3 * kWaves, nseg);
             const SegSig a2 = stage_sig(t, d, g2, sig_words, use_dir);
             const SegLeaves b1 = stage_leaves(a1, blocks, leaf_dw, last_dw);
-            // the node's leaf nibbles are the low 4 * fan-out bits of 'bits'
-            const uint32_t s0 = b0.ssh & 15u;
-            uint32_t bits = uint32_t(((uint64_t(b0.hi32) << 32) | b0.lo32) >> ((b0.ssh >> 4) & 28u));
-            uint32_t cells = 0u;
-#pragma unroll
-            for (uint32_t b = 0; b < 4; ++b)
-                if (s0 & (1u << b)) {
-                    cells |= (bits & 15u) << (4 * b);
-                    bits >>= 4;
-                }
-            ring_cells<SR, DIR, Off>(uint32_t(b0.blk >> 32), uint32_t(b0.blk), cells, x, y, B, VL, w, wc,
-                                     ring_head, ring_fill);
+            ring_cells<SR, DIR, Off>(uint32_t(b0.blk >> 32), uint32_t(b0.blk),
+                                     node_cells(b0.ssh, b0.lo32, b0.hi32), x, y, B, VL, w, wc, ring_head,
+                                     ring_fill);
             b0 = b1;
             a1 = a2;
             g2 = g3;
+        }
+        if (tl.code_off && strays && tl.win_log2 != kNoWindow) {
+            // the band's owner tile: its strays, 64 per wave at a time
+            const uint32_t band = ((DIR == K2_RIGHT) ? tl.win_row : tl.win_col) >> tl.win_log2;
+            const uint32_t s0 = stray_off[band], s1 = stray_off[band + 1];
+            const uint32_t lane = __lane_id();
+            for (uint32_t b = s0 + wave * 64u; b < s1; b += kThreads) {
+                const bool in = b + lane < s1;
+                const StrayRec r = strays[in ? b + lane : b];
+                const uint32_t s = in ? r.sig : 0u;
+                const uint32_t dw = (r.leaf >> 3) < last_dw ? (r.leaf >> 3) : last_dw;
+                const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
+                ring_cells<SR, DIR, Off>(uint32_t(r.blk >> 32), uint32_t(r.blk),
+                                         node_cells(s | ((r.leaf & 7u) << 6), lo32, hi32), x, y, B, VL, w,
+                                         wc, ring_head, ring_fill);
+            }
         }
         ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
         close_window<SR>(w, y, n_out, B);
@@ -849,6 +877,50 @@ __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict
     if (__lane_id() == 0 && found) atomicAdd(count, (unsigned long long)found);
 }
 
+// ------------------------------------------------------------- strays
+
+// Grouping the strays by band when a matrix is created: one wave per stray
+// segment, a lane per node.  The band is the node's first output >> qlog.
+__global__ __launch_bounds__(kThreads) void stray_count_kernel(const Seg *__restrict__ segs, uint32_t n_segs,
+                                                               const uint64_t *__restrict__ blocks, int dir,
+                                                               uint32_t qlog, uint32_t *__restrict__ counts) {
+    const uint32_t lane = __lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (uint32_t k = blockIdx.x * kWaves + wave; k < n_segs; k += gridDim.x * kWaves) {
+        const Seg sg = segs[k];
+        if (lane < sg.count) {
+            const uint64_t blk = blocks[sg.lo + lane];
+            const uint32_t o = dir == K2_RIGHT ? uint32_t(blk >> 32) : uint32_t(blk);
+            atomicAdd(&counts[o >> qlog], 1u);
+        }
+    }
+}
+
+// Each stray's record at its band's cursor (advanced); its first leaf is the
+// segment's plus the fan-outs of the nodes before it.
+__global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, const Seg *__restrict__ segs,
+                                                                 uint32_t n_segs,
+                                                                 const uint64_t *__restrict__ blocks, int dir,
+                                                                 uint32_t qlog, uint32_t *__restrict__ cursor,
+                                                                 StrayRec *__restrict__ out) {
+    const uint32_t lane = __lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t *__restrict__ sig_words = t.words[t.levels - 2];
+    for (uint32_t k = blockIdx.x * kWaves + wave; k < n_segs; k += gridDim.x * kWaves) {
+        const Seg sg = segs[k];
+        const bool in = lane < sg.count;
+        const uint32_t s = in ? nib(sig_words, uint64_t(sg.lo) + lane) : 0u;
+        uint32_t total;
+        const uint32_t ex = wave_scan(__popc(s), total);
+        if (in) {
+            const uint64_t blk = blocks[sg.lo + lane];
+            const uint32_t o = dir == K2_RIGHT ? uint32_t(blk >> 32) : uint32_t(blk);
+            const uint32_t pos = atomicAdd(&cursor[o >> qlog], 1u);
+            out[pos] = StrayRec{blk, sg.leaf + ex, s};
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 namespace {
@@ -904,7 +976,8 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
-                       m.d_cached_segs[DIR], m.d_cached, static_cast<const T *>(x),
+                       m.d_cached_segs[DIR], m.d_cached, m.d_strays[DIR], m.d_stray_off[DIR],
+                       static_cast<const T *>(x),
                        static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0);
     return hipGetLastError();
 }
@@ -1007,6 +1080,29 @@ int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const
     if (emit_codes) return run_descent<BooleanU32, K2_RIGHT, true>(m, 1, nullptr, nullptr, emit_codes, st);
     return dir == K2_RIGHT ? dispatch_descent<K2_RIGHT>(m, semiring, batch, x, y, st)
                            : dispatch_descent<K2_LEFT>(m, semiring, batch, x, y, st);
+}
+
+static uint32_t stray_grid(uint32_t n_segs) {
+    const uint32_t b = (n_segs + kWaves - 1) / kWaves;
+    return b < 65536 ? (b ? b : 1) : 65536;
+}
+
+int launch_stray_count(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *counts,
+                       void *stream) {
+    if (n_segs == 0) return hipSuccess;
+    hipLaunchKernelGGL(stray_count_kernel, dim3(stray_grid(n_segs)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), segs, n_segs, m.d_cached, dir,
+                       uint32_t(m.plan.window_log2), counts);
+    return hipGetLastError();
+}
+
+int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *cursor,
+                         StrayRec *out, void *stream) {
+    if (n_segs == 0) return hipSuccess;
+    hipLaunchKernelGGL(stray_scatter_kernel, dim3(stray_grid(n_segs)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), m.dev, segs, n_segs, m.d_cached, dir,
+                       uint32_t(m.plan.window_log2), cursor, out);
+    return hipGetLastError();
 }
 
 const char *hip_error_text(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }

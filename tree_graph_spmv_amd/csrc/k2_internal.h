@@ -61,6 +61,17 @@ struct Seg {
 };
 static_assert(sizeof(Seg) == 16, "segment layout");
 
+// A stray: a node of the cached level outside the dense quadrants, stored
+// again with its band's other strays so that a band tile can add its cells to
+// the band's window: the node's block origin (first row << 32 | first
+// column), the level-order index of its first leaf and its signature.
+struct StrayRec {
+    uint64_t blk;
+    uint32_t leaf;
+    uint32_t sig;
+};
+static_assert(sizeof(StrayRec) == 16, "stray layout");
+
 // The plan of a matrix: host top level, descent tiles in depth-first order and
 // the codes their first level starts from, and per product direction the
 // tiles of the cached level (a cached tile is 'count' segments starting at
@@ -94,6 +105,14 @@ struct Plan {
     uint32_t band_cap = 0;
     std::vector<Tile> band_groups[2], band_sub[2], rest_tiles[2];
     std::vector<uint64_t> skip[2];
+    // Strays (cached level, band_strays): per direction the segments of the
+    // nodes outside every band tile's ranges, and the number of bands of
+    // 2^window_log2 outputs.  Every band holding strays has one cached tile
+    // with code_off = 1 that adds them (the band's owner tile); matrix
+    // creation groups the strays by band on the device.
+    std::vector<Seg> stray_segs[2];
+    uint64_t stray_nodes[2] = {0, 0};
+    uint32_t n_bands[2] = {0, 0};
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -106,6 +125,8 @@ struct Layout {
     uint64_t codes_off = 0, tiles_off = 0, cached_off = 0, bases_off = 0;
     uint64_t groups_off[2] = {0, 0}, sub_off[2] = {0, 0}, rest_off[2] = {0, 0}, skip_off[2] = {0, 0};
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
+    uint64_t stray_segs_off[2] = {0, 0}, stray_off_off[2] = {0, 0}, stray_cur_off[2] = {0, 0};
+    uint64_t strays_off[2] = {0, 0};
     k2_mem_breakdown mem = {};
 };
 
@@ -139,6 +160,8 @@ struct Matrix {
     const uint64_t *d_skip[2] = {nullptr, nullptr};
     const Tile *d_cached_tiles[2] = {nullptr, nullptr};
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
+    const StrayRec *d_strays[2] = {nullptr, nullptr};   // grouped by band
+    const uint32_t *d_stray_off[2] = {nullptr, nullptr}; // band b: d_strays[off[b] .. off[b + 1])
     uint64_t *d_cached = nullptr;        // last internal level codes or null
     uint32_t window_elems = 0, window_batch = 0;
     size_t max_window_lds = 0;   // LDS bytes a product's window may take per workgroup
@@ -159,6 +182,13 @@ int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const
                    uint64_t *emit_codes, void *stream);
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
                   void *stream);
+// Strays of direction dir (Plan::stray_segs): count per band into counts
+// (n_bands entries, zeroed by the caller), or with 'cursor' (each band's
+// first slot, advanced) write each stray's record to 'out'.
+int launch_stray_count(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *counts,
+                       void *stream);
+int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *cursor,
+                         StrayRec *out, void *stream);
 const char *hip_error_text(int err);
 
 void set_hip_error(int err, const char *where);

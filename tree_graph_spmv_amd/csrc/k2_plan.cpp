@@ -30,7 +30,11 @@
 // one tile whose window is that band: the workgroup accumulates the band's
 // outputs in LDS (Q outputs x B vectors) and adds them to y once at the end,
 // so each band's part of y costs one coalesced pass instead of one atomic
-// per cell.  The sparse rest keeps one y atomic per cell.  (The kernels also
+// per cell.  With band_strays the nodes outside the dense quadrants (strays)
+// join their band's window too: every band holding some gets a tile, and the
+// device groups the strays by band when the matrix is created (their bands
+// come from the block origins it computes).  Otherwise the sparse rest keeps
+// one y atomic per cell, in separate tiles.  (The kernels also
 // accept windows on descent tiles; planning one per dense quadrant made many
 // small tiles and measured slower, so descent tiles carry none.)
 #include <algorithm>
@@ -129,11 +133,11 @@ struct Planner {
     }
 
     // Appends the segments of nodes [lo, lo + count) of the last internal level.
-    void push_segs(int dir, uint64_t lo, uint64_t count) {
+    static void push_segs(std::vector<Seg> &to, uint64_t lo, uint64_t count) {
         for (uint64_t i = 0; i < count; i += kSegNodes)
-            p.cached_segs[dir].push_back(
-                {uint32_t(lo + i), uint32_t(std::min<uint64_t>(kSegNodes, count - i)), 0u, 0u});
+            to.push_back({uint32_t(lo + i), uint32_t(std::min<uint64_t>(kSegNodes, count - i)), 0u, 0u});
     }
+    void push_segs(int dir, uint64_t lo, uint64_t count) { push_segs(p.cached_segs[dir], lo, count); }
 
     // Cached tiles of direction dir over nodes [lo, hi) of the last internal
     // level, no window: 'per' nodes per tile (cached_C if 0).
@@ -177,8 +181,7 @@ struct Planner {
     }
 
     // First leaf of every segment's first node, in parallel.
-    void set_leaves(int dir) {
-        std::vector<Seg> &sg = p.cached_segs[dir];
+    void set_leaves(std::vector<Seg> &sg) {
         const size_t n = sg.size();
         const unsigned nt = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
         std::vector<std::thread> pool;
@@ -353,7 +356,8 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     }
     // group boundaries: tile indexes where a new group starts (and the end)
     auto order_cached = [&](int dir, std::vector<size_t> groups) {
-        pl.set_leaves(dir);
+        pl.set_leaves(p.cached_segs[dir]);
+        pl.set_leaves(p.stray_segs[dir]);
         if (!o.xcd_remap) return;
         std::vector<uint64_t> w;
         for (const Tile &tl : p.cached_tiles[dir]) {
@@ -525,7 +529,12 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // chip's last-level cache can hold while their atomics arrive.
     const uint64_t band_min = std::max<uint64_t>(64, side * o.window_batch / 32);
     const int kb = block_log2(o, L - h);
+    const bool strays = cache && o.band_strays != 0;
     for (int dir = 0; dir < 2; ++dir) {
+        const uint64_t n_out = dir == K2_RIGHT ? t.n_rows : t.n_cols;
+        const uint64_t n_bands = (n_out + side - 1) >> (L - h);
+        if (strays && n_bands >= (1ull << 32)) return K2_E_UNSUPPORTED;
+        std::vector<char> has_tile(strays ? n_bands : 0, 0);
         // output coordinate of a quadrant's first cell
         auto out_of = [&](uint64_t code, int level) -> uint64_t {
             const uint64_t c = dir == K2_RIGHT ? even_bits(code >> 1) : even_bits(code);
@@ -564,6 +573,10 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                 if (cache) {
                     const size_t t0 = p.cached_tiles[dir].size();
                     pl.cached_band(dir, ranges, w);
+                    if (strays && p.cached_tiles[dir].size() > t0) {
+                        p.cached_tiles[dir][t0].code_off = 1;   // the band's owner tile
+                        has_tile[dense_units[i].first] = 1;
+                    }
                     for (size_t t = t0; t < p.cached_tiles[dir].size(); ++t) keyed.push_back({key, p.cached_tiles[dir][t]});
                     p.cached_tiles[dir].resize(t0);
                 }
@@ -625,6 +638,51 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         }
         rest_plain(dir, wr);
         if (!cache) continue;
+        if (strays) {
+            // strays: the runs of level l-2 outside the band tiles, and an
+            // owner tile (no segments) for every band they may reach that
+            // has none; a unit's nodes lie in its quadrant, whose output
+            // range gives the bands
+            std::vector<uint32_t> reach(n_bands + 1, 0);   // difference array
+            uint64_t run_lo = 0, run_hi = 0;
+            bool in_run = false;
+            for (size_t i = 0; i < units.size(); ++i) {
+                if (windowed[i]) continue;
+                const Unit &u = units[i];
+                const int lev = h <= d0 ? h : u.level;
+                const uint64_t first = out_of(u.qcode, lev), span = 1ull << (L - lev);
+                const uint64_t b0 = first >> (L - h);
+                const uint64_t b1 = std::min(n_bands, ((first + span - 1) >> (L - h)) + 1);
+                if (b0 < b1) {
+                    ++reach[b0];
+                    --reach[b1];
+                }
+                if (in_run && u.lo2 == run_hi) {
+                    run_hi = u.hi2;
+                    continue;
+                }
+                if (in_run) Planner::push_segs(p.stray_segs[dir], run_lo, run_hi - run_lo);
+                in_run = true;
+                run_lo = u.lo2;
+                run_hi = u.hi2;
+            }
+            if (in_run) Planner::push_segs(p.stray_segs[dir], run_lo, run_hi - run_lo);
+            for (const Seg &sg : p.stray_segs[dir]) p.stray_nodes[dir] += sg.count;
+            p.n_bands[dir] = uint32_t(n_bands);
+            uint32_t live = 0;
+            for (uint64_t b = 0; b < n_bands; ++b) {
+                live += reach[b];
+                if (!live || has_tile[b]) continue;
+                Tile w{};
+                (dir == K2_RIGHT ? w.win_row : w.win_col) = uint32_t(b << (L - h));
+                w.win_log2 = uint32_t(L - h);
+                w.level = uint32_t(last);
+                w.first = uint32_t(p.cached_segs[dir].size());
+                w.count = 0;
+                w.code_off = 1;
+                keyed.push_back({(b << (L - h)) >> kb, w});
+            }
+        }
         // the sparse rest in depth-first order: contiguous runs of level l-2
         // within one output block
         uint64_t run_lo = 0, run_hi = 0, run_key = 0;
@@ -635,7 +693,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
             for (size_t t = t0; t < p.cached_tiles[dir].size(); ++t) keyed.push_back({run_key, p.cached_tiles[dir][t]});
             p.cached_tiles[dir].resize(t0);
         };
-        for (size_t i = 0; i < units.size(); ++i) {
+        for (size_t i = 0; i < units.size() && !strays; ++i) {
             if (windowed[i]) continue;
             const Unit &u = units[i];
             const uint64_t key = out_of(ucodes[u.code_idx], u.level) >> kb;
@@ -699,6 +757,14 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
     for (int dir = 0; dir < 2; ++dir) {
         l.cached_tiles_off[dir] = take(cached ? sizeof(Tile) * plan.cached_tiles[dir].size() : 0, l.mem.tiles);
         l.cached_segs_off[dir] = take(cached ? sizeof(Seg) * plan.cached_segs[dir].size() : 0, l.mem.tiles);
+        // strays: their segments, each band's first record and a cursor per
+        // band (used while grouping), and the records (copies of cached-level
+        // entries, counted with the cached codes)
+        const bool st = cached && plan.n_bands[dir] > 0;
+        l.stray_segs_off[dir] = take(st ? sizeof(Seg) * plan.stray_segs[dir].size() : 0, l.mem.tiles);
+        l.stray_off_off[dir] = take(st ? 4 * (uint64_t(plan.n_bands[dir]) + 1) : 0, l.mem.tiles);
+        l.stray_cur_off[dir] = take(st ? 4 * uint64_t(plan.n_bands[dir]) : 0, l.mem.tiles);
+        l.strays_off[dir] = take(st ? sizeof(StrayRec) * plan.stray_nodes[dir] : 0, l.mem.cached_codes);
     }
     l.cached_off = take(cached ? 8 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
     l.mem.scratch = 0;
