@@ -148,3 +148,33 @@ def test_web_n20_d16(dev):
             torch.cuda.synchronize()
             check_parity(from_device(y, "plus_times"), want, "plus_times",
                          f"web_n20_d16 {direction} {mode}")
+
+
+def test_accumulate(dev):
+    """K2_SPMV_ACCUMULATE: y = y0 (+) A x, element by element against y0
+    combined with the oracle's product; band tiles that own their band
+    combine their window with y by plain loads and stores, the others add
+    atomically."""
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(7)
+    rows, cols = synth.rmat(11, 20000, seed=3)
+    n = 2 ** 11
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    combine = {"plus_times": lambda a, b: a.astype(np.float64) + b,
+               "boolean": np.maximum, "boolean_u32": np.bitwise_or, "tropical": np.minimum}
+    for var in (dict(), dict(band_strays=0), dict(window_elems=0)):
+        m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1, window_batch=1, **var), device=dev)
+        for mode, sr, direction, B in itertools.product(("tree", "cached"), ALL_SEMIRINGS, ("right", "left"),
+                                                        (1, 3)):
+            x = make_x(rng, sr, n, B)
+            y0 = make_x(rng, sr, n, B)
+            if sr == "boolean":   # a Boolean y holds 0 and 1
+                y0 = (y0 != 0).astype(np.float32)
+            y = to_device(y0, dev)
+            m.spmv(to_device(x, dev), y, direction=direction, semiring=sr, batch=B, mode=mode,
+                   accumulate=True)
+            torch.cuda.synchronize()
+            r = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
+            want = combine[sr](y0.reshape(r.shape), r)
+            check_parity(from_device(y, sr), want, sr, f"accumulate {var} {mode} {sr} {direction} B={B}")

@@ -144,17 +144,33 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes, 
     for which, (ctiles, ranges) in cached.items():
         seen = []
         owners = set()
+        per_band = {}
         for tl in ctiles:
-            if int(tl[3]):   # a band's owner tile: windowed, one per band
-                assert int(tl[3]) == 1 and tl[6] != 0xFFFFFFFF
+            assert int(tl[3]) in (0, 1, 2, 3)
+            if tl[6] != 0xFFFFFFFF:
                 band = (int(tl[4]) if which == 1 else int(tl[5])) >> int(tl[6])
+                per_band[band] = per_band.get(band, 0) + 1
+            if int(tl[3]) & 1:   # a band's owner tile: windowed, one per band
+                assert tl[6] != 0xFFFFFFFF
                 assert band not in owners, "one owner tile per band"
                 owners.add(band)
+        if owners:   # with strays every band has an owner (up to 2^20 bands)
+            log2 = int(next(tl[6] for tl in ctiles if int(tl[3]) & 1))
+            n_out = (cells_r.max() if which == 1 else cells_c.max()) + 1
+            assert owners >= set(range(int(n_out - 1) >> log2)), "a band without an owner tile"
+        for tl in ctiles:   # bit 1: the only tile of its band
+            if int(tl[3]) & 2:
+                assert tl[6] != 0xFFFFFFFF
+                band = (int(tl[4]) if which == 1 else int(tl[5])) >> int(tl[6])
+                assert per_band[band] == 1
+            elif tl[6] != 0xFFFFFFFF and owners:
+                band = (int(tl[4]) if which == 1 else int(tl[5])) >> int(tl[6])
+                assert per_band[band] > 1, "a band's only tile is marked"
         for tl in ctiles:
             first, count = int(tl[0]), int(tl[1])
             assert int(tl[2]) == last
             if count == 0:
-                assert (opts.xcd_remap and tl[6] == 0xFFFFFFFF) or int(tl[3]) == 1
+                assert (opts.xcd_remap and tl[6] == 0xFFFFFFFF) or int(tl[3]) & 1
                 continue
             total = 0
             for r, leaf in ranges[first:first + count]:
@@ -172,7 +188,7 @@ def check_plan(o, cells_r, cells_c, top, tiles, codes, cached, opts, all_codes, 
                 assert total <= 65536
         stray = strays[which] if strays else np.zeros((0, 2), np.uint64)
         if len(stray):
-            log2 = int(next(tl[6] for tl in ctiles if int(tl[3])))
+            log2 = int(next(tl[6] for tl in ctiles if int(tl[3]) & 1))
         for r, leaf in stray:   # each stray's band has an owner tile
             lo, n = int(r) >> 32, int(r) & 0xFFFFFFFF
             assert 1 <= n <= 64
@@ -358,7 +374,7 @@ def test_estimate_parts(case):
         extra = sum(32 * len(t.plan(opts, w)[1]) + 16 * len(t.plan(opts, w)[2]) for w in (1, 2))
         stray_tiles = stray_records = 0
         for w in (1, 2):   # strays: segments, band offsets and cursors; 16-byte records
-            owners = [tl for tl in t.plan(opts, w)[1] if int(tl[3])]
+            owners = [tl for tl in t.plan(opts, w)[1] if int(tl[3]) & 1]
             segs = t.plan(opts, w + 8)[2]
             if owners:
                 log2 = int(owners[0][6])

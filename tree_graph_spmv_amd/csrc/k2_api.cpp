@@ -532,7 +532,9 @@ k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semirin
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (m.timing) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(m.ev[0]), st), "timing");
     const uint32_t zero = semiring == K2_TROPICAL_F32 ? 0x7F800000u : 0u;
-    int e = accumulate ? int(hipSuccess) : launch_fill(d_y, n_out * batch, zero, stream);
+    // a cached product whose bands cover y writes every element itself
+    const bool fill = !accumulate && !(mode == K2_MODE_CACHED && !empty && cached_writes_all(m, direction, batch));
+    int e = fill ? launch_fill(d_y, n_out * batch, zero, stream) : int(hipSuccess);
     if (e != hipSuccess) {
         set_hip_error(e, "fill");
         return K2_E_HIP;
@@ -540,7 +542,7 @@ k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semirin
     if (m.timing) HIP_TRY(hipEventRecord(static_cast<hipEvent_t>(m.ev[1]), st), "timing");
     if (!empty)
         e = (mode == K2_MODE_CACHED)
-                ? launch_cached(m, direction, semiring, batch, d_x, d_y, stream)
+                ? launch_cached(m, direction, semiring, batch, d_x, d_y, accumulate ? 1 : 0, stream)
                 : launch_descent(m, direction, semiring, batch, d_x, d_y, nullptr, stream);
     if (e != hipSuccess) {
         set_hip_error(e, "spmv");
@@ -694,7 +696,7 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
     for (uint32_t level = 1; level <= max_levels && level < 0x7FFFFFFFu; ++level) {
         HIP_TRY(hipMemsetAsync(count, 0, 8, st), "search count");
         if (!empty)
-            e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, stream)
+            e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, 1, stream)
                          : launch_descent(m, direction, K2_BOOLEAN_U32X32, W, F, Y, nullptr, stream);
         if (e == hipSuccess) e = launch_bfs_mark(Y, V, F, d_dist, n * W, W, n_sources, int32_t(level), count, stream);
         if (e != hipSuccess) {

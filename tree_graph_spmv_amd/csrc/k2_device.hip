@@ -511,18 +511,31 @@ __device__ __forceinline__ Window<typename SR::T> open_window(const Tile &tl, ty
 }
 
 // Add a tile's window to y: one coalesced pass, skipping semiring zeros.
+// The only tile of its band (sole) writes y itself instead: it stores the
+// window (zeros included: y was not filled) or, accumulating, combines it
+// with y, with plain loads and stores.
 template <class SR>
 __device__ __forceinline__ void close_window(const Window<typename SR::T> &w,
                                              typename SR::T *__restrict__ y, uint64_t n_out,
-                                             uint32_t B) {
+                                             uint32_t B, bool sole, int accumulate) {
     using T = typename SR::T;
     if (!w.win) return;
     __syncthreads();
     const uint64_t rows = (w.out0 + w.rows <= n_out) ? w.rows : (n_out - w.out0);
     const uint32_t n = uint32_t(rows) * B;
-    for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
-        const T v = w.win[e];
-        if (SR::contributes_out(v)) SR::atomic(&y[w.out0 * B + e], v);
+    T *__restrict__ out = y + w.out0 * B;
+    if (sole && !accumulate) {
+        for (uint32_t e = threadIdx.x; e < n; e += kThreads) out[e] = w.win[e];
+    } else if (sole) {
+        for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+            const T v = w.win[e];
+            if (SR::contributes_out(v)) out[e] = SR::combine(out[e], v);
+        }
+    } else {
+        for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+            const T v = w.win[e];
+            if (SR::contributes_out(v)) SR::atomic(&out[e], v);
+        }
     }
     __syncthreads();
 }
@@ -633,7 +646,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     const uint64_t *__restrict__ blocks, const StrayRec *__restrict__ strays,
     const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    int use_dir) {
+    int use_dir, int accumulate) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
     __shared__ WaveCells<Off> s_cells[kWaves];
@@ -665,7 +678,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             a1 = a2;
             g2 = g3;
         }
-        if (tl.code_off && strays && tl.win_log2 != kNoWindow) {
+        if ((tl.code_off & 1u) && strays && tl.win_log2 != kNoWindow) {
             // the band's owner tile: its strays, 64 per wave at a time
             const uint32_t band = ((DIR == K2_RIGHT) ? tl.win_row : tl.win_col) >> tl.win_log2;
             const uint32_t s0 = stray_off[band], s1 = stray_off[band + 1];
@@ -682,7 +695,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             }
         }
         ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
-        close_window<SR>(w, y, n_out, B);
+        close_window<SR>(w, y, n_out, B, (tl.code_off & 2u) != 0, accumulate);
     }
 }
 
@@ -809,7 +822,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
         }
         __syncthreads();
       }
-      if (!EMIT) close_window<SR>(w, y, n_out, B);
+      if (!EMIT) close_window<SR>(w, y, n_out, B, false, 1);
     }
 }
 
@@ -963,7 +976,7 @@ bool narrow_offsets(const Matrix &m, uint32_t B) {
 }
 
 template <class SR, int DIR, class Off>
-int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t st) {
+int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumulate, hipStream_t st) {
     using T = typename SR::T;
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
     if (n_tiles == 0) return hipSuccess;
@@ -978,7 +991,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, hipStream_t 
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
                        m.d_cached_segs[DIR], m.d_cached, m.d_strays[DIR], m.d_stray_off[DIR],
                        static_cast<const T *>(x),
-                       static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0);
+                       static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0, accumulate);
     return hipGetLastError();
 }
 
@@ -1020,17 +1033,17 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
 }
 
 template <int DIR>
-int dispatch_cached(const Matrix &m, int semiring, uint32_t B, const void *x, void *y,
+int dispatch_cached(const Matrix &m, int semiring, uint32_t B, const void *x, void *y, int acc,
                     hipStream_t st) {
     switch (semiring) {
-    case K2_PLUS_TIMES_F32: return narrow_offsets(m, B) ? run_cached<PlusTimes, DIR, uint32_t>(m, B, x, y, st)
-                                                         : run_cached<PlusTimes, DIR, uint64_t>(m, B, x, y, st);
-    case K2_BOOLEAN_F32: return narrow_offsets(m, B) ? run_cached<BooleanF32, DIR, uint32_t>(m, B, x, y, st)
-                                                         : run_cached<BooleanF32, DIR, uint64_t>(m, B, x, y, st);
-    case K2_BOOLEAN_U32X32: return narrow_offsets(m, B) ? run_cached<BooleanU32, DIR, uint32_t>(m, B, x, y, st)
-                                                         : run_cached<BooleanU32, DIR, uint64_t>(m, B, x, y, st);
-    case K2_TROPICAL_F32: return narrow_offsets(m, B) ? run_cached<Tropical, DIR, uint32_t>(m, B, x, y, st)
-                                                         : run_cached<Tropical, DIR, uint64_t>(m, B, x, y, st);
+    case K2_PLUS_TIMES_F32: return narrow_offsets(m, B) ? run_cached<PlusTimes, DIR, uint32_t>(m, B, x, y, acc, st)
+                                                         : run_cached<PlusTimes, DIR, uint64_t>(m, B, x, y, acc, st);
+    case K2_BOOLEAN_F32: return narrow_offsets(m, B) ? run_cached<BooleanF32, DIR, uint32_t>(m, B, x, y, acc, st)
+                                                         : run_cached<BooleanF32, DIR, uint64_t>(m, B, x, y, acc, st);
+    case K2_BOOLEAN_U32X32: return narrow_offsets(m, B) ? run_cached<BooleanU32, DIR, uint32_t>(m, B, x, y, acc, st)
+                                                         : run_cached<BooleanU32, DIR, uint64_t>(m, B, x, y, acc, st);
+    case K2_TROPICAL_F32: return narrow_offsets(m, B) ? run_cached<Tropical, DIR, uint32_t>(m, B, x, y, acc, st)
+                                                         : run_cached<Tropical, DIR, uint64_t>(m, B, x, y, acc, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1068,10 +1081,16 @@ int launch_fill(void *y, uint64_t n_words32, uint32_t value, void *stream) {
 }
 
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
-                  void *stream) {
+                  int accumulate, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return dir == K2_RIGHT ? dispatch_cached<K2_RIGHT>(m, semiring, batch, x, y, st)
-                           : dispatch_cached<K2_LEFT>(m, semiring, batch, x, y, st);
+    return dir == K2_RIGHT ? dispatch_cached<K2_RIGHT>(m, semiring, batch, x, y, accumulate, st)
+                           : dispatch_cached<K2_LEFT>(m, semiring, batch, x, y, accumulate, st);
+}
+
+bool cached_writes_all(const Matrix &m, int dir, uint32_t batch) {
+    int use = 0;
+    window_bytes(m, batch, &use);
+    return use && m.plan.bands_cover[dir] && !m.plan.cached_tiles[dir].empty();
 }
 
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,

@@ -110,9 +110,13 @@ struct Plan {
     // 2^window_log2 outputs.  Every band holding strays has one cached tile
     // with code_off = 1 that adds them (the band's owner tile); matrix
     // creation groups the strays by band on the device.
+    // code_off bit 0 marks a band's owner tile, bit 1 a band's only tile
+    // (it stores its window into y instead of adding it); bands_cover: every
+    // band has exactly one tile, so a windowed product writes all of y.
     std::vector<Seg> stray_segs[2];
     uint64_t stray_nodes[2] = {0, 0};
     uint32_t n_bands[2] = {0, 0};
+    bool bands_cover[2] = {false, false};
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);
@@ -181,7 +185,10 @@ int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, int32_t *dist, uint64
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
                    uint64_t *emit_codes, void *stream);
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
-                  void *stream);
+                  int accumulate, void *stream);
+// Whether a cached product of this batch writes every element of y itself
+// (windows in use and every band its own tile's), so y needs no fill.
+bool cached_writes_all(const Matrix &m, int dir, uint32_t batch);
 // Strays of direction dir (Plan::stray_segs): count per band into counts
 // (n_bands entries, zeroed by the caller), or with 'cursor' (each band's
 // first slot, advanced) write each stray's record to 'out'.

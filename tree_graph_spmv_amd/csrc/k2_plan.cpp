@@ -669,10 +669,12 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
             if (in_run) Planner::push_segs(p.stray_segs[dir], run_lo, run_hi - run_lo);
             for (const Seg &sg : p.stray_segs[dir]) p.stray_nodes[dir] += sg.count;
             p.n_bands[dir] = uint32_t(n_bands);
+            // up to 2^20 bands every band gets a tile, so the bands cover y
+            const bool all_bands = n_bands <= (1u << 20);
             uint32_t live = 0;
             for (uint64_t b = 0; b < n_bands; ++b) {
                 live += reach[b];
-                if (!live || has_tile[b]) continue;
+                if ((!live && !all_bands) || has_tile[b]) continue;
                 Tile w{};
                 (dir == K2_RIGHT ? w.win_row : w.win_col) = uint32_t(b << (L - h));
                 w.win_log2 = uint32_t(L - h);
@@ -682,6 +684,20 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                 w.code_off = 1;
                 keyed.push_back({(b << (L - h)) >> kb, w});
             }
+            // a band with one tile: that tile alone writes the band's part of
+            // y (code_off bit 1), so it may store its window instead of
+            // adding it atomically; when every band is such, the cached
+            // product writes all of y and needs no fill
+            std::vector<uint32_t> per_band(n_bands, 0);
+            auto band_of = [&](const Tile &tl) {
+                return uint64_t(dir == K2_RIGHT ? tl.win_row : tl.win_col) >> tl.win_log2;
+            };
+            for (const auto &kt : keyed) ++per_band[band_of(kt.second)];
+            bool every = all_bands;
+            for (uint64_t b = 0; b < n_bands; ++b) every = every && per_band[b] == 1;
+            for (auto &kt : keyed)
+                if (per_band[band_of(kt.second)] == 1) kt.second.code_off |= 2u;
+            p.bands_cover[dir] = every;
         }
         // the sparse rest in depth-first order: contiguous runs of level l-2
         // within one output block
