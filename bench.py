@@ -39,6 +39,7 @@ def parse():
     p.add_argument("--offsets", default=None, choices=("auto", "directory", "scan"),
                    help="plan option (default: the library's)")
     p.add_argument("--xcd-remap", type=int, default=None, help="plan option (default: the library's)")
+    p.add_argument("--band-strays", type=int, default=None, help="plan option (default: the library's)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-stride", type=int, default=8,
                    help="oracle sample: the edges whose source is a multiple of this")
@@ -156,17 +157,19 @@ def main():
     log(f"built: nnz={tree.nnz} nodes={tree.nodes} levels={tree.levels} in {build_s:.1f}s")
 
     extra = {k: v for k, v in (("window_elems", args.window_elems), ("window_batch", args.window_batch),
-                               ("offsets", args.offsets), ("xcd_remap", args.xcd_remap)) if v is not None}
+                               ("offsets", args.offsets), ("xcd_remap", args.xcd_remap),
+                               ("band_strays", args.band_strays)) if v is not None}
     opts = k2.plan_defaults(tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"), **extra)
     est = tree.estimate(opts, semiring=semiring, batch=batch)
-    # load the kernels' code object first (a tiny product), so that the
-    # memory measured below is the matrix's and the vectors' alone
+    # run the same kernels once on a tiny matrix first (the runtime loads a
+    # kernel's code on its first launch), so that the memory measured below
+    # is the matrix's and the vectors' alone
     tiny = k2.Tree([0], [0], 4, 4)
-    tm = k2.Matrix(tiny, device=dev)
+    tm = k2.Matrix(tiny, opts, device=dev)
     tx = torch.zeros(4 * batch, dtype=torch.int32 if semiring == "boolean_u32" else torch.float32,
                      device=dev)
     for d in directions:
-        tm.spmv(tx, direction=d, semiring=semiring, batch=batch)
+        tm.spmv(tx, direction=d, semiring=semiring, batch=batch, mode=mode)
     torch.cuda.synchronize()
     del tm, tx
     xh = synth.workload_x(args.workload, n, batch=batch)   # one x and one y serve both directions
