@@ -46,6 +46,10 @@ struct PlusTimes {
     // tree-only products use the band groups: every cell's contribution is an
     // atomic add that the windows absorb
     static constexpr bool kTreeBands = true;
+    // window updates skip the zero tests: inputs are rarely zero, and adding
+    // a zero leaves a window word as it is (windows start at +0 and never
+    // hold -0)
+    static constexpr bool kWindowUnchecked = true;
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0.0f; }
     __device__ static bool contributes(T x) { return x != 0.0f; }
@@ -74,6 +78,7 @@ struct BooleanF32 {
     using T = float;
     // tree-only products take the depth-first tiles (see PlusTimes)
     static constexpr bool kTreeBands = false;
+    static constexpr bool kWindowUnchecked = false;
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0.0f; }
     __device__ static bool contributes(T x) { return (__float_as_uint(x) & 0x7FFFFFFFu) != 0u; }
@@ -94,6 +99,7 @@ struct BooleanU32 {
     using T = uint32_t;
     // tree-only products take the depth-first tiles (see PlusTimes)
     static constexpr bool kTreeBands = false;
+    static constexpr bool kWindowUnchecked = false;
     static constexpr uint32_t kZeroBits = 0u;
     __device__ static T zero() { return 0u; }
     __device__ static bool contributes(T x) { return x != 0u; }
@@ -113,6 +119,7 @@ struct Tropical {
     // tree-only products take the depth-first tiles: contributions equal
     // to the zero (x = +inf) issue no atomic, and relaxation steps skip most
     static constexpr bool kTreeBands = false;
+    static constexpr bool kWindowUnchecked = false;
     static constexpr uint32_t kZeroBits = 0x7F800000u;   // +inf
     __device__ static T zero() { return __uint_as_float(kZeroBits); }
     __device__ static bool contributes(T x) { return x < __uint_as_float(kZeroBits); }
@@ -307,6 +314,8 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
                                             const bool (&ok)[kUnroll], typename SR::T *__restrict__ out,
                                             uint32_t v) {
     using T = typename SR::T;
+    // no zero tests where the semiring allows (window updates only)
+    constexpr bool kUnchecked = kWin && SR::kWindowUnchecked;
     auto apply = [&](Off o, T c) {
         if constexpr (kWin) SR::lds_atomic(&out[o + v], c);
         else SR::atomic(&out[o + v], c);
@@ -318,17 +327,17 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
         for (int u = 0; u < kUnroll; ++u)
             if (ok[u]) {
                 if (yo[u] != cur) {
-                    if (SR::contributes_out(acc)) apply(cur, acc);
+                    if (kUnchecked || SR::contributes_out(acc)) apply(cur, acc);
                     acc = SR::zero();
                     cur = yo[u];
                 }
-                if (SR::contributes(xv[u])) acc = SR::combine(acc, SR::contrib(xv[u]));
+                if (kUnchecked || SR::contributes(xv[u])) acc = SR::combine(acc, SR::contrib(xv[u]));
             }
-        if (SR::contributes_out(acc)) apply(cur, acc);
+        if (kUnchecked || SR::contributes_out(acc)) apply(cur, acc);
     } else {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
-            if (ok[u] && SR::contributes(xv[u])) apply(yo[u], SR::contrib(xv[u]));
+            if (ok[u] && (kUnchecked || SR::contributes(xv[u]))) apply(yo[u], SR::contrib(xv[u]));
     }
 }
 
