@@ -486,20 +486,37 @@ __device__ __forceinline__ void ring_drain(const typename SR::T *__restrict__ x,
     fill = 0;
 }
 
+// A node's cells as a 16-bit mask (bit 4 b + q: cell q of the leaf for
+// child b) from ssh = s | p << 6 (signature s, first leaf nibble p of lo32)
+// and the two leaf-level dwords holding its leaf nibbles: they are the low
+// 4 * fan-out bits of (hi32:lo32) >> 4 p, in child order.
+__device__ __forceinline__ uint32_t node_cells(uint32_t ssh, uint32_t lo32, uint32_t hi32) {
+    const uint32_t s = ssh & 15u;
+    uint32_t bits = uint32_t(((uint64_t(hi32) << 32) | lo32) >> ((ssh >> 4) & 28u));
+    uint32_t cells = 0u;
+#pragma unroll
+    for (uint32_t b = 0; b < 4; ++b)
+        if (s & (1u << b)) {
+            cells |= (bits & 15u) << (4 * b);
+            bits >>= 4;
+        }
+    return cells;
+}
+
 // leaf_cells for a lane whose node has Morton code 'code', signature s and
-// first leaf 'off'.
+// first leaf 'off': its leaf nibbles come from two leaf-level dwords, loaded
+// by every lane at clamped indexes (last_dw: the level's last dword), so no
+// load sits under a branch.
 template <class SR, int DIR, class Off>
 __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
-                                             const uint64_t *__restrict__ leaf_words,
+                                             const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
                                              const typename SR::T *__restrict__ x,
                                              typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
                                              Window<typename SR::T> w, WaveCells<Off> *wc) {
-    uint32_t cells = 0u, j = 0u;
-#pragma unroll
-    for (uint32_t b = 0; b < 4; ++b)
-        if (s & (1u << b)) cells |= nib(leaf_words, uint64_t(off) + j++) << (4 * b);
-    leaf_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u, cells, x, y, B,
-                             VL, w, wc);
+    const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
+    const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
+    leaf_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u,
+                             node_cells(s | ((off & 7u) << 6), lo32, hi32), x, y, B, VL, w, wc);
 }
 
 // The window of tile 'tl' for this product (no window: win = null), its LDS
@@ -621,23 +638,6 @@ __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_
     b.lo32 = leaf_dw[dw];
     b.hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
     return b;
-}
-
-// A node's cells as a 16-bit mask (bit 4 b + q: cell q of the leaf for
-// child b) from ssh = s | p << 6 (signature s, first leaf nibble p of lo32)
-// and the two leaf-level dwords holding its leaf nibbles: they are the low
-// 4 * fan-out bits of (hi32:lo32) >> 4 p, in child order.
-__device__ __forceinline__ uint32_t node_cells(uint32_t ssh, uint32_t lo32, uint32_t hi32) {
-    const uint32_t s = ssh & 15u;
-    uint32_t bits = uint32_t(((uint64_t(hi32) << 32) | lo32) >> ((ssh >> 4) & 28u));
-    uint32_t cells = 0u;
-#pragma unroll
-    for (uint32_t b = 0; b < 4; ++b)
-        if (s & (1u << b)) {
-            cells |= (bits & 15u) << (4 * b);
-            bits >>= 4;
-        }
-    return cells;
 }
 
 // One product over the cached last internal level (Sec. 3.5): each workgroup
@@ -796,7 +796,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                                          (compact_even(cur[i]) * 4u);
         } else {
             const uint64_t *__restrict__ wd = t.words[last];
-            const uint64_t *__restrict__ leaf_words = t.words[last + 1];
+            const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[last + 1]);
+            const uint32_t last_dw = uint32_t((uint64_t(t.nodes[last + 1]) + 15u) / 16u * 2u - 1u);
             uint32_t leaf0 = 0;
             if (bases) {
                 // scan offsets: the tile's first leaf, plus the fan-outs of the
@@ -814,7 +815,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
             for (uint32_t seg = wave * 64; seg < cnt; seg += kThreads) {
                 const uint32_t i = seg + lane;
                 const bool valid = i < cnt;
-                const uint32_t s = valid ? nib(wd, uint64_t(lo) + i) : 0u;
+                const uint32_t s = nib(wd, uint64_t(lo) + (valid ? i : seg)) & (valid ? 15u : 0u);
                 const uint64_t code = valid ? cur[i] : 0ull;
                 uint32_t base = leaf0;
                 if (bases) {
@@ -825,7 +826,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 uint32_t total;
                 const uint32_t ex = wave_scan(__popc(s), total);   // the true fan-outs give the offsets
                 const bool skip = valid && nskip && in_ranges(skips + tl.win_row, nskip, lo + i);
-                leaf_segment<SR, DIR, Off>(code, skip ? 0u : s, base + ex, leaf_words, x, y, B, VL, w,
+                leaf_segment<SR, DIR, Off>(code, skip ? 0u : s, base + ex, leaf_dw, last_dw, x, y, B, VL, w,
                                            &s_cells[wave]);
             }
         }
