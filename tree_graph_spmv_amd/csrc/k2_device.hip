@@ -708,6 +708,105 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     }
 }
 
+// Tree-only band groups (Sec. 3.4 tiles over the dense quadrants of one
+// row / column band, into one LDS window): each wave takes sub-tiles w, w +
+// 4, ... of its workgroup's group and descends each on its own, level by
+// level, with wave scans and a frontier of at most 'cap' nodes per level in
+// the wave's LDS, so no workgroup barrier is needed before the window's
+// flush.  Frontier entries are Morton codes relative to the sub-tile's
+// window quadrant (at most 2 log2 Q bits); the leaf level's cells go through
+// the wave's ring as in the cached kernel.  Offsets: planned (bases, the
+// sub-tile's first child on each level) or, without them, the directory.
+template <class SR, int DIR, class Off>
+__global__ __launch_bounds__(kThreads, kOccupancy) void band_kernel(
+    DevTree t, const Tile *__restrict__ groups, const Tile *__restrict__ subs, uint32_t n_groups,
+    const uint64_t *__restrict__ tile_codes, const uint32_t *__restrict__ bases, uint32_t cap,
+    const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+    uint64_t n_out, int use_window) {
+    using T = typename SR::T;
+    extern __shared__ uint64_t s_dyn[];   // kWaves frontiers of 2 cap codes, then the window
+    __shared__ WaveCells<Off> s_cells[kWaves];
+    const int last = t.levels - 2;
+    const uint32_t lane = __lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint32_t *front = reinterpret_cast<uint32_t *>(s_dyn) + size_t(wave) * 2u * cap;
+    T *s_win = reinterpret_cast<T *>(reinterpret_cast<uint32_t *>(s_dyn) + size_t(kWaves) * 2u * cap);
+    WaveCells<Off> *wc = &s_cells[wave];
+    const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[last + 1]);
+    const uint32_t last_dw = uint32_t((uint64_t(t.nodes[last + 1]) + 15u) / 16u * 2u - 1u);
+    for (uint32_t gi = blockIdx.x; gi < n_groups; gi += gridDim.x) {
+        const Tile gr = groups[gi];
+        const Window<T> w = open_window<SR, DIR>(gr, s_win, use_window, B);
+        const int hq = t.levels - int(gr.win_log2);   // the window quadrants' level
+        uint32_t ring_head = 0, ring_fill = 0;
+        for (uint32_t si = wave; si < gr.count; si += kWaves) {
+            const Tile tl = subs[gr.first + si];
+            int d = int(tl.level);
+            uint32_t lo = tl.first, cnt = tl.count;
+            // the sub-tile's quadrant: the level-hq prefix of its codes
+            const uint64_t qc = tile_codes[tl.code_off] >> (2 * (d - hq));
+            uint32_t *cur = front, *nxt = front + cap;
+            for (uint32_t i = lane; i < cnt; i += 64)
+                cur[i] = uint32_t(tile_codes[tl.code_off + i] - (qc << (2 * (d - hq))));
+            wave_lds_sync();
+            while (d < last) {
+                const uint32_t base = bases ? bases[tl.base_off + uint32_t(d - int(tl.level))]
+                                            : wave_child_offset(t, d, lo);
+                const uint64_t *__restrict__ wd = t.words[d];
+                uint32_t running = 0;
+                for (uint32_t s0 = 0; s0 < cnt; s0 += 64) {
+                    const uint32_t i = s0 + lane;
+                    const bool valid = i < cnt;
+                    const uint32_t sg = nib(wd, uint64_t(lo) + (valid ? i : s0)) & (valid ? 15u : 0u);
+                    uint32_t total;
+                    const uint32_t ex = wave_scan(__popc(sg), total);
+                    if (sg) {
+                        const uint32_t c2 = cur[i] << 2;
+                        uint32_t p = running + ex;
+#pragma unroll
+                        for (uint32_t b = 0; b < 4; ++b)
+                            if (sg & (1u << b)) nxt[p++] = c2 | b;
+                    }
+                    running += total;
+                }
+                wave_lds_sync();
+                uint32_t *tmp = cur;
+                cur = nxt;
+                nxt = tmp;
+                lo = base;
+                cnt = running;
+                ++d;
+            }
+            // the last internal level: each node's cells into the ring
+            const uint32_t leaf0 = bases ? bases[tl.base_off + uint32_t(last - int(tl.level))]
+                                         : wave_child_offset(t, last, lo);
+            const uint64_t *__restrict__ wd = t.words[last];
+            const int sh = int(gr.win_log2);
+            const uint32_t qrow = uint32_t(compact_even(qc >> 1)) << sh, qcol = uint32_t(compact_even(qc)) << sh;
+            uint32_t running = 0;
+            for (uint32_t s0 = 0; s0 < cnt; s0 += 64) {
+                const uint32_t i = s0 + lane;
+                const bool valid = i < cnt;
+                const uint32_t sg = nib(wd, uint64_t(lo) + (valid ? i : s0)) & (valid ? 15u : 0u);
+                const uint32_t rel = valid ? cur[i] : 0u;
+                uint32_t total;
+                const uint32_t ex = wave_scan(__popc(sg), total);
+                const uint32_t off = leaf0 + running + ex;
+                const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
+                const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
+                ring_cells<SR, DIR, Off>(qrow + compact_even(uint64_t(rel) >> 1) * 4u,
+                                         qcol + compact_even(rel) * 4u,
+                                         node_cells(sg | ((off & 7u) << 6), lo32, hi32), x, y, B, VL, w, wc,
+                                         ring_head, ring_fill);
+                running += total;
+            }
+            wave_lds_sync();
+        }
+        ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
+        close_window<SR>(w, y, n_out, B, false, 1);
+    }
+}
+
 // Whether v lies in one of the n sorted disjoint ranges r[k] = (lo << 32) | hi.
 __device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32_t n, uint32_t v) {
     uint32_t a = 0, b = n;
@@ -1031,9 +1130,18 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     const size_t wb = SR::kTreeBands ? window_bytes(m, B, &use) : 0;
     if (use) {
         // the bands' dense quadrants into their windows, then the rest
-        int e = launch(m.d_band_groups[DIR], m.d_band_sub[DIR], p.band_groups[DIR].size(), nullptr,
-                       p.band_cap, 1, wb);
-        if (e != hipSuccess) return e;
+        if (!p.band_groups[DIR].empty()) {
+            auto kb = band_kernel<SR, DIR, Off>;
+            const size_t lds = size_t(kWaves) * 2 * p.band_cap * sizeof(uint32_t) + wb;
+            int e = set_lds_limit(reinterpret_cast<const void *>(kb), lds);
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(kb, dim3(grid_for(p.band_groups[DIR].size())), dim3(kThreads), lds, st, m.dev,
+                               m.d_band_groups[DIR], m.d_band_sub[DIR], uint32_t(p.band_groups[DIR].size()),
+                               m.d_codes, m.d_bases, p.band_cap, static_cast<const T *>(x),
+                               static_cast<T *>(y), B, VL, n_out, 1);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
         return launch(nullptr, m.d_rest[DIR], p.rest_tiles[DIR].size(), m.d_skip[DIR], p.tile_nodes, 0, 0);
     }
     if (p.window_log2 < 0 && SR::kTreeBands)   // no windows planned: every tile, in block order
