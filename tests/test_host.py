@@ -276,7 +276,8 @@ def test_tree_only_plan(case, opt):
     """Tree-only products, per direction: the band groups' tiles (with their
     band window) and the rest tiles minus their skip ranges cover the last
     internal level exactly once; a band tile's outputs lie in its window and
-    its subtree holds at most min(tile_nodes, 512) nodes per level; rest
+    its subtree holds at most min(tile_nodes, 256) nodes per level and lies
+    in one window quadrant (band kernels keep quadrant-relative codes); rest
     tiles come in output-block order (2^k * window_batch * 4 the largest
     power of 2 <= 16 MB)."""
     name, r, c, nr, nc, t, o = case
@@ -303,7 +304,7 @@ def test_tree_only_plan(case, opt):
         return cr[cell_start[la]:cell_start[lb]], cc[cell_start[la]:cell_start[lb]]
     all_codes = oracle_codes(o, last)
     _, _, codes = t.plan(opts, 0)
-    cap = min(opts.tile_nodes, 512)
+    cap = min(opts.tile_nodes, 256)
     wb = max(opts.window_batch, 1)
     kb = 0
     while kb < 30 and (2 << kb) * wb * 4 <= (16 << 20):
@@ -324,6 +325,7 @@ def test_tree_only_plan(case, opt):
                 rr, ccc = cells_of(a, b)
                 out = rr if out_is_row else ccc
                 assert np.all((out >= base) & (out < base + side)), "band output outside its window"
+                assert len(np.unique(rr // side)) <= 1 and len(np.unique(ccc // side)) <= 1, "sub-tile spans quadrants"
                 covered.append((a, b))
         _, rest, skips = t.plan(opts, 3 + w)
         keys = []

@@ -76,7 +76,7 @@ struct Planner {
     std::vector<uint64_t> tile_lo2;               // first last-internal-level node per descent tile
     std::vector<Tile> *sink = nullptr;            // where range() puts tiles (p.tiles if null)
     std::vector<uint64_t> sink_weight;            // last-internal-level nodes of the sink's tiles
-    static constexpr uint64_t kGroupCap = 4096;   // last-internal-level nodes per band group
+    static constexpr uint64_t kGroupCap = 8192;   // last-internal-level nodes per band group
 
     // Descendant index on level 'to' of boundary 'i' of level d.
     uint64_t down(int d, uint64_t i, int to) const {
@@ -369,7 +369,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         xcd_order(p.cached_tiles[dir], w, groups, uint32_t(last));
     };
     const bool cache = o.cache_last_level != 0;
-    p.band_cap = std::min<uint32_t>(o.tile_nodes, 512);
+    p.band_cap = std::min<uint32_t>(o.tile_nodes, 256);   // per-wave frontiers (band kernel)
     // Tree-only products: the descent tiles in block order, minus the
     // last-internal-level ranges 'wr' (sorted) that band groups cover.
     auto rest_plain = [&](int dir, const std::vector<std::pair<uint64_t, uint64_t>> &wr) {
