@@ -352,10 +352,10 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
 // non-zeros would otherwise send several lanes of one instruction to the same
 // word (serialised, and a failed compare-and-swap each).
 template <class SR, class Off, bool kRuns>
-__device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
-                                          const typename SR::T *__restrict__ x,
-                                          typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                          const Window<typename SR::T> &w) {
+__device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
+                                           const typename SR::T *__restrict__ x,
+                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                           const Window<typename SR::T> &w) {
     using T = typename SR::T;
     constexpr uint32_t R = WaveCells<Off>::kRound;
     constexpr int kUnroll = unroll_for<Off>();
@@ -384,6 +384,20 @@ __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t hea
             else apply_cells<SR, Off, kUnroll, kRuns, false>(xv, yo, ok, y, v);
         }
     }
+}
+
+// Runs pay where a cell's row is wide: with few vectors per cell the
+// interleaved order's shared x lines matter more (B = 1 right products of
+// the R-MAT workloads: 9.1 against 7.9 ms with runs).
+constexpr uint32_t kRunsMinBatch = 8;
+
+template <class SR, class Off, bool kMayRun>
+__device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
+                                          const typename SR::T *__restrict__ x,
+                                          typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+                                          const Window<typename SR::T> &w) {
+    if (kMayRun && B >= kRunsMinBatch) pass_cells<SR, Off, kMayRun>(wc, head, count, x, y, B, VL, w);
+    else pass_cells<SR, Off, false>(wc, head, count, x, y, B, VL, w);
 }
 
 // Leaf work of one wave over a segment of up to 64 nodes of the last internal
