@@ -288,6 +288,7 @@ struct Window {
     T *win;
     uint64_t out0;
     uint32_t rows;
+    bool runs;   // right products: combine runs of one output row (ring_pass)
 };
 
 // Row and column offsets within a node's 4x4 block of cell q of the leaf for
@@ -386,17 +387,12 @@ __device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t he
     }
 }
 
-// Runs pay where a cell's row is wide: with few vectors per cell the
-// interleaved order's shared x lines matter more (B = 1 right products of
-// the R-MAT workloads: 9.1 against 7.9 ms with runs).
-constexpr uint32_t kRunsMinBatch = 8;
-
 template <class SR, class Off, bool kMayRun>
 __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
                                           const typename SR::T *__restrict__ x,
                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
                                           const Window<typename SR::T> &w) {
-    if (kMayRun && B >= kRunsMinBatch) pass_cells<SR, Off, kMayRun>(wc, head, count, x, y, B, VL, w);
+    if (kMayRun && w.runs) pass_cells<SR, Off, kMayRun>(wc, head, count, x, y, B, VL, w);
     else pass_cells<SR, Off, false>(wc, head, count, x, y, B, VL, w);
 }
 
@@ -538,8 +534,8 @@ __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t
 // the planned window size.
 template <class SR, int DIR>
 __device__ __forceinline__ Window<typename SR::T> open_window(const Tile &tl, typename SR::T *lds,
-                                                              bool use, uint32_t B) {
-    Window<typename SR::T> w{nullptr, 0, 0};
+                                                              bool use, uint32_t B, int runs) {
+    Window<typename SR::T> w{nullptr, 0, 0, runs != 0};
     if (!use || tl.win_log2 == kNoWindow) return w;
     w.win = lds;
     w.out0 = (DIR == K2_RIGHT) ? tl.win_row : tl.win_col;
@@ -669,7 +665,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     const uint64_t *__restrict__ blocks, const StrayRec *__restrict__ strays,
     const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    int use_dir, int accumulate) {
+    int use_dir, int accumulate, int runs) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
     __shared__ WaveCells<Off> s_cells[kWaves];
@@ -682,7 +678,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
     WaveCells<Off> *wc = &s_cells[wave];
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
-        const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B);
+        const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B, runs);
         const uint32_t nseg = tl.count;
         uint32_t ring_head = 0, ring_fill = 0;   // the wave's queued cells
         uint32_t k = wave;
@@ -736,7 +732,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void band_kernel(
     DevTree t, const Tile *__restrict__ groups, const Tile *__restrict__ subs, uint32_t n_groups,
     const uint64_t *__restrict__ tile_codes, const uint32_t *__restrict__ bases, uint32_t cap,
     const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-    uint64_t n_out, int use_window) {
+    uint64_t n_out, int use_window, int runs) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // kWaves frontiers of 2 cap codes, then the window
     __shared__ WaveCells<Off> s_cells[kWaves];
@@ -750,7 +746,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void band_kernel(
     const uint32_t last_dw = uint32_t((uint64_t(t.nodes[last + 1]) + 15u) / 16u * 2u - 1u);
     for (uint32_t gi = blockIdx.x; gi < n_groups; gi += gridDim.x) {
         const Tile gr = groups[gi];
-        const Window<T> w = open_window<SR, DIR>(gr, s_win, use_window, B);
+        const Window<T> w = open_window<SR, DIR>(gr, s_win, use_window, B, runs);
         const int hq = t.levels - int(gr.win_log2);   // the window quadrants' level
         uint32_t ring_head = 0, ring_fill = 0;
         for (uint32_t si = wave; si < gr.count; si += kWaves) {
@@ -847,7 +843,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     const uint64_t *__restrict__ skips, const uint64_t *__restrict__ tile_codes, uint32_t cap,
     const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases) {
+    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
     __shared__ uint32_t s_tot[kWaves];
@@ -866,7 +862,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
           gr.count = 1;
           gr.win_log2 = kNoWindow;
       }
-      const Window<T> w = EMIT ? Window<T>{nullptr, 0, 0} : open_window<SR, DIR>(gr, s_win, use_window, B);
+      const Window<T> w = EMIT ? Window<T>{nullptr, 0, 0, false} : open_window<SR, DIR>(gr, s_win, use_window, B, runs);
       for (uint32_t si = 0; si < gr.count; ++si) {
         const Tile tl = tiles[gr.first + si];
         const uint32_t nskip = skips ? tl.win_col : 0u;
@@ -1114,7 +1110,8 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
                        m.d_cached_segs[DIR], m.d_cached, m.d_strays[DIR], m.d_stray_off[DIR],
                        static_cast<const T *>(x),
-                       static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0, accumulate);
+                       static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0, accumulate,
+                       m.plan.row_runs ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1135,7 +1132,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3(grid_for(n_items)), dim3(kThreads), lds, st, m.dev, groups, tiles,
                            uint32_t(n_items), skips, m.d_codes, cap, static_cast<const T *>(x),
-                           static_cast<T *>(y), B, VL, n_out, use, emit, m.d_bases);
+                           static_cast<T *>(y), B, VL, n_out, use, emit, m.d_bases, m.plan.row_runs ? 1 : 0);
         return hipGetLastError();
     };
     const Plan &p = m.plan;
@@ -1152,7 +1149,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
             hipLaunchKernelGGL(kb, dim3(grid_for(p.band_groups[DIR].size())), dim3(kThreads), lds, st, m.dev,
                                m.d_band_groups[DIR], m.d_band_sub[DIR], uint32_t(p.band_groups[DIR].size()),
                                m.d_codes, m.d_bases, p.band_cap, static_cast<const T *>(x),
-                               static_cast<T *>(y), B, VL, n_out, 1);
+                               static_cast<T *>(y), B, VL, n_out, 1, p.row_runs ? 1 : 0);
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -117,6 +117,9 @@ struct Plan {
     uint64_t stray_nodes[2] = {0, 0};
     uint32_t n_bands[2] = {0, 0};
     bool bands_cover[2] = {false, false};
+    // Right products combine runs of one output row among neighbouring
+    // cells (the leaves show many row pairs and few column pairs).
+    bool row_runs = false;
 };
 
 k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out);

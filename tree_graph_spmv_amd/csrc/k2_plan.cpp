@@ -292,6 +292,39 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     p.codes = codes[d0];
 
     const uint64_t n2 = t.nodes[last];
+    {   // row pairs and column pairs of cells inside the leaves (2 x 2
+        // blocks): a matrix whose rows hold runs of neighbouring non-zeros
+        // (many row pairs, few column pairs) gains from combining runs of
+        // one row in right products; one whose pairs are balanced loses the
+        // x locality the interleaved order gives (measured: web-like 2^27,
+        // 10% of cells in row pairs, 0.4% in column pairs: 8.5 against 19.6
+        // ms at B = 1 with runs; R-MAT 2^22, 2.3% each: 1.08 against 0.97)
+        const std::vector<uint64_t> &lw = t.words[L - 1];
+        const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+        std::vector<uint64_t> cnt(3 * size_t(nth), 0);
+        std::vector<std::thread> pool;
+        for (unsigned k = 0; k < nth; ++k)
+            pool.emplace_back([&, k]() {
+                uint64_t cells = 0, rows = 0, cols = 0;
+                for (size_t i = lw.size() * k / nth; i < lw.size() * (k + 1) / nth; ++i) {
+                    const uint64_t w = lw[i];
+                    cells += uint64_t(__builtin_popcountll(w));
+                    rows += uint64_t(__builtin_popcountll(w & (w >> 1) & 0x5555555555555555ull));
+                    cols += uint64_t(__builtin_popcountll(w & (w >> 2) & 0x3333333333333333ull));
+                }
+                cnt[3 * k] = cells;
+                cnt[3 * k + 1] = rows;
+                cnt[3 * k + 2] = cols;
+            });
+        for (auto &th : pool) th.join();
+        uint64_t cells = 0, rows = 0, cols = 0;
+        for (unsigned k = 0; k < nth; ++k) {
+            cells += cnt[3 * k];
+            rows += cnt[3 * k + 1];
+            cols += cnt[3 * k + 2];
+        }
+        p.row_runs = 2 * rows * 50 >= cells && rows >= 4 * cols && rows > 0;
+    }
     uint64_t cc = n2 / 2048;                      // enough tiles to fill the GPU
     cc = std::max<uint64_t>(256, std::min<uint64_t>(16384, cc));
     cc = (cc + 255) & ~uint64_t(255);
