@@ -49,6 +49,16 @@ def case(request):
     return request.param, r, c, nr, nc, k2.Tree(r, c, nr, nc), oracle.OracleTree(r, c, nr, nc)
 
 
+def test_build_threads(case):
+    """The tree does not depend on how many threads build it."""
+    name, r, c, nr, nc, t, o = case
+    for th in (1, 3):
+        t1 = k2.Tree(r, c, nr, nc, n_threads=th)
+        assert t1.level_nodes() == t.level_nodes()
+        for d in range(t.levels):
+            assert np.array_equal(t1.level_words(d), t.level_words(d)), (name, th, d)
+
+
 def test_build_matches_oracle(case):
     name, r, c, nr, nc, t, o = case
     assert t.levels == o.levels and t.nnz == o.nnz
