@@ -126,8 +126,8 @@ typedef struct {
        quadrants a windowed tile, and those nodes are added to their band's
        window too (strays), instead of one y atomic per cell from separate
        sparse tiles.  k2_matrix_create groups the strays by band on the
-       device (16 bytes per stray node and direction: its block origin,
-       first leaf and signature).  0: sparse tiles.  Default 1. */
+       device (16 bytes per stray node and direction: its block origin and
+       its cells, read from its leaves once).  0: sparse tiles.  Default 1. */
     int32_t band_strays;
 } k2_plan_opts;
 

@@ -705,12 +705,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             for (uint32_t b = s0 + wave * 64u; b < s1; b += kThreads) {
                 const bool in = b + lane < s1;
                 const StrayRec r = strays[in ? b + lane : b];
-                const uint32_t s = in ? r.sig : 0u;
-                const uint32_t dw = (r.leaf >> 3) < last_dw ? (r.leaf >> 3) : last_dw;
-                const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
-                ring_cells<SR, DIR, Off>(uint32_t(r.blk >> 32), uint32_t(r.blk),
-                                         node_cells(s | ((r.leaf & 7u) << 6), lo32, hi32), x, y, B, VL, w,
-                                         wc, ring_head, ring_fill);
+                ring_cells<SR, DIR, Off>(uint32_t(r.blk >> 32), uint32_t(r.blk), in ? r.cells : 0u, x, y, B,
+                                         VL, w, wc, ring_head, ring_fill);
             }
         }
         ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
@@ -1028,8 +1024,9 @@ __global__ __launch_bounds__(kThreads) void stray_count_kernel(const Seg *__rest
     }
 }
 
-// Each stray's record at its band's cursor (advanced); its first leaf is the
-// segment's plus the fan-outs of the nodes before it.
+// Each stray's record at its band's cursor (advanced), with its cells from
+// its leaves: its first leaf is the segment's plus the fan-outs of the nodes
+// before it.
 __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, const Seg *__restrict__ segs,
                                                                  uint32_t n_segs,
                                                                  const uint64_t *__restrict__ blocks, int dir,
@@ -1038,6 +1035,8 @@ __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, cons
     const uint32_t lane = __lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t *__restrict__ sig_words = t.words[t.levels - 2];
+    const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[t.levels - 1]);
+    const uint32_t last_dw = uint32_t((uint64_t(t.nodes[t.levels - 1]) + 15u) / 16u * 2u - 1u);
     for (uint32_t k = blockIdx.x * kWaves + wave; k < n_segs; k += gridDim.x * kWaves) {
         const Seg sg = segs[k];
         const bool in = lane < sg.count;
@@ -1046,9 +1045,13 @@ __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, cons
         const uint32_t ex = wave_scan(__popc(s), total);
         if (in) {
             const uint64_t blk = blocks[sg.lo + lane];
+            const uint32_t off = sg.leaf + ex;
+            const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
+            const uint32_t cells = node_cells(s | ((off & 7u) << 6), leaf_dw[dw],
+                                              leaf_dw[dw < last_dw ? dw + 1u : last_dw]);
             const uint32_t o = dir == K2_RIGHT ? uint32_t(blk >> 32) : uint32_t(blk);
             const uint32_t pos = atomicAdd(&cursor[o >> qlog], 1u);
-            out[pos] = StrayRec{blk, sg.leaf + ex, s};
+            out[pos] = StrayRec{blk, cells, 0u};
         }
     }
 }

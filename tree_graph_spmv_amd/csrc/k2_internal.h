@@ -64,11 +64,13 @@ static_assert(sizeof(Seg) == 16, "segment layout");
 // A stray: a node of the cached level outside the dense quadrants, stored
 // again with its band's other strays so that a band tile can add its cells to
 // the band's window: the node's block origin (first row << 32 | first
-// column), the level-order index of its first leaf and its signature.
+// column) and its cells as read from its leaves when the matrix is created
+// (bit 4 b + q: cell q of the leaf for child b), so that a product reads no
+// leaf at a stray's random position.
 struct StrayRec {
     uint64_t blk;
-    uint32_t leaf;
-    uint32_t sig;
+    uint32_t cells;
+    uint32_t pad;
 };
 static_assert(sizeof(StrayRec) == 16, "stray layout");
 
