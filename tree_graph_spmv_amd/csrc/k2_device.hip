@@ -752,18 +752,33 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void band_kernel(
             // the sub-tile's quadrant: the level-hq prefix of its codes
             const uint64_t qc = tile_codes[tl.code_off] >> (2 * (d - hq));
             uint32_t *cur = front, *nxt = front + cap;
+            // the signature word of node start + lane of level dd (clamped):
+            // a level's first chunk is loaded while the level above is
+            // expanded, since its first node (the planned base) is known
+            auto first_word = [&](int dd, uint32_t start) {
+                const uint32_t last_node = t.nodes[dd] - 1u;
+                return t.words[dd][(start + lane < last_node ? start + lane : last_node) >> 4];
+            };
+            uint64_t wpre = first_word(d, lo);
             for (uint32_t i = lane; i < cnt; i += 64)
                 cur[i] = uint32_t(tile_codes[tl.code_off + i] - (qc << (2 * (d - hq))));
             wave_lds_sync();
+            // nibble of node lo + i (i = s0 + lane) from the chunk's word
+            auto sig_of = [&](const uint64_t *__restrict__ wd, uint32_t s0, bool valid) {
+                const uint32_t i = s0 + lane;
+                const uint64_t word = s0 == 0 ? wpre : wd[(lo + (valid ? i : s0)) >> 4];
+                return valid ? uint32_t(word >> (((lo + i) & 15u) * 4u)) & 15u : 0u;
+            };
             while (d < last) {
                 const uint32_t base = bases ? bases[tl.base_off + uint32_t(d - int(tl.level))]
                                             : wave_child_offset(t, d, lo);
+                const uint64_t wnext = first_word(d + 1, base);
                 const uint64_t *__restrict__ wd = t.words[d];
                 uint32_t running = 0;
                 for (uint32_t s0 = 0; s0 < cnt; s0 += 64) {
                     const uint32_t i = s0 + lane;
                     const bool valid = i < cnt;
-                    const uint32_t sg = nib(wd, uint64_t(lo) + (valid ? i : s0)) & (valid ? 15u : 0u);
+                    const uint32_t sg = sig_of(wd, s0, valid);
                     uint32_t total;
                     const uint32_t ex = wave_scan(__popc(sg), total);
                     if (sg) {
@@ -781,6 +796,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void band_kernel(
                 nxt = tmp;
                 lo = base;
                 cnt = running;
+                wpre = wnext;
                 ++d;
             }
             // the last internal level: each node's cells into the ring
@@ -793,7 +809,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void band_kernel(
             for (uint32_t s0 = 0; s0 < cnt; s0 += 64) {
                 const uint32_t i = s0 + lane;
                 const bool valid = i < cnt;
-                const uint32_t sg = nib(wd, uint64_t(lo) + (valid ? i : s0)) & (valid ? 15u : 0u);
+                const uint32_t sg = sig_of(wd, s0, valid);
                 const uint32_t rel = valid ? cur[i] : 0u;
                 uint32_t total;
                 const uint32_t ex = wave_scan(__popc(sg), total);
