@@ -264,8 +264,10 @@ def test_scan_offsets(case):
         opts = k2.plan_defaults(tile_nodes=tile_nodes, offsets="scan")
         top, tiles, codes = t.plan(opts, 0)
         bases = t.plan_offsets(opts)
-        total = 0
-        lists = [tiles] + [t.plan(opts, w)[1] for w in (7, 8)]   # descent tiles, band tiles
+        used = np.zeros(bases.size, bool)
+        # descent tiles, rest tiles of both directions (copies of one cut,
+        # sharing its offsets), band tiles
+        lists = [tiles] + [t.plan(opts, w)[1] for w in (3, 4, 7, 8)]
         for lst in lists:
             for tl in lst:
                 level, first, at = int(tl[2]), int(tl[0]), int(tl[7])
@@ -273,8 +275,8 @@ def test_scan_offsets(case):
                 for d in range(level, L - 1):
                     node = int(offs[d][node]) if node < nodes[d] else nodes[d + 1]
                     assert int(bases[at + d - level]) == node, (name, d)
-                total += L - 1 - level
-        assert total == bases.size
+                used[at:at + L - 1 - level] = True
+        assert used.sum() <= bases.size
         dir_opts = k2.plan_defaults(tile_nodes=tile_nodes, offsets="directory")
         assert np.array_equal(t.plan(dir_opts, 0)[1][:, :7], tiles[:, :7])
         assert np.all(t.plan(dir_opts, 0)[1][:, 7] == 0)
@@ -342,6 +344,8 @@ def test_tree_only_plan(case, opt):
         for tl in rest:
             first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
             a, b = down(level, first), down(level, first + count)
+            assert b - a <= cap, "a rest tile holds at most min(tile_nodes, 256) nodes per level"
+            assert np.array_equal(codes[int(tl[3]):int(tl[3]) + count], all_codes[level][first:first + count])
             code = int(codes[int(tl[3])])
             coord = 0
             for k in range(level):

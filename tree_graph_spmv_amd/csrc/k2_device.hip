@@ -840,6 +840,107 @@ __device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32
     return a < n && uint32_t(r[a] >> 32) <= v;
 }
 
+// Tree-only rest tiles (Sec. 3.4 tiles outside the band groups, in
+// output-block order): each wave takes tiles w, w + 4, ... of the list and
+// descends each on its own as band_kernel does, with frontiers of at most
+// 'cap' absolute Morton codes per level in the wave's LDS, skipping the
+// last-internal-level ranges listed for the tile (skips + win_row, win_col
+// of them; their fan-outs still count towards the leaf offsets).  Outputs go
+// straight to y (no window), so no workgroup barrier at all.
+template <class SR, int DIR, class Off>
+__global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
+    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ skips,
+    const uint64_t *__restrict__ tile_codes, const uint32_t *__restrict__ bases, uint32_t cap,
+    const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
+    int runs) {
+    using T = typename SR::T;
+    extern __shared__ uint64_t s_dyn[];   // kWaves frontiers of 2 cap codes
+    __shared__ WaveCells<Off> s_cells[kWaves];
+    const int last = t.levels - 2;
+    const uint32_t lane = __lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint64_t *front = s_dyn + size_t(wave) * 2u * cap;
+    WaveCells<Off> *wc = &s_cells[wave];
+    const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[last + 1]);
+    const uint32_t last_dw = uint32_t((uint64_t(t.nodes[last + 1]) + 15u) / 16u * 2u - 1u);
+    const Window<T> w{nullptr, 0, 0, runs != 0};
+    uint32_t ring_head = 0, ring_fill = 0;
+    for (uint32_t ti = blockIdx.x * kWaves + wave; ti < n_tiles; ti += gridDim.x * kWaves) {
+        const Tile tl = tiles[ti];
+        const uint32_t nskip = skips ? tl.win_col : 0u;
+        int d = int(tl.level);
+        uint32_t lo = tl.first, cnt = tl.count;
+        uint64_t *cur = front, *nxt = front + cap;
+        // the signature word of node start + lane of level dd (clamped): a
+        // level's first chunk is loaded while the level above is expanded
+        auto first_word = [&](int dd, uint32_t start) {
+            const uint32_t last_node = t.nodes[dd] - 1u;
+            return t.words[dd][(start + lane < last_node ? start + lane : last_node) >> 4];
+        };
+        uint64_t wpre = first_word(d, lo);
+        for (uint32_t i = lane; i < cnt; i += 64) cur[i] = tile_codes[tl.code_off + i];
+        wave_lds_sync();
+        auto sig_of = [&](const uint64_t *__restrict__ wd, uint32_t s0, bool valid) {
+            const uint32_t i = s0 + lane;
+            const uint64_t word = s0 == 0 ? wpre : wd[(lo + (valid ? i : s0)) >> 4];
+            return valid ? uint32_t(word >> (((lo + i) & 15u) * 4u)) & 15u : 0u;
+        };
+        while (d < last) {
+            const uint32_t base = bases ? bases[tl.base_off + uint32_t(d - int(tl.level))]
+                                        : wave_child_offset(t, d, lo);
+            const uint64_t wnext = first_word(d + 1, base);
+            const uint64_t *__restrict__ wd = t.words[d];
+            uint32_t running = 0;
+            for (uint32_t s0 = 0; s0 < cnt; s0 += 64) {
+                const uint32_t i = s0 + lane;
+                const bool valid = i < cnt;
+                const uint32_t sg = sig_of(wd, s0, valid);
+                uint32_t total;
+                const uint32_t ex = wave_scan(__popc(sg), total);
+                if (sg) {
+                    const uint64_t c2 = cur[i] << 2;
+                    uint32_t p = running + ex;
+#pragma unroll
+                    for (uint32_t b = 0; b < 4; ++b)
+                        if (sg & (1u << b)) nxt[p++] = c2 | b;
+                }
+                running += total;
+            }
+            wave_lds_sync();
+            uint64_t *tmp = cur;
+            cur = nxt;
+            nxt = tmp;
+            lo = base;
+            cnt = running;
+            wpre = wnext;
+            ++d;
+        }
+        // the last internal level: each node's cells into the ring
+        const uint32_t leaf0 = bases ? bases[tl.base_off + uint32_t(last - int(tl.level))]
+                                     : wave_child_offset(t, last, lo);
+        const uint64_t *__restrict__ wd = t.words[last];
+        uint32_t running = 0;
+        for (uint32_t s0 = 0; s0 < cnt; s0 += 64) {
+            const uint32_t i = s0 + lane;
+            const bool valid = i < cnt;
+            const uint32_t sg = sig_of(wd, s0, valid);
+            const uint64_t code = valid ? cur[i] : 0ull;
+            uint32_t total;
+            const uint32_t ex = wave_scan(__popc(sg), total);
+            const bool skip = valid && nskip && in_ranges(skips + tl.win_row, nskip, lo + i);
+            const uint32_t off = leaf0 + running + ex;
+            const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
+            const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
+            ring_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u,
+                                     skip ? 0u : node_cells(sg | ((off & 7u) << 6), lo32, hi32), x, y, B,
+                                     VL, w, wc, ring_head, ring_fill);
+            running += total;
+        }
+        wave_lds_sync();
+    }
+    ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
+}
+
 // One product by tiled descent (Algorithm 1 with the tiles of Sec. 3.4): each
 // workgroup takes an item and, for each of its tiles, expands the tile level
 // by level inside LDS, then visits the leaves of its last-internal-level nodes
@@ -1156,6 +1257,19 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     };
     const Plan &p = m.plan;
     if (EMIT) return launch(nullptr, m.d_tiles, p.tiles.size(), nullptr, p.tile_nodes, 0, 0);
+    // the rest tiles, a wave each
+    auto rest = [&](const uint64_t *skips) -> int {
+        const size_t n = p.rest_tiles[DIR].size();
+        if (n == 0) return hipSuccess;
+        auto kr = rest_kernel<SR, DIR, Off>;
+        const size_t lds = size_t(kWaves) * 2 * p.rest_cap * sizeof(uint64_t);
+        int e = set_lds_limit(reinterpret_cast<const void *>(kr), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kr, dim3(grid_for((n + kWaves - 1) / kWaves)), dim3(kThreads), lds, st, m.dev,
+                           m.d_rest[DIR], uint32_t(n), skips, m.d_codes, m.d_bases, p.rest_cap,
+                           static_cast<const T *>(x), static_cast<T *>(y), B, VL, p.row_runs ? 1 : 0);
+        return hipGetLastError();
+    };
     int use = 0;
     const size_t wb = SR::kTreeBands ? window_bytes(m, B, &use) : 0;
     if (use) {
@@ -1172,10 +1286,10 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
-        return launch(nullptr, m.d_rest[DIR], p.rest_tiles[DIR].size(), m.d_skip[DIR], p.tile_nodes, 0, 0);
+        return rest(m.d_skip[DIR]);
     }
-    if (p.window_log2 < 0 && SR::kTreeBands)   // no windows planned: every tile, in block order
-        return launch(nullptr, m.d_rest[DIR], p.rest_tiles[DIR].size(), nullptr, p.tile_nodes, 0, 0);
+    if (p.window_log2 < 0 && SR::kTreeBands)   // no windows planned: every rest tile, in block order
+        return rest(nullptr);
     // every tile, depth first
     return launch(nullptr, m.d_tiles, p.tiles.size(), nullptr, p.tile_nodes, 0, 0);
 }

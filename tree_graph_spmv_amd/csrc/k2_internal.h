@@ -105,6 +105,8 @@ struct Plan {
     // skip[dir] (ranges (lo << 32) | hi, sorted): rest_tiles[dir] holds them
     // as tiles with win_row = first skip range, win_col = skip count.
     uint32_t band_cap = 0;
+    // rest tiles hold at most rest_cap nodes per level (a wave's frontier)
+    uint32_t rest_cap = 0;
     std::vector<Tile> band_groups[2], band_sub[2], rest_tiles[2];
     std::vector<uint64_t> skip[2];
     // Strays (cached level, band_strays): per direction the segments of the

@@ -76,6 +76,7 @@ struct Planner {
     std::vector<uint64_t> tile_lo2;               // first last-internal-level node per descent tile
     std::vector<Tile> *sink = nullptr;            // where range() puts tiles (p.tiles if null)
     std::vector<uint64_t> sink_weight;            // last-internal-level nodes of the sink's tiles
+    std::vector<uint64_t> sink_lo2;               // first last-internal-level node of the sink's tiles
     static constexpr uint64_t kGroupCap = 8192;   // last-internal-level nodes per band group
 
     // Descendant index on level 'to' of boundary 'i' of level d.
@@ -123,6 +124,7 @@ struct Planner {
             if (sink) {
                 sink->push_back(tl);
                 sink_weight.push_back(bound[j - a] - bound[i - a]);
+                sink_lo2.push_back(bound[i - a]);
             } else {
                 p.tiles.push_back(tl);
                 tile_weight.push_back(bound[j - a] - bound[i - a]);
@@ -342,42 +344,43 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles: the plain depth-first cut (windowed descent tiles, one
     // per dense quadrant, measured slower: many small tiles)
     pl.range(d0, 0, t.nodes[d0], 0, no_window());
-    {   // descent order per direction: by output block of the tile's first
-        // node, then depth first, so the tiles in flight update one slice of
-        // y (its lines stay in the last-level cache while the atomics land)
+    // descent order per direction: by output block of the tile's first node,
+    // then depth first, so the tiles in flight update one slice of y (its
+    // lines stay in the last-level cache while the atomics land)
+    auto block_order = [&](const std::vector<Tile> &tiles, int dir, std::vector<uint32_t> &order) {
         const int kb = block_log2(o, 0);
-        for (int dir = 0; dir < 2; ++dir) {
-            std::vector<std::pair<uint64_t, uint32_t>> key(p.tiles.size());
-            for (size_t i = 0; i < p.tiles.size(); ++i) {
-                const Tile &tl = p.tiles[i];
-                const uint64_t code = p.codes[tl.code_off];
-                const uint64_t c = dir == K2_RIGHT ? even_bits(code >> 1) : even_bits(code);
-                key[i] = {(c << (L - int(tl.level))) >> kb, uint32_t(i)};
-            }
-            std::stable_sort(key.begin(), key.end(),
-                             [](const auto &x, const auto &y) { return x.first < y.first; });
-            p.tile_order[dir].resize(key.size());
-            for (size_t i = 0; i < key.size(); ++i) p.tile_order[dir][i] = key[i].second;
+        std::vector<std::pair<uint64_t, uint32_t>> key(tiles.size());
+        for (size_t i = 0; i < tiles.size(); ++i) {
+            const Tile &tl = tiles[i];
+            const uint64_t code = p.codes[tl.code_off];
+            const uint64_t c = dir == K2_RIGHT ? even_bits(code >> 1) : even_bits(code);
+            key[i] = {(c << (L - int(tl.level))) >> kb, uint32_t(i)};
         }
-    }
+        std::stable_sort(key.begin(), key.end(), [](const auto &x, const auto &y) { return x.first < y.first; });
+        order.resize(key.size());
+        for (size_t i = 0; i < key.size(); ++i) order[i] = key[i].second;
+    };
+    for (int dir = 0; dir < 2; ++dir) block_order(p.tiles, dir, p.tile_order[dir]);
     p.use_directory = o.offsets == K2_OFFSETS_DIRECTORY;
-    if (!p.use_directory) {
-        // scan offsets: each descent tile's first child on every level it
-        // spans, by following its first node down (the host's rank query)
-        uint64_t total = 0;
-        for (Tile &tl : p.tiles) {
+    // scan offsets of a tile list: each tile's first child on every level it
+    // spans, by following its first node down (the host's rank query),
+    // appended to tile_bases
+    auto plan_bases = [&](std::vector<Tile> &tiles) -> k2_status {
+        if (p.use_directory) return K2_OK;
+        uint64_t total = p.tile_bases.size();
+        for (Tile &tl : tiles) {
             tl.base_off = uint32_t(total);
             total += uint64_t(last - int(tl.level) + 1);
         }
         if (total >= (1ull << 32)) return K2_E_UNSUPPORTED;
         p.tile_bases.resize(total);
-        const size_t nt = p.tiles.size();
+        const size_t nt = tiles.size();
         const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
         std::vector<std::thread> pool;
         for (unsigned k = 0; k < nth; ++k)
             pool.emplace_back([&, k]() {
                 for (size_t i = nt * k / nth; i < nt * (k + 1) / nth; ++i) {
-                    const Tile &tl = p.tiles[i];
+                    const Tile &tl = tiles[i];
                     uint64_t node = tl.first;
                     for (int d = int(tl.level); d <= last; ++d) {
                         node = child_offset(t, d, node);
@@ -386,6 +389,28 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                 }
             });
         for (auto &th : pool) th.join();
+        return K2_OK;
+    };
+    if (plan_bases(p.tiles) != K2_OK) return K2_E_UNSUPPORTED;
+    // rest tiles of tree-only plus-times products (a wave's job): the same
+    // depth-first cut with at most rest_cap nodes per level, in block order
+    p.rest_cap = std::min<uint32_t>(o.tile_nodes, 256);
+    std::vector<Tile> rest_cut;
+    std::vector<uint64_t> rest_w, rest_lo2;
+    std::vector<uint32_t> rest_order[2];
+    {
+        const uint64_t C0 = pl.C;
+        pl.C = p.rest_cap;
+        pl.sink = &rest_cut;
+        pl.sink_weight.clear();
+        pl.sink_lo2.clear();
+        pl.range(d0, 0, t.nodes[d0], 0, no_window());
+        pl.sink = nullptr;
+        pl.C = C0;
+        rest_w.swap(pl.sink_weight);
+        rest_lo2.swap(pl.sink_lo2);
+        for (int dir = 0; dir < 2; ++dir) block_order(rest_cut, dir, rest_order[dir]);
+        if (plan_bases(rest_cut) != K2_OK) return K2_E_UNSUPPORTED;
     }
     // group boundaries: tile indexes where a new group starts (and the end)
     auto order_cached = [&](int dir, std::vector<size_t> groups) {
@@ -403,14 +428,14 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     };
     const bool cache = o.cache_last_level != 0;
     p.band_cap = std::min<uint32_t>(o.tile_nodes, 256);   // per-wave frontiers (band kernel)
-    // Tree-only products: the descent tiles in block order, minus the
+    // Tree-only plus-times products: the rest tiles in block order, minus the
     // last-internal-level ranges 'wr' (sorted) that band groups cover.
     auto rest_plain = [&](int dir, const std::vector<std::pair<uint64_t, uint64_t>> &wr) {
-        for (uint32_t idx : p.tile_order[dir]) {
-            const uint64_t a = pl.tile_lo2[idx], b = a + pl.tile_weight[idx];
+        for (uint32_t idx : rest_order[dir]) {
+            const uint64_t a = rest_lo2[idx], b = a + rest_w[idx];
             auto it = std::lower_bound(wr.begin(), wr.end(), a,
                                        [](const std::pair<uint64_t, uint64_t> &r, uint64_t v) { return r.second <= v; });
-            Tile r = p.tiles[idx];
+            Tile r = rest_cut[idx];
             r.win_row = uint32_t(p.skip[dir].size());
             r.win_col = 0;
             uint64_t covered = 0;
@@ -428,35 +453,10 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         }
     };
     // Scan offsets of the band groups' sub-tiles (the rest tiles are copies of
-    // descent tiles and share their offsets).
+    // the rest cut and share its offsets).
     auto finish = [&]() -> k2_status {
-        if (!p.use_directory) {
-            uint64_t total = p.tile_bases.size();
-            for (int dir = 0; dir < 2; ++dir)
-                for (Tile &tl : p.band_sub[dir]) {
-                    tl.base_off = uint32_t(total);
-                    total += uint64_t(last - int(tl.level) + 1);
-                }
-            if (total >= (1ull << 32)) return K2_E_UNSUPPORTED;
-            p.tile_bases.resize(total);
-            const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-            for (int dir = 0; dir < 2; ++dir) {
-                const std::vector<Tile> &bs = p.band_sub[dir];
-                const size_t nt = bs.size();
-                std::vector<std::thread> pool;
-                for (unsigned k = 0; k < nth; ++k)
-                    pool.emplace_back([&, k]() {
-                        for (size_t i = nt * k / nth; i < nt * (k + 1) / nth; ++i) {
-                            uint64_t node = bs[i].first;
-                            for (int d = int(bs[i].level); d <= last; ++d) {
-                                node = child_offset(t, d, node);
-                                p.tile_bases[bs[i].base_off + uint32_t(d - int(bs[i].level))] = uint32_t(node);
-                            }
-                        }
-                    });
-                for (auto &th : pool) th.join();
-            }
-        }
+        for (int dir = 0; dir < 2; ++dir)
+            if (plan_bases(p.band_sub[dir]) != K2_OK) return K2_E_UNSUPPORTED;
         if (p.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
         return K2_OK;
     };
@@ -622,6 +622,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
                 pl.C = p.band_cap;
                 pl.sink = &p.band_sub[dir];
                 pl.sink_weight.clear();
+                pl.sink_lo2.clear();
                 for (size_t k = i; k < j; ++k) {
                     const Unit &u = units[dense_units[k].second];
                     const uint64_t cb = p.codes.size();
