@@ -211,8 +211,9 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
    right / left products and their segments (empty unless
    opts->cache_last_level); for tree-only right / left products, 3 / 4: the
    rest tiles and their skip ranges, 5 / 6: the band groups, 7 / 8: the
-   band groups' tiles, 9 / 10: the stray segments of right / left products.  Reports the host-top level d0, the number of tiles
-   and of aux entries (see k2_plan_tiles).  Errors: K2_E_INVALID_ARG. */
+   band groups' tiles, 9 / 10: the stray segments of right / left products.
+   Reports the host-top level d0, the number of tiles and of aux entries
+   (see k2_plan_tiles).  Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux);
 
@@ -228,20 +229,24 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
    batch fits them, first the band groups (which = 5 / 6), each a workgroup's
    job: 'count' tiles from tile 'first' of list 7 / 8 (descent tiles as for
    0, over the dense quadrants of one row / column band), sharing the
-   group's window (fields 4-6); then the rest tiles (which = 3 / 4): descent
-   tiles as for 0, in order of output block (2^k rows / columns, 2^k *
+   group's window (fields 4-6); then the rest tiles (which = 3 / 4): a
+   second depth-first cut like 0 with at most min(tile_nodes, 256) nodes per
+   level (each a wave's job), in order of output block (2^k rows / columns, 2^k *
    window_batch * 4 the largest power of 2 <= 16 MB; a tile's block is its
    first node's), that skip the last-internal-level nodes band groups cover:
    'window column' ranges from aux index 'window row', each aux[r] = (first
-   node << 32) | end node.  Without planned windows the rest tiles are every
-   descent tile, skipping nothing.
+   node << 32) | end node; a tile the groups cover whole is left out.
+   Without planned windows the rest tiles are the whole second cut,
+   skipping nothing.
    which = 1 / 2: 'count' segments of the last internal level from segment
    'first'; segment r is aux[2r] = (first node << 32) | node count (1..64)
    and aux[2r + 1] = the leaf-level index of its first node's first child.
-   With band_strays, a tile of 1 / 2 with code index 1 owns its band (row
-   band for 1, column band for 2, from the window fields) and also adds the
-   band's strays: the nodes of the segments of which = 9 / 10 (no tiles; aux
-   as for 1 / 2) whose block's first row (9) or column (10) lies in it.
+   With band_strays, a tile of 1 / 2 whose code index has bit 0 set owns its
+   band (row band for 1, column band for 2, from the window fields) and also
+   adds the band's strays: the nodes of the segments of which = 9 / 10 (no
+   tiles; aux as for 1 / 2) whose block's first row (9) or column (10) lies
+   in it.  Bit 1 of the code index marks the band's only tile, which stores
+   its window to y instead of adding it.
    Host arrays of 8*n_tiles and n_aux entries (sizes from k2_plan_info).
    Errors: K2_E_INVALID_ARG. */
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
