@@ -393,22 +393,52 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     };
     if (plan_bases(p.tiles) != K2_OK) return K2_E_UNSUPPORTED;
     // rest tiles of tree-only plus-times products (a wave's job): the same
-    // depth-first cut with at most rest_cap nodes per level, in block order
+    // depth-first cut with at most rest_cap nodes per level, in block order.
+    // Threads cut chunks of the top level (a tile never spans two chunks);
+    // the chunks' split codes are appended to the plan's codes in order.
     p.rest_cap = std::min<uint32_t>(o.tile_nodes, 256);
     std::vector<Tile> rest_cut;
     std::vector<uint64_t> rest_w, rest_lo2;
     std::vector<uint32_t> rest_order[2];
     {
-        const uint64_t C0 = pl.C;
-        pl.C = p.rest_cap;
-        pl.sink = &rest_cut;
-        pl.sink_weight.clear();
-        pl.sink_lo2.clear();
-        pl.range(d0, 0, t.nodes[d0], 0, no_window());
-        pl.sink = nullptr;
-        pl.C = C0;
-        rest_w.swap(pl.sink_weight);
-        rest_lo2.swap(pl.sink_lo2);
+        struct Part {
+            Plan plan;   // only its codes: the chunk's top codes, then its splits
+            std::vector<Tile> tiles;
+            std::vector<uint64_t> w, lo2;
+        };
+        const uint64_t ntop = t.nodes[d0];
+        const unsigned nth = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+        const uint64_t nparts = std::min<uint64_t>(ntop, uint64_t(nth) * 16);
+        std::vector<Part> parts(nparts);
+        std::atomic<uint64_t> next{0};
+        auto worker = [&]() {
+            for (;;) {
+                const uint64_t c = next.fetch_add(1);
+                if (c >= nparts) return;
+                const uint64_t a = ntop * c / nparts, b = ntop * (c + 1) / nparts;
+                Part &pt = parts[c];
+                pt.plan.codes.assign(codes[d0].begin() + int64_t(a), codes[d0].begin() + int64_t(b));
+                Planner q{t, p.rest_cap, pt.plan, last, cc};
+                q.sink = &pt.tiles;
+                q.range(d0, a, b, 0, no_window());
+                pt.w.swap(q.sink_weight);
+                pt.lo2.swap(q.sink_lo2);
+            }
+        };
+        std::vector<std::thread> pool;
+        for (unsigned k = 0; k < nth; ++k) pool.emplace_back(worker);
+        for (auto &th : pool) th.join();
+        for (Part &pt : parts) {
+            const uint64_t off = p.codes.size();
+            if (off + pt.plan.codes.size() >= (1ull << 32)) return K2_E_UNSUPPORTED;
+            p.codes.insert(p.codes.end(), pt.plan.codes.begin(), pt.plan.codes.end());
+            for (Tile tl : pt.tiles) {
+                tl.code_off = uint32_t(tl.code_off + off);
+                rest_cut.push_back(tl);
+            }
+            rest_w.insert(rest_w.end(), pt.w.begin(), pt.w.end());
+            rest_lo2.insert(rest_lo2.end(), pt.lo2.begin(), pt.lo2.end());
+        }
         for (int dir = 0; dir < 2; ++dir) block_order(rest_cut, dir, rest_order[dir]);
         if (plan_bases(rest_cut) != K2_OK) return K2_E_UNSUPPORTED;
     }
