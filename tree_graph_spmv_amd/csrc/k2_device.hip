@@ -942,43 +942,26 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
 }
 
 // One product by tiled descent (Algorithm 1 with the tiles of Sec. 3.4): each
-// workgroup takes an item and, for each of its tiles, expands the tile level
-// by level inside LDS, then visits the leaves of its last-internal-level nodes
-// in place.  An item is a group (groups non-null: 'count' tiles from tiles +
-// 'first', sharing the group's LDS window) or a single tile.  A tile with
-// skips (win_col ranges from skips + win_row) leaves the listed
-// last-internal-level nodes to other items.  With 'emit' set the kernel
-// writes the last level's block origins instead (building the cached level,
-// Sec. 3.5).
+// workgroup takes a tile, expands it level by level inside LDS, then visits
+// the leaves of its last-internal-level nodes in place, with the semiring's
+// atomics straight to y.  With 'emit' set the kernel writes the last level's
+// block origins instead (building the cached level, Sec. 3.5).
 template <class SR, int DIR, bool EMIT, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
-    DevTree t, const Tile *__restrict__ groups, const Tile *__restrict__ tiles, uint32_t n_items,
-    const uint64_t *__restrict__ skips, const uint64_t *__restrict__ tile_codes, uint32_t cap,
-    const typename SR::T *__restrict__ x,
-    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs) {
+    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ tile_codes,
+    uint32_t cap, const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B,
+    uint32_t VL, uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs) {
     using T = typename SR::T;
-    extern __shared__ uint64_t s_front[];   // 2 * cap codes, then the window
+    extern __shared__ uint64_t s_front[];   // 2 * cap codes
     __shared__ uint32_t s_tot[kWaves];
     __shared__ uint32_t s_segtot[4096 / 64];   // scan offsets: fan-out per leaf segment
     __shared__ uint32_t s_val;
     __shared__ WaveCells<Off> s_cells[kWaves];
     const int last = t.levels - 2;
     const uint32_t lane = __lane_id(), wave = threadIdx.x >> 6;
-    T *s_win = reinterpret_cast<T *>(s_front + 2 * size_t(cap));
-    for (uint32_t gi = blockIdx.x; gi < n_items; gi += gridDim.x) {
-      Tile gr;
-      if (groups) {
-          gr = groups[gi];
-      } else {
-          gr.first = gi;
-          gr.count = 1;
-          gr.win_log2 = kNoWindow;
-      }
-      const Window<T> w = EMIT ? Window<T>{nullptr, 0, 0, false} : open_window<SR, DIR>(gr, s_win, use_window, B, runs);
-      for (uint32_t si = 0; si < gr.count; ++si) {
-        const Tile tl = tiles[gr.first + si];
-        const uint32_t nskip = skips ? tl.win_col : 0u;
+    const Window<T> w{nullptr, 0, 0, !EMIT && runs != 0};
+    for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
+        const Tile tl = tiles[ti];
         int d = int(tl.level);
         uint32_t lo = tl.first, cnt = tl.count;
         uint64_t *cur = s_front, *nxt = s_front + cap;
@@ -1046,15 +1029,11 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                     base = wave_child_offset(t, last, lo + seg);
                 }
                 uint32_t total;
-                const uint32_t ex = wave_scan(__popc(s), total);   // the true fan-outs give the offsets
-                const bool skip = valid && nskip && in_ranges(skips + tl.win_row, nskip, lo + i);
-                leaf_segment<SR, DIR, Off>(code, skip ? 0u : s, base + ex, leaf_dw, last_dw, x, y, B, VL, w,
-                                           &s_cells[wave]);
+                const uint32_t ex = wave_scan(__popc(s), total);
+                leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_dw, last_dw, x, y, B, VL, w, &s_cells[wave]);
             }
         }
         __syncthreads();
-      }
-      if (!EMIT) close_window<SR>(w, y, n_out, B, false, 1);
     }
 }
 
@@ -1241,22 +1220,22 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     using T = typename SR::T;
     const uint32_t VL = lanes_per_node(B, DIR);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
-    auto k = descent_kernel<SR, DIR, EMIT, Off>;
-    // one launch over items (groups of tiles, or tiles); LDS: the frontier's
-    // two levels of 'cap' codes, then the window
-    auto launch = [&](const Tile *groups, const Tile *tiles, size_t n_items, const uint64_t *skips,
-                      uint32_t cap, int use, size_t win_bytes) -> int {
-        if (n_items == 0) return hipSuccess;
-        const size_t lds = size_t(2) * cap * sizeof(uint64_t) + win_bytes;
+    // every descent tile, depth first, a workgroup each; LDS: the frontier's
+    // two levels of tile_nodes codes
+    const Plan &p = m.plan;
+    auto descent = [&]() -> int {
+        const size_t n = p.tiles.size();
+        if (n == 0) return hipSuccess;
+        auto k = descent_kernel<SR, DIR, EMIT, Off>;
+        const size_t lds = size_t(2) * p.tile_nodes * sizeof(uint64_t);
         int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3(grid_for(n_items)), dim3(kThreads), lds, st, m.dev, groups, tiles,
-                           uint32_t(n_items), skips, m.d_codes, cap, static_cast<const T *>(x),
-                           static_cast<T *>(y), B, VL, n_out, use, emit, m.d_bases, m.plan.row_runs ? 1 : 0);
+        hipLaunchKernelGGL(k, dim3(grid_for(n)), dim3(kThreads), lds, st, m.dev, m.d_tiles, uint32_t(n), m.d_codes,
+                           p.tile_nodes, static_cast<const T *>(x), static_cast<T *>(y), B, VL, emit, m.d_bases,
+                           p.row_runs ? 1 : 0);
         return hipGetLastError();
     };
-    const Plan &p = m.plan;
-    if (EMIT) return launch(nullptr, m.d_tiles, p.tiles.size(), nullptr, p.tile_nodes, 0, 0);
+    if (EMIT) return descent();
     // the rest tiles, a wave each
     auto rest = [&](const uint64_t *skips) -> int {
         const size_t n = p.rest_tiles[DIR].size();
@@ -1290,8 +1269,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
     }
     if (p.window_log2 < 0 && SR::kTreeBands)   // no windows planned: every rest tile, in block order
         return rest(nullptr);
-    // every tile, depth first
-    return launch(nullptr, m.d_tiles, p.tiles.size(), nullptr, p.tile_nodes, 0, 0);
+    return descent();
 }
 
 template <int DIR>
