@@ -93,17 +93,15 @@ struct Plan {
     // spans, tile_bases[tiles[k].base_off + (d - tiles[k].level)] for d = level ..
     // last internal level (the last entry is its first leaf)
     std::vector<uint32_t> tile_bases;
-    // per direction, the order the descent tiles are taken in for products
-    // (by output block, then depth first)
-    std::vector<uint32_t> tile_order[2];
     // Tree-only products, per direction.  Band groups (when windows are
     // planned): a group (first, count = its sub-tiles in band_sub[dir], window
     // fields) descends the dense quadrants of one row / column band into one
-    // LDS window, with frontiers of at most band_cap nodes.  The rest: the
-    // descent tiles in tile_order[dir] that are not wholly inside windowed
-    // quadrants, each skipping the last-internal-level nodes listed for it in
-    // skip[dir] (ranges (lo << 32) | hi, sorted): rest_tiles[dir] holds them
-    // as tiles with win_row = first skip range, win_col = skip count.
+    // LDS window, with frontiers of at most band_cap nodes.  The rest: a
+    // second depth-first cut with at most rest_cap nodes per level, in
+    // output-block order, without the tiles wholly inside windowed quadrants,
+    // each skipping the last-internal-level nodes listed for it in skip[dir]
+    // (ranges (lo << 32) | hi, sorted): rest_tiles[dir] holds them as tiles
+    // with win_row = first skip range, win_col = skip count.
     uint32_t band_cap = 0;
     // rest tiles hold at most rest_cap nodes per level (a wave's frontier)
     uint32_t rest_cap = 0;

@@ -72,8 +72,6 @@ struct Planner {
     uint64_t cached_C;  // nodes per cached tile without a window
     static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
     static constexpr uint64_t kSparseTile = 8192; // nodes per sparse cached tile beside bands
-    std::vector<uint64_t> tile_weight;            // last-internal-level nodes per descent tile
-    std::vector<uint64_t> tile_lo2;               // first last-internal-level node per descent tile
     std::vector<Tile> *sink = nullptr;            // where range() puts tiles (p.tiles if null)
     std::vector<uint64_t> sink_weight;            // last-internal-level nodes of the sink's tiles
     std::vector<uint64_t> sink_lo2;               // first last-internal-level node of the sink's tiles
@@ -127,8 +125,6 @@ struct Planner {
                 sink_lo2.push_back(bound[i - a]);
             } else {
                 p.tiles.push_back(tl);
-                tile_weight.push_back(bound[j - a] - bound[i - a]);
-                tile_lo2.push_back(bound[i - a]);
             }
             i = j;
         }
@@ -344,9 +340,9 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     // descent tiles: the plain depth-first cut (windowed descent tiles, one
     // per dense quadrant, measured slower: many small tiles)
     pl.range(d0, 0, t.nodes[d0], 0, no_window());
-    // descent order per direction: by output block of the tile's first node,
-    // then depth first, so the tiles in flight update one slice of y (its
-    // lines stay in the last-level cache while the atomics land)
+    // order of a tile list per direction: by output block of the tile's first
+    // node, then depth first, so the tiles in flight update one slice of y
+    // (its lines stay in the last-level cache while the atomics land)
     auto block_order = [&](const std::vector<Tile> &tiles, int dir, std::vector<uint32_t> &order) {
         const int kb = block_log2(o, 0);
         std::vector<std::pair<uint64_t, uint32_t>> key(tiles.size());
@@ -360,7 +356,6 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         order.resize(key.size());
         for (size_t i = 0; i < key.size(); ++i) order[i] = key[i].second;
     };
-    for (int dir = 0; dir < 2; ++dir) block_order(p.tiles, dir, p.tile_order[dir]);
     p.use_directory = o.offsets == K2_OFFSETS_DIRECTORY;
     // scan offsets of a tile list: each tile's first child on every level it
     // spans, by following its first node down (the host's rank query),
