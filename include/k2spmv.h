@@ -77,8 +77,9 @@ typedef enum { K2_MODE_AUTO = 0, K2_MODE_TREE_ONLY = 1, K2_MODE_CACHED = 2 } k2_
 typedef struct {
     /* Tiled descent (Sec. 3.4): a tile is a contiguous node range whose
        subtree holds at most tile_nodes nodes on every level; one workgroup
-       descends a tile with its frontier in LDS.  256..4096, power of 2.
-       Default 1024. */
+       descends a tile with its frontier in LDS.  Tree-only plus-times
+       products cut their band sub-tiles and rest tiles at 256 nodes per
+       level instead, one wave each.  256..4096, power of 2.  Default 1024. */
     uint32_t tile_nodes;
     /* Host-side top (Sec. 3.4): the device starts from the deepest level with
        at most host_top_max nodes (never below the last internal level).
@@ -98,11 +99,13 @@ typedef struct {
        the lists.  0 keeps the block order.  Descent tiles keep their Z
        order either way.  Default 1. */
     int32_t xcd_remap;
-    /* Output windows for products over the cached level: Q is the largest
+    /* Output windows for products over the cached level and for tree-only
+       plus-times products (their band groups): Q is the largest
        power of 2 with Q * window_batch <= window_elems (at most 16384
        elements of 4 bytes; 0 disables).  A tile made of the dense Q x Q
        quadrants of one row band (right products) or column band (left
-       products) accumulates its outputs in LDS and adds them to y once.
+       products) accumulates its outputs in LDS and adds them to y once (a
+       band's only cached tile stores them instead).
        Products with more than window_batch vectors use the same windows
        while Q x batch elements fit one workgroup's LDS (fewer workgroups per
        CU), else direct atomics everywhere.  Defaults 4096 and 8. */
@@ -220,9 +223,10 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
 /* The tiles themselves, in the order the kernels take them.
    tiles[8k..8k+7] = (first, count, level, code index, window row, window
    column, log2 of the window side or 0xFFFFFFFF for no window, base index).
-   With scan offsets a descent tile's first child offsets on levels level ..
-   l-2 (the last its first leaf) are entries base index .. of the plan's
-   offsets (k2_plan_offsets); otherwise the base index is 0.
+   With scan offsets a tile's (descent, band or rest tile) first child
+   offsets on levels level .. l-2 (the last its first leaf) are entries
+   base index .. of the plan's offsets (k2_plan_offsets); otherwise the base
+   index is 0.
    which = 0: 'count' nodes of 'level' from node 'first', whose Morton codes
    (row bit above column bit per level, 2*level bits) are aux[code index ..].
    Tree-only right / left products take, when windows are planned and the
@@ -252,9 +256,9 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
 k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                         uint32_t *tiles, uint64_t n_tiles, uint64_t *aux, uint64_t n_aux);
 
-/* The scan offsets of the descent tiles (host only): with
-   K2_OFFSETS_SCAN (or AUTO), tile k's first child offsets on levels
-   tiles[k].level .. l-2 are bases[base index of tile k ..] (Sec. 3.2: the
+/* The scan offsets of the plan's tiles (host only: descent, band and rest
+   tiles): with K2_OFFSETS_SCAN (or AUTO), tile k's first child offsets on
+   levels tiles[k].level .. l-2 are bases[base index of tile k ..] (Sec. 3.2: the
    exclusive prefix sums of the fan-outs, sampled at the tile starts); empty
    with K2_OFFSETS_DIRECTORY.  *n_total receives the count; bases may be
    null to ask only for it, else it must hold n_bases >= that many entries.
