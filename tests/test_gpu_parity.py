@@ -131,7 +131,8 @@ def test_device_tree_and_cached_blocks(dev):
 
 def test_web_n20_d16(dev):
     """Web-like 2^20 (about 15M distinct edges): right and left plus-times,
-    tree-only and cached, against the oracle's full product."""
+    tree-only and cached, against the oracle's full product, overwriting y
+    and accumulating into it."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("web_n20_d16")
     tree = k2.Tree(rows, cols, n, n)
@@ -148,6 +149,14 @@ def test_web_n20_d16(dev):
             torch.cuda.synchronize()
             check_parity(from_device(y, "plus_times"), want, "plus_times",
                          f"web_n20_d16 {direction} {mode}")
+            # accumulating into y0: band groups and owner tiles add their
+            # windows to what y holds
+            y0 = np.random.default_rng(11).random(want.shape).astype(np.float32)
+            ya = to_device(y0, dev)
+            m.spmv(xd, ya, direction=direction, mode=mode, accumulate=True)
+            torch.cuda.synchronize()
+            check_parity(from_device(ya, "plus_times"), y0.astype(np.float64) + want, "plus_times",
+                         f"web_n20_d16 accumulate {direction} {mode}")
 
 
 def test_accumulate(dev):
