@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-stride", type=int, default=8,
                    help="oracle sample: the edges whose source is a multiple of this")
+    p.add_argument("--bfs", type=int, default=0,
+                   help="time multi-source searches from this many seeded sources instead of products")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -123,6 +125,36 @@ def cpu_baseline(rows, cols, n, x_by_dir, batch, directions, stride, semiring):
             "seconds": total_s}
 
 
+def search_bench(args, k2, tree, opts, n, mode, dev):
+    """Multi-source search (k2_bfs) from args.bfs seeded sources, right and
+    left: mean wall time of a whole search (every level, with its host read
+    of the level's count) over args.steps searches after args.warmup
+    two-level ones."""
+    import numpy as np
+    import torch
+    src = np.random.default_rng(9).integers(0, n, args.bfs).astype(np.uint32)
+    m = k2.Matrix(tree, opts, device=dev)
+    per = {}
+    for d in ("right", "left"):
+        for _ in range(max(args.warmup, 1)):
+            m.bfs(src, d, max_levels=2)
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(max(args.steps, 1)):
+            t0 = time.perf_counter()
+            dist, levels, reached = m.bfs(src, d, max_levels=1 << 16)
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            del dist
+        per[d] = {"levels": levels, "search_s": sum(times) / len(times), "min_s": min(times),
+                  "reached": int(reached.sum()) if reached is not None else None}
+        log(f"search {d}: {levels} levels, {per[d]['search_s']:.4f} s")
+    print(json.dumps({"metric": "multi_source_search_s", "unit": "s", "higher_is_better": False,
+                      "workload": args.workload, "mode": mode, "sources": args.bfs, "steps": args.steps,
+                      "warmup": args.warmup, "data": "synthetic", "per_direction": per,
+                      "kernel_source": kernel_source_hash()}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -160,6 +192,9 @@ def main():
                                ("offsets", args.offsets), ("xcd_remap", args.xcd_remap),
                                ("band_strays", args.band_strays)) if v is not None}
     opts = k2.plan_defaults(tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"), **extra)
+    if args.bfs:
+        search_bench(args, k2, tree, opts, n, mode, dev)
+        return
     est = tree.estimate(opts, semiring=semiring, batch=batch)
     # run the same kernels once on a tiny matrix first (the runtime loads a
     # kernel's code on its first launch), so that the memory measured below

@@ -1070,7 +1070,10 @@ __global__ __launch_bounds__(kThreads) void bfs_seed_kernel(const uint32_t *__re
 // After the level's product y = A (or, and) F: the newly reached bits are
 // y & ~V; they become the next frontier, join V and get distance 'level'.
 // y is left zero for the next product, which accumulates into it.  The
-// number of newly reached (vertex, source) pairs is added to *count.
+// number of newly reached (vertex, source) pairs is added to *count.  A lane
+// takes a word; the distances of a word's sources are 32 adjacent entries of
+// its vertex's row of dist, so the wave writes them together afterwards,
+// two fresh words per store (lanes 0-31 and 32-63, a lane per source).
 __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict__ y,
                                                             uint32_t *__restrict__ V,
                                                             uint32_t *__restrict__ F,
@@ -1078,27 +1081,43 @@ __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict
                                                             uint32_t W, uint32_t S, int32_t level,
                                                             unsigned long long *__restrict__ count) {
     const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    const uint32_t lane = __lane_id();
     uint32_t found = 0;
-    for (uint64_t e = uint64_t(blockIdx.x) * kThreads + threadIdx.x; e < n_words; e += stride) {
-        const uint32_t yw = y[e];
+    // e0: the wave's first word (uniform, so the shuffles below see every lane)
+    for (uint64_t e0 = uint64_t(blockIdx.x) * kThreads + (threadIdx.x & ~63u); e0 < n_words; e0 += stride) {
+        const uint64_t e = e0 + lane;
         uint32_t fresh = 0u;
-        if (yw) {
-            y[e] = 0u;
-            const uint32_t seen = V[e];
-            fresh = yw & ~seen;
-            if (fresh) {
-                V[e] = seen | fresh;
-                const uint64_t v = e / W;
-                const uint32_t j0 = uint32_t(e % W) * 32u;
-                for (uint32_t m = fresh; m; m &= m - 1u) dist[v * S + j0 + uint32_t(__builtin_ctz(m))] = level;
-                found += uint32_t(__popc(fresh));
+        if (e < n_words) {
+            const uint32_t yw = y[e];
+            if (yw) {
+                y[e] = 0u;
+                const uint32_t seen = V[e];
+                fresh = yw & ~seen;
+                if (fresh) V[e] = seen | fresh;
+            }
+            F[e] = fresh;
+        }
+        found += uint32_t(__popc(fresh));
+        uint64_t pending = __ballot(fresh != 0u);
+        while (pending) {
+            const uint32_t a = uint32_t(__builtin_ctzll(pending));
+            pending &= pending - 1u;
+            const uint32_t b = pending ? uint32_t(__builtin_ctzll(pending)) : a;
+            const bool second = pending != 0u;
+            if (second) pending &= pending - 1u;
+            const uint32_t from = lane < 32u ? a : b;
+            const uint32_t fw = uint32_t(__shfl(int(fresh), int(from)));
+            const uint32_t bit = lane & 31u;
+            if ((lane < 32u || second) && ((fw >> bit) & 1u)) {
+                const uint64_t we = e0 + from;
+                const uint32_t j = uint32_t(we % W) * 32u + bit;
+                if (j < S) dist[(we / W) * S + j] = level;
             }
         }
-        F[e] = fresh;
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) found += __shfl_xor(found, o);
-    if (__lane_id() == 0 && found) atomicAdd(count, (unsigned long long)found);
+    if (lane == 0 && found) atomicAdd(count, (unsigned long long)found);
 }
 
 // ------------------------------------------------------------- strays
