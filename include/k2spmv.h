@@ -324,20 +324,28 @@ k2_status k2_matrix_cached_blocks(const k2_matrix *matrix, uint64_t *blocks, uin
    over the packed frontier of the previous level (32 sources per uint32,
    K2_BOOLEAN_U32X32 with batch ceil(n_sources / 32)), with the matrix's
    cached level when it has one; a marking kernel keeps the entries not
-   reached before as the next frontier and writes their distance.  The search
-   stops after a level that reaches nothing new, or after max_levels levels.
+   reached before as the next frontier and records their level: as bit
+   planes of the packed words for levels below 64 (plane p holds bit p of the
+   level), from which one pass writes the whole distance table at the end
+   (or before level 64, whose marking then stores distances directly).  The
+   search stops after a level that reaches nothing new, or after max_levels
+   levels.
      sources            host array of n_sources vertex ids (< n; repeats are
                         independent searches)
      d_dist             device n x n_sources int32, row-major: d_dist[v *
                         n_sources + j] = hops from sources[j] to v, -1 if not
                         reached (overwritten)
      d_workspace        device, 256-byte aligned, k2_bfs_workspace_bytes bytes
-                        (caller-owned; the library allocates nothing)
+                        (caller-owned; the library allocates nothing): 9
+                        arrays of n ceil(n_sources / 32) words (frontier,
+                        reached set, product output, 6 level planes), a
+                        count and the sources
      levels             out: the last level that reached a new entry
      reached_per_level  optional host array of max_levels entries: entries
                         reached at each level run (the last run level's is 0
                         when the search converged)
-   Synchronous per level (the host reads one count).  Errors:
+   Synchronous: the host reads one count per level and the call returns once
+   the distance table is written.  Errors:
    K2_E_INVALID_ARG (null, non-square matrix, no sources, small or unaligned
    workspace), K2_E_INDEX_RANGE (a source >= n), K2_E_HIP. */
 k2_status k2_bfs_workspace_bytes(const k2_matrix *matrix, uint32_t n_sources, uint64_t *bytes);

@@ -635,8 +635,11 @@ namespace {
 
 // Workspace of a search: frontier, reached set and product output (n W
 // words each), the per-level count, the sources.
+// Search workspace: F, V, y and the kBfsPlanes level planes (n W words
+// each, contiguous: the init kernel clears them at once), the level count
+// and the sources.
 struct BfsSpace {
-    uint64_t words_off[3], count_off, src_off, bytes;
+    uint64_t words_off[3 + kBfsPlanes], count_off, src_off, bytes;
 };
 
 BfsSpace bfs_space(uint64_t n, uint32_t S) {
@@ -644,9 +647,9 @@ BfsSpace bfs_space(uint64_t n, uint32_t S) {
     auto a256 = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
     BfsSpace b{};
     uint64_t off = 0;
-    for (int k = 0; k < 3; ++k) {
+    for (uint32_t k = 0; k < 3 + kBfsPlanes; ++k) {
         b.words_off[k] = off;
-        off += n * W * 4;   // contiguous: the init kernel clears all three at once
+        off += n * W * 4;
     }
     off = a256(off);
     b.count_off = off;
@@ -681,24 +684,35 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
     uint32_t *F = reinterpret_cast<uint32_t *>(ws + sp.words_off[0]);
     uint32_t *V = reinterpret_cast<uint32_t *>(ws + sp.words_off[1]);
     uint32_t *Y = reinterpret_cast<uint32_t *>(ws + sp.words_off[2]);
+    uint32_t *planes = reinterpret_cast<uint32_t *>(ws + sp.words_off[3]);
     auto *count = reinterpret_cast<unsigned long long *>(ws + sp.count_off);
     uint32_t *src = reinterpret_cast<uint32_t *>(ws + sp.src_off);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const bool empty = m.nodes[m.levels - 2] == 0;
     HIP_TRY(hipMemcpyAsync(src, sources, uint64_t(n_sources) * 4, hipMemcpyHostToDevice, st), "search sources");
-    int e = launch_bfs_init(d_dist, n * n_sources, F, 3 * n * W, stream);
-    if (e == hipSuccess) e = launch_bfs_seed(src, n_sources, W, d_dist, F, V, stream);
+    int e = launch_bfs_init(F, (3 + uint64_t(kBfsPlanes)) * n * W, stream);
+    if (e == hipSuccess) e = launch_bfs_seed(src, n_sources, W, F, V, stream);
     if (e != hipSuccess) {
         set_hip_error(e, "search init");
         return K2_E_HIP;
     }
+    // levels below 2^kBfsPlanes go to the planes; the distance table is
+    // written from them once, at the end or before the first deeper level,
+    // whose marking then stores distances itself
+    bool table = false;
     *levels = 0;
     for (uint32_t level = 1; level <= max_levels && level < 0x7FFFFFFFu; ++level) {
         HIP_TRY(hipMemsetAsync(count, 0, 8, st), "search count");
-        if (!empty)
+        if (!table && level >= (1u << kBfsPlanes)) {
+            e = launch_bfs_dist(d_dist, V, planes, n * W, W, n_sources, stream);
+            table = true;
+        }
+        if (!empty && e == hipSuccess)
             e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, 1, stream)
                          : launch_descent(m, direction, K2_BOOLEAN_U32X32, W, F, Y, nullptr, stream);
-        if (e == hipSuccess) e = launch_bfs_mark(Y, V, F, d_dist, n * W, W, n_sources, int32_t(level), count, stream);
+        if (e == hipSuccess)
+            e = launch_bfs_mark(Y, V, F, table ? nullptr : planes, d_dist, n * W, W, n_sources, int32_t(level),
+                                count, stream);
         if (e != hipSuccess) {
             set_hip_error(e, "search level");
             return K2_E_HIP;
@@ -709,6 +723,14 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
         if (reached_per_level) reached_per_level[level - 1] = found;
         if (found == 0) break;
         *levels = level;
+    }
+    if (!table) {
+        e = launch_bfs_dist(d_dist, V, planes, n * W, W, n_sources, stream);
+        if (e != hipSuccess) {
+            set_hip_error(e, "search distances");
+            return K2_E_HIP;
+        }
+        HIP_TRY(hipStreamSynchronize(st), "search distances");
     }
     return K2_OK;
 }

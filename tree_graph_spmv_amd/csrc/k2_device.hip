@@ -1044,39 +1044,38 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
 // (rounded up) words per vertex, bit j % 32 of word j / 32 for source j;
 // dist is n x S int32.
 
-// dist = -1 everywhere; F, V and y (3 n W contiguous words) = 0.
-__global__ __launch_bounds__(kThreads) void bfs_init_kernel(int32_t *__restrict__ dist, uint64_t n_dist,
-                                                            uint32_t *__restrict__ words,
-                                                            uint64_t n_words) {
+// The search's packed words (F, V, y and the level planes, contiguous) = 0.
+__global__ __launch_bounds__(kThreads) void bfs_init_kernel(uint32_t *__restrict__ words, uint64_t n_words) {
     const uint64_t stride = uint64_t(gridDim.x) * kThreads;
-    for (uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x; i < n_dist; i += stride) dist[i] = -1;
     for (uint64_t i = uint64_t(blockIdx.x) * kThreads + threadIdx.x; i < n_words; i += stride) words[i] = 0u;
 }
 
-// Source j starts at distance 0 in the frontier and the reached set.
+// Source j starts at level 0 in the frontier and the reached set.
 __global__ __launch_bounds__(kThreads) void bfs_seed_kernel(const uint32_t *__restrict__ src, uint32_t S,
-                                                            uint32_t W, int32_t *__restrict__ dist,
-                                                            uint32_t *__restrict__ F,
+                                                            uint32_t W, uint32_t *__restrict__ F,
                                                             uint32_t *__restrict__ V) {
     const uint32_t j = blockIdx.x * kThreads + threadIdx.x;
     if (j >= S) return;
     const uint64_t v = src[j];
-    dist[v * S + j] = 0;
     const uint32_t bit = 1u << (j & 31u);
     atomicOr(&F[v * W + (j >> 5)], bit);
     atomicOr(&V[v * W + (j >> 5)], bit);
 }
 
 // After the level's product y = A (or, and) F: the newly reached bits are
-// y & ~V; they become the next frontier, join V and get distance 'level'.
-// y is left zero for the next product, which accumulates into it.  The
-// number of newly reached (vertex, source) pairs is added to *count.  A lane
-// takes a word; the distances of a word's sources are 32 adjacent entries of
-// its vertex's row of dist, so the wave writes them together afterwards,
-// two fresh words per store (lanes 0-31 and 32-63, a lane per source).
+// y & ~V; they become the next frontier and join V.  y is left zero for the
+// next product, which accumulates into it.  The number of newly reached
+// (vertex, source) pairs is added to *count.  A lane takes a word.  With
+// planes (levels below 2^kBfsPlanes) the level is recorded by or-ing the
+// fresh bits into plane p (n_words words from planes + p n_words) for each
+// set bit p of the level: whole-word stores of the packed layout.  Without,
+// the distances are stored: a word's sources are 32 adjacent entries of its
+// vertex's row of dist, so the wave writes them together, two fresh words
+// per store (lanes 0-31 and 32-63, a lane per source).
 __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict__ y,
                                                             uint32_t *__restrict__ V,
                                                             uint32_t *__restrict__ F,
+                                                            uint32_t *__restrict__ planes,
                                                             int32_t *__restrict__ dist, uint64_t n_words,
                                                             uint32_t W, uint32_t S, int32_t level,
                                                             unsigned long long *__restrict__ count) {
@@ -1093,11 +1092,17 @@ __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict
                 y[e] = 0u;
                 const uint32_t seen = V[e];
                 fresh = yw & ~seen;
-                if (fresh) V[e] = seen | fresh;
+                if (fresh) {
+                    V[e] = seen | fresh;
+                    if (planes)
+                        for (uint32_t p = 0; p < kBfsPlanes; ++p)
+                            if ((uint32_t(level) >> p) & 1u) planes[p * n_words + e] |= fresh;
+                }
             }
             F[e] = fresh;
         }
         found += uint32_t(__popc(fresh));
+        if (planes) continue;
         uint64_t pending = __ballot(fresh != 0u);
         while (pending) {
             const uint32_t a = uint32_t(__builtin_ctzll(pending));
@@ -1118,6 +1123,44 @@ __global__ __launch_bounds__(kThreads) void bfs_mark_kernel(uint32_t *__restrict
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) found += __shfl_xor(found, o);
     if (lane == 0 && found) atomicAdd(count, (unsigned long long)found);
+}
+
+// The distance table from the reached set and the level planes: entry (v, j)
+// is -1 where bit j of v's words in V is clear, else the level the planes
+// hold (0 for the sources).  A lane takes a word and writes its (up to) 32
+// entries, the word's segment of its vertex's row: 16-byte stores when
+// 'vec4' (S a multiple of 4 and dist 16-byte aligned), so every 128-byte
+// segment is written whole.
+__global__ __launch_bounds__(kThreads) void bfs_dist_kernel(int32_t *__restrict__ dist,
+                                                            const uint32_t *__restrict__ V,
+                                                            const uint32_t *__restrict__ planes,
+                                                            uint64_t n_words, uint32_t W, uint32_t S,
+                                                            int vec4) {
+    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    for (uint64_t e = uint64_t(blockIdx.x) * kThreads + threadIdx.x; e < n_words; e += stride) {
+        const uint32_t vw = V[e];
+        uint32_t pl[kBfsPlanes];
+#pragma unroll
+        for (uint32_t p = 0; p < kBfsPlanes; ++p) pl[p] = planes[p * n_words + e];
+        const uint64_t v = W == 1u ? e : e / W;
+        const uint32_t j0 = uint32_t(e - v * W) * 32u;
+        const uint32_t nj = S - j0 < 32u ? S - j0 : 32u;
+        int32_t *__restrict__ row = dist + v * S + j0;
+        auto entry = [&](uint32_t b) -> int32_t {
+            int32_t d = 0;
+#pragma unroll
+            for (uint32_t p = 0; p < kBfsPlanes; ++p) d |= int32_t((pl[p] >> b) & 1u) << p;
+            return ((vw >> b) & 1u) ? d : -1;
+        };
+        if (vec4 && nj == 32u) {
+#pragma unroll
+            for (uint32_t q = 0; q < 8u; ++q)
+                reinterpret_cast<int4 *>(row)[q] =
+                    make_int4(entry(4u * q), entry(4u * q + 1u), entry(4u * q + 2u), entry(4u * q + 3u));
+        } else {
+            for (uint32_t b = 0; b < nj; ++b) row[b] = entry(b);
+        }
+    }
 }
 
 // ------------------------------------------------------------- strays
@@ -1394,23 +1437,30 @@ static uint32_t small_grid(uint64_t items) {
     return uint32_t(b < 8192 ? (b ? b : 1) : 8192);
 }
 
-int launch_bfs_init(int32_t *dist, uint64_t n_dist, uint32_t *words, uint64_t n_words, void *stream) {
-    hipLaunchKernelGGL(bfs_init_kernel, dim3(small_grid(n_dist > n_words ? n_dist : n_words)), dim3(kThreads),
-                       0, static_cast<hipStream_t>(stream), dist, n_dist, words, n_words);
+int launch_bfs_init(uint32_t *words, uint64_t n_words, void *stream) {
+    hipLaunchKernelGGL(bfs_init_kernel, dim3(small_grid(n_words)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), words, n_words);
     return hipGetLastError();
 }
 
-int launch_bfs_seed(const uint32_t *src, uint32_t S, uint32_t W, int32_t *dist, uint32_t *F, uint32_t *V,
-                    void *stream) {
+int launch_bfs_seed(const uint32_t *src, uint32_t S, uint32_t W, uint32_t *F, uint32_t *V, void *stream) {
     hipLaunchKernelGGL(bfs_seed_kernel, dim3((S + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), src, S, W, dist, F, V);
+                       static_cast<hipStream_t>(stream), src, S, W, F, V);
     return hipGetLastError();
 }
 
-int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, int32_t *dist, uint64_t n_words, uint32_t W,
-                    uint32_t S, int32_t level, unsigned long long *count, void *stream) {
+int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, uint32_t *planes, int32_t *dist, uint64_t n_words,
+                    uint32_t W, uint32_t S, int32_t level, unsigned long long *count, void *stream) {
     hipLaunchKernelGGL(bfs_mark_kernel, dim3(small_grid(n_words)), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), y, V, F, dist, n_words, W, S, level, count);
+                       static_cast<hipStream_t>(stream), y, V, F, planes, dist, n_words, W, S, level, count);
+    return hipGetLastError();
+}
+
+int launch_bfs_dist(int32_t *dist, const uint32_t *V, const uint32_t *planes, uint64_t n_words, uint32_t W,
+                    uint32_t S, void *stream) {
+    const int vec4 = (S % 4u == 0u) && (reinterpret_cast<uintptr_t>(dist) % 16u == 0u);
+    hipLaunchKernelGGL(bfs_dist_kernel, dim3(small_grid(n_words)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), dist, V, planes, n_words, W, S, vec4);
     return hipGetLastError();
 }
 

@@ -182,11 +182,16 @@ struct Matrix {
 
 // Kernel launchers (k2_device.hip).  Return hipError_t as int.
 int launch_fill(void *y, uint64_t n_words32, uint32_t value, void *stream);
-int launch_bfs_init(int32_t *dist, uint64_t n_dist, uint32_t *words, uint64_t n_words, void *stream);
-int launch_bfs_seed(const uint32_t *src, uint32_t S, uint32_t W, int32_t *dist, uint32_t *F, uint32_t *V,
-                    void *stream);
-int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, int32_t *dist, uint64_t n_words, uint32_t W,
-                    uint32_t S, int32_t level, unsigned long long *count, void *stream);
+// Multi-source search: a level below 2^kBfsPlanes is recorded as bit planes
+// of the packed words (plane p holds bit p of each entry's level); the
+// distance table is written from them once.
+constexpr uint32_t kBfsPlanes = 6;
+int launch_bfs_init(uint32_t *words, uint64_t n_words, void *stream);
+int launch_bfs_seed(const uint32_t *src, uint32_t S, uint32_t W, uint32_t *F, uint32_t *V, void *stream);
+int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, uint32_t *planes, int32_t *dist, uint64_t n_words,
+                    uint32_t W, uint32_t S, int32_t level, unsigned long long *count, void *stream);
+int launch_bfs_dist(int32_t *dist, const uint32_t *V, const uint32_t *planes, uint64_t n_words, uint32_t W,
+                    uint32_t S, void *stream);
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
                    uint64_t *emit_codes, void *stream);
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
