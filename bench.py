@@ -45,6 +45,8 @@ def parse():
                    help="oracle sample: the edges whose source is a multiple of this")
     p.add_argument("--bfs", type=int, default=0,
                    help="time multi-source searches from this many seeded sources instead of products")
+    p.add_argument("--stream-mb", type=int, default=0,
+                   help="time out-of-core products streamed through a staging buffer of this many MB")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a 1 GiB device copy (counter calibration) and exit")
     return p.parse_args()
@@ -155,6 +157,42 @@ def search_bench(args, k2, tree, opts, n, mode, dev):
                       "kernel_source": kernel_source_hash()}))
 
 
+def stream_bench(args, k2, tree, opts, n, semiring, batch, directions, dev):
+    """Out-of-core products (k2_stream_*): the tree stays in host memory and
+    each product streams it through a staging buffer of args.stream_mb MB.
+    Reports each direction's mean wall time over args.steps products after
+    args.warmup, the bytes one product copies and the rate they imply."""
+    import numpy as np
+    import torch
+    import synth
+    t0 = time.perf_counter()
+    s = k2.Streamed(tree, args.stream_mb << 20, opts)
+    plan_s = time.perf_counter() - t0
+    buf = s.staging(dev)
+    xh = synth.workload_x(args.workload, n, batch=batch)
+    x = torch.from_numpy(xh.view(np.int32) if xh.dtype == np.uint32 else xh).to(dev)
+    y = torch.empty(n * batch, dtype=x.dtype, device=dev)
+    per = {}
+    for d in directions:
+        for _ in range(max(args.warmup, 1)):
+            s.spmv(x, y, direction=d, semiring=semiring, batch=batch, staging=buf)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(max(args.steps, 1)):
+            s.spmv(x, y, direction=d, semiring=semiring, batch=batch, staging=buf)
+        torch.cuda.synchronize()
+        sec = (time.perf_counter() - t0) / max(args.steps, 1)
+        per[d] = {"product_s": sec, "edges_per_s": tree.nnz / sec,
+                  "staged_gb_per_s": s.staged_bytes / sec / 1e9}
+        log(f"streamed {d}: {sec * 1e3:.1f} ms per product")
+    print(json.dumps({"metric": "streamed_product_edges_per_s", "unit": "edges/s", "higher_is_better": True,
+                      "workload": args.workload, "semiring": semiring, "batch": batch,
+                      "staging_mb": args.stream_mb, "chunks": s.n_chunks, "max_chunk_bytes": s.max_chunk_bytes,
+                      "staged_bytes_per_product": s.staged_bytes, "plan_s": plan_s, "steps": args.steps,
+                      "warmup": args.warmup, "data": "synthetic", "per_direction": per,
+                      "kernel_source": kernel_source_hash()}))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -194,6 +232,9 @@ def main():
     opts = k2.plan_defaults(tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"), **extra)
     if args.bfs:
         search_bench(args, k2, tree, opts, n, mode, dev)
+        return
+    if args.stream_mb:
+        stream_bench(args, k2, tree, opts, n, semiring, batch, directions, dev)
         return
     est = tree.estimate(opts, semiring=semiring, batch=batch)
     # run the same kernels once on a tiny matrix first (the runtime loads a

@@ -165,6 +165,7 @@ typedef struct {
 
 typedef struct k2_tree k2_tree;
 typedef struct k2_matrix k2_matrix;
+typedef struct k2_stream k2_stream;
 
 /* Fill 'opts' with the defaults above. */
 k2_status k2_plan_defaults(k2_plan_opts *opts);
@@ -352,6 +353,48 @@ k2_status k2_bfs_workspace_bytes(const k2_matrix *matrix, uint32_t n_sources, ui
 k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
                  uint32_t max_levels, int32_t *d_dist, void *d_workspace, uint64_t workspace_bytes,
                  void *stream, uint32_t *levels, uint64_t *reached_per_level);
+
+/* Out-of-core products (Sec. 7, the paper's direction for trees larger than
+   device memory): the tree stays in host memory and each product streams it
+   through a caller-owned device staging buffer, chunk by chunk.
+
+   k2_stream_create (host only, no HIP call) plans the depth-first descent
+   tiles of 'tree' with 'opts' (tile_nodes and host_top_max are used; the
+   tiles always carry planned scan offsets; no cached level, no windows) and
+   cuts them, in order, into chunks of consecutive tiles whose staged data
+   fits staging_bytes: per level the span of node words the chunk's tiles
+   reach (plus one word), then its tiles, start codes and scan offsets, each
+   part 256-byte aligned.  'tree' must outlive the stream.  Errors:
+   K2_E_INVALID_ARG, K2_E_ARENA_TOO_SMALL (one tile does not fit),
+   K2_E_HOST_OOM. */
+k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64_t staging_bytes,
+                           k2_stream **out);
+
+/* Chunk count, the largest chunk's staged bytes (the staging buffer a
+   product needs) and the bytes one product copies to the device. */
+k2_status k2_stream_info(const k2_stream *stream_plan, uint64_t *n_chunks, uint64_t *max_chunk_bytes,
+                         uint64_t *staged_bytes);
+
+/* Chunk 'chunk': its tiles [*first_tile, *end_tile) of the plan's descent
+   tiles (k2_plan_tiles which = 0, same options) and, for levels 0 ..
+   n_levels-1, the first staged word and the staged word count (0: none).
+   Errors: K2_E_INVALID_ARG. */
+k2_status k2_stream_chunk(const k2_stream *stream_plan, uint64_t chunk, uint64_t *first_tile,
+                          uint64_t *end_tile, uint64_t *lo_words, uint64_t *n_words, uint32_t n_levels);
+
+/* One product as k2_spmv (direction, semiring, batch, device x and y, flags
+   0 or K2_SPMV_ACCUMULATE), tree-only, with the tree streamed: per chunk its
+   level words, tiles, codes and offsets are copied from host memory into
+   d_staging (256-byte aligned, at least max_chunk_bytes) on 'stream' and the
+   chunk's tiles descended from there; stream order keeps a chunk's copies
+   behind the kernel of the chunk before.  Asynchronous like k2_spmv.
+   Errors: K2_E_INVALID_ARG (null, small or unaligned staging, overlapping
+   x and y), K2_E_HIP. */
+k2_status k2_stream_spmv(k2_stream *stream_plan, k2_direction direction, k2_semiring semiring,
+                         uint32_t batch, int32_t flags, const void *d_x, void *d_y, void *d_staging,
+                         uint64_t staging_bytes, void *stream);
+
+void k2_stream_destroy(k2_stream *stream_plan);
 
 const char *k2_status_string(k2_status status);
 

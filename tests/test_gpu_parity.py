@@ -157,6 +157,11 @@ def test_web_n20_d16(dev):
             torch.cuda.synchronize()
             check_parity(from_device(ya, "plus_times"), y0.astype(np.float64) + want, "plus_times",
                          f"web_n20_d16 accumulate {direction} {mode}")
+        # streamed from host memory through a 4 MB staging buffer
+        st = k2.Streamed(tree, 4 << 20)
+        y = st.spmv(xd, direction=direction)
+        torch.cuda.synchronize()
+        check_parity(from_device(y, "plus_times"), want, "plus_times", f"web_n20_d16 {direction} streamed")
 
 
 def test_accumulate(dev):
@@ -187,3 +192,44 @@ def test_accumulate(dev):
             r = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
             want = combine[sr](y0.reshape(r.shape), r)
             check_parity(from_device(y, sr), want, sr, f"accumulate {var} {mode} {sr} {direction} B={B}")
+
+
+def test_streamed(dev):
+    """Out-of-core products (k2_stream_*): the tree stays in host memory and
+    goes through a small staging buffer chunk by chunk; every semiring, both
+    directions, batches 1 and 3, overwriting and accumulating, against the
+    oracle, and against the resident tree-only product."""
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(17)
+    rows, cols, n = synth.workload_edges("rmat_s12_e32k")
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    m = k2.Matrix(tree, k2.plan_defaults(), device=dev)
+    combine = {"plus_times": lambda a, b: a.astype(np.float64) + b,
+               "boolean": np.maximum, "boolean_u32": np.bitwise_or, "tropical": np.minimum}
+    for staging in (1 << 15, 1 << 24):
+        s = k2.Streamed(tree, staging)
+        assert s.max_chunk_bytes <= staging
+        if staging == 1 << 15:
+            assert s.n_chunks > 4
+        buf = s.staging(dev)
+        for sr, direction, B in itertools.product(ALL_SEMIRINGS, ("right", "left"), (1, 3)):
+            x = make_x(rng, sr, n, B)
+            xd = to_device(x, dev)
+            y = s.spmv(xd, direction=direction, semiring=sr, batch=B, staging=buf)
+            torch.cuda.synchronize()
+            want = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
+            label = f"streamed {staging} {sr} {direction} B={B}"
+            check_parity(from_device(y, sr), want, sr, label)
+            if sr != "plus_times":   # exact semirings: the resident product agrees bit for bit
+                yr = m.spmv(xd, direction=direction, semiring=sr, batch=B, mode="tree")
+                torch.cuda.synchronize()
+                assert np.array_equal(from_device(y, sr), from_device(yr, sr)), label
+            y0 = make_x(rng, sr, n, B)
+            if sr == "boolean":
+                y0 = (y0 != 0).astype(np.float32)
+            ya = to_device(y0, dev)
+            s.spmv(xd, ya, direction=direction, semiring=sr, batch=B, accumulate=True, staging=buf)
+            torch.cuda.synchronize()
+            check_parity(from_device(ya, sr), combine[sr](y0.reshape(want.shape), want), sr, "accumulate " + label)
+

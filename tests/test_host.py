@@ -442,3 +442,48 @@ def test_threads_do_not_change_the_tree():
     t7 = k2.Tree(r, c, 8192, 8192, n_threads=7)
     for d in range(t1.levels):
         assert np.array_equal(t1.level_words(d), t7.level_words(d))
+
+
+def test_stream_chunks(case):
+    """Out-of-core plans: the chunks take the depth-first descent tiles in
+    order, each fits the staging size, and every level range of a chunk's
+    tiles lies inside the node words staged for that level (the leaf level
+    one word beyond, for the reads of a node's next leaf dword)."""
+    name, r, c, nr, nc, t, o = case
+    L = o.levels
+    last = L - 2
+    nodes = o.level_nodes()
+    if nodes[last] == 0:
+        return
+    offs = [o.child_offsets(d) for d in range(L - 1)]
+
+    def down(d, i, to):
+        while d < to:
+            i = int(offs[d][i]) if i < nodes[d] else nodes[d + 1]
+            d += 1
+        return i
+    opts = k2.plan_defaults(offsets="scan")
+    _, tiles, _ = t.plan(opts, 0)
+    for staging in (1 << 14, 1 << 16, 1 << 22):
+        try:
+            s = k2.Streamed(t, staging, opts)
+        except k2.K2Error as e:
+            assert e.status == k2.K2_E_ARENA_TOO_SMALL and staging == 1 << 14
+            continue
+        assert s.max_chunk_bytes <= staging and s.n_chunks >= 1
+        pos = 0
+        for ch in range(s.n_chunks):
+            a, b, lo, nw = s.chunk(ch, L)
+            assert a == pos and b > a
+            pos = b
+            for tl in tiles[a:b]:
+                first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
+                for d in range(level, L):
+                    x0, x1 = down(level, first, d), down(level, first + count, d)
+                    if x1 == x0:
+                        continue
+                    w0, w1 = int(lo[d]), int(lo[d]) + int(nw[d])
+                    assert w0 * 16 <= x0 and (x1 - 1) // 16 < w1, (name, staging, ch, d)
+                    if d == L - 1:   # the next leaf dword of the last leaf
+                        assert w1 == (nodes[d] + 15) // 16 or (x1 - 1) // 16 + 1 < w1
+        assert pos == len(tiles), (name, staging)

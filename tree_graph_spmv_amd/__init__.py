@@ -99,6 +99,12 @@ _SIGS = {
     "k2_matrix_set_timing": (ctypes.c_int, [_VP, ctypes.c_int32]),
     "k2_matrix_last_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_float),
                                              ctypes.POINTER(ctypes.c_float)]),
+    "k2_stream_create": (ctypes.c_int, [_VP, ctypes.POINTER(PlanOpts), ctypes.c_uint64, ctypes.POINTER(_VP)]),
+    "k2_stream_info": (ctypes.c_int, [_VP, _U64P, _U64P, _U64P]),
+    "k2_stream_chunk": (ctypes.c_int, [_VP, ctypes.c_uint64, _U64P, _U64P, _U64P, _U64P, ctypes.c_uint32]),
+    "k2_stream_spmv": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int32, _VP, _VP,
+                                      _VP, ctypes.c_uint64, _VP]),
+    "k2_stream_destroy": (None, [_VP]),
     "k2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "k2_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -355,3 +361,67 @@ class Matrix:
         _check(lib().k2_matrix_cached_blocks(self._h, out.ctypes.data_as(_U64P), n_nodes,
                                              _stream_handle(stream)), "k2_matrix_cached_blocks")
         return out[:n_nodes]
+
+
+class Streamed:
+    """Out-of-core products (k2_stream_*): the tree stays in host memory and
+    each product copies it chunk by chunk into a device staging buffer of at
+    most staging_bytes.  Creating one plans the chunks (host only); the
+    tree must stay alive."""
+
+    def __init__(self, tree, staging_bytes, opts=None):
+        h = _VP()
+        o = opts if opts is not None else plan_defaults()
+        _check(lib().k2_stream_create(tree._h, ctypes.byref(o), int(staging_bytes), ctypes.byref(h)),
+               "k2_stream_create")
+        self._h = h
+        self._tree = tree
+        self.n_rows, self.n_cols = tree.n_rows, tree.n_cols
+        nc, mb, sb = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
+        _check(lib().k2_stream_info(h, ctypes.byref(nc), ctypes.byref(mb), ctypes.byref(sb)), "k2_stream_info")
+        self.n_chunks, self.max_chunk_bytes, self.staged_bytes = nc.value, mb.value, sb.value
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.k2_stream_destroy(h)
+            self._h = None
+
+    def chunk(self, k, levels):
+        """(first tile, end tile, first staged word per level, staged words per level)."""
+        a, b = ctypes.c_uint64(), ctypes.c_uint64()
+        lo = np.zeros(levels, np.uint64)
+        nw = np.zeros(levels, np.uint64)
+        _check(lib().k2_stream_chunk(self._h, int(k), ctypes.byref(a), ctypes.byref(b),
+                                     lo.ctypes.data_as(_U64P), nw.ctypes.data_as(_U64P), int(levels)),
+               "k2_stream_chunk")
+        return a.value, b.value, lo, nw
+
+    def staging(self, device="cuda"):
+        """A device staging buffer that fits every chunk."""
+        import torch
+        return torch.empty(max(self.max_chunk_bytes, 256), dtype=torch.uint8, device=device)
+
+    def spmv(self, x, y=None, direction="right", semiring="plus_times", batch=1, accumulate=False,
+             staging=None, stream=None):
+        """As Matrix.spmv in tree mode, with the tree streamed from host memory."""
+        import torch
+        d = DIRECTIONS[direction]
+        n_in = self.n_cols if d == K2_RIGHT else self.n_rows
+        n_out = self.n_rows if d == K2_RIGHT else self.n_cols
+        dtype = torch.int32 if semiring == "boolean_u32" else torch.float32
+        if x.dtype != dtype or x.numel() != n_in * batch or not x.is_contiguous():
+            raise ValueError(f"x must be a contiguous {dtype} tensor of {n_in * batch} elements")
+        if y is None:
+            if accumulate:
+                raise ValueError("accumulate needs y")
+            y = torch.empty(n_out * batch, dtype=dtype, device=x.device)
+        elif y.dtype != dtype or y.numel() != n_out * batch or not y.is_contiguous():
+            raise ValueError(f"y must be a contiguous {dtype} tensor of {n_out * batch} elements")
+        if staging is None:
+            staging = self.staging(x.device)
+        _check(lib().k2_stream_spmv(self._h, d, SEMIRINGS[semiring], int(batch),
+                                    K2_SPMV_ACCUMULATE if accumulate else 0, _VP(x.data_ptr()),
+                                    _VP(y.data_ptr()), _VP(staging.data_ptr()), staging.numel(),
+                                    _stream_handle(stream)), "k2_stream_spmv")
+        return y

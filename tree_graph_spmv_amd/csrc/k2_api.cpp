@@ -5,6 +5,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <memory>
 #include <mutex>
 #include <thread>
 
@@ -21,6 +22,26 @@ struct k2_tree {
 
 struct k2_matrix {
     k2::Matrix m;
+};
+
+// A streamed (out-of-core) product plan: the descent tiles cut into chunks
+// whose staged data fits the staging buffer.
+struct k2_stream {
+    struct Chunk {
+        uint64_t t0 = 0, t1 = 0;            // tiles [t0, t1) of 'tiles'
+        uint64_t lo_word[k2::kMaxLevels];   // first staged word per level
+        uint64_t n_words[k2::kMaxLevels];   // staged words per level (0: none)
+        uint64_t word_off[k2::kMaxLevels];  // byte offset in the staging buffer
+        uint64_t tiles_off = 0, codes_off = 0, bases_off = 0, bytes = 0;
+        std::vector<k2::Tile> tiles;        // code_off / base_off relative to the chunk
+        std::vector<uint64_t> codes;
+        std::vector<uint32_t> bases;
+    };
+    const k2_tree *tree = nullptr;
+    uint32_t tile_nodes = 0;
+    bool row_runs = false;
+    std::vector<Chunk> chunks;
+    uint64_t max_bytes = 0, staged_bytes = 0;
 };
 
 namespace k2 {
@@ -734,6 +755,213 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
     }
     return K2_OK;
 }
+
+k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64_t staging_bytes,
+                           k2_stream **out) {
+    if (!tree || !out) return K2_E_INVALID_ARG;
+    k2_plan_opts o;
+    k2_plan_defaults(&o);
+    if (opts) o = *opts;
+    o.cache_last_level = 0;
+    o.offsets = K2_OFFSETS_SCAN;   // every tile carries its own child offsets
+    o.window_elems = 0;
+    if (!valid_opts(o)) return K2_E_INVALID_ARG;
+    const HostTree &t = tree->t;
+    const int L = t.levels;
+    std::unique_ptr<k2_stream> s(new (std::nothrow) k2_stream);
+    if (!s) return K2_E_HOST_OOM;
+    s->tree = tree;
+    s->tile_nodes = o.tile_nodes;
+    if (L < 2 || t.nodes[L - 2] == 0) {   // empty matrix: nothing to stream
+        *out = s.release();
+        return K2_OK;
+    }
+    Plan p;
+    try {
+        k2_status st = make_plan(t, o, &p);
+        if (st != K2_OK) return st;
+    } catch (const std::bad_alloc &) {
+        return K2_E_HOST_OOM;
+    }
+    s->row_runs = p.row_runs;
+    const int last = L - 2;
+    auto a256 = [](uint64_t v) { return (v + 255) & ~uint64_t(255); };
+    // tile k's node range on every level from its own to the leaves
+    auto ranges = [&](size_t k, uint64_t *tlo, uint64_t *thi) {
+        const Tile &tl = p.tiles[k];
+        uint64_t a = tl.first, b = uint64_t(tl.first) + tl.count;
+        for (int d = int(tl.level); d < L; ++d) {
+            tlo[d] = a;
+            thi[d] = b;
+            if (d < L - 1) {
+                a = p.tile_bases[tl.base_off + uint32_t(d - int(tl.level))];
+                b = child_offset(t, d, b);
+            }
+        }
+    };
+    // greedy chunks of consecutive tiles: per level the span of their ranges
+    // (plus one word: the leaf reads take the next dword), then the chunk's
+    // tiles, codes and scan offsets
+    const size_t nt = p.tiles.size();
+    uint64_t clo[kMaxLevels], chi[kMaxLevels], tlo[kMaxLevels], thi[kMaxLevels];
+    bool used[kMaxLevels];
+    auto span_words = [&](int d, uint64_t a, uint64_t b, uint64_t *w0) {
+        *w0 = a >> 4;
+        return std::min<uint64_t>((b + 15) / 16 + 1, (t.nodes[d] + 15) / 16) - *w0;
+    };
+    size_t k = 0;
+    while (k < nt) {
+        std::fill(used, used + kMaxLevels, false);
+        uint64_t ncodes = 0, nbases = 0;
+        size_t j = k;
+        for (; j < nt; ++j) {
+            const Tile &tl = p.tiles[j];
+            ranges(j, tlo, thi);
+            uint64_t bytes = 0;
+            for (int d = 0; d < L; ++d) {
+                const bool in = d >= int(tl.level);
+                if (!used[d] && !in) continue;
+                const uint64_t a = !used[d] ? tlo[d] : in ? std::min(clo[d], tlo[d]) : clo[d];
+                const uint64_t b = !used[d] ? thi[d] : in ? std::max(chi[d], thi[d]) : chi[d];
+                uint64_t w0;
+                bytes += a256(8 * span_words(d, a, b, &w0));
+            }
+            const uint64_t nc = ncodes + tl.count, nb = nbases + uint64_t(last - int(tl.level) + 1);
+            bytes += a256(sizeof(Tile) * (j - k + 1)) + a256(8 * nc) + a256(4 * nb);
+            if (bytes > staging_bytes) break;
+            for (int d = int(tl.level); d < L; ++d) {
+                clo[d] = used[d] ? std::min(clo[d], tlo[d]) : tlo[d];
+                chi[d] = used[d] ? std::max(chi[d], thi[d]) : thi[d];
+                used[d] = true;
+            }
+            ncodes = nc;
+            nbases = nb;
+        }
+        if (j == k) return K2_E_ARENA_TOO_SMALL;   // one tile does not fit
+        k2_stream::Chunk c;
+        c.t0 = k;
+        c.t1 = j;
+        uint64_t off = 0;
+        for (int d = 0; d < kMaxLevels; ++d) {
+            c.lo_word[d] = c.n_words[d] = c.word_off[d] = 0;
+            if (d >= L || !used[d]) continue;
+            c.n_words[d] = span_words(d, clo[d], chi[d], &c.lo_word[d]);
+            c.word_off[d] = off;
+            off += a256(8 * c.n_words[d]);
+        }
+        for (size_t q = k; q < j; ++q) {
+            Tile tl = p.tiles[q];
+            const uint64_t nb = uint64_t(last - int(tl.level) + 1);
+            c.codes.insert(c.codes.end(), p.codes.begin() + int64_t(tl.code_off),
+                           p.codes.begin() + int64_t(tl.code_off + tl.count));
+            c.bases.insert(c.bases.end(), p.tile_bases.begin() + int64_t(tl.base_off),
+                           p.tile_bases.begin() + int64_t(tl.base_off + nb));
+            tl.code_off = uint32_t(c.codes.size() - tl.count);
+            tl.base_off = uint32_t(c.bases.size() - nb);
+            c.tiles.push_back(tl);
+        }
+        c.tiles_off = off;
+        off += a256(sizeof(Tile) * c.tiles.size());
+        c.codes_off = off;
+        off += a256(8 * c.codes.size());
+        c.bases_off = off;
+        off += a256(4 * c.bases.size());
+        c.bytes = off;
+        s->max_bytes = std::max(s->max_bytes, off);
+        s->staged_bytes += off;
+        s->chunks.push_back(std::move(c));
+        k = j;
+    }
+    *out = s.release();
+    return K2_OK;
+}
+
+k2_status k2_stream_info(const k2_stream *s, uint64_t *n_chunks, uint64_t *max_chunk_bytes,
+                         uint64_t *staged_bytes) {
+    if (!s) return K2_E_INVALID_ARG;
+    if (n_chunks) *n_chunks = s->chunks.size();
+    if (max_chunk_bytes) *max_chunk_bytes = s->max_bytes;
+    if (staged_bytes) *staged_bytes = s->staged_bytes;
+    return K2_OK;
+}
+
+k2_status k2_stream_chunk(const k2_stream *s, uint64_t chunk, uint64_t *first_tile, uint64_t *end_tile,
+                          uint64_t *lo_words, uint64_t *n_words, uint32_t n_levels) {
+    if (!s || chunk >= s->chunks.size() || !first_tile || !end_tile) return K2_E_INVALID_ARG;
+    const k2_stream::Chunk &c = s->chunks[chunk];
+    *first_tile = c.t0;
+    *end_tile = c.t1;
+    for (uint32_t d = 0; d < n_levels && d < uint32_t(kMaxLevels); ++d) {
+        if (lo_words) lo_words[d] = c.lo_word[d];
+        if (n_words) n_words[d] = c.n_words[d];
+    }
+    return K2_OK;
+}
+
+k2_status k2_stream_spmv(k2_stream *s, k2_direction direction, k2_semiring semiring, uint32_t batch,
+                         int32_t flags, const void *d_x, void *d_y, void *d_staging, uint64_t staging_bytes,
+                         void *stream) {
+    if (!s || !d_x || !d_y || batch == 0) return K2_E_INVALID_ARG;
+    if (int(direction) != K2_RIGHT && int(direction) != K2_LEFT) return K2_E_INVALID_ARG;
+    if (int(semiring) < 0 || int(semiring) > 3) return K2_E_INVALID_ARG;
+    if ((flags & ~int32_t(K2_SPMV_ACCUMULATE)) != 0) return K2_E_INVALID_ARG;
+    if (!s->chunks.empty() && (!d_staging || staging_bytes < s->max_bytes ||
+                               (reinterpret_cast<uintptr_t>(d_staging) & 255)))
+        return K2_E_INVALID_ARG;
+    const HostTree &t = s->tree->t;
+    const uint64_t n_out = direction == K2_RIGHT ? t.n_rows : t.n_cols;
+    const uint64_t n_in = direction == K2_RIGHT ? t.n_cols : t.n_rows;
+    {   // x and y must not overlap
+        const char *xb = static_cast<const char *>(d_x), *yb = static_cast<const char *>(d_y);
+        const uint64_t xl = n_in * batch * 4, yl = n_out * batch * 4;
+        if (xb < yb + yl && yb < xb + xl) return K2_E_INVALID_ARG;
+    }
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int e = hipSuccess;
+    if (!(flags & K2_SPMV_ACCUMULATE)) {
+        e = launch_fill(d_y, n_out * batch, semiring == K2_TROPICAL_F32 ? 0x7F800000u : 0u, stream);
+        if (e != hipSuccess) {
+            set_hip_error(e, "fill");
+            return K2_E_HIP;
+        }
+    }
+    char *stage = static_cast<char *>(d_staging);
+    // stream order: a chunk's copies wait for the kernel of the chunk before
+    for (const k2_stream::Chunk &c : s->chunks) {
+        DevTree dv{};
+        dv.levels = t.levels;
+        dv.top_level = 0;
+        for (int d = 0; d < t.levels; ++d) {
+            dv.nodes[d] = uint32_t(t.nodes[d]);
+            dv.dir[d] = nullptr;
+            dv.words[d] = nullptr;
+            if (!c.n_words[d]) continue;
+            HIP_TRY(hipMemcpyAsync(stage + c.word_off[d], t.words[d].data() + c.lo_word[d], 8 * c.n_words[d],
+                                   hipMemcpyHostToDevice, st),
+                    "stream level words");
+            // offset so that the kernels' absolute word indexes land in the staged range
+            dv.words[d] = reinterpret_cast<const uint64_t *>(stage + c.word_off[d]) - c.lo_word[d];
+        }
+        HIP_TRY(hipMemcpyAsync(stage + c.tiles_off, c.tiles.data(), sizeof(Tile) * c.tiles.size(),
+                               hipMemcpyHostToDevice, st),
+                "stream tiles");
+        HIP_TRY(hipMemcpyAsync(stage + c.codes_off, c.codes.data(), 8 * c.codes.size(), hipMemcpyHostToDevice, st),
+                "stream codes");
+        HIP_TRY(hipMemcpyAsync(stage + c.bases_off, c.bases.data(), 4 * c.bases.size(), hipMemcpyHostToDevice, st),
+                "stream offsets");
+        e = launch_descent_tiles(dv, reinterpret_cast<const Tile *>(stage + c.tiles_off), c.tiles.size(),
+                                 reinterpret_cast<const uint64_t *>(stage + c.codes_off),
+                                 reinterpret_cast<const uint32_t *>(stage + c.bases_off), s->tile_nodes, t.n_rows,
+                                 t.n_cols, s->row_runs, direction, semiring, batch, d_x, d_y, stream);
+        if (e != hipSuccess) {
+            set_hip_error(e, "stream spmv");
+            return K2_E_HIP;
+        }
+    }
+    return K2_OK;
+}
+
+void k2_stream_destroy(k2_stream *s) { delete s; }
 
 const char *k2_status_string(k2_status status) {
     switch (status) {

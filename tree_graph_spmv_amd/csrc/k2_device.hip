@@ -1276,26 +1276,33 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     return hipGetLastError();
 }
 
+// Descent tiles, depth first, a workgroup each; LDS: the frontier's two
+// levels of 'cap' codes.
+template <class SR, int DIR, bool EMIT, class Off>
+int run_tiles(const DevTree &t, const Tile *tiles, size_t n, const uint64_t *codes, const uint32_t *bases,
+              uint32_t cap, const void *x, void *y, uint32_t B, uint64_t *emit, bool row_runs, hipStream_t st) {
+    using T = typename SR::T;
+    if (n == 0) return hipSuccess;
+    auto k = descent_kernel<SR, DIR, EMIT, Off>;
+    const size_t lds = size_t(2) * cap * sizeof(uint64_t);
+    int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k, dim3(grid_for(n)), dim3(kThreads), lds, st, t, tiles, uint32_t(n), codes, cap,
+                       static_cast<const T *>(x), static_cast<T *>(y), B, lanes_per_node(B, DIR), emit, bases,
+                       row_runs ? 1 : 0);
+    return hipGetLastError();
+}
+
 template <class SR, int DIR, bool EMIT, class Off = uint32_t>
 int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *emit,
                 hipStream_t st) {
     using T = typename SR::T;
     const uint32_t VL = lanes_per_node(B, DIR);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
-    // every descent tile, depth first, a workgroup each; LDS: the frontier's
-    // two levels of tile_nodes codes
     const Plan &p = m.plan;
     auto descent = [&]() -> int {
-        const size_t n = p.tiles.size();
-        if (n == 0) return hipSuccess;
-        auto k = descent_kernel<SR, DIR, EMIT, Off>;
-        const size_t lds = size_t(2) * p.tile_nodes * sizeof(uint64_t);
-        int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3(grid_for(n)), dim3(kThreads), lds, st, m.dev, m.d_tiles, uint32_t(n), m.d_codes,
-                           p.tile_nodes, static_cast<const T *>(x), static_cast<T *>(y), B, VL, emit, m.d_bases,
-                           p.row_runs ? 1 : 0);
-        return hipGetLastError();
+        return run_tiles<SR, DIR, EMIT, Off>(m.dev, m.d_tiles, p.tiles.size(), m.d_codes, m.d_bases, p.tile_nodes,
+                                             x, y, B, emit, p.row_runs, st);
     };
     if (EMIT) return descent();
     // the rest tiles, a wave each
@@ -1401,6 +1408,47 @@ int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const
     if (emit_codes) return run_descent<BooleanU32, K2_RIGHT, true>(m, 1, nullptr, nullptr, emit_codes, st);
     return dir == K2_RIGHT ? dispatch_descent<K2_RIGHT>(m, semiring, batch, x, y, st)
                            : dispatch_descent<K2_LEFT>(m, semiring, batch, x, y, st);
+}
+
+template <int DIR>
+int dispatch_tiles(const DevTree &t, const Tile *tiles, size_t n, const uint64_t *codes, const uint32_t *bases,
+                   uint32_t cap, bool narrow, bool row_runs, int semiring, uint32_t B, const void *x, void *y,
+                   hipStream_t st) {
+    switch (semiring) {
+    case K2_PLUS_TIMES_F32:
+        return narrow ? run_tiles<PlusTimes, DIR, false, uint32_t>(t, tiles, n, codes, bases, cap, x, y, B, nullptr,
+                                                                   row_runs, st)
+                      : run_tiles<PlusTimes, DIR, false, uint64_t>(t, tiles, n, codes, bases, cap, x, y, B, nullptr,
+                                                                   row_runs, st);
+    case K2_BOOLEAN_F32:
+        return narrow ? run_tiles<BooleanF32, DIR, false, uint32_t>(t, tiles, n, codes, bases, cap, x, y, B,
+                                                                    nullptr, row_runs, st)
+                      : run_tiles<BooleanF32, DIR, false, uint64_t>(t, tiles, n, codes, bases, cap, x, y, B,
+                                                                    nullptr, row_runs, st);
+    case K2_BOOLEAN_U32X32:
+        return narrow ? run_tiles<BooleanU32, DIR, false, uint32_t>(t, tiles, n, codes, bases, cap, x, y, B,
+                                                                    nullptr, row_runs, st)
+                      : run_tiles<BooleanU32, DIR, false, uint64_t>(t, tiles, n, codes, bases, cap, x, y, B,
+                                                                    nullptr, row_runs, st);
+    case K2_TROPICAL_F32:
+        return narrow ? run_tiles<Tropical, DIR, false, uint32_t>(t, tiles, n, codes, bases, cap, x, y, B, nullptr,
+                                                                  row_runs, st)
+                      : run_tiles<Tropical, DIR, false, uint64_t>(t, tiles, n, codes, bases, cap, x, y, B, nullptr,
+                                                                  row_runs, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+int launch_descent_tiles(const DevTree &t, const Tile *tiles, size_t n_tiles, const uint64_t *codes,
+                         const uint32_t *bases, uint32_t cap, uint32_t n_rows, uint32_t n_cols, bool row_runs,
+                         int dir, int semiring, uint32_t batch, const void *x, void *y, void *stream) {
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const bool narrow = uint64_t(n_rows > n_cols ? n_rows : n_cols) * batch <= 0xFFFFFFFFull;
+    return dir == K2_RIGHT
+               ? dispatch_tiles<K2_RIGHT>(t, tiles, n_tiles, codes, bases, cap, narrow, row_runs, semiring, batch,
+                                          x, y, st)
+               : dispatch_tiles<K2_LEFT>(t, tiles, n_tiles, codes, bases, cap, narrow, row_runs, semiring, batch, x,
+                                         y, st);
 }
 
 static uint32_t stray_grid(uint32_t n_segs) {

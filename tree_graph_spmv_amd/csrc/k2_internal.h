@@ -192,6 +192,11 @@ int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, uint32_t *planes, int
                     uint32_t W, uint32_t S, int32_t level, unsigned long long *count, void *stream);
 int launch_bfs_dist(int32_t *dist, const uint32_t *V, const uint32_t *planes, uint64_t n_words, uint32_t W,
                     uint32_t S, void *stream);
+// Descent tiles over a tree given by 't' alone (a streamed chunk: its level
+// words staged on the device), with scan offsets 'bases'.
+int launch_descent_tiles(const DevTree &t, const Tile *tiles, size_t n_tiles, const uint64_t *codes,
+                         const uint32_t *bases, uint32_t cap, uint32_t n_rows, uint32_t n_cols, bool row_runs,
+                         int dir, int semiring, uint32_t batch, const void *x, void *y, void *stream);
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
                    uint64_t *emit_codes, void *stream);
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
