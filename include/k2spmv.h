@@ -358,20 +358,24 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
    device memory): the tree stays in host memory and each product streams it
    through a caller-owned device staging buffer, chunk by chunk.
 
-   k2_stream_create (host only, no HIP call) plans the depth-first descent
-   tiles of 'tree' with 'opts' (tile_nodes and host_top_max are used; the
-   tiles always carry planned scan offsets; no cached level, no windows) and
-   cuts them, in order, into chunks of consecutive tiles whose staged data
-   fits staging_bytes: per level the span of node words the chunk's tiles
-   reach (plus one word), then its tiles, start codes and scan offsets, each
-   part 256-byte aligned.  'tree' must outlive the stream.  Errors:
-   K2_E_INVALID_ARG, K2_E_ARENA_TOO_SMALL (one tile does not fit),
-   K2_E_HOST_OOM. */
+   k2_stream_create plans the depth-first descent tiles of 'tree' with
+   'opts' (tile_nodes and host_top_max are used; the tiles always carry
+   planned scan offsets; no cached level, no windows) and cuts them, in
+   order, into chunks of consecutive tiles whose staged data fits half of
+   staging_bytes (products alternate between the two halves, copying one
+   chunk while the previous one is descended): per level the span of node
+   words the chunk's tiles reach (plus one word), then its tiles, start
+   codes and scan offsets, each part 256-byte aligned.  It also keeps a
+   page-locked host copy of the tree's words and the chunks' metadata
+   (hipHostMalloc; the size of the tree) for asynchronous copies; where that
+   allocation fails, products copy from the tree itself.  'tree' must
+   outlive the stream.  Errors: K2_E_INVALID_ARG, K2_E_ARENA_TOO_SMALL (one
+   tile does not fit half the staging), K2_E_HOST_OOM. */
 k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64_t staging_bytes,
                            k2_stream **out);
 
-/* Chunk count, the largest chunk's staged bytes (the staging buffer a
-   product needs) and the bytes one product copies to the device. */
+/* Chunk count, the largest chunk's staged bytes (a product needs a staging
+   buffer of twice this) and the bytes one product copies to the device. */
 k2_status k2_stream_info(const k2_stream *stream_plan, uint64_t *n_chunks, uint64_t *max_chunk_bytes,
                          uint64_t *staged_bytes);
 
@@ -385,9 +389,12 @@ k2_status k2_stream_chunk(const k2_stream *stream_plan, uint64_t chunk, uint64_t
 /* One product as k2_spmv (direction, semiring, batch, device x and y, flags
    0 or K2_SPMV_ACCUMULATE), tree-only, with the tree streamed: per chunk its
    level words, tiles, codes and offsets are copied from host memory into
-   d_staging (256-byte aligned, at least max_chunk_bytes) on 'stream' and the
-   chunk's tiles descended from there; stream order keeps a chunk's copies
-   behind the kernel of the chunk before.  Asynchronous like k2_spmv.
+   one half of d_staging (256-byte aligned, at least 2 max_chunk_bytes) on a
+   copy stream of the library's, and the chunk's tiles are descended from
+   there on 'stream'; events keep a half's copies behind the last kernel that
+   read it and each kernel behind its copies, so copies overlap the kernel of
+   the chunk before.  Asynchronous like k2_spmv; products of one stream plan
+   must not run concurrently.
    Errors: K2_E_INVALID_ARG (null, small or unaligned staging, overlapping
    x and y), K2_E_HIP. */
 k2_status k2_stream_spmv(k2_stream *stream_plan, k2_direction direction, k2_semiring semiring,

@@ -209,7 +209,7 @@ def test_streamed(dev):
                "boolean": np.maximum, "boolean_u32": np.bitwise_or, "tropical": np.minimum}
     for staging in (1 << 15, 1 << 24):
         s = k2.Streamed(tree, staging)
-        assert s.max_chunk_bytes <= staging
+        assert 2 * s.max_chunk_bytes <= staging
         if staging == 1 << 15:
             assert s.n_chunks > 4
         buf = s.staging(dev)

@@ -398,9 +398,9 @@ class Streamed:
         return a.value, b.value, lo, nw
 
     def staging(self, device="cuda"):
-        """A device staging buffer that fits every chunk."""
+        """A device staging buffer for products: two halves of the largest chunk."""
         import torch
-        return torch.empty(max(self.max_chunk_bytes, 256), dtype=torch.uint8, device=device)
+        return torch.empty(max(2 * self.max_chunk_bytes, 256), dtype=torch.uint8, device=device)
 
     def spmv(self, x, y=None, direction="right", semiring="plus_times", batch=1, accumulate=False,
              staging=None, stream=None):

@@ -42,6 +42,20 @@ struct k2_stream {
     bool row_runs = false;
     std::vector<Chunk> chunks;
     uint64_t max_bytes = 0, staged_bytes = 0;
+    // pinned host copy: every level's words at pin_words[d], then each
+    // chunk's tiles, codes and offsets laid out as in the staging buffer
+    char *pinned = nullptr;
+    uint64_t pin_words[k2::kMaxLevels] = {};
+    std::vector<uint64_t> pin_meta;   // per chunk, offset of its metadata block
+    // copies run on their own stream, one staging half ahead of the kernels
+    hipStream_t copy_stream = nullptr;
+    hipEvent_t copied[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr}, start = nullptr;
+    ~k2_stream() {
+        for (hipEvent_t e : {copied[0], copied[1], done[0], done[1], start})
+            if (e) (void)hipEventDestroy(e);
+        if (copy_stream) (void)hipStreamDestroy(copy_stream);
+        if (pinned) (void)hipHostFree(pinned);
+    }
 };
 
 namespace k2 {
@@ -828,7 +842,7 @@ k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64
             }
             const uint64_t nc = ncodes + tl.count, nb = nbases + uint64_t(last - int(tl.level) + 1);
             bytes += a256(sizeof(Tile) * (j - k + 1)) + a256(8 * nc) + a256(4 * nb);
-            if (bytes > staging_bytes) break;
+            if (bytes > staging_bytes / 2) break;   // two halves: copies run one chunk ahead
             for (int d = int(tl.level); d < L; ++d) {
                 clo[d] = used[d] ? std::min(clo[d], tlo[d]) : tlo[d];
                 chi[d] = used[d] ? std::max(chi[d], thi[d]) : thi[d];
@@ -872,6 +886,30 @@ k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64
         s->chunks.push_back(std::move(c));
         k = j;
     }
+    // the pinned host copy the products copy from (asynchronous copies need
+    // page-locked memory); without it they copy from the tree's own words
+    uint64_t pin_bytes = 0;
+    for (int d = 0; d < L; ++d) {
+        s->pin_words[d] = pin_bytes;
+        pin_bytes += a256(8 * t.words[d].size());
+    }
+    for (const k2_stream::Chunk &c : s->chunks) {
+        s->pin_meta.push_back(pin_bytes);
+        pin_bytes += c.bytes - c.tiles_off;
+    }
+    void *pin = nullptr;
+    if (hipHostMalloc(&pin, pin_bytes, hipHostMallocDefault) == hipSuccess && pin) {
+        s->pinned = static_cast<char *>(pin);
+        for (int d = 0; d < L; ++d)
+            std::memcpy(s->pinned + s->pin_words[d], t.words[d].data(), 8 * t.words[d].size());
+        for (size_t q = 0; q < s->chunks.size(); ++q) {
+            const k2_stream::Chunk &c = s->chunks[q];
+            char *m = s->pinned + s->pin_meta[q];
+            std::memcpy(m, c.tiles.data(), sizeof(Tile) * c.tiles.size());
+            std::memcpy(m + (c.codes_off - c.tiles_off), c.codes.data(), 8 * c.codes.size());
+            std::memcpy(m + (c.bases_off - c.tiles_off), c.bases.data(), 4 * c.bases.size());
+        }
+    }
     *out = s.release();
     return K2_OK;
 }
@@ -905,7 +943,7 @@ k2_status k2_stream_spmv(k2_stream *s, k2_direction direction, k2_semiring semir
     if (int(direction) != K2_RIGHT && int(direction) != K2_LEFT) return K2_E_INVALID_ARG;
     if (int(semiring) < 0 || int(semiring) > 3) return K2_E_INVALID_ARG;
     if ((flags & ~int32_t(K2_SPMV_ACCUMULATE)) != 0) return K2_E_INVALID_ARG;
-    if (!s->chunks.empty() && (!d_staging || staging_bytes < s->max_bytes ||
+    if (!s->chunks.empty() && (!d_staging || staging_bytes < 2 * s->max_bytes ||
                                (reinterpret_cast<uintptr_t>(d_staging) & 255)))
         return K2_E_INVALID_ARG;
     const HostTree &t = s->tree->t;
@@ -925,38 +963,62 @@ k2_status k2_stream_spmv(k2_stream *s, k2_direction direction, k2_semiring semir
             return K2_E_HIP;
         }
     }
+    if (s->chunks.empty()) return K2_OK;
+    if (!s->copy_stream) {
+        HIP_TRY(hipStreamCreateWithFlags(&s->copy_stream, hipStreamNonBlocking), "stream copies");
+        for (hipEvent_t *e : {&s->copied[0], &s->copied[1], &s->done[0], &s->done[1], &s->start})
+            HIP_TRY(hipEventCreateWithFlags(e, hipEventDisableTiming), "stream events");
+    }
+    // the copies start after what the caller queued before this product
+    HIP_TRY(hipEventRecord(s->start, st), "stream events");
+    HIP_TRY(hipStreamWaitEvent(s->copy_stream, s->start, 0), "stream events");
     char *stage = static_cast<char *>(d_staging);
-    // stream order: a chunk's copies wait for the kernel of the chunk before
-    for (const k2_stream::Chunk &c : s->chunks) {
+    for (size_t q = 0; q < s->chunks.size(); ++q) {
+        const k2_stream::Chunk &c = s->chunks[q];
+        const int h = int(q & 1);
+        char *half = stage + uint64_t(h) * s->max_bytes;
+        // the half's last kernel (this product's or an earlier one's) is done
+        HIP_TRY(hipStreamWaitEvent(s->copy_stream, s->done[h], 0), "stream events");
         DevTree dv{};
         dv.levels = t.levels;
         dv.top_level = 0;
         for (int d = 0; d < t.levels; ++d) {
             dv.nodes[d] = uint32_t(t.nodes[d]);
-            dv.dir[d] = nullptr;
-            dv.words[d] = nullptr;
             if (!c.n_words[d]) continue;
-            HIP_TRY(hipMemcpyAsync(stage + c.word_off[d], t.words[d].data() + c.lo_word[d], 8 * c.n_words[d],
-                                   hipMemcpyHostToDevice, st),
+            const void *src = s->pinned ? static_cast<const void *>(s->pinned + s->pin_words[d] + 8 * c.lo_word[d])
+                                        : static_cast<const void *>(t.words[d].data() + c.lo_word[d]);
+            HIP_TRY(hipMemcpyAsync(half + c.word_off[d], src, 8 * c.n_words[d], hipMemcpyHostToDevice,
+                                   s->copy_stream),
                     "stream level words");
             // offset so that the kernels' absolute word indexes land in the staged range
-            dv.words[d] = reinterpret_cast<const uint64_t *>(stage + c.word_off[d]) - c.lo_word[d];
+            dv.words[d] = reinterpret_cast<const uint64_t *>(half + c.word_off[d]) - c.lo_word[d];
         }
-        HIP_TRY(hipMemcpyAsync(stage + c.tiles_off, c.tiles.data(), sizeof(Tile) * c.tiles.size(),
-                               hipMemcpyHostToDevice, st),
-                "stream tiles");
-        HIP_TRY(hipMemcpyAsync(stage + c.codes_off, c.codes.data(), 8 * c.codes.size(), hipMemcpyHostToDevice, st),
-                "stream codes");
-        HIP_TRY(hipMemcpyAsync(stage + c.bases_off, c.bases.data(), 4 * c.bases.size(), hipMemcpyHostToDevice, st),
-                "stream offsets");
-        e = launch_descent_tiles(dv, reinterpret_cast<const Tile *>(stage + c.tiles_off), c.tiles.size(),
-                                 reinterpret_cast<const uint64_t *>(stage + c.codes_off),
-                                 reinterpret_cast<const uint32_t *>(stage + c.bases_off), s->tile_nodes, t.n_rows,
+        if (s->pinned) {
+            HIP_TRY(hipMemcpyAsync(half + c.tiles_off, s->pinned + s->pin_meta[q], c.bytes - c.tiles_off,
+                                   hipMemcpyHostToDevice, s->copy_stream),
+                    "stream tiles");
+        } else {
+            HIP_TRY(hipMemcpyAsync(half + c.tiles_off, c.tiles.data(), sizeof(Tile) * c.tiles.size(),
+                                   hipMemcpyHostToDevice, s->copy_stream),
+                    "stream tiles");
+            HIP_TRY(hipMemcpyAsync(half + c.codes_off, c.codes.data(), 8 * c.codes.size(), hipMemcpyHostToDevice,
+                                   s->copy_stream),
+                    "stream codes");
+            HIP_TRY(hipMemcpyAsync(half + c.bases_off, c.bases.data(), 4 * c.bases.size(), hipMemcpyHostToDevice,
+                                   s->copy_stream),
+                    "stream offsets");
+        }
+        HIP_TRY(hipEventRecord(s->copied[h], s->copy_stream), "stream events");
+        HIP_TRY(hipStreamWaitEvent(st, s->copied[h], 0), "stream events");
+        e = launch_descent_tiles(dv, reinterpret_cast<const Tile *>(half + c.tiles_off), c.tiles.size(),
+                                 reinterpret_cast<const uint64_t *>(half + c.codes_off),
+                                 reinterpret_cast<const uint32_t *>(half + c.bases_off), s->tile_nodes, t.n_rows,
                                  t.n_cols, s->row_runs, direction, semiring, batch, d_x, d_y, stream);
         if (e != hipSuccess) {
             set_hip_error(e, "stream spmv");
             return K2_E_HIP;
         }
+        HIP_TRY(hipEventRecord(s->done[h], st), "stream events");
     }
     return K2_OK;
 }
