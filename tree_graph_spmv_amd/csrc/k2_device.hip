@@ -1163,6 +1163,44 @@ __global__ __launch_bounds__(kThreads) void bfs_dist_kernel(int32_t *__restrict_
     }
 }
 
+// bfs_dist_kernel when the sources fill whole words (S = 32 W) and dist is
+// 16-byte aligned: word e's entries are dist[32 e .. 32 e + 32), so thread q
+// writes entries 4 q .. 4 q + 3 of word q / 8 with one 16-byte store and a
+// wave writes 1 KB of consecutive entries; a thread takes two such chunks a
+// grid apart per round, their loads issued together.
+__global__ __launch_bounds__(kThreads) void bfs_dist32_kernel(int32_t *__restrict__ dist,
+                                                              const uint32_t *__restrict__ V,
+                                                              const uint32_t *__restrict__ planes,
+                                                              uint64_t n_words) {
+    const uint64_t grid = uint64_t(gridDim.x) * kThreads, n = n_words * 8u;
+    for (uint64_t q0 = uint64_t(blockIdx.x) * kThreads + threadIdx.x; q0 < n; q0 += 2u * grid) {
+        uint32_t vw[2], pl[2][kBfsPlanes];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint64_t q = q0 + uint64_t(k) * grid;
+            const uint64_t e = (q < n ? q : q0) >> 3;
+            const uint32_t b0 = uint32_t(q & 7u) * 4u;
+            vw[k] = V[e] >> b0;
+#pragma unroll
+            for (uint32_t p = 0; p < kBfsPlanes; ++p) pl[k][p] = planes[p * n_words + e] >> b0;
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint64_t q = q0 + uint64_t(k) * grid;
+            if (q >= n) break;
+            int32_t d[4];
+#pragma unroll
+            for (uint32_t b = 0; b < 4u; ++b) {
+                int32_t l = 0;
+#pragma unroll
+                for (uint32_t p = 0; p < kBfsPlanes; ++p) l |= int32_t((pl[k][p] >> b) & 1u) << p;
+                d[b] = ((vw[k] >> b) & 1u) ? l : -1;
+            }
+            reinterpret_cast<int4 *>(dist)[q] = make_int4(d[0], d[1], d[2], d[3]);
+        }
+    }
+}
+
 // ------------------------------------------------------------- strays
 
 // Grouping the strays by band when a matrix is created: one wave per stray
@@ -1506,7 +1544,13 @@ int launch_bfs_mark(uint32_t *y, uint32_t *V, uint32_t *F, uint32_t *planes, int
 
 int launch_bfs_dist(int32_t *dist, const uint32_t *V, const uint32_t *planes, uint64_t n_words, uint32_t W,
                     uint32_t S, void *stream) {
-    const int vec4 = (S % 4u == 0u) && (reinterpret_cast<uintptr_t>(dist) % 16u == 0u);
+    const bool aligned = reinterpret_cast<uintptr_t>(dist) % 16u == 0u;
+    if (aligned && S == 32u * W) {
+        hipLaunchKernelGGL(bfs_dist32_kernel, dim3(small_grid(n_words * 8u)), dim3(kThreads), 0,
+                           static_cast<hipStream_t>(stream), dist, V, planes, n_words);
+        return hipGetLastError();
+    }
+    const int vec4 = (S % 4u == 0u) && aligned;
     hipLaunchKernelGGL(bfs_dist_kernel, dim3(small_grid(n_words)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), dist, V, planes, n_words, W, S, vec4);
     return hipGetLastError();
