@@ -10,6 +10,8 @@
   levels, directories and cached codes.
 * Errors: out-of-range edges, bad options.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -487,3 +489,28 @@ def test_stream_chunks(case):
                     if d == L - 1:   # the next leaf dword of the last leaf
                         assert w1 == (nodes[d] + 15) // 16 or (x1 - 1) // 16 + 1 < w1
         assert pos == len(tiles), (name, staging)
+
+
+def test_stream_arguments():
+    """k2_stream_spmv refuses bad arguments before touching the device:
+    a staging buffer under two chunks, an unaligned one, overlapping x and
+    y, an unknown direction, semiring or flag."""
+    rows, cols, n = synth.workload_edges("rmat_s12_e32k")
+    t = k2.Tree(rows, cols, n, n)
+    s = k2.Streamed(t, 1 << 16)
+    lib = k2.lib()
+    VP = ctypes.c_void_p
+    x, y, stage = VP(1 << 20), VP(1 << 30), VP(1 << 34)
+    need = 2 * s.max_chunk_bytes
+
+    def call(direction=k2.K2_RIGHT, semiring=0, batch=1, flags=0, xp=x, yp=y, sp=stage, sb=need):
+        return lib.k2_stream_spmv(s._h, direction, semiring, batch, flags, xp, yp, sp, sb, None)
+    assert call(sb=need - 256) == k2.K2_E_INVALID_ARG
+    assert call(sp=VP((1 << 34) + 64)) == k2.K2_E_INVALID_ARG
+    assert call(yp=VP((1 << 20) + 64)) == k2.K2_E_INVALID_ARG
+    assert call(direction=7) == k2.K2_E_INVALID_ARG
+    assert call(semiring=9) == k2.K2_E_INVALID_ARG
+    assert call(flags=0x2) == k2.K2_E_INVALID_ARG
+    assert call(batch=0) == k2.K2_E_INVALID_ARG
+    with pytest.raises(k2.K2Error):
+        k2.Streamed(t, 1 << 10)
