@@ -841,8 +841,9 @@ __device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32
 }
 
 // Tree-only rest tiles (Sec. 3.4 tiles outside the band groups, in
-// output-block order): each wave takes tiles w, w + 4, ... of the list and
-// descends each on its own as band_kernel does, with frontiers of at most
+// output-block order): wave w of workgroup g takes tile 4 g + w of the list,
+// then the tiles a whole grid of waves further on, and descends each on its
+// own as band_kernel does, with frontiers of at most
 // 'cap' absolute Morton codes per level in the wave's LDS, skipping the
 // last-internal-level ranges listed for the tile (skips + win_row, win_col
 // of them; their fan-outs still count towards the leaf offsets).  Outputs go
