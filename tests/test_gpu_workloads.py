@@ -105,9 +105,9 @@ def test_symrmat_s24_e256m_boolean(dev):
 
 def test_web_n27_d9_batch8(dev):
     """Web-like 2^27, ~1.2G edges, plus-times over 8 vectors, last internal
-    level cached (the benchmark's configuration) and tree-only: sampled
-    outputs within the fp32 tolerance, right and left; the all-ones product
-    gives out-degrees."""
+    level cached (the benchmark's configuration), tree-only and streamed
+    from host memory: sampled outputs within the fp32 tolerance, right and
+    left; the all-ones product gives out-degrees."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("web_n27_d9")
     tree = k2.Tree(rows, cols, n, n)
@@ -121,6 +121,16 @@ def test_web_n27_d9_batch8(dev):
             check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction} {mode}",
                           k=3000, seed=3)
             del y
+    # the tree streamed from host memory through 256 MB of staging (out of core)
+    st = k2.Streamed(tree, 256 << 20)
+    buf = st.staging(dev)
+    for direction in ("right", "left"):
+        y = st.spmv(xd, direction=direction, batch=8, staging=buf)
+        torch.cuda.synchronize()
+        check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction} streamed",
+                      k=3000, seed=5)
+        del y
+    del st, buf
     ones = torch.ones(n, device=dev)
     deg = m.spmv(ones, direction="right").cpu().numpy()
     idx = sample_idx(n, 3000, 4)
