@@ -317,8 +317,11 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
     using T = typename SR::T;
     // no zero tests where the semiring allows (window updates only)
     constexpr bool kUnchecked = kWin && SR::kWindowUnchecked;
+    // plus-times window outputs o are byte offsets, the others element indexes
+    char *const wv = reinterpret_cast<char *>(out) + v * uint32_t(sizeof(T));
     auto apply = [&](Off o, T c) {
-        if constexpr (kWin) SR::lds_atomic(&out[o + v], c);
+        if constexpr (kWin && SR::kTreeBands) SR::lds_atomic(reinterpret_cast<T *>(wv + uint32_t(o)), c);
+        else if constexpr (kWin) SR::lds_atomic(&out[o + v], c);
         else SR::atomic(&out[o + v], c);
     };
     if constexpr (kRuns) {
@@ -416,7 +419,10 @@ __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_
     const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
     // offsets of the block's first cell; a cell adds its in-block offset * B
     const Off xb = Off((DIR == K2_RIGHT) ? col0 : row0) * B;
-    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * B;
+    // plus-times window outputs as byte offsets into the window (one add
+    // per update; measured slower for the packed Boolean semiring)
+    const uint32_t yB = (SR::kTreeBands && w.win) ? B * uint32_t(sizeof(typename SR::T)) : B;
+    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * yB;
     constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
     constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
     for (uint32_t round = 0; round < total; round += R) {
@@ -427,7 +433,7 @@ __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_
             m &= m - 1u;
             if (pos >= round) {
                 wc->xo[pos - round] = xb + __umul24((kInTable >> sh) & 3u, B);
-                wc->yo[pos - round] = yb + __umul24((kOutTable >> sh) & 3u, B);
+                wc->yo[pos - round] = yb + __umul24((kOutTable >> sh) & 3u, yB);
             }
             ++pos;
         }
@@ -455,7 +461,10 @@ __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_
     const uint32_t pos0 = wave_scan(__popc(cells), total);
     const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
     const Off xb = Off((DIR == K2_RIGHT) ? col0 : row0) * B;
-    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * B;
+    // plus-times window outputs as byte offsets into the window (one add
+    // per update; measured slower for the packed Boolean semiring)
+    const uint32_t yB = (SR::kTreeBands && w.win) ? B * uint32_t(sizeof(typename SR::T)) : B;
+    const Off yb = Off(((DIR == K2_RIGHT) ? row0 : col0) - obase) * yB;
     constexpr uint32_t kInTable = (DIR == K2_RIGHT) ? kCellColTable : kCellRowTable;
     constexpr uint32_t kOutTable = (DIR == K2_RIGHT) ? kCellRowTable : kCellColTable;
     const uint32_t G = 64 / VL;
@@ -470,7 +479,7 @@ __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_
             if (pos >= done) {
                 const uint32_t at = (head + fill + (pos - done)) & (R - 1u);
                 wc->xo[at] = xb + __umul24((kInTable >> sh) & 3u, B);
-                wc->yo[at] = yb + __umul24((kOutTable >> sh) & 3u, B);
+                wc->yo[at] = yb + __umul24((kOutTable >> sh) & 3u, yB);
             }
             ++pos;
         }
