@@ -270,7 +270,7 @@ __device__ __forceinline__ void wave_lds_sync() {
 // through the buffer kRound at a time (one round in the common case).  Off is
 // uint32_t when every offset fits, else uint64_t (half as many per round).
 template <class Off>
-struct WaveCells {
+struct alignas(16) WaveCells {
     static constexpr uint32_t kRound = 512 / sizeof(Off);
     Off xo[kRound];
     Off yo[kRound];
@@ -372,13 +372,33 @@ __device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t he
         // slots past count repeat cell 'base' for the loads and skip the atomics
         Off xo[kUnroll], yo[kUnroll];
         bool ok[kUnroll];
+        if constexpr (kRuns && sizeof(Off) == 4 && kUnroll == 8) {
+            // a lane group's 8 cells are 8 consecutive slots from a multiple
+            // of 8 (head and k0 both are: the ring advances by whole passes
+            // of G x 8 cells), so they never wrap and load as 16-byte words
+            const uint32_t at = (head + k0) & (R - 8u);   // R - 8: the same value, known aligned
+            const uint4 xa = *reinterpret_cast<const uint4 *>(&wc->xo[at]);
+            const uint4 xb = *reinterpret_cast<const uint4 *>(&wc->xo[at + 4u]);
+            const uint4 ya = *reinterpret_cast<const uint4 *>(&wc->yo[at]);
+            const uint4 yb = *reinterpret_cast<const uint4 *>(&wc->yo[at + 4u]);
+            const Off x0 = wc->xo[(head + base) & (R - 1u)];
+            const uint32_t xs[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
+            const uint32_t ys[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const uint32_t k = k0 + uint32_t(u) * step;
-            ok[u] = k < count;
-            const uint32_t at = (head + (ok[u] ? k : base)) & (R - 1u);
-            xo[u] = wc->xo[at];
-            yo[u] = wc->yo[at];
+            for (int u = 0; u < kUnroll; ++u) {
+                ok[u] = k0 + uint32_t(u) < count;
+                xo[u] = ok[u] ? Off(xs[u]) : x0;
+                yo[u] = Off(ys[u]);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const uint32_t k = k0 + uint32_t(u) * step;
+                ok[u] = k < count;
+                const uint32_t at = (head + (ok[u] ? k : base)) & (R - 1u);
+                xo[u] = wc->xo[at];
+                yo[u] = wc->yo[at];
+            }
         }
         for (uint32_t v = lv; v < B; v += VL) {
             T xv[kUnroll];
