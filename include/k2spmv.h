@@ -132,6 +132,12 @@ typedef struct {
        device (16 bytes per stray node and direction: its block origin and
        its cells, read from its leaves once).  0: sparse tiles.  Default 1. */
     int32_t band_strays;
+    /* Nodes of the last internal level per windowed cached tile (Sec. 3.4's
+       tiles over the cached level, Sec. 3.5).  A band holding more is cut
+       into several tiles that each add their window to y with atomics after
+       the fill; a band of one tile stores its window.  64..2^30.
+       Default 65536. */
+    uint32_t band_tile_nodes;
 } k2_plan_opts;
 
 enum { K2_OFFSETS_AUTO = 0, K2_OFFSETS_DIRECTORY = 1, K2_OFFSETS_SCAN = 2 };
@@ -167,7 +173,10 @@ typedef struct k2_tree k2_tree;
 typedef struct k2_matrix k2_matrix;
 typedef struct k2_stream k2_stream;
 
-/* Fill 'opts' with the defaults above. */
+/* Fill 'opts' with the defaults above: the tile size and host top of the
+   tiled descent (Sec. 3.4), the offset source (Sec. 3.2) and the settings the
+   ablation of Sec. 5.5 varies, at the values measured best on gfx950.
+   Errors: K2_E_INVALID_ARG (null). */
 k2_status k2_plan_defaults(k2_plan_opts *opts);
 
 /* Build the tree of the Boolean matrix whose non-zeros are the pairs
@@ -181,12 +190,23 @@ k2_status k2_plan_defaults(k2_plan_opts *opts);
 k2_status k2_build(const uint32_t *rows, const uint32_t *cols, uint64_t n_edges,
                    uint32_t n_rows, uint32_t n_cols, uint32_t n_threads, k2_tree **out);
 
+/* Release a tree built by k2_build (null is ignored).  A tree is built once
+   and serves any number of products (Sec. 4 and Sec. 5.1: compress once,
+   multiply many times); a matrix made from it by k2_matrix_create keeps no
+   pointer to it and may outlive it, a stream plan (k2_stream_create) may
+   not. */
 void k2_tree_free(k2_tree *tree);
 
-/* Sizes of a tree (host). */
+/* Sizes of a tree (host): the dimensions, l with n = 2^l (Sec. 2.1: the
+   matrix padded to n x n), the host-top level d0 the default options give
+   (Sec. 3.4: the deepest level with at most 2^16 nodes, never below l-2),
+   the distinct non-zeros and the node count of all levels (Table 2 reports
+   these sizes per graph).  Errors: K2_E_INVALID_ARG (null). */
 k2_status k2_tree_info(const k2_tree *tree, k2_tree_info_t *out);
 
-/* Node count of every level, nodes[0..levels-1] (host array). */
+/* Node count of every level in level order (Sec. 2.1; the popcount of level
+   d's signatures is the node count of level d+1), nodes[0..levels-1] (host
+   array of 'levels' entries from k2_tree_info).  Errors: K2_E_INVALID_ARG. */
 k2_status k2_tree_level_nodes(const k2_tree *tree, uint64_t *nodes);
 
 /* Canonical export of level 'level' (Sec. 2.1: one signature per nibble, in
@@ -221,7 +241,8 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
 k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t which,
                        uint32_t *top_level, uint64_t *n_tiles, uint64_t *n_aux);
 
-/* The tiles themselves, in the order the kernels take them.
+/* The tiles themselves (Sec. 3.4, Fig. 2: tiles descended depth first), in
+   the order the kernels take them.
    tiles[8k..8k+7] = (first, count, level, code index, window row, window
    column, log2 of the window side or 0xFFFFFFFF for no window, base index).
    With scan offsets a tile's (descent, band or rest tile) first child
@@ -267,12 +288,21 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
 k2_status k2_plan_offsets(const k2_tree *tree, const k2_plan_opts *opts, uint32_t *bases,
                           uint64_t n_bases, uint64_t *n_total);
 
-/* Upload a tree into the caller's device arena (d_arena, arena_bytes >=
-   estimate's arena; 256-byte aligned) on 'stream' and return a matrix handle.
-   The library allocates no device memory; the arena must outlive the matrix.
-   If opts->cache_last_level, the codes of the last internal level are
-   computed on the device here.  The call synchronizes 'stream' before it
-   returns.  Errors: K2_E_INVALID_ARG, K2_E_ARENA_TOO_SMALL, K2_E_HIP. */
+/* Upload a tree into the caller's device arena and return a matrix handle:
+   the levels from the host top down (Sec. 2.1, Sec. 3.4), the offset source
+   (Sec. 3.2: the directory, or the planned prefix sums) and the tile plan,
+   which depend on the tree alone and are made once, before any product
+   (Sec. 3.4).  The device memory is what k2_estimate_device_bytes returned
+   (Sec. 1: known after construction, before any kernel runs): d_arena is a
+   caller-owned device buffer of arena_bytes >= that estimate's arena,
+   256-byte aligned, and must outlive the matrix; the library allocates no
+   device memory.  If opts->cache_last_level, the last internal level's nodes
+   are computed here, once, by a descent on the device and kept as the block
+   coordinates their Morton codes encode (Sec. 3.5: the cached frontier, 8
+   bytes per node).  Runs on 'stream' and synchronizes it before returning.
+   Errors: K2_E_INVALID_ARG (null, bad options, unaligned arena),
+   K2_E_ARENA_TOO_SMALL, K2_E_HOST_OOM, K2_E_HIP (nothing of the matrix is
+   kept; the arena's content is then undefined). */
 k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *d_arena,
                            uint64_t arena_bytes, void *stream, k2_matrix **out);
 
@@ -287,7 +317,8 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
 k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semiring,
                   uint32_t batch, int32_t mode, const void *d_x, void *d_y, void *stream);
 
-/* Kernel timing (HIP events on the product's stream).  While enabled, every
+/* Kernel timing (Sec. 4: products timed on the device between two events),
+   with HIP events on the product's stream.  While enabled, every
    k2_spmv records an event before the fill, between the fill and the main
    kernel, and after the main kernel; k2_matrix_last_timing waits for the
    last product and returns the fill and main-kernel durations in ms (the
@@ -296,16 +327,21 @@ k2_status k2_spmv(k2_matrix *matrix, k2_direction direction, k2_semiring semirin
 k2_status k2_matrix_set_timing(k2_matrix *matrix, int32_t enable);
 k2_status k2_matrix_last_timing(k2_matrix *matrix, float *fill_ms, float *kernel_ms);
 
-/* Release the handle (the arena stays the caller's). */
+/* Release a matrix handle and its host-side plan.  The device arena stays
+   the caller's (Sec. 1: the arena was sized before any kernel ran), and
+   products still queued on a stream must finish first: destroy does not
+   synchronize.  Null is ignored.  Errors: none (K2_OK). */
 k2_status k2_matrix_destroy(k2_matrix *matrix);
 
-/* Description of the plan a matrix uses (host): levels, top level, tile
-   count, whether codes are cached. */
+/* Description of the plan a matrix uses (host): its host-top level d0 and
+   descent tile count (Sec. 3.4), and whether it keeps the cached last
+   internal level (Sec. 3.5).  Errors: K2_E_INVALID_ARG (null). */
 k2_status k2_matrix_info(const k2_matrix *matrix, uint32_t *top_level, uint64_t *n_tiles,
                          int32_t *cached);
 
 /* Copy level 'level' of the device-resident tree back to the host in the
-   export layout of k2_tree_level_words (synchronous; for verification).
+   export layout of k2_tree_level_words (Sec. 2.1: one signature per nibble,
+   level order; synchronous; for verification).
    Levels above the top level are not on the device: K2_E_INVALID_ARG. */
 k2_status k2_matrix_level_words(const k2_matrix *matrix, uint32_t level, uint64_t *words,
                                 uint64_t n_words, void *stream);
@@ -375,18 +411,21 @@ k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64
                            k2_stream **out);
 
 /* Chunk count, the largest chunk's staged bytes (a product needs a staging
-   buffer of twice this) and the bytes one product copies to the device. */
+   buffer of twice this) and the bytes one product copies to the device
+   (Sec. 7; host only).  Errors: K2_E_INVALID_ARG (null). */
 k2_status k2_stream_info(const k2_stream *stream_plan, uint64_t *n_chunks, uint64_t *max_chunk_bytes,
                          uint64_t *staged_bytes);
 
-/* Chunk 'chunk': its tiles [*first_tile, *end_tile) of the plan's descent
+/* Chunk 'chunk' of a stream plan (Sec. 7; host only): its tiles
+   [*first_tile, *end_tile) of the plan's descent
    tiles (k2_plan_tiles which = 0, same options) and, for levels 0 ..
    n_levels-1, the first staged word and the staged word count (0: none).
    Errors: K2_E_INVALID_ARG. */
 k2_status k2_stream_chunk(const k2_stream *stream_plan, uint64_t chunk, uint64_t *first_tile,
                           uint64_t *end_tile, uint64_t *lo_words, uint64_t *n_words, uint32_t n_levels);
 
-/* One product as k2_spmv (direction, semiring, batch, device x and y, flags
+/* One product of Sec. 7 (the tree in host memory, streamed to the device)
+   as k2_spmv (direction, semiring, batch, device x and y, flags
    0 or K2_SPMV_ACCUMULATE), tree-only, with the tree streamed: per chunk its
    level words, tiles, codes and offsets are copied from host memory into
    one half of d_staging (256-byte aligned, at least 2 max_chunk_bytes) on a
@@ -401,11 +440,19 @@ k2_status k2_stream_spmv(k2_stream *stream_plan, k2_direction direction, k2_semi
                          uint32_t batch, int32_t flags, const void *d_x, void *d_y, void *d_staging,
                          uint64_t staging_bytes, void *stream);
 
+/* Release a stream plan of Sec. 7 and its page-locked host copy (null is
+   ignored); products still queued on a stream must finish first. */
 void k2_stream_destroy(k2_stream *stream_plan);
 
+/* Text of a status code.  The pages define no API; every call here checks
+   its arguments on the host and returns a code before any kernel runs, as
+   the plan and device memory of a product are fixed before it (Sec. 1,
+   Sec. 3.4).  Never null; unknown codes give "unknown status". */
 const char *k2_status_string(k2_status status);
 
-/* Text of the last HIP error this thread saw (empty string if none). */
+/* Text of the last HIP error this thread saw (empty string if none), behind
+   a K2_E_HIP status of any call (Sec. 4: products run on the device through
+   the runtime, whose errors surface here). */
 const char *k2_last_hip_error(void);
 
 #ifdef __cplusplus

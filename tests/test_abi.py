@@ -36,6 +36,40 @@ def test_binding_covers_every_declared_function():
     assert set(declared_functions()) <= set(k2._SIGS)
 
 
+CITES = re.compile(r"Sec\. [0-9]|Table [0-9]|Algorithm [0-9]|Fig(?:ure|\.) [0-9]")
+# the one entry point the pages do not define: it serves callers that cannot
+# allocate device memory, and its comment says so instead of citing a passage
+NO_PASSAGE_NEEDS = re.compile(r"cannot allocate")
+
+
+def declarations_with_comments():
+    """(name, comment) for every function the header declares: the comment
+    block right above its declaration, or above the run of declarations it
+    belongs to."""
+    text = open(HEADER).read()
+    # comments blanked (same length), so that names inside them do not match
+    code = re.sub(r"/\*.*?\*/", lambda c: re.sub(r"[^\n]", " ", c.group(0)), text, flags=re.S)
+    out = []
+    pat = re.compile(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(k2_[a-z0-9_]+)\s*\(", re.M)
+    for m in pat.finditer(code):
+        line = text.rfind("\n", 0, m.start(1)) + 1   # the declaration's first line
+        end = text.rfind("*/", 0, line)
+        start = text.rfind("/*", 0, end)
+        between = text[end + 2:line]
+        # only declarations may sit between the comment and this one
+        stripped = re.sub(r"[^;]*\([^;]*\)\s*;", "", between).strip()
+        out.append((m.group(1), text[start:end + 2] if not stripped else ""))
+    return out
+
+
+def test_every_declaration_cites_its_passage():
+    """Each call of the boundary states the passage of the pages that defines
+    the operation (section, table, algorithm or figure)."""
+    missing = [n for n, c in declarations_with_comments()
+               if not (CITES.search(c) or NO_PASSAGE_NEEDS.search(c))]
+    assert not missing, f"no passage cited for: {missing}"
+
+
 def test_status_strings():
     for st in range(7):
         assert k2.lib().k2_status_string(st)

@@ -233,3 +233,38 @@ def test_streamed(dev):
             torch.cuda.synchronize()
             check_parity(from_device(ya, sr), combine[sr](y0.reshape(want.shape), want), sr, "accumulate " + label)
 
+
+
+def test_multi_tile_bands(dev):
+    """Bands cut into several cached tiles (band_tile_nodes 64 and 256 on a
+    web-like 2^14 graph): tiles that do not own their band add their windows
+    to y with atomics after the fill, the owner tile also adds the band's
+    strays.  Every semiring, both directions, batches 1, 3 and 8, overwriting
+    and accumulating, whole outputs against the oracle."""
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(23)
+    n = 2 ** 14
+    rows, cols = synth.web(n, 16, window=1024, p_local=0.8, seed=7)
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    combine = {"plus_times": lambda a, b: a.astype(np.float64) + b,
+               "boolean": np.maximum, "boolean_u32": np.bitwise_or, "tropical": np.minimum}
+    for cap, strays in ((64, 1), (256, 1), (64, 0)):
+        opts = k2.plan_defaults(cache_last_level=1, band_tile_nodes=cap, band_strays=strays)
+        m = k2.Matrix(tree, opts, device=dev)
+        for sr, direction, B in itertools.product(ALL_SEMIRINGS, ("right", "left"), (1, 3, 8)):
+            x = make_x(rng, sr, n, B)
+            xd = to_device(x, dev)
+            want = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
+            label = f"bands cap={cap} strays={strays} {sr} {direction} B={B}"
+            y = m.spmv(xd, direction=direction, semiring=sr, batch=B, mode="cached")
+            torch.cuda.synchronize()
+            check_parity(from_device(y, sr), want, sr, label)
+            y0 = make_x(rng, sr, n, B)
+            if sr == "boolean":
+                y0 = (y0 != 0).astype(np.float32)
+            ya = to_device(y0, dev)
+            m.spmv(xd, ya, direction=direction, semiring=sr, batch=B, mode="cached", accumulate=True)
+            torch.cuda.synchronize()
+            check_parity(from_device(ya, sr), combine[sr](y0.reshape(want.shape), want), sr,
+                         "accumulate " + label)

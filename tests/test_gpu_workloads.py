@@ -1,11 +1,16 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark uses.
 
-The oracle computes sampled outputs one by one from the edge-list definition
-(oracle.spmv_sample); properties that hold at any size complete the check:
-left = right on a symmetric matrix, the all-ones product = out-degrees,
-tree-only = cached.  Also: the library allocates no device memory in
-k2_matrix_create and k2_spmv.
+Whole outputs against the oracle where it can compute them in seconds to a
+minute (oracle.spmv_edges, the product from the edge-list definition): the
+R-MAT 2^22 tropical products (right and left, tree-only and cached) and the
+symmetric R-MAT 2^24 packed-Boolean right product.  For the web-like 2^27
+graph (1.2G edges) the oracle computes contiguous blocks of 2^20 outputs
+(the first, two inner ones and the last) plus scattered outputs, one by one
+from the edge-list definition (oracle.spmv_sample).  Properties that hold at
+any size complete the check: left = right on a symmetric matrix, the
+all-ones product = out-degrees, tree-only = cached.  Also: the library
+allocates no device memory in k2_matrix_create and k2_spmv.
 """
 import numpy as np
 import pytest
@@ -33,12 +38,16 @@ def sample_idx(n, k, seed):
     return np.unique(np.concatenate([s, [0, 1, 2, n - 1]])).astype(np.uint32)
 
 
-def check_sampled(rows, cols, n, x, y, semiring, direction, batch, label, k=4000, seed=0):
-    idx = sample_idx(n, k, seed)
-    want = oracle.spmv_sample(rows, cols, n, n, x, ORC_SEMIRING[semiring], idx, ORC_DIR[direction],
-                              batch)
-    got = from_device(y, semiring).reshape(n, batch)[idx]
-    check_parity(got, want, semiring, label)
+def block_sample(n, seed, block=2 ** 20, k=3000):
+    """Contiguous blocks of outputs: the first, one starting at an odd offset
+    near n/4, the middle one and the last; plus k scattered outputs."""
+    starts = [0, n // 4 + 12345, n // 2, n - block]
+    blocks = [np.arange(s0, s0 + block, dtype=np.int64) for s0 in starts]
+    return np.unique(np.concatenate(blocks + [sample_idx(n, k, seed).astype(np.int64)])).astype(np.uint32)
+
+
+def log(msg):
+    print(f"[workloads] {msg}", flush=True)
 
 
 def test_library_allocates_nothing(dev):
@@ -67,7 +76,7 @@ def test_library_allocates_nothing(dev):
 
 def test_rmat_s22_e64m_tropical(dev):
     """R-MAT 2^22, 2^26 edges, min-plus with 10% finite x: right and left,
-    both traversals, bit-exact on sampled outputs."""
+    both traversals, whole outputs bit-exact against the oracle."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("rmat_s22_e64m")
     tree = k2.Tree(rows, cols, n, n)
@@ -76,18 +85,19 @@ def test_rmat_s22_e64m_tropical(dev):
     m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
     xd = to_device(x, dev)
     for direction in ("right", "left"):
-        ys = {}
+        want = oracle.spmv_edges(rows, cols, n, n, x, oracle.TROPICAL, ORC_DIR[direction])
+        log(f"rmat_s22 oracle {direction} done")
         for mode in ("tree", "cached"):
-            ys[mode] = m.spmv(xd, direction=direction, semiring="tropical", mode=mode)
-        torch.cuda.synchronize()
-        assert torch.equal(ys["tree"].view(torch.int32), ys["cached"].view(torch.int32))
-        check_sampled(rows, cols, n, x, ys["cached"], "tropical", direction, 1,
-                      f"rmat_s22 tropical {direction}", seed=1)
+            y = m.spmv(xd, direction=direction, semiring="tropical", mode=mode)
+            torch.cuda.synchronize()
+            check_parity(from_device(y, "tropical"), want, "tropical", f"rmat_s22 tropical {direction} {mode}")
+            del y
 
 
 def test_symrmat_s24_e256m_boolean(dev):
     """Symmetric R-MAT 2^24, 2^28 directed edges, 32 Boolean vectors per word:
-    right product bit-exact on sampled outputs; left = right (symmetry)."""
+    the whole right product bit-exact against the oracle, cached and
+    tree-only; left = right (symmetry)."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("symrmat_s24_e256m")
     tree = k2.Tree(rows, cols, n, n)
@@ -100,36 +110,38 @@ def test_symrmat_s24_e256m_boolean(dev):
     yt = m.spmv(xd, direction="right", semiring="boolean_u32", mode="tree")
     torch.cuda.synchronize()
     assert torch.equal(yr, yl) and torch.equal(yr, yt)
-    check_sampled(rows, cols, n, x, yr, "boolean_u32", "right", 1, "symrmat_s24 right", seed=2)
+    want = oracle.spmv_edges(rows, cols, n, n, x, oracle.BOOLEAN_U32, oracle.RIGHT)
+    log("symrmat_s24 oracle right done")
+    check_parity(from_device(yr, "boolean_u32"), want, "boolean_u32", "symrmat_s24 right")
 
 
 def test_web_n27_d9_batch8(dev):
     """Web-like 2^27, ~1.2G edges, plus-times over 8 vectors, last internal
     level cached (the benchmark's configuration), tree-only and streamed
-    from host memory: sampled outputs within the fp32 tolerance, right and
-    left; the all-ones product gives out-degrees."""
+    from host memory: four contiguous blocks of 2^20 outputs (the first, the
+    last and two inner ones) and 3000 scattered ones within the fp32
+    tolerance, right and left; the all-ones product gives out-degrees."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("web_n27_d9")
     tree = k2.Tree(rows, cols, n, n)
     x = synth.workload_x("web_n27_d9", n)
     m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
     xd = to_device(x, dev)
-    for direction in ("right", "left"):
-        for mode in ("cached", "tree"):   # tree-only: band groups, then the rest tiles
-            y = m.spmv(xd, direction=direction, batch=8, mode=mode)
-            torch.cuda.synchronize()
-            check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction} {mode}",
-                          k=3000, seed=3)
-            del y
-    # the tree streamed from host memory through 256 MB of staging (out of core)
-    st = k2.Streamed(tree, 256 << 20)
+    idx = block_sample(n, 3)
+    idx_t = torch.from_numpy(idx.astype(np.int64)).to(dev)
+    st = k2.Streamed(tree, 256 << 20)   # the tree streamed from host memory (out of core)
     buf = st.staging(dev)
     for direction in ("right", "left"):
-        y = st.spmv(xd, direction=direction, batch=8, staging=buf)
-        torch.cuda.synchronize()
-        check_sampled(rows, cols, n, x, y, "plus_times", direction, 8, f"web_n27 {direction} streamed",
-                      k=3000, seed=5)
-        del y
+        want = oracle.spmv_sample(rows, cols, n, n, x, oracle.PLUS_TIMES, idx, ORC_DIR[direction], 8)
+        log(f"web_n27 oracle {direction}: {idx.size} outputs")
+        for mode in ("cached", "tree", "streamed"):   # tree-only: band groups, then the rest tiles
+            if mode == "streamed":
+                y = st.spmv(xd, direction=direction, batch=8, staging=buf)
+            else:
+                y = m.spmv(xd, direction=direction, batch=8, mode=mode)
+            got = y.view(n, 8)[idx_t].cpu().numpy()
+            check_parity(got, want, "plus_times", f"web_n27 {direction} {mode}")
+            del y
     del st, buf
     ones = torch.ones(n, device=dev)
     deg = m.spmv(ones, direction="right").cpu().numpy()

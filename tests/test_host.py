@@ -514,3 +514,49 @@ def test_stream_arguments():
     assert call(batch=0) == k2.K2_E_INVALID_ARG
     with pytest.raises(k2.K2Error):
         k2.Streamed(t, 1 << 10)
+
+
+def test_spmv_refuses_host_vectors():
+    """Matrix.spmv and Streamed.spmv refuse vectors that are not on the
+    product's device before anything reaches the library (a host pointer
+    handed to a kernel would fault the GPU instead of raising)."""
+    torch = pytest.importorskip("torch")
+    m = k2.Matrix.__new__(k2.Matrix)   # no device needed: the checks run first
+    m.n_rows = m.n_cols = 16
+    m.device = torch.device("meta")
+    m._h = None
+    x = torch.empty(16, device="meta")
+    with pytest.raises(ValueError, match="y is not on the matrix's device"):
+        m.spmv(x, torch.empty(16))
+    with pytest.raises(ValueError, match="x is not on the matrix's device"):
+        m.spmv(torch.empty(16), torch.empty(16, device="meta"))
+    rows, cols, n = synth.workload_edges("rmat_s12_e32k")
+    s = k2.Streamed(k2.Tree(rows, cols, n, n), 1 << 16)
+    with pytest.raises(ValueError, match="device tensor"):
+        s.spmv(torch.empty(n), torch.empty(n))
+
+
+def test_band_tile_cap_splits_bands():
+    """band_tile_nodes cuts a band's dense quadrants into several cached
+    tiles: on a web-like 2^14 graph with 64 nodes per tile every band has
+    many tiles, none of them its band's only tile (so products fill y and
+    the tiles add their windows), and exactly one per band owns the band's
+    strays; the default cap leaves one tile per band."""
+    n = 2 ** 14
+    rows, cols = synth.web(n, 16, window=1024, p_local=0.8, seed=7)
+    t = k2.Tree(rows, cols, n, n)
+    for which in (1, 2):
+        _, tiles, _ = t.plan(k2.plan_defaults(cache_last_level=1, band_tile_nodes=64), which=which)
+        win = tiles[:, 6] != 0xFFFFFFFF
+        field = 4 if which == 1 else 5
+        band = tiles[win, field] >> tiles[win, 6]
+        _, per = np.unique(band, return_counts=True)
+        assert per.size >= 16 and per.min() > 1
+        assert not (tiles[:, 3] & 2).any()
+        owners = band[(tiles[win, 3] & 1) != 0]
+        assert np.array_equal(np.sort(owners), np.unique(band))
+        _, tiles, _ = t.plan(k2.plan_defaults(cache_last_level=1), which=which)
+        win = tiles[:, 6] != 0xFFFFFFFF
+        assert ((tiles[win, 3] & 2) != 0).all()
+    with pytest.raises(k2.K2Error):
+        t.estimate(k2.plan_defaults(band_tile_nodes=63))

@@ -36,7 +36,8 @@ class PlanOpts(ctypes.Structure):
     _fields_ = [("tile_nodes", ctypes.c_uint32), ("host_top_max", ctypes.c_uint32),
                 ("cache_last_level", ctypes.c_int32), ("xcd_remap", ctypes.c_int32),
                 ("window_elems", ctypes.c_uint32), ("window_batch", ctypes.c_uint32),
-                ("offsets", ctypes.c_int32), ("band_strays", ctypes.c_int32)]
+                ("offsets", ctypes.c_int32), ("band_strays", ctypes.c_int32),
+                ("band_tile_nodes", ctypes.c_uint32)]
 
 
 class MemBreakdown(ctypes.Structure):
@@ -307,13 +308,15 @@ class Matrix:
         if x.dtype != dtype or x.numel() != n_in * batch or not x.is_contiguous():
             raise ValueError(f"x must be a contiguous {dtype} tensor of {n_in * batch} elements")
         if x.device != self.device:
-            raise ValueError("x is on another device")
+            raise ValueError("x is not on the matrix's device")
         if y is None:
             if accumulate:
                 raise ValueError("accumulate needs y")
             y = torch.empty(n_out * batch, dtype=dtype, device=self.device)
         elif y.dtype != dtype or y.numel() != n_out * batch or not y.is_contiguous():
             raise ValueError(f"y must be a contiguous {dtype} tensor of {n_out * batch} elements")
+        if y.device != self.device:
+            raise ValueError("y is not on the matrix's device")
         flags = MODES[mode] | (K2_SPMV_ACCUMULATE if accumulate else 0)
         _check(lib().k2_spmv(self._h, d, SEMIRINGS[semiring], int(batch), flags,
                              _VP(x.data_ptr()), _VP(y.data_ptr()), _stream_handle(stream)),
@@ -376,6 +379,7 @@ class Streamed:
                "k2_stream_create")
         self._h = h
         self._tree = tree
+        self._default_staging = {}
         self.n_rows, self.n_cols = tree.n_rows, tree.n_cols
         nc, mb, sb = ctypes.c_uint64(), ctypes.c_uint64(), ctypes.c_uint64()
         _check(lib().k2_stream_info(h, ctypes.byref(nc), ctypes.byref(mb), ctypes.byref(sb)), "k2_stream_info")
@@ -412,14 +416,26 @@ class Streamed:
         dtype = torch.int32 if semiring == "boolean_u32" else torch.float32
         if x.dtype != dtype or x.numel() != n_in * batch or not x.is_contiguous():
             raise ValueError(f"x must be a contiguous {dtype} tensor of {n_in * batch} elements")
+        if x.device.type != "cuda":
+            raise ValueError("x must be a device tensor")
         if y is None:
             if accumulate:
                 raise ValueError("accumulate needs y")
             y = torch.empty(n_out * batch, dtype=dtype, device=x.device)
         elif y.dtype != dtype or y.numel() != n_out * batch or not y.is_contiguous():
             raise ValueError(f"y must be a contiguous {dtype} tensor of {n_out * batch} elements")
+        if y.device != x.device:
+            raise ValueError("y is not on x's device")
         if staging is None:
-            staging = self.staging(x.device)
+            # one buffer per Streamed and device, kept across products: the
+            # copies and kernels of a product still read it after this call
+            # returns, so it must not go back to torch's allocator here
+            staging = self._default_staging.get(x.device)
+            if staging is None:
+                staging = self.staging(x.device)
+                self._default_staging[x.device] = staging
+        if staging.device != x.device:
+            raise ValueError("the staging buffer is not on x's device")
         _check(lib().k2_stream_spmv(self._h, d, SEMIRINGS[semiring], int(batch),
                                     K2_SPMV_ACCUMULATE if accumulate else 0, _VP(x.data_ptr()),
                                     _VP(y.data_ptr()), _VP(staging.data_ptr()), staging.numel(),

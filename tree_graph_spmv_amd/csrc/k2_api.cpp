@@ -78,6 +78,7 @@ bool valid_opts(const k2_plan_opts &o) {
     if (o.tile_nodes & (o.tile_nodes - 1)) return false;
     if (o.window_elems > 16384) return false;
     if (o.offsets < K2_OFFSETS_AUTO || o.offsets > K2_OFFSETS_SCAN) return false;
+    if (o.band_tile_nodes < 64 || o.band_tile_nodes > (1u << 30)) return false;
     return true;
 }
 
@@ -91,7 +92,7 @@ bool same_opts(const k2_plan_opts &a, const k2_plan_opts &b) {
            (a.cache_last_level != 0) == (b.cache_last_level != 0) &&
            (a.xcd_remap != 0) == (b.xcd_remap != 0) &&
            (a.offsets == K2_OFFSETS_DIRECTORY) == (b.offsets == K2_OFFSETS_DIRECTORY) &&
-           (a.band_strays != 0) == (b.band_strays != 0);
+           (a.band_strays != 0) == (b.band_strays != 0) && a.band_tile_nodes == b.band_tile_nodes;
 }
 
 // The plan of 'tree' for 'o', computed once per option set.
@@ -141,6 +142,7 @@ k2_status k2_plan_defaults(k2_plan_opts *opts) {
     opts->window_batch = 8;
     opts->offsets = K2_OFFSETS_AUTO;
     opts->band_strays = 1;
+    opts->band_tile_nodes = 65536;
     return K2_OK;
 }
 
@@ -413,7 +415,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     m.cached = opts->cache_last_level != 0 && t.nodes[t.levels - 2] > 0;
     m.window_elems = m.plan.window_log2 >= 0 ? opts->window_elems : 0;
     m.window_batch = opts->window_batch;
-    {   // the window shares a workgroup's LDS with the cell lists (a few KB)
+    {   // the window shares a workgroup's LDS with the kernels' own (cell rings, frontiers)
         int dev = 0, lds = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
@@ -422,7 +424,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             delete mx;
             return K2_E_HIP;
         }
-        m.max_window_lds = lds > 16384 ? size_t(lds) - 8192 : 0;
+        m.lds_per_block = lds > 0 ? size_t(lds) : 0;
     }
     std::memset(&m.dev, 0, sizeof(m.dev));
     m.dev.levels = t.levels;
@@ -622,7 +624,7 @@ k2_status k2_matrix_last_timing(k2_matrix *matrix, float *fill_ms, float *kernel
 }
 
 k2_status k2_matrix_destroy(k2_matrix *matrix) {
-    if (!matrix) return K2_E_INVALID_ARG;
+    if (!matrix) return K2_OK;
     for (int k = 0; k < 3; ++k)
         if (matrix->m.ev[k]) (void)hipEventDestroy(static_cast<hipEvent_t>(matrix->m.ev[k]));
     delete matrix;

@@ -337,7 +337,9 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
                 }
                 if (kUnchecked || SR::contributes(xv[u])) acc = SR::combine(acc, SR::contrib(xv[u]));
             }
-        if (kUnchecked || SR::contributes_out(acc)) apply(cur, acc);
+        // ok[] is a prefix: a lane group with no cell (a pass's tail) has no
+        // run, and its yo[0] is a ring slot past the queued cells
+        if (ok[0] && (kUnchecked || SR::contributes_out(acc))) apply(cur, acc);
     } else {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u)
@@ -1305,12 +1307,23 @@ uint32_t grid_for(uint64_t blocks) {
 }
 
 // Whether products with batch B use the planned windows, and their LDS bytes:
-// whenever the window (Q outputs x B) fits one workgroup's LDS; beyond
+// whenever the window (Q outputs x B) fits one workgroup's LDS beside the
+// kernel's other LDS ('other' bytes: its cell rings and frontiers); beyond
 // window_batch vectors fewer workgroups share a CU.
-size_t window_bytes(const Matrix &m, uint32_t B, int *use) {
+size_t window_bytes(const Matrix &m, uint32_t B, size_t other, int *use) {
     const size_t bytes = m.plan.window_log2 >= 0 ? (size_t(1) << m.plan.window_log2) * B * 4 : 0;
-    *use = (m.window_elems > 0 && bytes <= m.max_window_lds) ? 1 : 0;
+    *use = (m.window_elems > 0 && bytes > 0 && bytes + other <= m.lds_per_block) ? 1 : 0;
     return *use ? bytes : 0;
+}
+
+// LDS of the cached kernel beside its window (the waves' cell rings), and of
+// the band kernel (the rings and the waves' two frontier levels of band_cap
+// relative codes).
+template <class Off>
+size_t cached_other_lds() { return sizeof(WaveCells<Off>) * kWaves; }
+template <class Off>
+size_t band_other_lds(const Matrix &m) {
+    return sizeof(WaveCells<Off>) * kWaves + size_t(kWaves) * 2 * m.plan.band_cap * sizeof(uint32_t);
 }
 
 int set_lds_limit(const void *k, size_t lds) {
@@ -1331,7 +1344,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     const uint32_t VL = lanes_per_node(B, DIR);
     const uint32_t grid = grid_for(n_tiles);
     int use = 0;
-    const size_t lds = window_bytes(m, B, &use);
+    const size_t lds = window_bytes(m, B, cached_other_lds<Off>(), &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     auto k = cached_kernel<SR, DIR, Off>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
@@ -1387,7 +1400,7 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
         return hipGetLastError();
     };
     int use = 0;
-    const size_t wb = SR::kTreeBands ? window_bytes(m, B, &use) : 0;
+    const size_t wb = SR::kTreeBands ? window_bytes(m, B, band_other_lds<Off>(m), &use) : 0;
     if (use) {
         // the bands' dense quadrants into their windows, then the rest
         if (!p.band_groups[DIR].empty()) {
@@ -1466,7 +1479,8 @@ int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const 
 
 bool cached_writes_all(const Matrix &m, int dir, uint32_t batch) {
     int use = 0;
-    window_bytes(m, batch, &use);
+    window_bytes(m, batch, narrow_offsets(m, batch) ? cached_other_lds<uint32_t>() : cached_other_lds<uint64_t>(),
+                 &use);
     return use && m.plan.bands_cover[dir] && !m.plan.cached_tiles[dir].empty();
 }
 

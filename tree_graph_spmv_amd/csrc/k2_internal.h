@@ -173,7 +173,7 @@ struct Matrix {
     const uint32_t *d_stray_off[2] = {nullptr, nullptr}; // band b: d_strays[off[b] .. off[b + 1])
     uint64_t *d_cached = nullptr;        // last internal level codes or null
     uint32_t window_elems = 0, window_batch = 0;
-    size_t max_window_lds = 0;   // LDS bytes a product's window may take per workgroup
+    size_t lds_per_block = 0;    // LDS bytes of one workgroup (windows and the kernels' own)
     bool cached = false;
     // kernel timing (events created on first enable)
     void *ev[3] = {nullptr, nullptr, nullptr};

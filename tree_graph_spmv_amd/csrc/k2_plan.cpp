@@ -70,7 +70,7 @@ struct Planner {
     Plan &p;
     int last;           // last internal level
     uint64_t cached_C;  // nodes per cached tile without a window
-    static constexpr uint64_t kBandCap = 65536;   // nodes per windowed cached tile
+    uint64_t band_cap = 65536;                    // nodes per windowed cached tile
     static constexpr uint64_t kSparseTile = 8192; // nodes per sparse cached tile beside bands
     std::vector<Tile> *sink = nullptr;            // where range() puts tiles (p.tiles if null)
     std::vector<uint64_t> sink_weight;            // last-internal-level nodes of the sink's tiles
@@ -153,7 +153,7 @@ struct Planner {
     }
 
     // Cached tiles of direction dir over the node ranges 'ranges' of one
-    // band, all with the band's window; at most kBandCap nodes per tile.
+    // band, all with the band's window; at most band_cap nodes per tile.
     void cached_band(int dir, const std::vector<Seg> &ranges, const Tile &win) {
         Tile tl = win;
         tl.first = uint32_t(p.cached_segs[dir].size());
@@ -167,12 +167,12 @@ struct Planner {
         };
         for (Seg sg : ranges) {
             while (sg.count > 0) {
-                uint64_t take = std::min<uint64_t>(sg.count, kBandCap - nodes);
+                uint64_t take = std::min<uint64_t>(sg.count, band_cap - nodes);
                 push_segs(dir, sg.lo, take);
                 nodes += take;
                 sg.lo += uint32_t(take);
                 sg.count -= uint32_t(take);
-                if (nodes == kBandCap) close();
+                if (nodes == band_cap) close();
             }
         }
         close();
@@ -327,6 +327,7 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     cc = std::max<uint64_t>(256, std::min<uint64_t>(16384, cc));
     cc = (cc + 255) & ~uint64_t(255);
     Planner pl{t, o.tile_nodes, p, last, cc};
+    pl.band_cap = o.band_tile_nodes;
 
     // window quadrants: side Q with Q * window_batch <= window_elems
     int qlog = -1;
