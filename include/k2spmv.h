@@ -390,6 +390,30 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
                  uint32_t max_levels, int32_t *d_dist, void *d_workspace, uint64_t workspace_bytes,
                  void *stream, uint32_t *levels, uint64_t *reached_per_level);
 
+/* Bytes of the library's fixed scratch array (64 MiB), the workspace of
+   k2_bfs_noalloc. */
+#define K2_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* k2_bfs for callers that cannot allocate device memory (code that must not
+   call hipMalloc: tight serving loops, harnesses that forbid allocation):
+   the same search and results, with no workspace argument.  Its workspace
+   (k2_bfs_workspace_bytes of this matrix and n_sources, at most
+   K2_NOALLOC_SCRATCH_BYTES) is a fixed array inside the library's code
+   object, which each GPU the library runs on holds from the library's load
+   until the process ends; its device address is looked up on the first
+   call on each device.  The call allocates no memory: the caller passes the
+   matrix, the sources (host) and d_dist (device, n x n_sources int32, as for
+   k2_bfs).  Every call on a GPU uses that GPU's one array and leaves its
+   last contents there (the search clears what must start at zero), so
+   calls that overlap on one GPU, from several threads or streams, race and
+   must be serialized by the caller.  Synchronous like k2_bfs.
+   Errors: as k2_bfs, plus K2_E_UNSUPPORTED when the workspace of this
+   search (about 36 n ceil(n_sources / 32) bytes) exceeds
+   K2_NOALLOC_SCRATCH_BYTES; nothing runs then. */
+k2_status k2_bfs_noalloc(k2_matrix *matrix, k2_direction direction, const uint32_t *sources,
+                         uint32_t n_sources, uint32_t max_levels, int32_t *d_dist, void *stream,
+                         uint32_t *levels, uint64_t *reached_per_level);
+
 /* Out-of-core products (Sec. 7, the paper's direction for trees larger than
    device memory): the tree stays in host memory and each product streams it
    through a caller-owned device staging buffer, chunk by chunk.

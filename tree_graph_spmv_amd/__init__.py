@@ -96,6 +96,8 @@ _SIGS = {
     "k2_bfs_workspace_bytes": (ctypes.c_int, [_VP, ctypes.c_uint32, _U64P]),
     "k2_bfs": (ctypes.c_int, [_VP, ctypes.c_int, _U32P, ctypes.c_uint32, ctypes.c_uint32, _VP, _VP,
                               ctypes.c_uint64, _VP, _U32P, _U64P]),
+    "k2_bfs_noalloc": (ctypes.c_int, [_VP, ctypes.c_int, _U32P, ctypes.c_uint32, ctypes.c_uint32, _VP, _VP,
+                                      _U32P, _U64P]),
     "k2_matrix_cached_blocks": (ctypes.c_int, [_VP, _U64P, ctypes.c_uint64, _VP]),
     "k2_matrix_set_timing": (ctypes.c_int, [_VP, ctypes.c_int32]),
     "k2_matrix_last_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_float),
@@ -348,6 +350,28 @@ class Matrix:
                             _VP(workspace.data_ptr()), workspace.numel(), _stream_handle(stream),
                             ctypes.byref(levels),
                             reached.ctypes.data_as(_U64P) if reached is not None else None), "k2_bfs")
+        if reached is not None:
+            reached = reached[:min(levels.value + 1, max_levels)]
+        return dist, levels.value, reached
+
+    def bfs_noalloc(self, sources, dist, direction="right", max_levels=2 ** 31 - 1, stream=None):
+        """The search of bfs() through k2_bfs_noalloc, whose workspace is the
+        library's fixed scratch array: the caller passes the (n,
+        len(sources)) int32 device tensor dist, and nothing is allocated on
+        the device.  Returns (dist, levels, reached) like bfs()."""
+        src, sp = _u32(sources)
+        n = self.n_rows
+        if dist.numel() != n * src.size or str(dist.dtype) != "torch.int32" or not dist.is_contiguous():
+            raise ValueError("dist must be a contiguous int32 tensor of n x len(sources)")
+        if dist.device != self.device:
+            raise ValueError("dist is not on the matrix's device")
+        levels = ctypes.c_uint32()
+        max_levels = int(min(max_levels, 2 ** 31 - 1))
+        reached = np.zeros(max(max_levels, 1), np.uint64) if max_levels <= (1 << 16) else None
+        _check(lib().k2_bfs_noalloc(self._h, DIRECTIONS[direction], sp, src.size, max_levels,
+                                    _VP(dist.data_ptr()), _stream_handle(stream), ctypes.byref(levels),
+                                    reached.ctypes.data_as(_U64P) if reached is not None else None),
+               "k2_bfs_noalloc")
         if reached is not None:
             reached = reached[:min(levels.value + 1, max_levels)]
         return dist, levels.value, reached

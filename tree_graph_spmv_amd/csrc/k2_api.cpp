@@ -704,18 +704,27 @@ k2_status k2_bfs_workspace_bytes(const k2_matrix *matrix, uint32_t n_sources, ui
     return K2_OK;
 }
 
-k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
-                 uint32_t max_levels, int32_t *d_dist, void *d_workspace, uint64_t workspace_bytes,
-                 void *stream, uint32_t *levels, uint64_t *reached_per_level) {
-    if (!matrix || !sources || n_sources == 0 || !d_dist || !d_workspace || !levels) return K2_E_INVALID_ARG;
+namespace {
+
+// Arguments of a search, checked on the host before anything runs.
+k2_status bfs_check(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
+                    const int32_t *d_dist, const uint32_t *levels) {
+    if (!matrix || !sources || n_sources == 0 || !d_dist || !levels) return K2_E_INVALID_ARG;
     if (int(direction) != K2_RIGHT && int(direction) != K2_LEFT) return K2_E_INVALID_ARG;
-    Matrix &m = matrix->m;
+    const Matrix &m = matrix->m;
     if (m.n_rows != m.n_cols) return K2_E_INVALID_ARG;
-    const uint64_t n = m.n_rows;
     for (uint32_t j = 0; j < n_sources; ++j)
-        if (sources[j] >= n) return K2_E_INDEX_RANGE;
+        if (sources[j] >= m.n_rows) return K2_E_INDEX_RANGE;
+    return K2_OK;
+}
+
+// The search of k2_bfs over a checked workspace of at least
+// bfs_space(n, n_sources).bytes bytes.
+k2_status bfs_run(Matrix &m, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
+                  uint32_t max_levels, int32_t *d_dist, void *d_workspace, void *stream, uint32_t *levels,
+                  uint64_t *reached_per_level) {
+    const uint64_t n = m.n_rows;
     const BfsSpace sp = bfs_space(n, n_sources);
-    if (workspace_bytes < sp.bytes || (reinterpret_cast<uintptr_t>(d_workspace) & 255)) return K2_E_INVALID_ARG;
     const uint32_t W = (n_sources + 31) / 32;
     char *ws = static_cast<char *>(d_workspace);
     uint32_t *F = reinterpret_cast<uint32_t *>(ws + sp.words_off[0]);
@@ -770,6 +779,36 @@ k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sour
         HIP_TRY(hipStreamSynchronize(st), "search distances");
     }
     return K2_OK;
+}
+
+}  // namespace
+
+k2_status k2_bfs(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
+                 uint32_t max_levels, int32_t *d_dist, void *d_workspace, uint64_t workspace_bytes,
+                 void *stream, uint32_t *levels, uint64_t *reached_per_level) {
+    k2_status st = bfs_check(matrix, direction, sources, n_sources, d_dist, levels);
+    if (st != K2_OK) return st;
+    if (!d_workspace) return K2_E_INVALID_ARG;
+    const BfsSpace sp = bfs_space(matrix->m.n_rows, n_sources);
+    if (workspace_bytes < sp.bytes || (reinterpret_cast<uintptr_t>(d_workspace) & 255)) return K2_E_INVALID_ARG;
+    return bfs_run(matrix->m, direction, sources, n_sources, max_levels, d_dist, d_workspace, stream, levels,
+                   reached_per_level);
+}
+
+k2_status k2_bfs_noalloc(k2_matrix *matrix, k2_direction direction, const uint32_t *sources, uint32_t n_sources,
+                         uint32_t max_levels, int32_t *d_dist, void *stream, uint32_t *levels,
+                         uint64_t *reached_per_level) {
+    k2_status st = bfs_check(matrix, direction, sources, n_sources, d_dist, levels);
+    if (st != K2_OK) return st;
+    if (bfs_space(matrix->m.n_rows, n_sources).bytes > kNoAllocScratchBytes) return K2_E_UNSUPPORTED;
+    void *ws = nullptr;
+    const int e = noalloc_scratch(&ws);
+    if (e != hipSuccess) {
+        set_hip_error(e, "search scratch");
+        return K2_E_HIP;
+    }
+    return bfs_run(matrix->m, direction, sources, n_sources, max_levels, d_dist, ws, stream, levels,
+                   reached_per_level);
 }
 
 k2_status k2_stream_create(const k2_tree *tree, const k2_plan_opts *opts, uint64_t staging_bytes,

@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "k2_internal.h"
 
@@ -1557,6 +1558,36 @@ int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_s
 }
 
 const char *hip_error_text(int err) { return hipGetErrorString(static_cast<hipError_t>(err)); }
+
+// ------------------------------------------------------------- scratch
+
+// Workspace of k2_bfs_noalloc, for callers that cannot allocate device
+// memory: a fixed array in the library's code object, which every GPU the
+// library runs on holds until the process ends.  Host code never uses the
+// name itself (on the host it is a stand-in, not a device address): the
+// device address comes from hipGetSymbolAddress, once per device, and is
+// passed to the kernels like any workspace.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+int noalloc_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *per_device[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!per_device[dev]) {   // first call on this device, with it current
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        per_device[dev] = p;
+    }
+    *ptr = per_device[dev];
+    return hipSuccess;
+}
 
 }  // namespace k2
 

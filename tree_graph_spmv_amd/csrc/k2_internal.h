@@ -212,6 +212,11 @@ int launch_stray_count(const Matrix &m, int dir, const Seg *segs, uint32_t n_seg
 int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *cursor,
                          StrayRec *out, void *stream);
 const char *hip_error_text(int err);
+// The device address of the library's fixed scratch array on the current
+// device (k2_bfs_noalloc's workspace, K2_NOALLOC_SCRATCH_BYTES bytes),
+// looked up once per device.
+constexpr uint64_t kNoAllocScratchBytes = K2_NOALLOC_SCRATCH_BYTES;
+int noalloc_scratch(void **ptr);
 
 void set_hip_error(int err, const char *where);
 
