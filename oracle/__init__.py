@@ -118,14 +118,16 @@ class OracleTree:
         h = ctypes.c_void_p()
         _check(lib.orc_build(rp, cp, r.size, int(n_rows), int(n_cols), ctypes.byref(h)))
         self._h = h
+        self._lib = lib   # kept for __del__, which may run after module teardown
         self.n_rows, self.n_cols = int(n_rows), int(n_cols)
         self.levels = lib.orc_levels(h)
         self.nnz = int(lib.orc_nnz(h))
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            _load().orc_free(h)
+        lib = getattr(self, "_lib", None)
+        if h is not None and h.value and lib is not None:
+            lib.orc_free(h)
             self._h = None
 
     def level_nodes(self):

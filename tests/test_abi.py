@@ -1,20 +1,23 @@
-"""The C-ABI library loads and exports every function include/k2spmv.h
-declares (no compute call: this runs without a GPU)."""
+"""The C-ABI library loads and exports every function include/*.h declares
+(no compute call: this runs without a GPU)."""
 import ctypes
+import glob
 import os
 import re
 
 import tree_graph_spmv_amd as k2
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
-                      "k2spmv.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "k2spmv.h")
+HEADERS = sorted(glob.glob(os.path.join(INCLUDE, "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(k2_[a-z0-9_]+)\s*\(",
-                       text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(k2_[a-z0-9_]+)\s*\(",
+                            text, flags=re.M)
     return sorted(set(names))
 
 
@@ -46,7 +49,13 @@ def declarations_with_comments():
     """(name, comment) for every function the header declares: the comment
     block right above its declaration, or above the run of declarations it
     belongs to."""
-    text = open(HEADER).read()
+    out = []
+    for h in HEADERS:
+        out += _declarations_with_comments(open(h).read())
+    return out
+
+
+def _declarations_with_comments(text):
     # comments blanked (same length), so that names inside them do not match
     code = re.sub(r"/\*.*?\*/", lambda c: re.sub(r"[^\n]", " ", c.group(0)), text, flags=re.S)
     out = []

@@ -108,6 +108,8 @@ _SIGS = {
     "k2_stream_spmv": (ctypes.c_int, [_VP, ctypes.c_int, ctypes.c_int, ctypes.c_uint32, ctypes.c_int32, _VP, _VP,
                                       _VP, ctypes.c_uint64, _VP]),
     "k2_stream_destroy": (None, [_VP]),
+    "k2_probe_run": (ctypes.c_int, [ctypes.c_int32, _VP, _VP, _VP, ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.c_uint32, ctypes.c_uint32, _VP, ctypes.POINTER(ctypes.c_float)]),
     "k2_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "k2_last_hip_error": (ctypes.c_char_p, []),
 }
@@ -465,3 +467,20 @@ class Streamed:
                                     _VP(y.data_ptr()), _VP(staging.data_ptr()), staging.numel(),
                                     _stream_handle(stream)), "k2_stream_spmv")
         return y
+
+
+PROBES = {"copy": 0, "read": 1, "write": 2, "update_seq_atomic": 3, "update_seq_store": 4,
+          "gather_rows": 5, "scatter_rows_atomic": 6, "lds_add_f32": 7, "lds_cas_f32": 8,
+          "lds_add_u32": 9, "gather_rows_nt": 10, "gather_rows_buf_nt": 11, "gather_rows_buf_sys": 12}
+
+
+def probe(kind, a, b, idx=None, n=0, row_elems=1, reps=0, stream=None):
+    """One timed launch of a ceiling microbenchmark (k2_probe_run): a, b
+    torch device tensors (a may be None where unused), idx a uint32 (as
+    int32) device tensor of row indexes or None; returns milliseconds."""
+    ms = ctypes.c_float()
+    _check(lib().k2_probe_run(PROBES[kind], _VP(a.data_ptr()) if a is not None else None,
+                              _VP(b.data_ptr()), _VP(idx.data_ptr()) if idx is not None else None,
+                              int(n), b.numel(), int(row_elems), int(reps), _stream_handle(stream),
+                              ctypes.byref(ms)), "k2_probe_run")
+    return float(ms.value)

@@ -15,7 +15,7 @@ DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-munsaf
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-pthread", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__"]
 
-SOURCES = [("k2_device.hip", DEVICE_FLAGS), ("k2_build.cpp", HOST_FLAGS),
+SOURCES = [("k2_device.hip", DEVICE_FLAGS), ("k2_probe.hip", DEVICE_FLAGS), ("k2_build.cpp", HOST_FLAGS),
            ("k2_plan.cpp", HOST_FLAGS), ("k2_api.cpp", HOST_FLAGS)]
 
 

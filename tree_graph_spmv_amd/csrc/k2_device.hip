@@ -1418,8 +1418,12 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
         }
         return rest(m.d_skip[DIR]);
     }
-    if (p.window_log2 < 0 && SR::kTreeBands)   // no windows planned: every rest tile, in block order
-        return rest(nullptr);
+    // No band groups in this direction (no windows planned, or too few
+    // dense quadrants): the rest tiles cover the whole tree with no skips,
+    // each descended by one wave without workgroup barriers, for every
+    // semiring.  With band groups but a batch too wide for their windows
+    // (their rest tiles skip the groups' ranges): the workgroup descent.
+    if (p.band_groups[DIR].empty()) return rest(nullptr);
     return descent();
 }
 
