@@ -146,6 +146,12 @@ constexpr int kWaves = kThreads / 64;
 // the 8 wave slots of each SIMD (64 VGPRs); the leaf phase is latency-bound,
 // so resident waves matter more than registers.
 constexpr int kOccupancy = 8;
+// Threads of the cached-level kernel's workgroups (one band tile each).
+// Measured on web-like 2^27 at batch 8: 512 or 1024 threads per band keep
+// fewer bands in flight per XCD (L2 hit rate 0.58 -> 0.65, a quarter fewer
+// bytes read) but their waves wait at the window's closing barrier and
+// collide in its compare-and-swaps: right product 11.1 -> 13.9 / 33 ms.
+constexpr int kCachedThreads = 256;
 
 __device__ __forceinline__ uint32_t nib(const uint64_t *__restrict__ w, uint64_t i) {
     return uint32_t(w[i >> 4] >> ((i & 15) * 4)) & 0xFu;
@@ -255,6 +261,27 @@ __device__ __forceinline__ uint32_t wave_child_offset(const DevTree &t, int d, u
     return __shfl(c, 0) + t.dir[d][blk];
 }
 
+// wave_child_offset for a level given by its signature words and directory.
+__device__ __forceinline__ uint32_t wave_child_offset_of(const uint64_t *__restrict__ words,
+                                                         const uint32_t *__restrict__ dir, uint32_t i) {
+    const unsigned lane = __lane_id();
+    const uint32_t blk = i >> 8;
+    const uint32_t wi = i >> 4;
+    const uint32_t w = blk * kWordsPerBlock + lane;
+    uint32_t c = 0;
+    if (lane < kWordsPerBlock && w <= wi) {
+        uint64_t v = words[w];
+        if (w == wi) {
+            const unsigned sh = (i & 15) * 4;
+            v = sh ? (v & ((1ull << sh) - 1)) : 0ull;
+        }
+        c = __popcll(v);
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) c += __shfl_xor(c, o, 16);
+    return __shfl(c, 0) + dir[blk];
+}
+
 // Orders a wave's LDS writes before its later LDS reads by other lanes.
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -357,8 +384,10 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
 // atomic: in a right product the cells of one row of a 4x4 block, and of
 // horizontally adjacent blocks, are neighbours in Z order, so a row of many
 // non-zeros would otherwise send several lanes of one instruction to the same
-// word (serialised, and a failed compare-and-swap each).
-template <class SR, class Off, bool kRuns>
+// word (serialised, and a failed compare-and-swap each).  kFull: count is
+// exactly G x kUnroll (a full pass of the ring), so no slot needs a bounds
+// test (about 5% fewer VALU instructions in a windowed right product).
+template <class SR, class Off, bool kRuns, bool kFull = false>
 __device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
                                            const typename SR::T *__restrict__ x,
                                            typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
@@ -375,7 +404,15 @@ __device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t he
         // slots past count repeat cell 'base' for the loads and skip the atomics
         Off xo[kUnroll], yo[kUnroll];
         bool ok[kUnroll];
-        if constexpr (kRuns && sizeof(Off) == 4 && kUnroll == 8) {
+        if constexpr (kFull) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const uint32_t at = (head + k0 + uint32_t(u) * step) & (R - 1u);
+                ok[u] = true;
+                xo[u] = wc->xo[at];
+                yo[u] = wc->yo[at];
+            }
+        } else if constexpr (kRuns && sizeof(Off) == 4 && kUnroll == 8) {
             // a lane group's 8 cells are 8 consecutive slots from a multiple
             // of 8 (head and k0 both are: the ring advances by whole passes
             // of G x 8 cells), so they never wrap and load as 16-byte words
@@ -413,13 +450,13 @@ __device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t he
     }
 }
 
-template <class SR, class Off, bool kMayRun>
+template <class SR, class Off, bool kMayRun, bool kFull = false>
 __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
                                           const typename SR::T *__restrict__ x,
                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
                                           const Window<typename SR::T> &w) {
-    if (kMayRun && w.runs) pass_cells<SR, Off, kMayRun>(wc, head, count, x, y, B, VL, w);
-    else pass_cells<SR, Off, false>(wc, head, count, x, y, B, VL, w);
+    if (kMayRun && w.runs) pass_cells<SR, Off, kMayRun, kFull>(wc, head, count, x, y, B, VL, w);
+    else pass_cells<SR, Off, false, kFull>(wc, head, count, x, y, B, VL, w);
 }
 
 // Leaf work of one wave over a segment of up to 64 nodes of the last internal
@@ -509,8 +546,10 @@ __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_
         fill += now;
         done += now;
         wave_lds_sync();
+        const bool full = P == G * uint32_t(kUnroll);
         while (fill >= P) {
-            ring_pass<SR, Off, DIR == K2_RIGHT>(wc, head, P, x, y, B, VL, w);
+            if (full) ring_pass<SR, Off, DIR == K2_RIGHT, true>(wc, head, P, x, y, B, VL, w);
+            else ring_pass<SR, Off, DIR == K2_RIGHT, false>(wc, head, P, x, y, B, VL, w);
             head = (head + P) & (R - 1u);
             fill -= P;
         }
@@ -564,7 +603,7 @@ __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t
 // The window of tile 'tl' for this product (no window: win = null), its LDS
 // set to the semiring zero.  'use' is false when the batch is too wide for
 // the planned window size.
-template <class SR, int DIR>
+template <class SR, int DIR, int kT = kThreads>
 __device__ __forceinline__ Window<typename SR::T> open_window(const Tile &tl, typename SR::T *lds,
                                                               bool use, uint32_t B, int runs) {
     Window<typename SR::T> w{nullptr, 0, 0, runs != 0};
@@ -573,7 +612,7 @@ __device__ __forceinline__ Window<typename SR::T> open_window(const Tile &tl, ty
     w.out0 = (DIR == K2_RIGHT) ? tl.win_row : tl.win_col;
     w.rows = 1u << tl.win_log2;
     const uint32_t n = w.rows * B;
-    for (uint32_t e = threadIdx.x; e < n; e += kThreads) lds[e] = SR::zero();
+    for (uint32_t e = threadIdx.x; e < n; e += kT) lds[e] = SR::zero();
     __syncthreads();
     return w;
 }
@@ -582,7 +621,7 @@ __device__ __forceinline__ Window<typename SR::T> open_window(const Tile &tl, ty
 // The only tile of its band (sole) writes y itself instead: it stores the
 // window (zeros included: y was not filled) or, accumulating, combines it
 // with y, with plain loads and stores.
-template <class SR>
+template <class SR, int kT = kThreads>
 __device__ __forceinline__ void close_window(const Window<typename SR::T> &w,
                                              typename SR::T *__restrict__ y, uint64_t n_out,
                                              uint32_t B, bool sole, int accumulate) {
@@ -593,14 +632,14 @@ __device__ __forceinline__ void close_window(const Window<typename SR::T> &w,
     const uint32_t n = uint32_t(rows) * B;
     T *__restrict__ out = y + w.out0 * B;
     if (sole && !accumulate) {
-        for (uint32_t e = threadIdx.x; e < n; e += kThreads) out[e] = w.win[e];
+        for (uint32_t e = threadIdx.x; e < n; e += kT) out[e] = w.win[e];
     } else if (sole) {
-        for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+        for (uint32_t e = threadIdx.x; e < n; e += kT) {
             const T v = w.win[e];
             if (SR::contributes_out(v)) out[e] = SR::combine(out[e], v);
         }
     } else {
-        for (uint32_t e = threadIdx.x; e < n; e += kThreads) {
+        for (uint32_t e = threadIdx.x; e < n; e += kT) {
             const T v = w.win[e];
             if (SR::contributes_out(v)) SR::atomic(&out[e], v);
         }
@@ -648,14 +687,15 @@ __device__ __forceinline__ Seg stage_seg(const Seg *__restrict__ segs, uint32_t 
     return g;
 }
 
-// With use_dir the segment's first leaf comes from the directory on the
+// With kUseDir the segment's first leaf comes from the directory on the
 // device, else from the plan.
-__device__ __forceinline__ SegSig stage_sig(const DevTree &t, int d, const Seg &g,
-                                            const uint64_t *__restrict__ sig_words, int use_dir) {
+template <bool kUseDir>
+__device__ __forceinline__ SegSig stage_sig(const uint32_t *__restrict__ dir, const Seg &g,
+                                            const uint64_t *__restrict__ sig_words) {
     SegSig a;
     a.lo = g.lo;
     a.count = g.count;
-    a.leaf = (use_dir && g.count) ? wave_child_offset(t, d, g.lo) : g.leaf;
+    a.leaf = (kUseDir && g.count) ? wave_child_offset_of(sig_words, dir, g.lo) : g.leaf;
     const uint32_t lane = __lane_id();
     a.word = sig_words[(g.lo + (lane < g.count ? lane : 0u)) >> 4];
     return a;
@@ -691,36 +731,34 @@ __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_
 // tile (code_off = 1) then adds the band's strays (strays[stray_off[band]
 // .. stray_off[band + 1]), each with its block origin, first leaf and
 // signature) to the same window.
-template <class SR, int DIR, class Off>
-__global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
-    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
+template <class SR, int DIR, class Off, bool kUseDir, int kT>
+__global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
+    const uint64_t *__restrict__ sig_words, const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
+    const uint32_t *__restrict__ dir, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
     const uint64_t *__restrict__ blocks, const StrayRec *__restrict__ strays,
     const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    int use_dir, int accumulate, int runs) {
+    int accumulate, int runs) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // the window
-    __shared__ WaveCells<Off> s_cells[kWaves];
-    const int d = t.levels - 2;
+    constexpr int kW = kT / 64;
+    __shared__ WaveCells<Off> s_cells[kW];
     // uniform, so that segment descriptors are scalar loads
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint64_t *__restrict__ sig_words = t.words[d];
-    const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[d + 1]);
-    const uint32_t last_dw = uint32_t((uint64_t(t.nodes[d + 1]) + 15u) / 16u * 2u - 1u);
     WaveCells<Off> *wc = &s_cells[wave];
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
-        const Window<T> w = open_window<SR, DIR>(tl, reinterpret_cast<T *>(s_dyn), use_window, B, runs);
+        const Window<T> w = open_window<SR, DIR, kT>(tl, reinterpret_cast<T *>(s_dyn), use_window, B, runs);
         const uint32_t nseg = tl.count;
         uint32_t ring_head = 0, ring_fill = 0;   // the wave's queued cells
         uint32_t k = wave;
-        Seg g2 = stage_seg(segs, tl.first, k + 2 * kWaves, nseg);
-        SegSig a1 = stage_sig(t, d, stage_seg(segs, tl.first, k + kWaves, nseg), sig_words, use_dir);
-        SegLeaves b0 = stage_leaves(stage_sig(t, d, stage_seg(segs, tl.first, k, nseg), sig_words, use_dir),
+        Seg g2 = stage_seg(segs, tl.first, k + 2 * kW, nseg);
+        SegSig a1 = stage_sig<kUseDir>(dir, stage_seg(segs, tl.first, k + kW, nseg), sig_words);
+        SegLeaves b0 = stage_leaves(stage_sig<kUseDir>(dir, stage_seg(segs, tl.first, k, nseg), sig_words),
                                     blocks, leaf_dw, last_dw);
-        for (; k < nseg; k += kWaves) {
-            const Seg g3 = stage_seg(segs, tl.first, k + 3 * kWaves, nseg);
-            const SegSig a2 = stage_sig(t, d, g2, sig_words, use_dir);
+        for (; k < nseg; k += kW) {
+            const Seg g3 = stage_seg(segs, tl.first, k + 3 * kW, nseg);
+            const SegSig a2 = stage_sig<kUseDir>(dir, g2, sig_words);
             const SegLeaves b1 = stage_leaves(a1, blocks, leaf_dw, last_dw);
             ring_cells<SR, DIR, Off>(uint32_t(b0.blk >> 32), uint32_t(b0.blk),
                                      node_cells(b0.ssh, b0.lo32, b0.hi32), x, y, B, VL, w, wc, ring_head,
@@ -734,7 +772,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             const uint32_t band = ((DIR == K2_RIGHT) ? tl.win_row : tl.win_col) >> tl.win_log2;
             const uint32_t s0 = stray_off[band], s1 = stray_off[band + 1];
             const uint32_t lane = __lane_id();
-            for (uint32_t b = s0 + wave * 64u; b < s1; b += kThreads) {
+            for (uint32_t b = s0 + wave * 64u; b < s1; b += kT) {
                 const bool in = b + lane < s1;
                 const StrayRec r = strays[in ? b + lane : b];
                 ring_cells<SR, DIR, Off>(uint32_t(r.blk >> 32), uint32_t(r.blk), in ? r.cells : 0u, x, y, B,
@@ -742,7 +780,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void cached_kernel(
             }
         }
         ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
-        close_window<SR>(w, y, n_out, B, (tl.code_off & 2u) != 0, accumulate);
+        close_window<SR, kT>(w, y, n_out, B, (tl.code_off & 2u) != 0, accumulate);
     }
 }
 
@@ -1289,12 +1327,20 @@ __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, cons
 
 namespace {
 
-// Lanes per cell: B rounded up to a power of 2 (at most 64).  Right products
-// take at least 4: neighbouring cells of a list (Z order) often share a row,
-// and with 64 cells per instruction their LDS compare-and-swaps keep
-// colliding (B = 1: 35 ms against 14 ms for the left product at 2^27).
-uint32_t lanes_per_node(uint32_t B, int dir) {
-    uint32_t v = dir == K2_RIGHT ? 4u : 1u;
+// Lanes per cell: B rounded up to a power of 2 (at most 64).  Right
+// products over the cached level take at least 4: neighbouring cells of a
+// list (Z order) often share a row, and with 64 cells per instruction their
+// LDS float adds (compare-and-swap loops) keep colliding and retrying (B =
+// 1: 35 ms against 14 ms for the left product at 2^27); with one lane per
+// cell a ring pass also gives each lane only two cells, so fewer gathers are
+// in flight (packed Boolean R-MAT 2^24: 3.95 -> 4.13 ms).  Tree-only
+// products take B lanes, except plus-times right products (the same
+// collisions): the other semirings' atomics (max, or, min) resolve
+// collisions in one instruction (packed Boolean R-MAT 2^24 tree-only: 7.54
+// -> 6.66 ms).
+template <class SR>
+uint32_t lanes_per_node(uint32_t B, int dir, bool cached) {
+    uint32_t v = (dir == K2_RIGHT && (cached || SR::kTreeBands)) ? 4u : 1u;
     while (v < B && v < 64) v <<= 1;
     return v;
 }
@@ -1321,7 +1367,7 @@ size_t window_bytes(const Matrix &m, uint32_t B, size_t other, int *use) {
 // the band kernel (the rings and the waves' two frontier levels of band_cap
 // relative codes).
 template <class Off>
-size_t cached_other_lds() { return sizeof(WaveCells<Off>) * kWaves; }
+size_t cached_other_lds() { return sizeof(WaveCells<Off>) * (kCachedThreads / 64); }
 template <class Off>
 size_t band_other_lds(const Matrix &m) {
     return sizeof(WaveCells<Off>) * kWaves + size_t(kWaves) * 2 * m.plan.band_cap * sizeof(uint32_t);
@@ -1342,19 +1388,23 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     using T = typename SR::T;
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
     if (n_tiles == 0) return hipSuccess;
-    const uint32_t VL = lanes_per_node(B, DIR);
+    const uint32_t VL = lanes_per_node<SR>(B, DIR, true);
     const uint32_t grid = grid_for(n_tiles);
     int use = 0;
     const size_t lds = window_bytes(m, B, cached_other_lds<Off>(), &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
-    auto k = cached_kernel<SR, DIR, Off>;
+    const bool use_dir = m.plan.use_directory;
+    auto k = use_dir ? cached_kernel<SR, DIR, Off, true, kCachedThreads> : cached_kernel<SR, DIR, Off, false, kCachedThreads>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k, dim3(grid), dim3(kThreads), lds, st, m.dev, m.d_cached_tiles[DIR], n_tiles,
+    const int d = m.levels - 2;
+    const uint32_t last_dw = uint32_t((uint64_t(m.dev.nodes[d + 1]) + 15u) / 16u * 2u - 1u);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(kCachedThreads), lds, st, m.dev.words[d],
+                       reinterpret_cast<const uint32_t *>(m.dev.words[d + 1]), last_dw, m.dev.dir[d],
+                       m.d_cached_tiles[DIR], n_tiles,
                        m.d_cached_segs[DIR], m.d_cached, m.d_strays[DIR], m.d_stray_off[DIR],
                        static_cast<const T *>(x),
-                       static_cast<T *>(y), B, VL, n_out, use, m.plan.use_directory ? 1 : 0, accumulate,
-                       m.plan.row_runs ? 1 : 0);
+                       static_cast<T *>(y), B, VL, n_out, use, accumulate, m.plan.row_runs ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1370,7 +1420,7 @@ int run_tiles(const DevTree &t, const Tile *tiles, size_t n, const uint64_t *cod
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid_for(n)), dim3(kThreads), lds, st, t, tiles, uint32_t(n), codes, cap,
-                       static_cast<const T *>(x), static_cast<T *>(y), B, lanes_per_node(B, DIR), emit, bases,
+                       static_cast<const T *>(x), static_cast<T *>(y), B, lanes_per_node<SR>(B, DIR, false), emit, bases,
                        row_runs ? 1 : 0);
     return hipGetLastError();
 }
@@ -1379,7 +1429,7 @@ template <class SR, int DIR, bool EMIT, class Off = uint32_t>
 int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *emit,
                 hipStream_t st) {
     using T = typename SR::T;
-    const uint32_t VL = lanes_per_node(B, DIR);
+    const uint32_t VL = lanes_per_node<SR>(B, DIR, false);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     const Plan &p = m.plan;
     auto descent = [&]() -> int {
