@@ -585,7 +585,7 @@ def main():
                          "within_estimate": bool(used <= est["total"]),
                          "breakdown": est,
                          # 8 bytes per node of the last internal level; the rest of
-                         # cached_codes is the stray records (16 bytes per stray and direction)
+                         # cached_codes is the stray records (8 bytes per stray and direction)
                          "cached_level": 8 * nodes[-2] if mode == "cached" else 0,
                          "stray_records": (est["cached_codes"] - 8 * nodes[-2]) if mode == "cached" else 0,
                          "arena_without_strays": tree.estimate(k2.plan_defaults(

@@ -129,8 +129,9 @@ typedef struct {
        quadrants a windowed tile, and those nodes are added to their band's
        window too (strays), instead of one y atomic per cell from separate
        sparse tiles.  k2_matrix_create groups the strays by band on the
-       device (16 bytes per stray node and direction: its block origin and
-       its cells, read from its leaves once).  0: sparse tiles.  Default 1. */
+       device (8 bytes per stray node and direction: its block's coordinates
+       and its cells, read from its leaves once).  0: sparse tiles.
+       Default 1. */
     int32_t band_strays;
     /* Nodes of the last internal level per windowed cached tile (Sec. 3.4's
        tiles over the cached level, Sec. 3.5).  A band holding more is cut
@@ -153,7 +154,7 @@ typedef struct {
     uint64_t top_codes;   /* Morton codes of the tile starts (host top + splits) */
     uint64_t tiles;       /* the tile plan */
     uint64_t cached_codes;/* 8 bytes per node of the last internal level, plus
-                             16 per stray node and direction (band_strays), or 0 */
+                             8 per stray node and direction (band_strays), or 0 */
     uint64_t scratch;     /* transient product memory (0: frontiers live in LDS) */
     uint64_t alignment;   /* padding between parts */
     uint64_t arena;       /* sum of the above */

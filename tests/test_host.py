@@ -398,7 +398,7 @@ def test_estimate_parts(case):
                 log2 = int(owners[0][6])
                 nb = ((nr if w == 1 else nc) + (1 << log2) - 1) >> log2
                 stray_tiles += 16 * len(segs) + 4 * (nb + 1) + 4 * nb
-                stray_records += 16 * sum(int(r) & 0xFFFFFFFF for r, _ in segs)
+                stray_records += 8 * sum(int(r) & 0xFFFFFFFF for r, _ in segs)
             else:
                 assert len(segs) == 0
         L = o.levels

@@ -769,14 +769,16 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
         }
         if ((tl.code_off & 1u) && strays && tl.win_log2 != kNoWindow) {
             // the band's owner tile: its strays, 64 per wave at a time
-            const uint32_t band = ((DIR == K2_RIGHT) ? tl.win_row : tl.win_col) >> tl.win_log2;
+            const uint32_t band0 = (DIR == K2_RIGHT) ? tl.win_row : tl.win_col;
+            const uint32_t band = band0 >> tl.win_log2;
             const uint32_t s0 = stray_off[band], s1 = stray_off[band + 1];
             const uint32_t lane = __lane_id();
             for (uint32_t b = s0 + wave * 64u; b < s1; b += kT) {
                 const bool in = b + lane < s1;
                 const StrayRec r = strays[in ? b + lane : b];
-                ring_cells<SR, DIR, Off>(uint32_t(r.blk >> 32), uint32_t(r.blk), in ? r.cells : 0u, x, y, B,
-                                         VL, w, wc, ring_head, ring_fill);
+                const uint32_t o = band0 + r.out_in_band(), i = uint32_t(r.in());
+                ring_cells<SR, DIR, Off>(DIR == K2_RIGHT ? o : i, DIR == K2_RIGHT ? i : o, in ? r.cells() : 0u, x, y,
+                                         B, VL, w, wc, ring_head, ring_fill);
             }
         }
         ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
@@ -1317,8 +1319,9 @@ __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, cons
             const uint32_t cells = node_cells(s | ((off & 7u) << 6), leaf_dw[dw],
                                               leaf_dw[dw < last_dw ? dw + 1u : last_dw]);
             const uint32_t o = dir == K2_RIGHT ? uint32_t(blk >> 32) : uint32_t(blk);
+            const uint32_t i = dir == K2_RIGHT ? uint32_t(blk) : uint32_t(blk >> 32);
             const uint32_t pos = atomicAdd(&cursor[o >> qlog], 1u);
-            out[pos] = StrayRec{blk, cells, 0u};
+            out[pos] = StrayRec::make(cells, o & ((1u << qlog) - 1u), i);
         }
     }
 }

@@ -7,6 +7,14 @@
 
 #include "../../include/k2spmv.h"
 
+// Functions of the structures below that both the host code and the HIP
+// kernels call.
+#if defined(__HIP__)
+#define K2_HD __host__ __device__
+#else
+#define K2_HD
+#endif
+
 namespace k2 {
 
 constexpr int kMaxLevels = 32;     // n <= 2^32
@@ -63,16 +71,23 @@ static_assert(sizeof(Seg) == 16, "segment layout");
 
 // A stray: a node of the cached level outside the dense quadrants, stored
 // again with its band's other strays so that a band tile can add its cells to
-// the band's window: the node's block origin (first row << 32 | first
-// column) and its cells as read from its leaves when the matrix is created
-// (bit 4 b + q: cell q of the leaf for child b), so that a product reads no
-// leaf at a stray's random position.
+// the band's window, in 8 bytes: its cells as read from its leaves when the
+// matrix is created (bit 4 b + q: cell q of the leaf for child b; bits
+// 48-63), so that a product reads no leaf at a stray's random position; its
+// block's output coordinate relative to the band, in blocks (bits 36-47; a
+// band has at most 16384 outputs, 4096 blocks); and its block's input
+// coordinate, in blocks (bits 0-35).  Outputs are rows for right products
+// (row bands) and columns for left products.
 struct StrayRec {
-    uint64_t blk;
-    uint32_t cells;
-    uint32_t pad;
+    uint64_t bits;
+    K2_HD static StrayRec make(uint32_t cells, uint32_t out_in_band, uint64_t in) {
+        return StrayRec{(uint64_t(cells) << 48) | (uint64_t(out_in_band >> 2) << 36) | (in >> 2)};
+    }
+    K2_HD uint32_t cells() const { return uint32_t(bits >> 48); }
+    K2_HD uint32_t out_in_band() const { return uint32_t((bits >> 36) & 0xFFFu) << 2; }
+    K2_HD uint64_t in() const { return (bits & 0xFFFFFFFFFull) << 2; }
 };
-static_assert(sizeof(StrayRec) == 16, "stray layout");
+static_assert(sizeof(StrayRec) == 8, "stray layout");
 
 // The plan of a matrix: host top level, descent tiles in depth-first order and
 // the codes their first level starts from, and per product direction the
