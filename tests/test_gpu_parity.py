@@ -268,3 +268,25 @@ def test_multi_tile_bands(dev):
             torch.cuda.synchronize()
             check_parity(from_device(ya, sr), combine[sr](y0.reshape(want.shape), want), sr,
                          "accumulate " + label)
+
+
+def test_wide_batch_windows(dev):
+    """Batches 75 and 76 on a web-like 2^14 graph: a 512-row band window of
+    75-76 vectors leaves no room for the band kernel's frontiers (tree-only
+    plus-times products then take the groups' sub-tiles and the rest tiles
+    a wave each, without windows) but fits the cached kernel's window.
+    Whole outputs against the oracle, both directions, tree-only and
+    cached."""
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(29)
+    n = 2 ** 14
+    rows, cols = synth.web(n, 16, window=1024, p_local=0.8, seed=11)
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    for B, direction, mode in itertools.product((75, 76), ("right", "left"), ("tree", "cached")):
+        x = make_x(rng, "plus_times", n, B)
+        y = m.spmv(to_device(x, dev), direction=direction, batch=B, mode=mode)
+        torch.cuda.synchronize()
+        want = ref.spmv(x, oracle.PLUS_TIMES, ORC_DIR[direction], B)
+        check_parity(from_device(y, "plus_times"), want, "plus_times", f"wide batch {B} {direction} {mode}")
