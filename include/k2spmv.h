@@ -85,9 +85,11 @@ typedef struct {
        at most host_top_max nodes (never below the last internal level).
        Default 65536. */
     uint32_t host_top_max;
-    /* Keep the last internal level's nodes on the device, 8 bytes per node
-       (Sec. 3.5, "k2+F"; stored as the block coordinates their Morton codes
-       encode).  Default 0. */
+    /* Keep the last internal level's nodes on the device (Sec. 3.5, "k2+F"),
+       10 bytes per node: the block coordinates their Morton codes encode (8
+       bytes, the pages' cached codes) and the node's cells as its leaves
+       give them (2 bytes), so that a product reads neither the level's
+       signatures nor its leaves.  Default 0. */
     int32_t cache_last_level;
     /* Order of the cached-level tiles for the MI355X's 8 XCDs (each with
        its own L2; workgroup b runs on XCD b % 8).  The tiles are kept in
@@ -153,8 +155,9 @@ typedef struct {
                              child offsets of the descent tiles (scan) */
     uint64_t top_codes;   /* Morton codes of the tile starts (host top + splits) */
     uint64_t tiles;       /* the tile plan */
-    uint64_t cached_codes;/* 8 bytes per node of the last internal level, plus
-                             8 per stray node and direction (band_strays), or 0 */
+    uint64_t cached_codes;/* 10 bytes per node of the last internal level (block
+                             coordinates and cells), plus 8 per stray node and
+                             direction (band_strays), or 0 */
     uint64_t scratch;     /* transient product memory (0: frontiers live in LDS) */
     uint64_t alignment;   /* padding between parts */
     uint64_t arena;       /* sum of the above */

@@ -413,7 +413,7 @@ def test_estimate_parts(case):
         tree_only = sum(32 * (len(t.plan(opts, 3 + w)[1]) + len(t.plan(opts, 5 + w)[1]) +
                               len(t.plan(opts, 7 + w)[1])) + 8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
         assert est["tiles"] == 32 * len(tiles) + tree_only + (extra + stray_tiles if cached else 0)
-        assert est["cached_codes"] == (8 * nodes[L - 2] + stray_records if cached else 0)
+        assert est["cached_codes"] == (10 * nodes[L - 2] + stray_records if cached else 0)
         parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
                                      "scratch", "alignment"))
         assert est["arena"] == parts and est["arena"] % 256 == 0

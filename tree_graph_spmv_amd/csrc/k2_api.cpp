@@ -533,6 +533,14 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             set_hip_error(e, "cache last internal level");
             return fail(K2_E_HIP);
         }
+        m.d_cells = reinterpret_cast<uint16_t *>(m.arena + m.layout.cells_off);
+        for (int dir = 0; dir < 2; ++dir) {
+            const int ec = launch_node_cells(m, m.d_cached_segs[dir], uint32_t(m.plan.cached_segs[dir].size()), stream);
+            if (ec != hipSuccess) {
+                set_hip_error(ec, "cached cells");
+                return fail(K2_E_HIP);
+            }
+        }
         for (int dir = 0; dir < 2; ++dir) {
             const k2_status s = group_strays(m, dir, st_h);
             if (s != K2_OK) return fail(s);

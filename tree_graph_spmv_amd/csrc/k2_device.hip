@@ -722,6 +722,24 @@ __device__ __forceinline__ SegLeaves stage_leaves(const SegSig &a, const uint64_
     return b;
 }
 
+// A segment's nodes with their cells kept since the matrix was created:
+// the lane's node's block origin and its cells (0 past the segment).
+struct SegNodes {
+    uint64_t blk;
+    uint32_t cells;
+};
+__device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__restrict__ blocks,
+                                                const uint16_t *__restrict__ cells16) {
+    const uint32_t lane = __lane_id();
+    const bool in = lane < g.count;
+    const uint32_t i = g.lo + (in ? lane : 0u);
+    SegNodes d;
+    d.blk = blocks[i];
+    const uint32_t c = cells16[i];
+    d.cells = in ? c : 0u;
+    return d;
+}
+
 // One product over the cached last internal level (Sec. 3.5): each workgroup
 // takes a tile, a list of segments of up to 64 nodes of that level, each
 // with its first leaf's index; wave w takes segments w, w + 4, ...  A wave
@@ -735,7 +753,7 @@ template <class SR, int DIR, class Off, bool kUseDir, int kT>
 __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
     const uint64_t *__restrict__ sig_words, const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
     const uint32_t *__restrict__ dir, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
-    const uint64_t *__restrict__ blocks, const StrayRec *__restrict__ strays,
+    const uint64_t *__restrict__ blocks, const uint16_t *__restrict__ cells16, const StrayRec *__restrict__ strays,
     const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
     int accumulate, int runs) {
@@ -752,6 +770,20 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
         const uint32_t nseg = tl.count;
         uint32_t ring_head = 0, ring_fill = 0;   // the wave's queued cells
         uint32_t k = wave;
+        if constexpr (!kUseDir) {
+            // the nodes' cells kept since creation: two stages, a descriptor
+            // two segments ahead and the nodes one ahead
+            Seg g1 = stage_seg(segs, tl.first, k + kW, nseg);
+            SegNodes d0 = stage_nodes(stage_seg(segs, tl.first, k, nseg), blocks, cells16);
+            for (; k < nseg; k += kW) {
+                const Seg g2 = stage_seg(segs, tl.first, k + 2 * kW, nseg);
+                const SegNodes d1 = stage_nodes(g1, blocks, cells16);
+                ring_cells<SR, DIR, Off>(uint32_t(d0.blk >> 32), uint32_t(d0.blk), d0.cells, x, y, B, VL, w, wc,
+                                         ring_head, ring_fill);
+                d0 = d1;
+                g1 = g2;
+            }
+        } else {
         Seg g2 = stage_seg(segs, tl.first, k + 2 * kW, nseg);
         SegSig a1 = stage_sig<kUseDir>(dir, stage_seg(segs, tl.first, k + kW, nseg), sig_words);
         SegLeaves b0 = stage_leaves(stage_sig<kUseDir>(dir, stage_seg(segs, tl.first, k, nseg), sig_words),
@@ -766,6 +798,7 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
             b0 = b1;
             a1 = a2;
             g2 = g3;
+        }
         }
         if ((tl.code_off & 1u) && strays && tl.win_log2 != kNoWindow) {
             // the band's owner tile: its strays, 64 per wave at a time
@@ -1326,6 +1359,30 @@ __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, cons
     }
 }
 
+// The cells of every node of the given segments of the cached level, from
+// its leaves: one wave per segment, a lane per node.
+__global__ __launch_bounds__(kThreads) void node_cells_kernel(DevTree t, const Seg *__restrict__ segs,
+                                                              uint32_t n_segs, uint16_t *__restrict__ out) {
+    const uint32_t lane = __lane_id();
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint64_t *__restrict__ sig_words = t.words[t.levels - 2];
+    const uint32_t *__restrict__ leaf_dw = reinterpret_cast<const uint32_t *>(t.words[t.levels - 1]);
+    const uint32_t last_dw = uint32_t((uint64_t(t.nodes[t.levels - 1]) + 15u) / 16u * 2u - 1u);
+    for (uint32_t k = blockIdx.x * kWaves + wave; k < n_segs; k += gridDim.x * kWaves) {
+        const Seg sg = segs[k];
+        const bool in = lane < sg.count;
+        const uint32_t s = in ? nib(sig_words, uint64_t(sg.lo) + lane) : 0u;
+        uint32_t total;
+        const uint32_t ex = wave_scan(__popc(s), total);
+        if (in) {
+            const uint32_t off = sg.leaf + ex;
+            const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
+            out[sg.lo + lane] = uint16_t(node_cells(s | ((off & 7u) << 6), leaf_dw[dw],
+                                                    leaf_dw[dw < last_dw ? dw + 1u : last_dw]));
+        }
+    }
+}
+
 // ------------------------------------------------------------- launchers
 
 namespace {
@@ -1405,7 +1462,8 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     hipLaunchKernelGGL(k, dim3(grid), dim3(kCachedThreads), lds, st, m.dev.words[d],
                        reinterpret_cast<const uint32_t *>(m.dev.words[d + 1]), last_dw, m.dev.dir[d],
                        m.d_cached_tiles[DIR], n_tiles,
-                       m.d_cached_segs[DIR], m.d_cached, m.d_strays[DIR], m.d_stray_off[DIR],
+                       m.d_cached_segs[DIR], m.d_cached, use_dir ? nullptr : m.d_cells, m.d_strays[DIR],
+                       m.d_stray_off[DIR],
                        static_cast<const T *>(x),
                        static_cast<T *>(y), B, VL, n_out, use, accumulate, m.plan.row_runs ? 1 : 0);
     return hipGetLastError();
@@ -1616,6 +1674,13 @@ int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_s
     hipLaunchKernelGGL(stray_scatter_kernel, dim3(stray_grid(n_segs)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), m.dev, segs, n_segs, m.d_cached, dir,
                        uint32_t(m.plan.window_log2), cursor, out);
+    return hipGetLastError();
+}
+
+int launch_node_cells(const Matrix &m, const Seg *segs, uint32_t n_segs, void *stream) {
+    if (n_segs == 0) return hipSuccess;
+    hipLaunchKernelGGL(node_cells_kernel, dim3(stray_grid(n_segs)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), m.dev, segs, n_segs, m.d_cells);
     return hipGetLastError();
 }
 

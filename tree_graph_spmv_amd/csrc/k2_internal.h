@@ -151,6 +151,7 @@ struct Layout {
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     uint64_t stray_segs_off[2] = {0, 0}, stray_off_off[2] = {0, 0}, stray_cur_off[2] = {0, 0};
     uint64_t strays_off[2] = {0, 0};
+    uint64_t cells_off = 0;                // per node of the cached level: its cells (16 bits)
     k2_mem_breakdown mem = {};
 };
 
@@ -187,6 +188,7 @@ struct Matrix {
     const StrayRec *d_strays[2] = {nullptr, nullptr};   // grouped by band
     const uint32_t *d_stray_off[2] = {nullptr, nullptr}; // band b: d_strays[off[b] .. off[b + 1])
     uint64_t *d_cached = nullptr;        // last internal level codes or null
+    uint16_t *d_cells = nullptr;         // their cells (bit 4 b + q: cell q of the leaf for child b)
     uint32_t window_elems = 0, window_batch = 0;
     size_t lds_per_block = 0;    // LDS bytes of one workgroup (windows and the kernels' own)
     bool cached = false;
@@ -226,6 +228,9 @@ int launch_stray_count(const Matrix &m, int dir, const Seg *segs, uint32_t n_seg
                        void *stream);
 int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *cursor,
                          StrayRec *out, void *stream);
+// The cells of the nodes of the cached level that the segments cover, read
+// from their leaves, into m.d_cells.
+int launch_node_cells(const Matrix &m, const Seg *segs, uint32_t n_segs, void *stream);
 const char *hip_error_text(int err);
 // The device address of the library's fixed scratch array on the current
 // device (k2_bfs_noalloc's workspace, K2_NOALLOC_SCRATCH_BYTES bytes),
