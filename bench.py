@@ -154,6 +154,18 @@ def probe_bench(which, reps=5):
                         per_launch=n_idx, unit="G rows/s",
                         note=f"2^27 rows of {4 * R} bytes gathered at uniform random rows of a "
                              f"{4 * R}x2^27-byte x, {how}")
+                if R == 8:
+                    # the same gathers from an x that the caches hold: 1 MB
+                    # (inside every XCD's 4 MB L2) and 128 MB (inside the
+                    # 256 MB MALL, not the L2s)
+                    for lg, where in ((15, "L2"), (22, "MALL")):
+                        xs = x[: (1 << lg) * R]
+                        ids = torch.randint(0, 1 << lg, (n_idx,), device=dev, dtype=torch.int32)
+                        run(f"gather_rows_R{R}_{where}", "gather_rows", xs, out, ids, n=n_idx, row_elems=R,
+                            r=1 << lg, per_launch=n_idx, unit="G rows/s",
+                            note=f"2^27 rows of {4 * R} bytes gathered at uniform random rows of a "
+                                 f"{4 * R}x2^{lg}-byte x (resident in the {where}), plain loads")
+                        del ids
             if want("scatter"):
                 y = torch.zeros(rows * R, device=dev)
                 src = torch.rand(n_idx * R, device=dev)
