@@ -438,6 +438,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     for (int d = m.plan.top_level; d < t.levels; ++d) {
         char *p = m.arena + m.layout.words_off[d];
         m.dev.words[d] = reinterpret_cast<const uint64_t *>(p);
+        m.dev.words_end[d] = uint32_t(t.words[d].size());
         if (!t.words[d].empty()) {
             hipError_t e = hipMemcpyAsync(p, t.words[d].data(), t.words[d].size() * 8,
                                           hipMemcpyHostToDevice, st_h);
@@ -1041,6 +1042,7 @@ k2_status k2_stream_spmv(k2_stream *s, k2_direction direction, k2_semiring semir
                     "stream level words");
             // offset so that the kernels' absolute word indexes land in the staged range
             dv.words[d] = reinterpret_cast<const uint64_t *>(half + c.word_off[d]) - c.lo_word[d];
+            dv.words_end[d] = uint32_t(c.lo_word[d] + c.n_words[d]);
         }
         if (s->pinned) {
             HIP_TRY(hipMemcpyAsync(half + c.tiles_off, s->pinned + s->pin_meta[q], c.bytes - c.tiles_off,

@@ -164,6 +164,9 @@ struct DevTree {
     const uint64_t *words[kMaxLevels];   // per level (nullptr above the top)
     const uint32_t *dir[kMaxLevels];     // per internal level
     uint32_t nodes[kMaxLevels];
+    // one past the last word index of words[d] that may be read: the level's
+    // word count, or the end of the staged range in out-of-core products
+    uint32_t words_end[kMaxLevels];
     int levels;
     int top_level;
 };
