@@ -86,10 +86,13 @@ typedef struct {
        Default 65536. */
     uint32_t host_top_max;
     /* Keep the last internal level's nodes on the device (Sec. 3.5, "k2+F"),
-       10 bytes per node: the block coordinates their Morton codes encode (8
-       bytes, the pages' cached codes) and the node's cells as its leaves
-       give them (2 bytes), so that a product reads neither the level's
-       signatures nor its leaves.  Default 0. */
+       12 bytes per node: the block coordinates their Morton codes encode (8
+       bytes, the pages' cached codes) and a 4-byte node word with the
+       node's cells as its leaves give them and, when every cached tile has
+       a band window of at most 1024 rows, the block's place inside its
+       window's quadrant; a product then reads neither the level's
+       signatures nor its leaves, and with band windows only the node words.
+       Default 0. */
     int32_t cache_last_level;
     /* Order of the cached-level tiles for the MI355X's 8 XCDs (each with
        its own L2; workgroup b runs on XCD b % 8).  The tiles are kept in
@@ -155,9 +158,9 @@ typedef struct {
                              child offsets of the descent tiles (scan) */
     uint64_t top_codes;   /* Morton codes of the tile starts (host top + splits) */
     uint64_t tiles;       /* the tile plan */
-    uint64_t cached_codes;/* 10 bytes per node of the last internal level (block
-                             coordinates and cells), plus 8 per stray node and
-                             direction (band_strays), or 0 */
+    uint64_t cached_codes;/* 12 bytes per node of the last internal level (block
+                             coordinates and node words), plus 8 per stray node
+                             and direction (band_strays), or 0 */
     uint64_t scratch;     /* transient product memory (0: frontiers live in LDS) */
     uint64_t alignment;   /* padding between parts */
     uint64_t arena;       /* sum of the above */
@@ -339,7 +342,10 @@ k2_status k2_matrix_destroy(k2_matrix *matrix);
 
 /* Description of the plan a matrix uses (host): its host-top level d0 and
    descent tile count (Sec. 3.4), and whether it keeps the cached last
-   internal level (Sec. 3.5).  Errors: K2_E_INVALID_ARG (null). */
+   internal level (Sec. 3.5): *cached = 0 no, 1 yes, 2 yes and its products
+   read only the 4-byte node words (every cached tile has a band window of
+   at most 1024 rows; see cache_last_level).  Errors: K2_E_INVALID_ARG
+   (null). */
 k2_status k2_matrix_info(const k2_matrix *matrix, uint32_t *top_level, uint64_t *n_tiles,
                          int32_t *cached);
 

@@ -252,6 +252,9 @@ def test_multi_tile_bands(dev):
     for cap, strays in ((64, 1), (256, 1), (64, 0)):
         opts = k2.plan_defaults(cache_last_level=1, band_tile_nodes=cap, band_strays=strays)
         m = k2.Matrix(tree, opts, device=dev)
+        # with strays every cached tile has a 512-row window: the products
+        # read the node words only; without, the sparse tiles need the origins
+        assert m.packed_nodes == (strays == 1)
         for sr, direction, B in itertools.product(ALL_SEMIRINGS, ("right", "left"), (1, 3, 8)):
             x = make_x(rng, sr, n, B)
             xd = to_device(x, dev)

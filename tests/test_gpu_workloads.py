@@ -126,6 +126,7 @@ def test_web_n27_d9_batch8(dev):
     tree = k2.Tree(rows, cols, n, n)
     x = synth.workload_x("web_n27_d9", n)
     m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+    assert m.packed_nodes   # the benchmark's products read the 4-byte node words
     xd = to_device(x, dev)
     idx = block_sample(n, 3)
     idx_t = torch.from_numpy(idx.astype(np.int64)).to(dev)

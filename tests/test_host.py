@@ -391,7 +391,7 @@ def test_estimate_parts(case):
         top, tiles, codes = t.plan(opts, 0)
         extra = sum(32 * len(t.plan(opts, w)[1]) + 16 * len(t.plan(opts, w)[2]) for w in (1, 2))
         stray_tiles = stray_records = 0
-        for w in (1, 2):   # strays: segments, band offsets and cursors; 16-byte records
+        for w in (1, 2):   # strays: segments, band offsets and cursors; 8-byte records
             owners = [tl for tl in t.plan(opts, w)[1] if int(tl[3]) & 1]
             segs = t.plan(opts, w + 8)[2]
             if owners:
@@ -412,8 +412,9 @@ def test_estimate_parts(case):
         # descent tiles, the tree-only lists of both directions, the cached tiles
         tree_only = sum(32 * (len(t.plan(opts, 3 + w)[1]) + len(t.plan(opts, 5 + w)[1]) +
                               len(t.plan(opts, 7 + w)[1])) + 8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
-        assert est["tiles"] == 32 * len(tiles) + tree_only + (extra + stray_tiles if cached else 0)
-        assert est["cached_codes"] == (10 * nodes[L - 2] + stray_records if cached else 0)
+        # cached: plus 4 bytes of creation status
+        assert est["tiles"] == 32 * len(tiles) + tree_only + (extra + stray_tiles + 4 if cached else 0)
+        assert est["cached_codes"] == (12 * nodes[L - 2] + stray_records if cached else 0)
         parts = sum(est[k] for k in ("tree", "directory", "top_codes", "tiles", "cached_codes",
                                      "scratch", "alignment"))
         assert est["arena"] == parts and est["arena"] % 256 == 0

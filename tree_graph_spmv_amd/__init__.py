@@ -281,6 +281,8 @@ class Matrix:
         _check(lib().k2_matrix_info(h, ctypes.byref(top), ctypes.byref(nt), ctypes.byref(cached)),
                "k2_matrix_info")
         self.top_level, self.n_tiles, self.cached = int(top.value), int(nt.value), bool(cached.value)
+        # the cached level's products read only its 4-byte node words
+        self.packed_nodes = cached.value == 2
 
     def __del__(self):
         h = getattr(self, "_h", None)

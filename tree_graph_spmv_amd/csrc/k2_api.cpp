@@ -534,13 +534,43 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             set_hip_error(e, "cache last internal level");
             return fail(K2_E_HIP);
         }
-        m.d_cells = reinterpret_cast<uint16_t *>(m.arena + m.layout.cells_off);
+        m.d_nodew = reinterpret_cast<uint32_t *>(m.arena + m.layout.cells_off);
+        uint32_t *status = reinterpret_cast<uint32_t *>(m.arena + m.layout.status_off);
+        // packed node words when every cached tile with segments has a
+        // window of at most 1024 rows (a block's place in its quadrant then
+        // takes 2 x 8 bits; the XCD order's padding tiles hold none)
+        bool packed = !m.plan.use_directory && m.plan.window_log2 >= 2 && m.plan.window_log2 <= 10;
+        for (int dir = 0; dir < 2 && packed; ++dir)
+            for (const Tile &tl : m.plan.cached_tiles[dir])
+                if (tl.count && tl.win_log2 != uint32_t(m.plan.window_log2)) {
+                    packed = false;
+                    break;
+                }
+        hipError_t es = hipMemsetAsync(status, 0, 4, st_h);
+        if (es != hipSuccess) {
+            set_hip_error(int(es), "cached cells");
+            return fail(K2_E_HIP);
+        }
         for (int dir = 0; dir < 2; ++dir) {
-            const int ec = launch_node_cells(m, m.d_cached_segs[dir], uint32_t(m.plan.cached_segs[dir].size()), stream);
+            const int ec = launch_node_cells(m, const_cast<Seg *>(m.d_cached_segs[dir]),
+                                             uint32_t(m.plan.cached_segs[dir].size()), packed ? m.plan.window_log2 : 0,
+                                             status, stream);
             if (ec != hipSuccess) {
                 set_hip_error(ec, "cached cells");
                 return fail(K2_E_HIP);
             }
+        }
+        if (packed) {
+            // every segment inside one quadrant, as the plan cuts them (else
+            // the products keep reading the 8-byte block origins)
+            uint32_t st = 1;
+            es = hipMemcpyAsync(&st, status, 4, hipMemcpyDeviceToHost, st_h);
+            if (es == hipSuccess) es = hipStreamSynchronize(st_h);
+            if (es != hipSuccess) {
+                set_hip_error(int(es), "cached cells");
+                return fail(K2_E_HIP);
+            }
+            m.packed = st == 0;
         }
         for (int dir = 0; dir < 2; ++dir) {
             const k2_status s = group_strays(m, dir, st_h);
@@ -645,7 +675,7 @@ k2_status k2_matrix_info(const k2_matrix *matrix, uint32_t *top_level, uint64_t 
     if (!matrix) return K2_E_INVALID_ARG;
     if (top_level) *top_level = uint32_t(matrix->m.plan.top_level);
     if (n_tiles) *n_tiles = matrix->m.plan.tiles.size();
-    if (cached) *cached = matrix->m.cached ? 1 : 0;
+    if (cached) *cached = matrix->m.cached ? (matrix->m.packed ? 2 : 1) : 0;
     return K2_OK;
 }
 

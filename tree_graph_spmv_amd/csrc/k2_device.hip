@@ -739,15 +739,22 @@ struct SegNodes {
     uint64_t blk;
     uint32_t cells;
 };
+template <bool kPacked>
 __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__restrict__ blocks,
-                                                const uint16_t *__restrict__ cells16) {
+                                                const uint32_t *__restrict__ nodew) {
     const uint32_t lane = __lane_id();
     const bool in = lane < g.count;
     const uint32_t i = g.lo + (in ? lane : 0u);
     SegNodes d;
-    d.blk = blocks[i];
-    const uint32_t c = cells16[i];
-    d.cells = in ? c : 0u;
+    const uint32_t wv = nodew[i];
+    if constexpr (kPacked) {
+        // the block's place in the segment's quadrant, whose first row and
+        // column the segment holds
+        d.blk = (uint64_t(g.leaf + ((wv >> 14) & 0x3FCu)) << 32) | (g.pad + ((wv >> 22) & 0x3FCu));
+    } else {
+        d.blk = blocks[i];
+    }
+    d.cells = in ? (wv & 0xFFFFu) : 0u;
     return d;
 }
 
@@ -760,11 +767,11 @@ __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__
 // tile (code_off = 1) then adds the band's strays (strays[stray_off[band]
 // .. stray_off[band + 1]), each with its block origin, first leaf and
 // signature) to the same window.
-template <class SR, int DIR, class Off, bool kUseDir, int kT>
+template <class SR, int DIR, class Off, bool kUseDir, bool kPacked, int kT>
 __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
     const uint64_t *__restrict__ sig_words, const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
     const uint32_t *__restrict__ dir, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
-    const uint64_t *__restrict__ blocks, const uint16_t *__restrict__ cells16, const StrayRec *__restrict__ strays,
+    const uint64_t *__restrict__ blocks, const uint32_t *__restrict__ nodew, const StrayRec *__restrict__ strays,
     const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
     int accumulate, int runs) {
@@ -785,10 +792,10 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
             // the nodes' cells kept since creation: two stages, a descriptor
             // two segments ahead and the nodes one ahead
             Seg g1 = stage_seg(segs, tl.first, k + kW, nseg);
-            SegNodes d0 = stage_nodes(stage_seg(segs, tl.first, k, nseg), blocks, cells16);
+            SegNodes d0 = stage_nodes<kPacked>(stage_seg(segs, tl.first, k, nseg), blocks, nodew);
             for (; k < nseg; k += kW) {
                 const Seg g2 = stage_seg(segs, tl.first, k + 2 * kW, nseg);
-                const SegNodes d1 = stage_nodes(g1, blocks, cells16);
+                const SegNodes d1 = stage_nodes<kPacked>(g1, blocks, nodew);
                 ring_cells<SR, DIR, Off>(uint32_t(d0.blk >> 32), uint32_t(d0.blk), d0.cells, x, y, B, VL, w, wc,
                                          ring_head, ring_fill);
                 d0 = d1;
@@ -1417,10 +1424,15 @@ __global__ __launch_bounds__(kThreads) void stray_scatter_kernel(DevTree t, cons
     }
 }
 
-// The cells of every node of the given segments of the cached level, from
-// its leaves: one wave per segment, a lane per node.
-__global__ __launch_bounds__(kThreads) void node_cells_kernel(DevTree t, const Seg *__restrict__ segs,
-                                                              uint32_t n_segs, uint16_t *__restrict__ out) {
+// The node word of every node of the given segments of the cached level:
+// its cells from its leaves and, with qlog > 0, its block's place in its
+// 2^qlog-sided quadrant; the segment's (leaf, pad) then become the quadrant's
+// first row and column, and status bit 0 is set when a segment's nodes lie
+// in more than one quadrant.  One wave per segment, a lane per node.
+__global__ __launch_bounds__(kThreads) void node_cells_kernel(DevTree t, Seg *__restrict__ segs, uint32_t n_segs,
+                                                              const uint64_t *__restrict__ blocks, uint32_t qlog,
+                                                              uint32_t *__restrict__ out,
+                                                              uint32_t *__restrict__ status) {
     const uint32_t lane = __lane_id();
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const uint64_t *__restrict__ sig_words = t.words[t.levels - 2];
@@ -1432,11 +1444,28 @@ __global__ __launch_bounds__(kThreads) void node_cells_kernel(DevTree t, const S
         const uint32_t s = in ? nib(sig_words, uint64_t(sg.lo) + lane) : 0u;
         uint32_t total;
         const uint32_t ex = wave_scan(__popc(s), total);
+        uint32_t word = 0u, qr = 0u, qc = 0u;
         if (in) {
             const uint32_t off = sg.leaf + ex;
             const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
-            out[sg.lo + lane] = uint16_t(node_cells(s | ((off & 7u) << 6), leaf_dw[dw],
-                                                    leaf_dw[dw < last_dw ? dw + 1u : last_dw]));
+            word = node_cells(s | ((off & 7u) << 6), leaf_dw[dw], leaf_dw[dw < last_dw ? dw + 1u : last_dw]);
+            if (qlog) {
+                const uint64_t blk = blocks[sg.lo + lane];
+                const uint32_t r0 = uint32_t(blk >> 32), c0 = uint32_t(blk), m = (1u << qlog) - 1u;
+                qr = r0 & ~m;
+                qc = c0 & ~m;
+                word |= ((r0 & m) >> 2) << 16 | ((c0 & m) >> 2) << 24;
+            }
+            out[sg.lo + lane] = word;
+        }
+        if (qlog) {
+            // lane 0 holds a node (count >= 1): every node in its quadrant?
+            const uint32_t r = __builtin_amdgcn_readfirstlane(qr), c = __builtin_amdgcn_readfirstlane(qc);
+            if (in && (qr != r || qc != c)) atomicOr(status, 1u);
+            if (lane == 0) {
+                segs[k].leaf = r;
+                segs[k].pad = c;
+            }
         }
     }
 }
@@ -1512,7 +1541,9 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     const size_t lds = window_bytes(m, B, cached_other_lds<Off>(), &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     const bool use_dir = m.plan.use_directory;
-    auto k = use_dir ? cached_kernel<SR, DIR, Off, true, kCachedThreads> : cached_kernel<SR, DIR, Off, false, kCachedThreads>;
+    auto k = use_dir    ? cached_kernel<SR, DIR, Off, true, false, kCachedThreads>
+             : m.packed ? cached_kernel<SR, DIR, Off, false, true, kCachedThreads>
+                        : cached_kernel<SR, DIR, Off, false, false, kCachedThreads>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     const int d = m.levels - 2;
@@ -1520,7 +1551,7 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
     hipLaunchKernelGGL(k, dim3(grid), dim3(kCachedThreads), lds, st, m.dev.words[d],
                        reinterpret_cast<const uint32_t *>(m.dev.words[d + 1]), last_dw, m.dev.dir[d],
                        m.d_cached_tiles[DIR], n_tiles,
-                       m.d_cached_segs[DIR], m.d_cached, use_dir ? nullptr : m.d_cells, m.d_strays[DIR],
+                       m.d_cached_segs[DIR], m.d_cached, use_dir ? nullptr : m.d_nodew, m.d_strays[DIR],
                        m.d_stray_off[DIR],
                        static_cast<const T *>(x),
                        static_cast<T *>(y), B, VL, n_out, use, accumulate, m.plan.row_runs ? 1 : 0);
@@ -1735,10 +1766,11 @@ int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_s
     return hipGetLastError();
 }
 
-int launch_node_cells(const Matrix &m, const Seg *segs, uint32_t n_segs, void *stream) {
+int launch_node_cells(const Matrix &m, Seg *segs, uint32_t n_segs, int qlog, uint32_t *status, void *stream) {
     if (n_segs == 0) return hipSuccess;
     hipLaunchKernelGGL(node_cells_kernel, dim3(stray_grid(n_segs)), dim3(kThreads), 0,
-                       static_cast<hipStream_t>(stream), m.dev, segs, n_segs, m.d_cells);
+                       static_cast<hipStream_t>(stream), m.dev, segs, n_segs, m.d_cached, uint32_t(qlog),
+                       m.d_nodew, status);
     return hipGetLastError();
 }
 

@@ -151,7 +151,11 @@ struct Layout {
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     uint64_t stray_segs_off[2] = {0, 0}, stray_off_off[2] = {0, 0}, stray_cur_off[2] = {0, 0};
     uint64_t strays_off[2] = {0, 0};
-    uint64_t cells_off = 0;                // per node of the cached level: its cells (16 bits)
+    // per node of the cached level, its node word: its cells (bits 0-15) and,
+    // with packed nodes, its block's row and column inside its Q x Q quadrant
+    // (in blocks of 4, bits 16-23 and 24-31)
+    uint64_t cells_off = 0;
+    uint64_t status_off = 0;               // creation checks (4 bytes)
     k2_mem_breakdown mem = {};
 };
 
@@ -191,7 +195,11 @@ struct Matrix {
     const StrayRec *d_strays[2] = {nullptr, nullptr};   // grouped by band
     const uint32_t *d_stray_off[2] = {nullptr, nullptr}; // band b: d_strays[off[b] .. off[b + 1])
     uint64_t *d_cached = nullptr;        // last internal level codes or null
-    uint16_t *d_cells = nullptr;         // their cells (bit 4 b + q: cell q of the leaf for child b)
+    uint32_t *d_nodew = nullptr;         // their node words (cells: bit 4 b + q, cell q of the leaf for child b)
+    // Packed nodes: every cached segment lies in one Q x Q quadrant (Q = 2^
+    // plan.window_log2 <= 1024), whose origin its Seg holds in (leaf, pad);
+    // a product then reads 4 bytes per node (the node word) instead of 10.
+    bool packed = false;
     uint32_t window_elems = 0, window_batch = 0;
     size_t lds_per_block = 0;    // LDS bytes of one workgroup (windows and the kernels' own)
     bool cached = false;
@@ -231,9 +239,12 @@ int launch_stray_count(const Matrix &m, int dir, const Seg *segs, uint32_t n_seg
                        void *stream);
 int launch_stray_scatter(const Matrix &m, int dir, const Seg *segs, uint32_t n_segs, uint32_t *cursor,
                          StrayRec *out, void *stream);
-// The cells of the nodes of the cached level that the segments cover, read
-// from their leaves, into m.d_cells.
-int launch_node_cells(const Matrix &m, const Seg *segs, uint32_t n_segs, void *stream);
+// The node words of the nodes of the cached level that the segments cover,
+// their cells read from their leaves, into m.d_nodew.  With qlog (> 0) the
+// words also hold each block's place in its 2^qlog-sided quadrant, each
+// segment's (leaf, pad) are overwritten with its quadrant's first row and
+// column, and *status gets bit 0 set if a segment's nodes span quadrants.
+int launch_node_cells(const Matrix &m, Seg *segs, uint32_t n_segs, int qlog, uint32_t *status, void *stream);
 const char *hip_error_text(int err);
 // The device address of the library's fixed scratch array on the current
 // device (k2_bfs_noalloc's workspace, K2_NOALLOC_SCRATCH_BYTES bytes),

@@ -843,7 +843,8 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
         l.strays_off[dir] = take(st ? sizeof(StrayRec) * plan.stray_nodes[dir] : 0, l.mem.cached_codes);
     }
     l.cached_off = take(cached ? 8 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
-    l.cells_off = take(cached ? 2 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
+    l.cells_off = take(cached ? 4 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
+    l.status_off = take(cached ? 4 : 0, l.mem.tiles);
     l.mem.scratch = 0;
     l.mem.alignment = off - raw;
     l.mem.arena = off;
