@@ -596,10 +596,12 @@ def main():
                          "used": int(used), "library_allocated": int(lib_alloc),
                          "within_estimate": bool(used <= est["total"]),
                          "breakdown": est,
-                         # 8 bytes per node of the last internal level; the rest of
-                         # cached_codes is the stray records (8 bytes per stray and direction)
+                         # 8 bytes (block origin) and 4 (node word) per node of the
+                         # last internal level; the rest of cached_codes is the stray
+                         # records (8 bytes per stray and direction)
                          "cached_level": 8 * nodes[-2] if mode == "cached" else 0,
-                         "stray_records": (est["cached_codes"] - 8 * nodes[-2]) if mode == "cached" else 0,
+                         "node_words": 4 * nodes[-2] if mode == "cached" else 0,
+                         "stray_records": (est["cached_codes"] - 12 * nodes[-2]) if mode == "cached" else 0,
                          "arena_without_strays": tree.estimate(k2.plan_defaults(
                              tile_nodes=args.tile_nodes, cache_last_level=int(mode == "cached"),
                              **{**extra, "band_strays": 0}), semiring=semiring, batch=batch)["arena"],
