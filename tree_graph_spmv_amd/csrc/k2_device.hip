@@ -298,9 +298,9 @@ __device__ __forceinline__ void wave_lds_sync() {
 // most 4 leaves of 4 cells, so a segment has at most 1024 cells; they go
 // through the buffer kRound at a time (one round in the common case).  Off is
 // uint32_t when every offset fits, else uint64_t (half as many per round).
-template <class Off>
+template <class Off, uint32_t kSlots = 512 / sizeof(Off)>
 struct alignas(16) WaveCells {
-    static constexpr uint32_t kRound = 512 / sizeof(Off);
+    static constexpr uint32_t kRound = kSlots;
     Off xo[kRound];
     Off yo[kRound];
 };
@@ -388,13 +388,13 @@ __device__ __forceinline__ void apply_cells(const typename SR::T (&xv)[kUnroll],
 // word (serialised, and a failed compare-and-swap each).  kFull: count is
 // exactly G x kUnroll (a full pass of the ring), so no slot needs a bounds
 // test (about 5% fewer VALU instructions in a windowed right product).
-template <class SR, class Off, bool kRuns, bool kFull = false>
-__device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
+template <class SR, class Off, bool kRuns, bool kFull = false, uint32_t kSlots>
+__device__ __forceinline__ void pass_cells(const WaveCells<Off, kSlots> *wc, uint32_t head, uint32_t count,
                                            const typename SR::T *__restrict__ x,
                                            typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
                                            const Window<typename SR::T> &w) {
     using T = typename SR::T;
-    constexpr uint32_t R = WaveCells<Off>::kRound;
+    constexpr uint32_t R = kSlots;
     constexpr int kUnroll = unroll_for<Off>();
     const uint32_t lane = __lane_id();
     const uint32_t G = 64 / VL, g = lane / VL, lv = lane % VL;
@@ -451,8 +451,8 @@ __device__ __forceinline__ void pass_cells(const WaveCells<Off> *wc, uint32_t he
     }
 }
 
-template <class SR, class Off, bool kMayRun, bool kFull = false>
-__device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t head, uint32_t count,
+template <class SR, class Off, bool kMayRun, bool kFull = false, uint32_t kSlots>
+__device__ __forceinline__ void ring_pass(const WaveCells<Off, kSlots> *wc, uint32_t head, uint32_t count,
                                           const typename SR::T *__restrict__ x,
                                           typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
                                           const Window<typename SR::T> &w) {
@@ -469,12 +469,12 @@ __device__ __forceinline__ void ring_pass(const WaveCells<Off> *wc, uint32_t hea
 // counts.  Phase B (VL adjacent lanes per cell, one per vector): gather x for
 // kUnroll cells, then apply the semiring's atomics, to the LDS window when
 // the tile has one, else to y.  No workgroup barrier.
-template <class SR, int DIR, class Off>
+template <class SR, int DIR, class Off, uint32_t kSlots>
 __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_t cells,
                                            const typename SR::T *__restrict__ x,
                                            typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                           Window<typename SR::T> w, WaveCells<Off> *wc) {
-    constexpr uint32_t R = WaveCells<Off>::kRound;
+                                           Window<typename SR::T> w, WaveCells<Off, kSlots> *wc) {
+    constexpr uint32_t R = kSlots;
     uint32_t total;
     const uint32_t pos0 = wave_scan(__popc(cells), total);
     const uint32_t obase = w.win ? uint32_t(w.out0) : 0u;
@@ -510,13 +510,13 @@ __device__ __forceinline__ void leaf_cells(uint32_t row0, uint32_t col0, uint32_
 // (G x kUnroll cells, at most the ring) is queued it runs, so a segment's
 // last few cells wait for the next segment instead of taking a pass of
 // their own.  ring_drain runs what is left at the end of a tile.
-template <class SR, int DIR, class Off>
+template <class SR, int DIR, class Off, uint32_t kSlots>
 __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_t cells,
                                            const typename SR::T *__restrict__ x,
                                            typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                           const Window<typename SR::T> &w, WaveCells<Off> *wc,
+                                           const Window<typename SR::T> &w, WaveCells<Off, kSlots> *wc,
                                            uint32_t &head, uint32_t &fill) {
-    constexpr uint32_t R = WaveCells<Off>::kRound;
+    constexpr uint32_t R = kSlots;
     constexpr int kUnroll = unroll_for<Off>();
     uint32_t total;
     const uint32_t pos0 = wave_scan(__popc(cells), total);
@@ -558,10 +558,10 @@ __device__ __forceinline__ void ring_cells(uint32_t row0, uint32_t col0, uint32_
     }
 }
 
-template <class SR, int DIR, class Off>
+template <class SR, int DIR, class Off, uint32_t kSlots>
 __device__ __forceinline__ void ring_drain(const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y,
                                            uint32_t B, uint32_t VL, const Window<typename SR::T> &w,
-                                           WaveCells<Off> *wc, uint32_t &head, uint32_t &fill) {
+                                           WaveCells<Off, kSlots> *wc, uint32_t &head, uint32_t &fill) {
     if (fill) ring_pass<SR, Off, DIR == K2_RIGHT>(wc, head, fill, x, y, B, VL, w);
     wave_lds_sync();
     head = 0;
@@ -589,12 +589,12 @@ __device__ __forceinline__ uint32_t node_cells(uint32_t ssh, uint32_t lo32, uint
 // first leaf 'off': its leaf nibbles come from two leaf-level dwords, loaded
 // by every lane at clamped indexes (last_dw: the level's last dword), so no
 // load sits under a branch.
-template <class SR, int DIR, class Off>
+template <class SR, int DIR, class Off, uint32_t kSlots>
 __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
                                              const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
                                              const typename SR::T *__restrict__ x,
                                              typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                             Window<typename SR::T> w, WaveCells<Off> *wc) {
+                                             Window<typename SR::T> w, WaveCells<Off, kSlots> *wc) {
     const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
     const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
     leaf_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u,
@@ -767,7 +767,7 @@ __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__
 // tile (code_off = 1) then adds the band's strays (strays[stray_off[band]
 // .. stray_off[band + 1]), each with its block origin, first leaf and
 // signature) to the same window.
-template <class SR, int DIR, class Off, bool kUseDir, bool kPacked, int kT>
+template <class SR, int DIR, class Off, bool kUseDir, bool kPacked, int kT, uint32_t kSlots>
 __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
     const uint64_t *__restrict__ sig_words, const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
     const uint32_t *__restrict__ dir, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
@@ -778,10 +778,10 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
     using T = typename SR::T;
     extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];   // the window (16-byte reads when stored)
     constexpr int kW = kT / 64;
-    __shared__ WaveCells<Off> s_cells[kW];
+    __shared__ WaveCells<Off, kSlots> s_cells[kW];
     // uniform, so that segment descriptors are scalar loads
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    WaveCells<Off> *wc = &s_cells[wave];
+    WaveCells<Off, kSlots> *wc = &s_cells[wave];
     for (uint32_t ti = blockIdx.x; ti < n_tiles; ti += gridDim.x) {
         const Tile tl = tiles[ti];
         const Window<T> w = open_window<SR, DIR, kT>(tl, reinterpret_cast<T *>(s_dyn), use_window, B, runs);
@@ -1474,20 +1474,17 @@ __global__ __launch_bounds__(kThreads) void node_cells_kernel(DevTree t, Seg *__
 
 namespace {
 
-// Lanes per cell: B rounded up to a power of 2 (at most 64).  Right
-// products over the cached level take at least 4: neighbouring cells of a
-// list (Z order) often share a row, and with 64 cells per instruction their
-// LDS float adds (compare-and-swap loops) keep colliding and retrying (B =
-// 1: 35 ms against 14 ms for the left product at 2^27); with one lane per
-// cell a ring pass also gives each lane only two cells, so fewer gathers are
-// in flight (packed Boolean R-MAT 2^24: 3.95 -> 4.13 ms).  Tree-only
-// products take B lanes, except plus-times right products (the same
-// collisions): the other semirings' atomics (max, or, min) resolve
-// collisions in one instruction (packed Boolean R-MAT 2^24 tree-only: 7.54
-// -> 6.66 ms).
+// Lanes per cell: B rounded up to a power of 2 (at most 64).  Plus-times
+// right products take at least 4: neighbouring cells of a list (Z order)
+// often share a row, and with 64 cells per instruction their LDS float adds
+// (compare-and-swap loops) keep colliding and retrying (B = 1: 35 ms
+// against 14 ms for the left product at 2^27).  The other semirings' atomics
+// (max, or, min) resolve collisions in one instruction, so they take B lanes
+// (packed Boolean R-MAT 2^24 tree-only: 7.54 -> 6.66 ms); cached products
+// then size the ring to a full pass (run_cached).
 template <class SR>
-uint32_t lanes_per_node(uint32_t B, int dir, bool cached) {
-    uint32_t v = (dir == K2_RIGHT && (cached || SR::kTreeBands)) ? 4u : 1u;
+uint32_t lanes_per_node(uint32_t B, int dir, bool) {
+    uint32_t v = (dir == K2_RIGHT && SR::kTreeBands) ? 4u : 1u;
     while (v < B && v < 64) v <<= 1;
     return v;
 }
@@ -1513,8 +1510,8 @@ size_t window_bytes(const Matrix &m, uint32_t B, size_t other, int *use) {
 // LDS of the cached kernel beside its window (the waves' cell rings), and of
 // the band kernel (the rings and the waves' two frontier levels of band_cap
 // relative codes).
-template <class Off>
-size_t cached_other_lds() { return sizeof(WaveCells<Off>) * (kCachedThreads / 64); }
+template <class Off, uint32_t kSlots = 512 / sizeof(Off)>
+size_t cached_other_lds() { return sizeof(WaveCells<Off, kSlots>) * (kCachedThreads / 64); }
 template <class Off>
 size_t band_other_lds(const Matrix &m) {
     return sizeof(WaveCells<Off>) * kWaves + size_t(kWaves) * 2 * m.plan.band_cap * sizeof(uint32_t);
@@ -1530,20 +1527,20 @@ bool narrow_offsets(const Matrix &m, uint32_t B) {
     return uint64_t(m.n_rows > m.n_cols ? m.n_rows : m.n_cols) * B <= 0xFFFFFFFFull;
 }
 
-template <class SR, int DIR, class Off>
-int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumulate, hipStream_t st) {
+// One launch of the cached kernel with kSlots ring slots per wave.
+template <class SR, int DIR, class Off, uint32_t kSlots>
+int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, void *y, int accumulate,
+                    hipStream_t st) {
     using T = typename SR::T;
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
-    if (n_tiles == 0) return hipSuccess;
-    const uint32_t VL = lanes_per_node<SR>(B, DIR, true);
     const uint32_t grid = grid_for(n_tiles);
     int use = 0;
-    const size_t lds = window_bytes(m, B, cached_other_lds<Off>(), &use);
+    const size_t lds = window_bytes(m, B, cached_other_lds<Off, kSlots>(), &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     const bool use_dir = m.plan.use_directory;
-    auto k = use_dir    ? cached_kernel<SR, DIR, Off, true, false, kCachedThreads>
-             : m.packed ? cached_kernel<SR, DIR, Off, false, true, kCachedThreads>
-                        : cached_kernel<SR, DIR, Off, false, false, kCachedThreads>;
+    auto k = use_dir    ? cached_kernel<SR, DIR, Off, true, false, kCachedThreads, kSlots>
+             : m.packed ? cached_kernel<SR, DIR, Off, false, true, kCachedThreads, kSlots>
+                        : cached_kernel<SR, DIR, Off, false, false, kCachedThreads, kSlots>;
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     const int d = m.levels - 2;
@@ -1556,6 +1553,24 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
                        static_cast<const T *>(x),
                        static_cast<T *>(y), B, VL, n_out, use, accumulate, m.plan.row_runs ? 1 : 0);
     return hipGetLastError();
+}
+
+// The wave's ring holds one full pass, 64 / VL lane groups x kUnroll cells:
+// with one or two lanes per cell (batches 1 and 2) a 128-slot ring would let
+// a lane load 2 or 4 cells per pass, too few gathers in flight (web-like
+// 2^20 left, R-MAT 2^22 tropical: the 512-slot ring with one lane per cell
+// measured 0.84 -> 0.58 ms); at B = 1 its 16 KB per workgroup still leave
+// eight workgroups per CU.
+template <class SR, int DIR, class Off>
+int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumulate, hipStream_t st) {
+    if (m.plan.cached_tiles[DIR].empty()) return hipSuccess;
+    const uint32_t VL = lanes_per_node<SR>(B, DIR, true);
+    constexpr uint32_t k1 = 512 / sizeof(Off);
+    if constexpr (!(DIR == K2_RIGHT && SR::kTreeBands)) {   // those take 4 lanes or more
+        if (VL == 1) return run_cached_with<SR, DIR, Off, 4 * k1>(m, B, VL, x, y, accumulate, st);
+        if (VL == 2) return run_cached_with<SR, DIR, Off, 2 * k1>(m, B, VL, x, y, accumulate, st);
+    }
+    return run_cached_with<SR, DIR, Off, k1>(m, B, VL, x, y, accumulate, st);
 }
 
 // Descent tiles, depth first, a workgroup each; LDS: the frontier's two
