@@ -824,12 +824,21 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
             const uint32_t band = band0 >> tl.win_log2;
             const uint32_t s0 = stray_off[band], s1 = stray_off[band + 1];
             const uint32_t lane = __lane_id();
-            for (uint32_t b = s0 + wave * 64u; b < s1; b += kT) {
-                const bool in = b + lane < s1;
-                const StrayRec r = strays[in ? b + lane : b];
-                const uint32_t o = band0 + r.out_in_band(), i = uint32_t(r.in());
-                ring_cells<SR, DIR, Off>(DIR == K2_RIGHT ? o : i, DIR == K2_RIGHT ? i : o, in ? r.cells() : 0u, x, y,
-                                         B, VL, w, wc, ring_head, ring_fill);
+            // each group's records load while the wave works on the group
+            // before; every call has at < s1, and lanes past the band's last
+            // record read that record (no branch around the load)
+            auto rec = [&](uint32_t at) { return strays[at + lane < s1 ? at + lane : s1 - 1u]; };
+            uint32_t b = s0 + wave * 64u;
+            if (b < s1) {
+                StrayRec r = rec(b);
+                for (; b < s1; b += kT) {
+                    const StrayRec rn = rec(b + kT < s1 ? b + kT : b);
+                    const bool in = b + lane < s1;
+                    const uint32_t o = band0 + r.out_in_band(), i = uint32_t(r.in());
+                    ring_cells<SR, DIR, Off>(DIR == K2_RIGHT ? o : i, DIR == K2_RIGHT ? i : o, in ? r.cells() : 0u,
+                                             x, y, B, VL, w, wc, ring_head, ring_fill);
+                    r = rn;
+                }
             }
         }
         ring_drain<SR, DIR, Off>(x, y, B, VL, w, wc, ring_head, ring_fill);
