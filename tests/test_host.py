@@ -561,3 +561,57 @@ def test_band_tile_cap_splits_bands():
         assert ((tiles[win, 3] & 2) != 0).all()
     with pytest.raises(k2.K2Error):
         t.estimate(k2.plan_defaults(band_tile_nodes=63))
+
+
+def _spread(v):
+    v = v.astype(np.uint64)
+    out = np.zeros_like(v)
+    for b in range(32):
+        out |= ((v >> np.uint64(b)) & np.uint64(1)) << np.uint64(2 * b)
+    return out
+
+
+def _compact(m):
+    out = np.zeros_like(m)
+    for b in range(32):
+        out |= ((m >> np.uint64(2 * b)) & np.uint64(1)) << np.uint64(b)
+    return out
+
+
+@pytest.mark.parametrize("name", ["web14", "banded", "rmat14"])
+@pytest.mark.parametrize("cap", [65536, 64])
+def test_cached_segments_in_one_quadrant(name, cap):
+    """The packed node words rest on the plan cutting every windowed cached
+    tile's segments inside one Q x Q quadrant of the tile's band (Sec. 3.4
+    tiles over a band's dense quadrants): checked against the nodes of level
+    l-2 rebuilt from the edges (the distinct 4x4 blocks in Morton order)."""
+    if name == "web14":
+        n = 2 ** 14
+        r, c = synth.web(n, 16, window=1024, p_local=0.8, seed=7)
+        nr = nc = n
+    else:
+        r, c, nr, nc = CASES[name]()
+    t = k2.Tree(r, c, nr, nc)
+    blocks = np.unique((_spread(r.astype(np.uint64) >> np.uint64(2)) << np.uint64(1)) |
+                       _spread(c.astype(np.uint64) >> np.uint64(2)))
+    assert blocks.size == t.level_nodes()[t.levels - 2]
+    row0 = (_compact(blocks >> np.uint64(1)) * 4).astype(np.int64)
+    col0 = (_compact(blocks) * 4).astype(np.int64)
+    opts = k2.plan_defaults(cache_last_level=1, band_tile_nodes=cap)
+    checked = 0
+    for which in (1, 2):
+        _, tiles, segs = t.plan(opts, which=which)
+        lo = (segs[:, 0] >> np.uint64(32)).astype(np.int64)
+        cnt = (segs[:, 0] & np.uint64(0xFFFFFFFF)).astype(np.int64)
+        for tl in tiles:
+            if int(tl[6]) == 0xFFFFFFFF or int(tl[1]) == 0:
+                continue
+            q = 1 << int(tl[6])
+            band0 = int(tl[4]) if which == 1 else int(tl[5])
+            for k in range(int(tl[0]), int(tl[0]) + int(tl[1])):
+                a, b = lo[k], lo[k] + cnt[k]
+                qr, qc = row0[a:b] // q, col0[a:b] // q
+                assert (qr == qr[0]).all() and (qc == qc[0]).all()
+                assert (qr[0] if which == 1 else qc[0]) * q == band0
+                checked += 1
+    assert checked > 0 or name == "rmat14"
