@@ -670,7 +670,8 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(uint32_t *__restrict__ y
     for (uint64_t k = n4 * 4 + i; k < n; k += stride) y[k] = value;
 }
 
-// Pipeline state of one segment of a cached tile, in three stages: its
+// Pipeline state of one segment of a cached tile in the directory ablation
+// (kUseDir), in three stages: its
 // descriptor (uniform: a scalar load), issued three segments ahead; the
 // 64-bit signature word holding each lane's node, two segments ahead; and
 // (SegLeaves) one segment ahead: the lane's node's block origin (first row
@@ -759,14 +760,18 @@ __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__
 }
 
 // One product over the cached last internal level (Sec. 3.5): each workgroup
-// takes a tile, a list of segments of up to 64 nodes of that level, each
-// with its first leaf's index; wave w takes segments w, w + 4, ...  A wave
-// works on four of its segments at once: while it visits the leaves of one,
-// the block origins and leaf signatures of the next, the signatures of the
-// one after and the descriptor of the third are in flight.  A band's owner
-// tile (code_off = 1) then adds the band's strays (strays[stray_off[band]
-// .. stray_off[band + 1]), each with its block origin, first leaf and
-// signature) to the same window.
+// takes a tile, a list of segments of up to 64 nodes of that level; wave w
+// takes segments w, w + 4, ...  With the node words kept since creation
+// (!kUseDir) a wave works on three of its segments at once: while it lists
+// the cells of one, the node words (and, unless kPacked, the block origins)
+// of the next and the descriptor of the one after are in flight; kPacked
+// segments carry their quadrant's origin, so the node words alone give each
+// block's origin.  With kUseDir (the directory ablation) the wave reads the
+// signatures, the directory and the leaves instead, four segments at once.
+// A band's owner tile (code_off = 1) then adds the band's strays
+// (strays[stray_off[band] .. stray_off[band + 1]): each with its cells, its
+// output coordinate in the band and its input block) to the same window.
+// kSlots: the cell ring of each wave (one full pass).
 template <class SR, int DIR, class Off, bool kUseDir, bool kPacked, int kT, uint32_t kSlots>
 __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
     const uint64_t *__restrict__ sig_words, const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
