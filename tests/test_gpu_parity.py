@@ -293,3 +293,26 @@ def test_wide_batch_windows(dev):
         torch.cuda.synchronize()
         want = ref.spmv(x, oracle.PLUS_TIMES, ORC_DIR[direction], B)
         check_parity(from_device(y, "plus_times"), want, "plus_times", f"wide batch {B} {direction} {mode}")
+
+
+def test_ring_per_lane_count(dev):
+    """Cached products size each wave's cell ring to one full pass: 512 slots
+    at one lane per cell (batch 1, and every batch-1 max / or / min right
+    product), 256 at two (batch 2), 128 from four.  Web-like 2^14 and R-MAT
+    2^14 graphs, every semiring, both directions, batches 1 and 2, whole
+    outputs against the oracle (the passes run full and drain at each tile's
+    end)."""
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(31)
+    graphs = (("web14", synth.web(2 ** 14, 16, window=1024, p_local=0.8, seed=13), 2 ** 14),
+              ("rmat14", synth.rmat(14, 200000, seed=14), 2 ** 14))
+    for label, (rows, cols), n in graphs:
+        tree = k2.Tree(rows, cols, n, n)
+        ref = oracle.OracleTree(rows, cols, n, n)
+        m = k2.Matrix(tree, k2.plan_defaults(cache_last_level=1), device=dev)
+        for sr, direction, B in itertools.product(ALL_SEMIRINGS, ("right", "left"), (1, 2)):
+            x = make_x(rng, sr, n, B)
+            y = m.spmv(to_device(x, dev), direction=direction, semiring=sr, batch=B, mode="cached")
+            torch.cuda.synchronize()
+            want = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
+            check_parity(from_device(y, sr), want, sr, f"ring {label} {sr} {direction} B={B}")
