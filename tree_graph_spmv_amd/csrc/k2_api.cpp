@@ -535,6 +535,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             return fail(K2_E_HIP);
         }
         m.d_nodew = reinterpret_cast<uint32_t *>(m.arena + m.layout.cells_off);
+        m.d_inmask = reinterpret_cast<uint32_t *>(m.arena + m.layout.inmask_off);
         uint32_t *status = reinterpret_cast<uint32_t *>(m.arena + m.layout.status_off);
         // packed node words when every cached tile with segments has a
         // window of at most 1024 rows (a block's place in its quadrant then
@@ -786,6 +787,9 @@ k2_status bfs_run(Matrix &m, k2_direction direction, const uint32_t *sources, ui
     // whose marking then stores distances itself
     bool table = false;
     *levels = 0;
+    // (vertex, source) pairs in the frontier: the products list only the
+    // cells of frontier rows while fewer than half the rows can hold one
+    unsigned long long frontier = n_sources;
     for (uint32_t level = 1; level <= max_levels && level < 0x7FFFFFFFu; ++level) {
         HIP_TRY(hipMemsetAsync(count, 0, 8, st), "search count");
         if (!table && level >= (1u << kBfsPlanes)) {
@@ -793,7 +797,7 @@ k2_status bfs_run(Matrix &m, k2_direction direction, const uint32_t *sources, ui
             table = true;
         }
         if (!empty && e == hipSuccess)
-            e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, 1, stream)
+            e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, 1, stream, frontier < n / 2)
                          : launch_descent(m, direction, K2_BOOLEAN_U32X32, W, F, Y, nullptr, stream);
         if (e == hipSuccess)
             e = launch_bfs_mark(Y, V, F, table ? nullptr : planes, d_dist, n * W, W, n_sources, int32_t(level),
@@ -806,6 +810,7 @@ k2_status bfs_run(Matrix &m, k2_direction direction, const uint32_t *sources, ui
         HIP_TRY(hipMemcpyAsync(&found, count, 8, hipMemcpyDeviceToHost, st), "search count");
         HIP_TRY(hipStreamSynchronize(st), "search level");
         if (reached_per_level) reached_per_level[level - 1] = found;
+        frontier = found;
         if (found == 0) break;
         *levels = level;
     }

@@ -759,6 +759,50 @@ __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__
     return d;
 }
 
+// Cells of a 4x4 block whose input (its column in a right product, its row
+// in a left one) is one of the set bits of in4 (bit c: the block's input
+// origin + c), as a 16-bit cell mask (bit 4 b + q as in node_cells).
+constexpr uint32_t cells_on_input(bool right, uint32_t c) {
+    uint32_t m = 0;
+    for (uint32_t t = 0; t < 16; ++t)
+        if (((cell_offset_table(!right) >> (2 * t)) & 3u) == c) m |= 1u << t;
+    return m;
+}
+template <int DIR>
+__device__ __forceinline__ uint32_t cells_with_inputs(uint32_t in4) {
+    constexpr bool kR = DIR == K2_RIGHT;
+    return ((in4 & 1u) ? cells_on_input(kR, 0) : 0u) | ((in4 & 2u) ? cells_on_input(kR, 1) : 0u) |
+           ((in4 & 4u) ? cells_on_input(kR, 2) : 0u) | ((in4 & 8u) ? cells_on_input(kR, 3) : 0u);
+}
+// The input bit array's word holding the bits of a block's 4 inputs from
+// input origin in0 (a multiple of 4), and those 4 bits.
+__device__ __forceinline__ uint32_t inmask_word(const uint32_t *__restrict__ inmask, uint32_t in0) {
+    return inmask[in0 >> 5];
+}
+__device__ __forceinline__ uint32_t inmask_bits(uint32_t word, uint32_t in0) { return (word >> (in0 & 31u)) & 15u; }
+
+// The input bit array of a product: bit i of word i / 32 is set when input
+// row i has a contributing vector (one of x[i B .. i B + B - 1] is not the
+// semiring's zero); rows past n_in read 0.  A wave writes the two words of
+// its 64 rows from one ballot.
+template <class SR>
+__global__ __launch_bounds__(kThreads) void inmask_kernel(const typename SR::T *__restrict__ x, uint64_t n_in,
+                                                          uint32_t B, uint32_t *__restrict__ mask) {
+    const uint64_t stride = uint64_t(gridDim.x) * kThreads;
+    const uint64_t n_words = (n_in + 31) / 32;
+    for (uint64_t i0 = uint64_t(blockIdx.x) * kThreads + (threadIdx.x & ~63u); i0 < n_in; i0 += stride) {
+        const uint64_t i = i0 + __lane_id();
+        bool c = false;
+        if (i < n_in)
+            for (uint32_t v = 0; v < B; ++v) c = c || SR::contributes(x[i * B + v]);
+        const uint64_t bal = __ballot(c);
+        if (__lane_id() == 0) {
+            mask[i0 >> 5] = uint32_t(bal);
+            if ((i0 >> 5) + 1 < n_words) mask[(i0 >> 5) + 1] = uint32_t(bal >> 32);
+        }
+    }
+}
+
 // One product over the cached last internal level (Sec. 3.5): each workgroup
 // takes a tile, a list of segments of up to 64 nodes of that level; wave w
 // takes segments w, w + 4, ...  With the node words kept since creation
@@ -771,15 +815,20 @@ __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__
 // A band's owner tile (code_off = 1) then adds the band's strays
 // (strays[stray_off[band] .. stray_off[band + 1]): each with its cells, its
 // output coordinate in the band and its input block) to the same window.
-// kSlots: the cell ring of each wave (one full pass).
-template <class SR, int DIR, class Off, bool kUseDir, bool kPacked, int kT, uint32_t kSlots>
+// kSlots: the cell ring of each wave (one full pass).  kFilter (the max /
+// or / min semirings): the listing keeps only the cells whose input row has
+// a contributing vector (inmask), so the passes gather x for those alone;
+// the pipeline then loads each segment's node words two segments ahead and
+// its input bits one ahead, and each stray group's records two groups ahead
+// and their input bits one ahead.
+template <class SR, int DIR, class Off, bool kUseDir, bool kPacked, int kT, uint32_t kSlots, bool kFilter>
 __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
     const uint64_t *__restrict__ sig_words, const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
     const uint32_t *__restrict__ dir, const Tile *__restrict__ tiles, uint32_t n_tiles, const Seg *__restrict__ segs,
     const uint64_t *__restrict__ blocks, const uint32_t *__restrict__ nodew, const StrayRec *__restrict__ strays,
     const uint32_t *__restrict__ stray_off, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, uint64_t n_out, int use_window,
-    int accumulate, int runs) {
+    int accumulate, int runs, const uint32_t *__restrict__ inmask) {
     using T = typename SR::T;
     extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];   // the window (16-byte reads when stored)
     constexpr int kW = kT / 64;
@@ -793,7 +842,27 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
         const uint32_t nseg = tl.count;
         uint32_t ring_head = 0, ring_fill = 0;   // the wave's queued cells
         uint32_t k = wave;
-        if constexpr (!kUseDir) {
+        // a node's input origin (its block's first column, right; row, left)
+        auto in0_of = [&](const SegNodes &d) { return DIR == K2_RIGHT ? uint32_t(d.blk) : uint32_t(d.blk >> 32); };
+        if constexpr (!kUseDir && kFilter) {
+            // descriptor three segments ahead, node words two, input bits one
+            Seg g2 = stage_seg(segs, tl.first, k + 2 * kW, nseg);
+            SegNodes d0 = stage_nodes<kPacked>(stage_seg(segs, tl.first, k, nseg), blocks, nodew);
+            SegNodes d1 = stage_nodes<kPacked>(stage_seg(segs, tl.first, k + kW, nseg), blocks, nodew);
+            uint32_t m0 = inmask_word(inmask, in0_of(d0));
+            for (; k < nseg; k += kW) {
+                const Seg g3 = stage_seg(segs, tl.first, k + 3 * kW, nseg);
+                const SegNodes d2 = stage_nodes<kPacked>(g2, blocks, nodew);
+                const uint32_t m1 = inmask_word(inmask, in0_of(d1));
+                const uint32_t cells = d0.cells & cells_with_inputs<DIR>(inmask_bits(m0, in0_of(d0)));
+                ring_cells<SR, DIR, Off>(uint32_t(d0.blk >> 32), uint32_t(d0.blk), cells, x, y, B, VL, w, wc,
+                                         ring_head, ring_fill);
+                d0 = d1;
+                d1 = d2;
+                m0 = m1;
+                g2 = g3;
+            }
+        } else if constexpr (!kUseDir) {
             // the nodes' cells kept since creation: two stages, a descriptor
             // two segments ahead and the nodes one ahead
             Seg g1 = stage_seg(segs, tl.first, k + kW, nseg);
@@ -834,7 +903,23 @@ __global__ __launch_bounds__(kT, kOccupancy * kThreads / kT) void cached_kernel(
             // record read that record (no branch around the load)
             auto rec = [&](uint32_t at) { return strays[at + lane < s1 ? at + lane : s1 - 1u]; };
             uint32_t b = s0 + wave * 64u;
-            if (b < s1) {
+            if (kFilter && b < s1) {
+                // records two groups ahead, their input bits one ahead
+                StrayRec r = rec(b), r1 = rec(b + kT < s1 ? b + kT : b);
+                uint32_t m0 = inmask_word(inmask, uint32_t(r.in()));
+                for (; b < s1; b += kT) {
+                    const StrayRec r2 = rec(b + 2 * kT < s1 ? b + 2 * kT : b);
+                    const uint32_t m1 = inmask_word(inmask, uint32_t(r1.in()));
+                    const bool in = b + lane < s1;
+                    const uint32_t o = band0 + r.out_in_band(), i = uint32_t(r.in());
+                    const uint32_t cells = in ? r.cells() & cells_with_inputs<DIR>(inmask_bits(m0, i)) : 0u;
+                    ring_cells<SR, DIR, Off>(DIR == K2_RIGHT ? o : i, DIR == K2_RIGHT ? i : o, cells, x, y, B, VL,
+                                             w, wc, ring_head, ring_fill);
+                    r = r1;
+                    r1 = r2;
+                    m0 = m1;
+                }
+            } else if (b < s1) {
                 StrayRec r = rec(b);
                 for (; b < s1; b += kT) {
                     const StrayRec rn = rec(b + kT < s1 ? b + kT : b);
@@ -1544,7 +1629,7 @@ bool narrow_offsets(const Matrix &m, uint32_t B) {
 // One launch of the cached kernel with kSlots ring slots per wave.
 template <class SR, int DIR, class Off, uint32_t kSlots>
 int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, void *y, int accumulate,
-                    hipStream_t st) {
+                    bool want_filter, hipStream_t st) {
     using T = typename SR::T;
     const uint32_t n_tiles = uint32_t(m.plan.cached_tiles[DIR].size());
     const uint32_t grid = grid_for(n_tiles);
@@ -1552,9 +1637,25 @@ int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, voi
     const size_t lds = window_bytes(m, B, cached_other_lds<Off, kSlots>(), &use);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     const bool use_dir = m.plan.use_directory;
-    auto k = use_dir    ? cached_kernel<SR, DIR, Off, true, false, kCachedThreads, kSlots>
-             : m.packed ? cached_kernel<SR, DIR, Off, false, true, kCachedThreads, kSlots>
-                        : cached_kernel<SR, DIR, Off, false, false, kCachedThreads, kSlots>;
+    // the max / or / min semirings list only the cells whose input row has a
+    // contributing vector (plus-times inputs are rarely zero)
+    constexpr bool kF = !SR::kWindowUnchecked;
+    const bool filter = kF && !use_dir && want_filter;
+    auto k = use_dir    ? cached_kernel<SR, DIR, Off, true, false, kCachedThreads, kSlots, false>
+             : m.packed ? (filter ? cached_kernel<SR, DIR, Off, false, true, kCachedThreads, kSlots, kF>
+                                  : cached_kernel<SR, DIR, Off, false, true, kCachedThreads, kSlots, false>)
+                        : (filter ? cached_kernel<SR, DIR, Off, false, false, kCachedThreads, kSlots, kF>
+                                  : cached_kernel<SR, DIR, Off, false, false, kCachedThreads, kSlots, false>);
+    if (filter) {
+        const uint64_t n_in = DIR == K2_RIGHT ? m.n_cols : m.n_rows;
+        const uint64_t waves = (n_in + 63) / 64;
+        const uint64_t blocks = (waves + kWaves - 1) / kWaves;
+        const uint32_t g = uint32_t(blocks < 8192 ? (blocks ? blocks : 1) : 8192);
+        hipLaunchKernelGGL(inmask_kernel<SR>, dim3(g), dim3(kThreads), 0, st, static_cast<const T *>(x), n_in, B,
+                           m.d_inmask);
+        int e0 = hipGetLastError();
+        if (e0 != hipSuccess) return e0;
+    }
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     const int d = m.levels - 2;
@@ -1565,7 +1666,8 @@ int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, voi
                        m.d_cached_segs[DIR], m.d_cached, use_dir ? nullptr : m.d_nodew, m.d_strays[DIR],
                        m.d_stray_off[DIR],
                        static_cast<const T *>(x),
-                       static_cast<T *>(y), B, VL, n_out, use, accumulate, m.plan.row_runs ? 1 : 0);
+                       static_cast<T *>(y), B, VL, n_out, use, accumulate, m.plan.row_runs ? 1 : 0,
+                       filter ? m.d_inmask : nullptr);
     return hipGetLastError();
 }
 
@@ -1576,15 +1678,15 @@ int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, voi
 // measured 0.84 -> 0.58 ms); at B = 1 its 16 KB per workgroup still leave
 // eight workgroups per CU.
 template <class SR, int DIR, class Off>
-int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumulate, hipStream_t st) {
+int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumulate, bool filter, hipStream_t st) {
     if (m.plan.cached_tiles[DIR].empty()) return hipSuccess;
     const uint32_t VL = lanes_per_node<SR>(B, DIR, true);
     constexpr uint32_t k1 = 512 / sizeof(Off);
     if constexpr (!(DIR == K2_RIGHT && SR::kTreeBands)) {   // those take 4 lanes or more
-        if (VL == 1) return run_cached_with<SR, DIR, Off, 4 * k1>(m, B, VL, x, y, accumulate, st);
-        if (VL == 2) return run_cached_with<SR, DIR, Off, 2 * k1>(m, B, VL, x, y, accumulate, st);
+        if (VL == 1) return run_cached_with<SR, DIR, Off, 4 * k1>(m, B, VL, x, y, accumulate, filter, st);
+        if (VL == 2) return run_cached_with<SR, DIR, Off, 2 * k1>(m, B, VL, x, y, accumulate, filter, st);
     }
-    return run_cached_with<SR, DIR, Off, k1>(m, B, VL, x, y, accumulate, st);
+    return run_cached_with<SR, DIR, Off, k1>(m, B, VL, x, y, accumulate, filter, st);
 }
 
 // Descent tiles, depth first, a workgroup each; LDS: the frontier's two
@@ -1662,17 +1764,17 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
 }
 
 template <int DIR>
-int dispatch_cached(const Matrix &m, int semiring, uint32_t B, const void *x, void *y, int acc,
+int dispatch_cached(const Matrix &m, int semiring, uint32_t B, const void *x, void *y, int acc, bool f,
                     hipStream_t st) {
     switch (semiring) {
-    case K2_PLUS_TIMES_F32: return narrow_offsets(m, B) ? run_cached<PlusTimes, DIR, uint32_t>(m, B, x, y, acc, st)
-                                                         : run_cached<PlusTimes, DIR, uint64_t>(m, B, x, y, acc, st);
-    case K2_BOOLEAN_F32: return narrow_offsets(m, B) ? run_cached<BooleanF32, DIR, uint32_t>(m, B, x, y, acc, st)
-                                                         : run_cached<BooleanF32, DIR, uint64_t>(m, B, x, y, acc, st);
-    case K2_BOOLEAN_U32X32: return narrow_offsets(m, B) ? run_cached<BooleanU32, DIR, uint32_t>(m, B, x, y, acc, st)
-                                                         : run_cached<BooleanU32, DIR, uint64_t>(m, B, x, y, acc, st);
-    case K2_TROPICAL_F32: return narrow_offsets(m, B) ? run_cached<Tropical, DIR, uint32_t>(m, B, x, y, acc, st)
-                                                         : run_cached<Tropical, DIR, uint64_t>(m, B, x, y, acc, st);
+    case K2_PLUS_TIMES_F32: return narrow_offsets(m, B) ? run_cached<PlusTimes, DIR, uint32_t>(m, B, x, y, acc, f, st)
+                                                         : run_cached<PlusTimes, DIR, uint64_t>(m, B, x, y, acc, f, st);
+    case K2_BOOLEAN_F32: return narrow_offsets(m, B) ? run_cached<BooleanF32, DIR, uint32_t>(m, B, x, y, acc, f, st)
+                                                         : run_cached<BooleanF32, DIR, uint64_t>(m, B, x, y, acc, f, st);
+    case K2_BOOLEAN_U32X32: return narrow_offsets(m, B) ? run_cached<BooleanU32, DIR, uint32_t>(m, B, x, y, acc, f, st)
+                                                         : run_cached<BooleanU32, DIR, uint64_t>(m, B, x, y, acc, f, st);
+    case K2_TROPICAL_F32: return narrow_offsets(m, B) ? run_cached<Tropical, DIR, uint32_t>(m, B, x, y, acc, f, st)
+                                                         : run_cached<Tropical, DIR, uint64_t>(m, B, x, y, acc, f, st);
     }
     return hipErrorInvalidValue;
 }
@@ -1710,10 +1812,10 @@ int launch_fill(void *y, uint64_t n_words32, uint32_t value, void *stream) {
 }
 
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
-                  int accumulate, void *stream) {
+                  int accumulate, void *stream, bool filter) {
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return dir == K2_RIGHT ? dispatch_cached<K2_RIGHT>(m, semiring, batch, x, y, accumulate, st)
-                           : dispatch_cached<K2_LEFT>(m, semiring, batch, x, y, accumulate, st);
+    return dir == K2_RIGHT ? dispatch_cached<K2_RIGHT>(m, semiring, batch, x, y, accumulate, filter, st)
+                           : dispatch_cached<K2_LEFT>(m, semiring, batch, x, y, accumulate, filter, st);
 }
 
 bool cached_writes_all(const Matrix &m, int dir, uint32_t batch) {

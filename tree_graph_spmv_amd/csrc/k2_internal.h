@@ -156,6 +156,7 @@ struct Layout {
     // (in blocks of 4, bits 16-23 and 24-31)
     uint64_t cells_off = 0;
     uint64_t status_off = 0;               // creation checks (4 bytes)
+    uint64_t inmask_off = 0;               // input bit array of exact-semiring cached products
     k2_mem_breakdown mem = {};
 };
 
@@ -196,6 +197,10 @@ struct Matrix {
     const uint32_t *d_stray_off[2] = {nullptr, nullptr}; // band b: d_strays[off[b] .. off[b + 1])
     uint64_t *d_cached = nullptr;        // last internal level codes or null
     uint32_t *d_nodew = nullptr;         // their node words (cells: bit 4 b + q, cell q of the leaf for child b)
+    // Cached products of the max / or / min semirings first mark the input
+    // rows with a contributing vector here (a bit each), so that the
+    // listing drops the cells of the others before any x gather.
+    uint32_t *d_inmask = nullptr;
     // Packed nodes: every cached segment lies in one Q x Q quadrant (Q = 2^
     // plan.window_log2 <= 1024), whose origin its Seg holds in (leaf, pad);
     // a product then reads 4 bytes per node (the node word) instead of 10.
@@ -227,8 +232,10 @@ int launch_descent_tiles(const DevTree &t, const Tile *tiles, size_t n_tiles, co
                          int dir, int semiring, uint32_t batch, const void *x, void *y, void *stream);
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
                    uint64_t *emit_codes, void *stream);
+// filter (max / or / min semirings): list only the cells whose input row
+// has a contributing vector (worth it unless most rows have one)
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
-                  int accumulate, void *stream);
+                  int accumulate, void *stream, bool filter = true);
 // Whether a cached product of this batch writes every element of y itself
 // (windows in use and every band its own tile's), so y needs no fill.
 bool cached_writes_all(const Matrix &m, int dir, uint32_t batch);
