@@ -429,6 +429,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
     std::memset(&m.dev, 0, sizeof(m.dev));
     m.dev.levels = t.levels;
     m.dev.top_level = m.plan.top_level;
+    m.d_inmask = reinterpret_cast<uint32_t *>(m.arena + m.layout.inmask_off);
     hipStream_t st_h = static_cast<hipStream_t>(stream);
     auto fail = [&](k2_status s) {
         delete mx;
@@ -535,7 +536,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             return fail(K2_E_HIP);
         }
         m.d_nodew = reinterpret_cast<uint32_t *>(m.arena + m.layout.cells_off);
-        m.d_inmask = reinterpret_cast<uint32_t *>(m.arena + m.layout.inmask_off);
+
         uint32_t *status = reinterpret_cast<uint32_t *>(m.arena + m.layout.status_off);
         // packed node words when every cached tile with segments has a
         // window of at most 1024 rows (a block's place in its quadrant then
@@ -798,7 +799,8 @@ k2_status bfs_run(Matrix &m, k2_direction direction, const uint32_t *sources, ui
         }
         if (!empty && e == hipSuccess)
             e = m.cached ? launch_cached(m, direction, K2_BOOLEAN_U32X32, W, F, Y, 1, stream, frontier < n / 2)
-                         : launch_descent(m, direction, K2_BOOLEAN_U32X32, W, F, Y, nullptr, stream);
+                         : launch_descent(m, direction, K2_BOOLEAN_U32X32, W, F, Y, nullptr, stream,
+                                          frontier < n / 2);
         if (e == hipSuccess)
             e = launch_bfs_mark(Y, V, F, table ? nullptr : planes, d_dist, n * W, W, n_sources, int32_t(level),
                                 count, stream);

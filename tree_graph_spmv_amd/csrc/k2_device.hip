@@ -589,16 +589,46 @@ __device__ __forceinline__ uint32_t node_cells(uint32_t ssh, uint32_t lo32, uint
 // first leaf 'off': its leaf nibbles come from two leaf-level dwords, loaded
 // by every lane at clamped indexes (last_dw: the level's last dword), so no
 // load sits under a branch.
-template <class SR, int DIR, class Off, uint32_t kSlots>
+// Cells of a 4x4 block whose input (its column in a right product, its row
+// in a left one) is one of the set bits of in4 (bit c: the block's input
+// origin + c), as a 16-bit cell mask (bit 4 b + q as in node_cells).
+constexpr uint32_t cells_on_input(bool right, uint32_t c) {
+    uint32_t m = 0;
+    for (uint32_t t = 0; t < 16; ++t)
+        if (((cell_offset_table(!right) >> (2 * t)) & 3u) == c) m |= 1u << t;
+    return m;
+}
+template <int DIR>
+__device__ __forceinline__ uint32_t cells_with_inputs(uint32_t in4) {
+    constexpr bool kR = DIR == K2_RIGHT;
+    return ((in4 & 1u) ? cells_on_input(kR, 0) : 0u) | ((in4 & 2u) ? cells_on_input(kR, 1) : 0u) |
+           ((in4 & 4u) ? cells_on_input(kR, 2) : 0u) | ((in4 & 8u) ? cells_on_input(kR, 3) : 0u);
+}
+// The input bit array's word holding the bits of a block's 4 inputs from
+// input origin in0 (a multiple of 4), and those 4 bits.
+__device__ __forceinline__ uint32_t inmask_word(const uint32_t *__restrict__ inmask, uint32_t in0) {
+    return inmask[in0 >> 5];
+}
+__device__ __forceinline__ uint32_t inmask_bits(uint32_t word, uint32_t in0) { return (word >> (in0 & 31u)) & 15u; }
+
+// kFilter: keep only the cells whose input row has a contributing vector
+// (inmask); its word loads with the leaf words.
+template <class SR, int DIR, class Off, bool kFilter, uint32_t kSlots>
 __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
                                              const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
                                              const typename SR::T *__restrict__ x,
                                              typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                             Window<typename SR::T> w, WaveCells<Off, kSlots> *wc) {
+                                             Window<typename SR::T> w, WaveCells<Off, kSlots> *wc,
+                                             const uint32_t *__restrict__ inmask) {
     const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
     const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
-    leaf_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u,
-                             node_cells(s | ((off & 7u) << 6), lo32, hi32), x, y, B, VL, w, wc);
+    const uint32_t row0 = compact_even(code >> 1) * 4u, col0 = compact_even(code) * 4u;
+    uint32_t cells = node_cells(s | ((off & 7u) << 6), lo32, hi32);
+    if constexpr (kFilter) {
+        const uint32_t in0 = DIR == K2_RIGHT ? col0 : row0;
+        cells &= cells_with_inputs<DIR>(inmask_bits(inmask_word(inmask, in0), in0));
+    }
+    leaf_cells<SR, DIR, Off>(row0, col0, cells, x, y, B, VL, w, wc);
 }
 
 // The window of tile 'tl' for this product (no window: win = null), its LDS
@@ -758,28 +788,6 @@ __device__ __forceinline__ SegNodes stage_nodes(const Seg &g, const uint64_t *__
     d.cells = in ? (wv & 0xFFFFu) : 0u;
     return d;
 }
-
-// Cells of a 4x4 block whose input (its column in a right product, its row
-// in a left one) is one of the set bits of in4 (bit c: the block's input
-// origin + c), as a 16-bit cell mask (bit 4 b + q as in node_cells).
-constexpr uint32_t cells_on_input(bool right, uint32_t c) {
-    uint32_t m = 0;
-    for (uint32_t t = 0; t < 16; ++t)
-        if (((cell_offset_table(!right) >> (2 * t)) & 3u) == c) m |= 1u << t;
-    return m;
-}
-template <int DIR>
-__device__ __forceinline__ uint32_t cells_with_inputs(uint32_t in4) {
-    constexpr bool kR = DIR == K2_RIGHT;
-    return ((in4 & 1u) ? cells_on_input(kR, 0) : 0u) | ((in4 & 2u) ? cells_on_input(kR, 1) : 0u) |
-           ((in4 & 4u) ? cells_on_input(kR, 2) : 0u) | ((in4 & 8u) ? cells_on_input(kR, 3) : 0u);
-}
-// The input bit array's word holding the bits of a block's 4 inputs from
-// input origin in0 (a multiple of 4), and those 4 bits.
-__device__ __forceinline__ uint32_t inmask_word(const uint32_t *__restrict__ inmask, uint32_t in0) {
-    return inmask[in0 >> 5];
-}
-__device__ __forceinline__ uint32_t inmask_bits(uint32_t word, uint32_t in0) { return (word >> (in0 & 31u)) & 15u; }
 
 // The input bit array of a product: bit i of word i / 32 is set when input
 // row i has a contributing vector (one of x[i B .. i B + B - 1] is not the
@@ -1070,12 +1078,12 @@ __device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32
 // last-internal-level ranges listed for the tile (skips + win_row, win_col
 // of them; their fan-outs still count towards the leaf offsets).  Outputs go
 // straight to y (no window), so no workgroup barrier at all.
-template <class SR, int DIR, class Off>
+template <class SR, int DIR, class Off, bool kFilter = false>
 __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ skips,
     const uint64_t *__restrict__ tile_codes, const uint32_t *__restrict__ bases, uint32_t cap,
     const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-    int runs) {
+    int runs, const uint32_t *__restrict__ inmask) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // kWaves frontiers of 2 cap codes
     __shared__ WaveCells<Off> s_cells[kWaves];
@@ -1154,9 +1162,14 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
             const uint32_t off = leaf0 + running + ex;
             const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
             const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
-            ring_cells<SR, DIR, Off>(compact_even(code >> 1) * 4u, compact_even(code) * 4u,
-                                     skip ? 0u : node_cells(sg | ((off & 7u) << 6), lo32, hi32), x, y, B,
-                                     VL, w, wc, ring_head, ring_fill);
+            const uint32_t row0 = compact_even(code >> 1) * 4u, col0 = compact_even(code) * 4u;
+            uint32_t cells = skip ? 0u : node_cells(sg | ((off & 7u) << 6), lo32, hi32);
+            if constexpr (kFilter) {
+                // only the cells whose input row has a contributing vector
+                const uint32_t in0 = DIR == K2_RIGHT ? col0 : row0;
+                cells &= cells_with_inputs<DIR>(inmask_bits(inmask_word(inmask, in0), in0));
+            }
+            ring_cells<SR, DIR, Off>(row0, col0, cells, x, y, B, VL, w, wc, ring_head, ring_fill);
             running += total;
         }
         wave_lds_sync();
@@ -1198,11 +1211,12 @@ __device__ __forceinline__ uint32_t staged_nib(const uint64_t *sig, uint32_t w0,
 // the leaves of its last-internal-level nodes in place, with the semiring's
 // atomics straight to y.  With 'emit' set the kernel writes the last level's
 // block origins instead (building the cached level, Sec. 3.5).
-template <class SR, int DIR, bool EMIT, class Off>
+template <class SR, int DIR, bool EMIT, class Off, bool kFilter = false>
 __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ tile_codes,
     uint32_t cap, const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B,
-    uint32_t VL, uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs) {
+    uint32_t VL, uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs,
+    const uint32_t *__restrict__ inmask) {
     using T = typename SR::T;
     // 2 * cap codes (the frontier's two levels), then two buffers of
     // cap / 16 + 1 signature words
@@ -1300,7 +1314,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 }
                 uint32_t total;
                 const uint32_t ex = wave_scan(__popc(s), total);
-                leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_dw, last_dw, x, y, B, VL, w, &s_cells[wave]);
+                leaf_segment<SR, DIR, Off, kFilter>(code, s, base + ex, leaf_dw, last_dw, x, y, B, VL, w,
+                                                    &s_cells[wave], inmask);
             }
         }
         __syncthreads();
@@ -1626,6 +1641,17 @@ bool narrow_offsets(const Matrix &m, uint32_t B) {
     return uint64_t(m.n_rows > m.n_cols ? m.n_rows : m.n_cols) * B <= 0xFFFFFFFFull;
 }
 
+// The input bit array of a product over x (n_in rows of B vectors).
+template <class SR>
+int launch_inmask(const Matrix &m, uint64_t n_in, uint32_t B, const void *x, hipStream_t st) {
+    const uint64_t waves = (n_in + 63) / 64;
+    const uint64_t blocks = (waves + kWaves - 1) / kWaves;
+    const uint32_t g = uint32_t(blocks < 8192 ? (blocks ? blocks : 1) : 8192);
+    hipLaunchKernelGGL(inmask_kernel<SR>, dim3(g), dim3(kThreads), 0, st, static_cast<const typename SR::T *>(x),
+                       n_in, B, m.d_inmask);
+    return hipGetLastError();
+}
+
 // One launch of the cached kernel with kSlots ring slots per wave.
 template <class SR, int DIR, class Off, uint32_t kSlots>
 int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, void *y, int accumulate,
@@ -1647,13 +1673,7 @@ int run_cached_with(const Matrix &m, uint32_t B, uint32_t VL, const void *x, voi
                         : (filter ? cached_kernel<SR, DIR, Off, false, false, kCachedThreads, kSlots, kF>
                                   : cached_kernel<SR, DIR, Off, false, false, kCachedThreads, kSlots, false>);
     if (filter) {
-        const uint64_t n_in = DIR == K2_RIGHT ? m.n_cols : m.n_rows;
-        const uint64_t waves = (n_in + 63) / 64;
-        const uint64_t blocks = (waves + kWaves - 1) / kWaves;
-        const uint32_t g = uint32_t(blocks < 8192 ? (blocks ? blocks : 1) : 8192);
-        hipLaunchKernelGGL(inmask_kernel<SR>, dim3(g), dim3(kThreads), 0, st, static_cast<const T *>(x), n_in, B,
-                           m.d_inmask);
-        int e0 = hipGetLastError();
+        const int e0 = launch_inmask<SR>(m, DIR == K2_RIGHT ? m.n_cols : m.n_rows, B, x, st);
         if (e0 != hipSuccess) return e0;
     }
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
@@ -1693,41 +1713,51 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
 // levels of 'cap' codes.
 template <class SR, int DIR, bool EMIT, class Off>
 int run_tiles(const DevTree &t, const Tile *tiles, size_t n, const uint64_t *codes, const uint32_t *bases,
-              uint32_t cap, const void *x, void *y, uint32_t B, uint64_t *emit, bool row_runs, hipStream_t st) {
+              uint32_t cap, const void *x, void *y, uint32_t B, uint64_t *emit, bool row_runs, hipStream_t st,
+              const uint32_t *inmask = nullptr) {
     using T = typename SR::T;
     if (n == 0) return hipSuccess;
-    auto k = descent_kernel<SR, DIR, EMIT, Off>;
+    auto k = inmask ? descent_kernel<SR, DIR, EMIT, Off, !EMIT && !SR::kWindowUnchecked>
+                    : descent_kernel<SR, DIR, EMIT, Off, false>;
     const size_t lds = (size_t(2) * cap + 2u * (cap / 16u + 1u)) * sizeof(uint64_t);
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid_for(n)), dim3(kThreads), lds, st, t, tiles, uint32_t(n), codes, cap,
                        static_cast<const T *>(x), static_cast<T *>(y), B, lanes_per_node<SR>(B, DIR, false), emit, bases,
-                       row_runs ? 1 : 0);
+                       row_runs ? 1 : 0, inmask);
     return hipGetLastError();
 }
 
 template <class SR, int DIR, bool EMIT, class Off = uint32_t>
 int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *emit,
-                hipStream_t st) {
+                hipStream_t st, bool want_filter = true) {
     using T = typename SR::T;
     const uint32_t VL = lanes_per_node<SR>(B, DIR, false);
     const uint64_t n_out = DIR == K2_RIGHT ? m.n_rows : m.n_cols;
     const Plan &p = m.plan;
+    // the max / or / min semirings: the leaf level keeps only the cells whose
+    // input row has a contributing vector (the input bit array, built first)
+    const bool filter = !EMIT && !SR::kWindowUnchecked && want_filter && m.d_inmask;
+    if (filter) {
+        const int e0 = launch_inmask<SR>(m, DIR == K2_RIGHT ? m.n_cols : m.n_rows, B, x, st);
+        if (e0 != hipSuccess) return e0;
+    }
+    const uint32_t *inmask = filter ? m.d_inmask : nullptr;
     auto descent = [&]() -> int {
         return run_tiles<SR, DIR, EMIT, Off>(m.dev, m.d_tiles, p.tiles.size(), m.d_codes, m.d_bases, p.tile_nodes,
-                                             x, y, B, emit, p.row_runs, st);
+                                             x, y, B, emit, p.row_runs, st, inmask);
     };
     if (EMIT) return descent();
     // a list of tiles of at most rest_cap nodes per level, a wave each
     auto waves = [&](const Tile *tiles, size_t n, const uint64_t *skips) -> int {
         if (n == 0) return hipSuccess;
-        auto kr = rest_kernel<SR, DIR, Off>;
+        auto kr = inmask ? rest_kernel<SR, DIR, Off, !SR::kWindowUnchecked> : rest_kernel<SR, DIR, Off, false>;
         const size_t lds = size_t(kWaves) * 2 * p.rest_cap * sizeof(uint64_t);
         int e = set_lds_limit(reinterpret_cast<const void *>(kr), lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kr, dim3(grid_for((n + kWaves - 1) / kWaves)), dim3(kThreads), lds, st, m.dev,
                            tiles, uint32_t(n), skips, m.d_codes, m.d_bases, p.rest_cap,
-                           static_cast<const T *>(x), static_cast<T *>(y), B, VL, p.row_runs ? 1 : 0);
+                           static_cast<const T *>(x), static_cast<T *>(y), B, VL, p.row_runs ? 1 : 0, inmask);
         return hipGetLastError();
     };
     auto rest = [&](const uint64_t *skips) -> int {
@@ -1780,21 +1810,21 @@ int dispatch_cached(const Matrix &m, int semiring, uint32_t B, const void *x, vo
 }
 
 template <int DIR>
-int dispatch_descent(const Matrix &m, int semiring, uint32_t B, const void *x, void *y,
+int dispatch_descent(const Matrix &m, int semiring, uint32_t B, const void *x, void *y, bool f,
                      hipStream_t st) {
     switch (semiring) {
     case K2_PLUS_TIMES_F32: return narrow_offsets(m, B)
-                   ? run_descent<PlusTimes, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
-                   : run_descent<PlusTimes, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+                   ? run_descent<PlusTimes, DIR, false, uint32_t>(m, B, x, y, nullptr, st, f)
+                   : run_descent<PlusTimes, DIR, false, uint64_t>(m, B, x, y, nullptr, st, f);
     case K2_BOOLEAN_F32: return narrow_offsets(m, B)
-                   ? run_descent<BooleanF32, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
-                   : run_descent<BooleanF32, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+                   ? run_descent<BooleanF32, DIR, false, uint32_t>(m, B, x, y, nullptr, st, f)
+                   : run_descent<BooleanF32, DIR, false, uint64_t>(m, B, x, y, nullptr, st, f);
     case K2_BOOLEAN_U32X32: return narrow_offsets(m, B)
-                   ? run_descent<BooleanU32, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
-                   : run_descent<BooleanU32, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+                   ? run_descent<BooleanU32, DIR, false, uint32_t>(m, B, x, y, nullptr, st, f)
+                   : run_descent<BooleanU32, DIR, false, uint64_t>(m, B, x, y, nullptr, st, f);
     case K2_TROPICAL_F32: return narrow_offsets(m, B)
-                   ? run_descent<Tropical, DIR, false, uint32_t>(m, B, x, y, nullptr, st)
-                   : run_descent<Tropical, DIR, false, uint64_t>(m, B, x, y, nullptr, st);
+                   ? run_descent<Tropical, DIR, false, uint32_t>(m, B, x, y, nullptr, st, f)
+                   : run_descent<Tropical, DIR, false, uint64_t>(m, B, x, y, nullptr, st, f);
     }
     return hipErrorInvalidValue;
 }
@@ -1826,11 +1856,11 @@ bool cached_writes_all(const Matrix &m, int dir, uint32_t batch) {
 }
 
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
-                   uint64_t *emit_codes, void *stream) {
+                   uint64_t *emit_codes, void *stream, bool filter) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (emit_codes) return run_descent<BooleanU32, K2_RIGHT, true>(m, 1, nullptr, nullptr, emit_codes, st);
-    return dir == K2_RIGHT ? dispatch_descent<K2_RIGHT>(m, semiring, batch, x, y, st)
-                           : dispatch_descent<K2_LEFT>(m, semiring, batch, x, y, st);
+    return dir == K2_RIGHT ? dispatch_descent<K2_RIGHT>(m, semiring, batch, x, y, filter, st)
+                           : dispatch_descent<K2_LEFT>(m, semiring, batch, x, y, filter, st);
 }
 
 template <int DIR>

@@ -231,7 +231,7 @@ int launch_descent_tiles(const DevTree &t, const Tile *tiles, size_t n_tiles, co
                          const uint32_t *bases, uint32_t cap, uint32_t n_rows, uint32_t n_cols, bool row_runs,
                          int dir, int semiring, uint32_t batch, const void *x, void *y, void *stream);
 int launch_descent(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,
-                   uint64_t *emit_codes, void *stream);
+                   uint64_t *emit_codes, void *stream, bool filter = true);
 // filter (max / or / min semirings): list only the cells whose input row
 // has a contributing vector (worth it unless most rows have one)
 int launch_cached(const Matrix &m, int dir, int semiring, uint32_t batch, const void *x, void *y,

@@ -845,11 +845,11 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
     l.cached_off = take(cached ? 8 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
     l.cells_off = take(cached ? 4 * t.nodes[t.levels - 2] : 0, l.mem.cached_codes);
     l.status_off = take(cached ? 4 : 0, l.mem.tiles);
-    // cached products of the max / or / min semirings: a bit per input row
-    // (does any of its vectors contribute), rebuilt by every such product
+    // products of the max / or / min semirings: a bit per input row (does
+    // any of its vectors contribute), rebuilt by every such product
     l.mem.scratch = 0;
     const uint64_t nmax = t.n_rows > t.n_cols ? t.n_rows : t.n_cols;
-    l.inmask_off = take(cached ? 4 * ((nmax + 31) / 32) : 0, l.mem.scratch);
+    l.inmask_off = take(4 * ((nmax + 31) / 32), l.mem.scratch);
     l.mem.alignment = off - raw;
     l.mem.arena = off;
 }
