@@ -161,10 +161,10 @@ typedef struct {
     uint64_t cached_codes;/* 12 bytes per node of the last internal level (block
                              coordinates and node words), plus 8 per stray node
                              and direction (band_strays), or 0 */
-    uint64_t scratch;     /* transient product memory: with the cached level, a
-                             bit per input row (max(n_rows, n_cols) bits) that
-                             cached products of the max / or / min semirings
-                             rebuild from x; 0 otherwise (frontiers live in LDS) */
+    uint64_t scratch;     /* transient product memory: a bit per input row
+                             (max(n_rows, n_cols) bits) that products of the
+                             max / or / min semirings rebuild from x (the
+                             frontiers live in LDS) */
     uint64_t alignment;   /* padding between parts */
     uint64_t arena;       /* sum of the above */
     uint64_t vectors;     /* x and y */
@@ -321,10 +321,10 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
    are device arrays of the lengths given at the top of this file (float, or
    uint32 for K2_BOOLEAN_U32X32); they must not overlap.  y is overwritten.
    'mode' picks the traversal (k2_mode), optionally or-ed with
-   K2_SPMV_ACCUMULATE.  Cached products of the max / or / min semirings
-   first mark, in the matrix's arena, the input rows with a contributing
-   vector and then list only those rows' cells: two such products of one
-   matrix must not run at the same time (on different streams).  Errors
+   K2_SPMV_ACCUMULATE.  Products of the max / or / min semirings first
+   mark, in the matrix's arena, the input rows with a contributing vector
+   and then list only those rows' cells: two such products of one matrix
+   must not run at the same time (on different streams).  Errors
    (nothing launched):
    K2_E_INVALID_ARG (null, batch 0, bad enum, K2_MODE_CACHED without cached
    codes), K2_E_HIP (launch failure). */
