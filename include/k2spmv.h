@@ -265,15 +265,17 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
    batch fits them, first the band groups (which = 5 / 6), each a workgroup's
    job: 'count' tiles from tile 'first' of list 7 / 8 (descent tiles as for
    0, over the dense quadrants of one row / column band), sharing the
-   group's window (fields 4-6); then the rest tiles (which = 3 / 4): a
-   second depth-first cut like 0 with at most min(tile_nodes, 256) nodes per
-   level (each a wave's job), in order of output block (2^k rows / columns, 2^k *
+   group's window (fields 4-6); then the rest tiles (which = 3 / 4) that
+   the groups do not cover whole.  The rest tiles are a second depth-first
+   cut like 0 with at most min(tile_nodes, 256) nodes per level (each a
+   wave's job), in order of output block (2^k rows / columns, 2^k *
    window_batch * 4 the largest power of 2 <= 16 MB; a tile's block is its
-   first node's), that skip the last-internal-level nodes band groups cover:
-   'window column' ranges from aux index 'window row', each aux[r] = (first
-   node << 32) | end node; a tile the groups cover whole is left out.
-   Without planned windows the rest tiles are the whole second cut,
-   skipping nothing.
+   first node's); after band groups a tile skips the last-internal-level
+   nodes they cover: 'window column' ranges from aux index 'window row',
+   each aux[r] = (first node << 32) | end node, or 0xFFFFFFFF in 'window
+   column' for a tile they cover whole.  Products without band groups (the
+   max / or / min semirings, a batch too wide for the windows, no windows
+   planned) take every rest tile, skipping nothing: the whole second cut.
    which = 1 / 2: 'count' segments of the last internal level from segment
    'first'; segment r is aux[2r] = (first node << 32) | node count (1..64)
    and aux[2r + 1] = the leaf-level index of its first node's first child.

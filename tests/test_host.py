@@ -293,7 +293,9 @@ def test_tree_only_plan(case, opt):
     its subtree holds at most min(tile_nodes, 256) nodes per level and lies
     in one window quadrant (band kernels keep quadrant-relative codes); rest
     tiles come in output-block order (2^k * window_batch * 4 the largest
-    power of 2 <= 16 MB)."""
+    power of 2 <= 16 MB) and, their skips ignored (a tile the groups cover
+    whole has skip count 0xFFFFFFFF), are the whole second cut: they too
+    cover the level exactly once."""
     name, r, c, nr, nc, t, o = case
     opts = k2.plan_defaults(**opt)
     L = o.levels
@@ -342,7 +344,7 @@ def test_tree_only_plan(case, opt):
                 assert len(np.unique(rr // side)) <= 1 and len(np.unique(ccc // side)) <= 1, "sub-tile spans quadrants"
                 covered.append((a, b))
         _, rest, skips = t.plan(opts, 3 + w)
-        keys = []
+        keys, spans = [], []
         for tl in rest:
             first, count, level = int(tl[0]), int(tl[1]), int(tl[2])
             a, b = down(level, first), down(level, first + count)
@@ -353,6 +355,10 @@ def test_tree_only_plan(case, opt):
             for k in range(level):
                 coord |= ((code >> (2 * k + (1 if out_is_row else 0))) & 1) << k
             keys.append((coord << (L - level)) >> kb)
+            spans.append((a, b))
+            if int(tl[5]) == 0xFFFFFFFF:   # the groups cover it whole
+                assert groups.size and b > a
+                continue
             pos = a
             for sk in skips[int(tl[4]):int(tl[4]) + int(tl[5])]:
                 lo, hi = int(sk) >> 32, int(sk) & 0xFFFFFFFF
@@ -365,12 +371,13 @@ def test_tree_only_plan(case, opt):
             assert int(tl[5]) == 0 or (b - a) > sum((int(x) & 0xFFFFFFFF) - (int(x) >> 32)
                                                     for x in skips[int(tl[4]):int(tl[4]) + int(tl[5])])
         assert keys == sorted(keys)
-        covered.sort()
-        pos = 0
-        for a, b in covered:
-            assert a == pos, (name, w, "tree-only items must cover the level exactly once")
-            pos = b
-        assert pos == nodes[last]
+        for items in (covered, spans):
+            items.sort()
+            pos = 0
+            for a, b in items:
+                assert a == pos, (name, w, "tree-only items must cover the level exactly once")
+                pos = b
+            assert pos == nodes[last]
 
 
 def test_top_level(case):
@@ -409,9 +416,13 @@ def test_estimate_parts(case):
         else:
             assert est["directory"] == 4 * t.plan_offsets(opts).size
         assert est["top_codes"] == 8 * len(codes)
-        # descent tiles, the tree-only lists of both directions, the cached tiles
+        # descent tiles, the tree-only lists of both directions (with band
+        # groups, a 4-byte index per rest tile they leave), the cached tiles
         tree_only = sum(32 * (len(t.plan(opts, 3 + w)[1]) + len(t.plan(opts, 5 + w)[1]) +
                               len(t.plan(opts, 7 + w)[1])) + 8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
+        for w in (0, 1):
+            if len(t.plan(opts, 5 + w)[1]):
+                tree_only += 4 * sum(int(tl[5]) != 0xFFFFFFFF for tl in t.plan(opts, 3 + w)[1])
         # cached: plus 4 bytes of creation status
         assert est["tiles"] == 32 * len(tiles) + tree_only + (extra + stray_tiles + 4 if cached else 0)
         assert est["cached_codes"] == (12 * nodes[L - 2] + stray_records if cached else 0)

@@ -496,12 +496,14 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
         const char *sb = up(m.layout.sub_off[dir], pn.band_sub[dir].data(), pn.band_sub[dir].size() * sizeof(Tile));
         const char *r = up(m.layout.rest_off[dir], pn.rest_tiles[dir].data(), pn.rest_tiles[dir].size() * sizeof(Tile));
         const char *k = up(m.layout.skip_off[dir], pn.skip[dir].data(), pn.skip[dir].size() * 8);
+        const char *tk = up(m.layout.take_off[dir], pn.rest_take[dir].data(), pn.rest_take[dir].size() * 4);
         const char *bad = reinterpret_cast<const char *>(1);
-        if (g == bad || sb == bad || r == bad || k == bad) return fail(K2_E_HIP);
+        if (g == bad || sb == bad || r == bad || k == bad || tk == bad) return fail(K2_E_HIP);
         m.d_band_groups[dir] = reinterpret_cast<const Tile *>(g);
         m.d_band_sub[dir] = reinterpret_cast<const Tile *>(sb);
         m.d_rest[dir] = reinterpret_cast<const Tile *>(r);
         m.d_skip[dir] = reinterpret_cast<const uint64_t *>(k);
+        m.d_rest_take[dir] = reinterpret_cast<const uint32_t *>(tk);
     }
     if (!m.plan.tiles.empty()) {
         hipError_t e = hipMemcpyAsync(const_cast<Tile *>(m.d_tiles), m.plan.tiles.data(),

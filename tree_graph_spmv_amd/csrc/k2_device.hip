@@ -611,24 +611,16 @@ __device__ __forceinline__ uint32_t inmask_word(const uint32_t *__restrict__ inm
 }
 __device__ __forceinline__ uint32_t inmask_bits(uint32_t word, uint32_t in0) { return (word >> (in0 & 31u)) & 15u; }
 
-// kFilter: keep only the cells whose input row has a contributing vector
-// (inmask); its word loads with the leaf words.
-template <class SR, int DIR, class Off, bool kFilter, uint32_t kSlots>
+template <class SR, int DIR, class Off, uint32_t kSlots>
 __device__ __forceinline__ void leaf_segment(uint64_t code, uint32_t s, uint32_t off,
                                              const uint32_t *__restrict__ leaf_dw, uint32_t last_dw,
                                              const typename SR::T *__restrict__ x,
                                              typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-                                             Window<typename SR::T> w, WaveCells<Off, kSlots> *wc,
-                                             const uint32_t *__restrict__ inmask) {
+                                             Window<typename SR::T> w, WaveCells<Off, kSlots> *wc) {
     const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
     const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
     const uint32_t row0 = compact_even(code >> 1) * 4u, col0 = compact_even(code) * 4u;
-    uint32_t cells = node_cells(s | ((off & 7u) << 6), lo32, hi32);
-    if constexpr (kFilter) {
-        const uint32_t in0 = DIR == K2_RIGHT ? col0 : row0;
-        cells &= cells_with_inputs<DIR>(inmask_bits(inmask_word(inmask, in0), in0));
-    }
-    leaf_cells<SR, DIR, Off>(row0, col0, cells, x, y, B, VL, w, wc);
+    leaf_cells<SR, DIR, Off>(row0, col0, node_cells(s | ((off & 7u) << 6), lo32, hi32), x, y, B, VL, w, wc);
 }
 
 // The window of tile 'tl' for this product (no window: win = null), its LDS
@@ -1070,20 +1062,21 @@ __device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32
     return a < n && uint32_t(r[a] >> 32) <= v;
 }
 
-// Tree-only rest tiles (Sec. 3.4 tiles outside the band groups, in
-// output-block order): wave w of workgroup g takes tile 4 g + w of the list,
-// then the tiles a whole grid of waves further on, and descends each on its
-// own as band_kernel does, with frontiers of at most
-// 'cap' absolute Morton codes per level in the wave's LDS, skipping the
-// last-internal-level ranges listed for the tile (skips + win_row, win_col
-// of them; their fan-outs still count towards the leaf offsets).  Outputs go
-// straight to y (no window), so no workgroup barrier at all.
+// Tree-only rest tiles (a second depth-first cut of Sec. 3.4, in
+// output-block order): wave w of workgroup g takes tile 4 g + w of the list
+// (or of the tiles 'take' lists), then the tiles a whole grid of waves
+// further on, and descends each on its own as band_kernel does, with
+// frontiers of at most 'cap' absolute Morton codes per level in the wave's
+// LDS.  With 'skips' (after band groups) it skips the last-internal-level
+// ranges listed for the tile (skips + win_row, win_col of them; their
+// fan-outs still count towards the leaf offsets).  Outputs go straight to y
+// (no window), so no workgroup barrier at all.
 template <class SR, int DIR, class Off, bool kFilter = false>
 __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
-    DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ skips,
-    const uint64_t *__restrict__ tile_codes, const uint32_t *__restrict__ bases, uint32_t cap,
-    const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B, uint32_t VL,
-    int runs, const uint32_t *__restrict__ inmask) {
+    DevTree t, const Tile *__restrict__ tiles, const uint32_t *__restrict__ take, uint32_t n_tiles,
+    const uint64_t *__restrict__ skips, const uint64_t *__restrict__ tile_codes,
+    const uint32_t *__restrict__ bases, uint32_t cap, const typename SR::T *__restrict__ x,
+    typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, int runs, const uint32_t *__restrict__ inmask) {
     using T = typename SR::T;
     extern __shared__ uint64_t s_dyn[];   // kWaves frontiers of 2 cap codes
     __shared__ WaveCells<Off> s_cells[kWaves];
@@ -1097,7 +1090,8 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
     const Window<T> w{nullptr, 0, 0, runs != 0};
     uint32_t ring_head = 0, ring_fill = 0;
     for (uint32_t ti = blockIdx.x * kWaves + wave; ti < n_tiles; ti += gridDim.x * kWaves) {
-        const Tile tl = tiles[ti];
+        const Tile tl = tiles[take ? take[ti] : ti];
+        if (skips && tl.win_col == kWholeRest) continue;   // all of it skipped
         const uint32_t nskip = skips ? tl.win_col : 0u;
         int d = int(tl.level);
         uint32_t lo = tl.first, cnt = tl.count;
@@ -1211,12 +1205,11 @@ __device__ __forceinline__ uint32_t staged_nib(const uint64_t *sig, uint32_t w0,
 // the leaves of its last-internal-level nodes in place, with the semiring's
 // atomics straight to y.  With 'emit' set the kernel writes the last level's
 // block origins instead (building the cached level, Sec. 3.5).
-template <class SR, int DIR, bool EMIT, class Off, bool kFilter = false>
+template <class SR, int DIR, bool EMIT, class Off>
 __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
     DevTree t, const Tile *__restrict__ tiles, uint32_t n_tiles, const uint64_t *__restrict__ tile_codes,
     uint32_t cap, const typename SR::T *__restrict__ x, typename SR::T *__restrict__ y, uint32_t B,
-    uint32_t VL, uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs,
-    const uint32_t *__restrict__ inmask) {
+    uint32_t VL, uint64_t *__restrict__ emit, const uint32_t *__restrict__ bases, int runs) {
     using T = typename SR::T;
     // 2 * cap codes (the frontier's two levels), then two buffers of
     // cap / 16 + 1 signature words
@@ -1314,8 +1307,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void descent_kernel(
                 }
                 uint32_t total;
                 const uint32_t ex = wave_scan(__popc(s), total);
-                leaf_segment<SR, DIR, Off, kFilter>(code, s, base + ex, leaf_dw, last_dw, x, y, B, VL, w,
-                                                    &s_cells[wave], inmask);
+                leaf_segment<SR, DIR, Off>(code, s, base + ex, leaf_dw, last_dw, x, y, B, VL, w, &s_cells[wave]);
             }
         }
         __syncthreads();
@@ -1713,18 +1705,16 @@ int run_cached(const Matrix &m, uint32_t B, const void *x, void *y, int accumula
 // levels of 'cap' codes.
 template <class SR, int DIR, bool EMIT, class Off>
 int run_tiles(const DevTree &t, const Tile *tiles, size_t n, const uint64_t *codes, const uint32_t *bases,
-              uint32_t cap, const void *x, void *y, uint32_t B, uint64_t *emit, bool row_runs, hipStream_t st,
-              const uint32_t *inmask = nullptr) {
+              uint32_t cap, const void *x, void *y, uint32_t B, uint64_t *emit, bool row_runs, hipStream_t st) {
     using T = typename SR::T;
     if (n == 0) return hipSuccess;
-    auto k = inmask ? descent_kernel<SR, DIR, EMIT, Off, !EMIT && !SR::kWindowUnchecked>
-                    : descent_kernel<SR, DIR, EMIT, Off, false>;
+    auto k = descent_kernel<SR, DIR, EMIT, Off>;
     const size_t lds = (size_t(2) * cap + 2u * (cap / 16u + 1u)) * sizeof(uint64_t);
     int e = set_lds_limit(reinterpret_cast<const void *>(k), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(grid_for(n)), dim3(kThreads), lds, st, t, tiles, uint32_t(n), codes, cap,
                        static_cast<const T *>(x), static_cast<T *>(y), B, lanes_per_node<SR>(B, DIR, false), emit, bases,
-                       row_runs ? 1 : 0, inmask);
+                       row_runs ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1743,54 +1733,50 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
         if (e0 != hipSuccess) return e0;
     }
     const uint32_t *inmask = filter ? m.d_inmask : nullptr;
-    auto descent = [&]() -> int {
+    if (EMIT)   // the cached level's block origins: the depth-first tiles
         return run_tiles<SR, DIR, EMIT, Off>(m.dev, m.d_tiles, p.tiles.size(), m.d_codes, m.d_bases, p.tile_nodes,
-                                             x, y, B, emit, p.row_runs, st, inmask);
-    };
-    if (EMIT) return descent();
+                                             x, y, B, emit, p.row_runs, st);
     // a list of tiles of at most rest_cap nodes per level, a wave each
-    auto waves = [&](const Tile *tiles, size_t n, const uint64_t *skips) -> int {
+    auto waves = [&](const uint32_t *take, size_t n, const uint64_t *skips) -> int {
         if (n == 0) return hipSuccess;
         auto kr = inmask ? rest_kernel<SR, DIR, Off, !SR::kWindowUnchecked> : rest_kernel<SR, DIR, Off, false>;
         const size_t lds = size_t(kWaves) * 2 * p.rest_cap * sizeof(uint64_t);
         int e = set_lds_limit(reinterpret_cast<const void *>(kr), lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kr, dim3(grid_for((n + kWaves - 1) / kWaves)), dim3(kThreads), lds, st, m.dev,
-                           tiles, uint32_t(n), skips, m.d_codes, m.d_bases, p.rest_cap,
+                           m.d_rest[DIR], take, uint32_t(n), skips, m.d_codes, m.d_bases, p.rest_cap,
                            static_cast<const T *>(x), static_cast<T *>(y), B, VL, p.row_runs ? 1 : 0, inmask);
         return hipGetLastError();
     };
-    auto rest = [&](const uint64_t *skips) -> int {
-        return waves(m.d_rest[DIR], p.rest_tiles[DIR].size(), skips);
+    // the rest tiles the band groups leave, each skipping what the groups
+    // cover; or all of them, skips ignored: the whole tree
+    auto rest = [&](bool after_groups) -> int {
+        return after_groups ? waves(m.d_rest_take[DIR], p.rest_take[DIR].size(), m.d_skip[DIR])
+                            : waves(nullptr, p.rest_tiles[DIR].size(), nullptr);
     };
     int use = 0;
     const size_t wb = SR::kTreeBands ? window_bytes(m, B, band_other_lds<Off>(m), &use) : 0;
-    if (use) {
+    if (use && !p.band_groups[DIR].empty()) {
         // the bands' dense quadrants into their windows, then the rest
-        if (!p.band_groups[DIR].empty()) {
-            auto kb = band_kernel<SR, DIR, Off>;
-            const size_t lds = size_t(kWaves) * 2 * p.band_cap * sizeof(uint32_t) + wb;
-            int e = set_lds_limit(reinterpret_cast<const void *>(kb), lds);
-            if (e != hipSuccess) return e;
-            hipLaunchKernelGGL(kb, dim3(grid_for(p.band_groups[DIR].size())), dim3(kThreads), lds, st, m.dev,
-                               m.d_band_groups[DIR], m.d_band_sub[DIR], uint32_t(p.band_groups[DIR].size()),
-                               m.d_codes, m.d_bases, p.band_cap, static_cast<const T *>(x),
-                               static_cast<T *>(y), B, VL, n_out, 1, p.row_runs ? 1 : 0);
-            e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
-        return rest(m.d_skip[DIR]);
+        auto kb = band_kernel<SR, DIR, Off>;
+        const size_t lds = size_t(kWaves) * 2 * p.band_cap * sizeof(uint32_t) + wb;
+        int e = set_lds_limit(reinterpret_cast<const void *>(kb), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kb, dim3(grid_for(p.band_groups[DIR].size())), dim3(kThreads), lds, st, m.dev,
+                           m.d_band_groups[DIR], m.d_band_sub[DIR], uint32_t(p.band_groups[DIR].size()),
+                           m.d_codes, m.d_bases, p.band_cap, static_cast<const T *>(x),
+                           static_cast<T *>(y), B, VL, n_out, 1, p.row_runs ? 1 : 0);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return rest(true);
     }
-    // No band groups in this direction (no windows planned, or too few
-    // dense quadrants): the rest tiles cover the whole tree with no skips,
-    // each descended by one wave without workgroup barriers, for every
-    // semiring.  With band groups but no windows for them (the max / or /
-    // min semirings, or a batch too wide): the workgroup descent of the
-    // depth-first tiles.  (The groups' sub-tiles and the rest tiles with
-    // their skips, a wave each, cover the tree too, but measured slower on
-    // R-MAT 2^22 tropical: 1.30 -> 1.52 ms.)
-    if (p.band_groups[DIR].empty()) return rest(nullptr);
-    return descent();
+    // No band groups, or no windows for them (the max / or / min semirings,
+    // or a batch too wide): the whole second cut, each tile descended by one
+    // wave without workgroup barriers.  (Measured on R-MAT 2^22 tropical
+    // against the workgroup descent of the depth-first tiles: 1.26 -> 0.91
+    // ms right, 1.19 -> 0.90 left; the groups' sub-tiles plus the rest
+    // tiles with their skips, a wave each, took 1.52.)
+    return rest(false);
 }
 
 template <int DIR>

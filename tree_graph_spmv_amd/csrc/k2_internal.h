@@ -45,6 +45,9 @@ uint64_t child_offset(const HostTree &t, int d, uint64_t i);
 // a window (win_log2 != kNoWindow) lies inside the 2^win_log2 x 2^win_log2
 // quadrant at (win_row, win_col) and accumulates its outputs in LDS.
 constexpr uint32_t kNoWindow = 0xFFFFFFFFu;
+// Skip count of a rest tile that band groups cover whole.
+constexpr uint32_t kWholeRest = 0xFFFFFFFFu;
+
 struct Tile {
     uint32_t first;
     uint32_t count;
@@ -113,14 +116,18 @@ struct Plan {
     // fields) descends the dense quadrants of one row / column band into one
     // LDS window, with frontiers of at most band_cap nodes.  The rest: a
     // second depth-first cut with at most rest_cap nodes per level, in
-    // output-block order, without the tiles wholly inside windowed quadrants,
-    // each skipping the last-internal-level nodes listed for it in skip[dir]
-    // (ranges (lo << 32) | hi, sorted): rest_tiles[dir] holds them as tiles
-    // with win_row = first skip range, win_col = skip count.
+    // output-block order, each skipping the last-internal-level nodes listed
+    // for it in skip[dir] (ranges (lo << 32) | hi, sorted): rest_tiles[dir]
+    // holds them as tiles with win_row = first skip range, win_col = skip
+    // count, or kWholeRest for a tile wholly inside windowed quadrants.
+    // Plus-times products take after the groups the tiles rest_take[dir]
+    // lists (the others, in block order); products without groups take the
+    // whole list, its skips ignored: the whole second cut.
     uint32_t band_cap = 0;
     // rest tiles hold at most rest_cap nodes per level (a wave's frontier)
     uint32_t rest_cap = 0;
     std::vector<Tile> band_groups[2], band_sub[2], rest_tiles[2];
+    std::vector<uint32_t> rest_take[2];
     std::vector<uint64_t> skip[2];
     // Strays (cached level, band_strays): per direction the segments of the
     // nodes outside every band tile's ranges, and the number of bands of
@@ -148,6 +155,7 @@ struct Layout {
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
     uint64_t codes_off = 0, tiles_off = 0, cached_off = 0, bases_off = 0;
     uint64_t groups_off[2] = {0, 0}, sub_off[2] = {0, 0}, rest_off[2] = {0, 0}, skip_off[2] = {0, 0};
+    uint64_t take_off[2] = {0, 0};
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     uint64_t stray_segs_off[2] = {0, 0}, stray_off_off[2] = {0, 0}, stray_cur_off[2] = {0, 0};
     uint64_t strays_off[2] = {0, 0};
@@ -191,6 +199,7 @@ struct Matrix {
     const Tile *d_band_groups[2] = {nullptr, nullptr}, *d_band_sub[2] = {nullptr, nullptr};
     const Tile *d_rest[2] = {nullptr, nullptr};
     const uint64_t *d_skip[2] = {nullptr, nullptr};
+    const uint32_t *d_rest_take[2] = {nullptr, nullptr};
     const Tile *d_cached_tiles[2] = {nullptr, nullptr};
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
     const StrayRec *d_strays[2] = {nullptr, nullptr};   // grouped by band

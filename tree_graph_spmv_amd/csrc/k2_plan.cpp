@@ -454,8 +454,9 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     };
     const bool cache = o.cache_last_level != 0;
     p.band_cap = std::min<uint32_t>(o.tile_nodes, 256);   // per-wave frontiers (band kernel)
-    // Tree-only plus-times products: the rest tiles in block order, minus the
-    // last-internal-level ranges 'wr' (sorted) that band groups cover.
+    // Tree-only products: the rest tiles in block order, minus the
+    // last-internal-level ranges 'wr' (sorted) that band groups cover; with
+    // groups, the list of those they do not cover whole.
     auto rest_plain = [&](int dir, const std::vector<std::pair<uint64_t, uint64_t>> &wr) {
         for (uint32_t idx : rest_order[dir]) {
             const uint64_t a = rest_lo2[idx], b = a + rest_w[idx];
@@ -473,7 +474,9 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
             }
             if (covered == b - a && b > a) {   // wholly inside band groups
                 p.skip[dir].resize(r.win_row);
-                continue;
+                r.win_col = kWholeRest;
+            } else if (!wr.empty()) {
+                p.rest_take[dir].push_back(uint32_t(p.rest_tiles[dir].size()));
             }
             p.rest_tiles[dir].push_back(r);
         }
@@ -829,6 +832,7 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
         l.sub_off[dir] = take(sizeof(Tile) * plan.band_sub[dir].size(), l.mem.tiles);
         l.rest_off[dir] = take(sizeof(Tile) * plan.rest_tiles[dir].size(), l.mem.tiles);
         l.skip_off[dir] = take(8 * plan.skip[dir].size(), l.mem.tiles);
+        l.take_off[dir] = take(4 * plan.rest_take[dir].size(), l.mem.tiles);
     }
     for (int dir = 0; dir < 2; ++dir) {
         l.cached_tiles_off[dir] = take(cached ? sizeof(Tile) * plan.cached_tiles[dir].size() : 0, l.mem.tiles);
