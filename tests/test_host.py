@@ -416,13 +416,16 @@ def test_estimate_parts(case):
         else:
             assert est["directory"] == 4 * t.plan_offsets(opts).size
         assert est["top_codes"] == 8 * len(codes)
-        # descent tiles, the tree-only lists of both directions (with band
-        # groups, a 4-byte index per rest tile they leave), the cached tiles
-        tree_only = sum(32 * (len(t.plan(opts, 3 + w)[1]) + len(t.plan(opts, 5 + w)[1]) +
-                              len(t.plan(opts, 7 + w)[1])) + 8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
+        # descent tiles, the tree-only lists (the rest tiles once at 16
+        # bytes, per direction their order at 4 bytes and, with band groups,
+        # a 16-byte entry per rest tile the groups leave), the cached tiles
+        n_rest = len(t.plan(opts, 3)[1])
+        tree_only = 16 * n_rest + sum(4 * n_rest + 32 * (len(t.plan(opts, 5 + w)[1]) + len(t.plan(opts, 7 + w)[1])) +
+                                      8 * len(t.plan(opts, 3 + w)[2]) for w in (0, 1))
         for w in (0, 1):
+            assert len(t.plan(opts, 3 + w)[1]) == n_rest
             if len(t.plan(opts, 5 + w)[1]):
-                tree_only += 4 * sum(int(tl[5]) != 0xFFFFFFFF for tl in t.plan(opts, 3 + w)[1])
+                tree_only += 16 * sum(int(tl[5]) != 0xFFFFFFFF for tl in t.plan(opts, 3 + w)[1])
         # cached: plus 4 bytes of creation status
         assert est["tiles"] == 32 * len(tiles) + tree_only + (extra + stray_tiles + 4 if cached else 0)
         assert est["cached_codes"] == (12 * nodes[L - 2] + stray_records if cached else 0)

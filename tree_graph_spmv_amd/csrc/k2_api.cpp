@@ -234,11 +234,36 @@ k2_status k2_estimate_device_bytes(const k2_tree *tree, const k2_plan_opts *opts
 namespace {
 
 // The tile list and aux entry count k2_plan_tiles exports for 'which'.
-void plan_list(const Plan &p, int which, const std::vector<Tile> **list, uint64_t *naux) {
+// The rest tiles of a direction are built into 'tmp' in its block order,
+// with their skip ranges after band groups (0xFFFFFFFF: covered whole).
+void plan_list(const Plan &p, int which, std::vector<Tile> &tmp, const std::vector<Tile> **list,
+               uint64_t *naux) {
     switch (which) {
     case 0: *list = &p.tiles; *naux = p.codes.size(); break;
     case 1: case 2: *list = &p.cached_tiles[which - 1]; *naux = 2 * p.cached_segs[which - 1].size(); break;
-    case 3: case 4: *list = &p.rest_tiles[which - 3]; *naux = p.skip[which - 3].size(); break;
+    case 3: case 4: {
+        const int dir = which - 3;
+        const std::vector<RestTake> &take = p.rest_take[dir];
+        const bool groups = !p.band_groups[dir].empty();
+        size_t t = 0;
+        tmp.clear();
+        tmp.reserve(p.rest_order[dir].size());
+        for (uint32_t idx : p.rest_order[dir]) {
+            const RestTile &rt = p.rest_cut[idx];
+            Tile tl{rt.first, rt.count(), rt.level(), rt.code_off, 0, 0, 0xFFFFFFFFu, rt.base_off};
+            if (t < take.size() && take[t].tile == idx) {
+                tl.win_row = take[t].skip_row;
+                tl.win_col = take[t].skip_count;
+                ++t;
+            } else if (groups) {
+                tl.win_col = 0xFFFFFFFFu;
+            }
+            tmp.push_back(tl);
+        }
+        *list = &tmp;
+        *naux = p.skip[dir].size();
+        break;
+    }
     case 5: case 6: *list = &p.band_groups[which - 5]; *naux = 0; break;
     case 7: case 8: *list = &p.band_sub[which - 7]; *naux = 0; break;
     default: {
@@ -265,9 +290,10 @@ k2_status k2_plan_info(const k2_tree *tree, const k2_plan_opts *opts, int32_t wh
     }
     if (st != K2_OK) return st;
     if (top_level) *top_level = uint32_t(plan.top_level);
+    std::vector<Tile> tmp;
     const std::vector<Tile> *list = nullptr;
     uint64_t naux = 0;
-    plan_list(plan, which, &list, &naux);
+    plan_list(plan, which, tmp, &list, &naux);
     if (n_tiles) *n_tiles = list->size();
     if (n_aux) *n_aux = naux;
     return K2_OK;
@@ -284,9 +310,10 @@ k2_status k2_plan_tiles(const k2_tree *tree, const k2_plan_opts *opts, int32_t w
         return K2_E_HOST_OOM;
     }
     if (st != K2_OK) return st;
+    std::vector<Tile> tmp;
     const std::vector<Tile> *lp = nullptr;
     uint64_t naux = 0;
-    plan_list(plan, which, &lp, &naux);
+    plan_list(plan, which, tmp, &lp, &naux);
     const std::vector<Tile> &list = *lp;
     if (n_tiles < list.size() || n_aux < naux) return K2_E_INVALID_ARG;
     if ((!tiles && !list.empty()) || (!aux && naux)) return K2_E_INVALID_ARG;
@@ -480,7 +507,7 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             return fail(K2_E_HIP);
         }
     }
-    for (int dir = 0; dir < 2; ++dir) {
+    {
         auto up = [&](uint64_t off, const void *src, uint64_t bytes) -> const char * {
             if (!bytes) return nullptr;
             char *dst = m.arena + off;
@@ -491,19 +518,26 @@ k2_status k2_matrix_create(const k2_tree *tree, const k2_plan_opts *opts, void *
             }
             return dst;
         };
-        const Plan &pn = m.plan;
-        const char *g = up(m.layout.groups_off[dir], pn.band_groups[dir].data(), pn.band_groups[dir].size() * sizeof(Tile));
-        const char *sb = up(m.layout.sub_off[dir], pn.band_sub[dir].data(), pn.band_sub[dir].size() * sizeof(Tile));
-        const char *r = up(m.layout.rest_off[dir], pn.rest_tiles[dir].data(), pn.rest_tiles[dir].size() * sizeof(Tile));
-        const char *k = up(m.layout.skip_off[dir], pn.skip[dir].data(), pn.skip[dir].size() * 8);
-        const char *tk = up(m.layout.take_off[dir], pn.rest_take[dir].data(), pn.rest_take[dir].size() * 4);
         const char *bad = reinterpret_cast<const char *>(1);
-        if (g == bad || sb == bad || r == bad || k == bad || tk == bad) return fail(K2_E_HIP);
-        m.d_band_groups[dir] = reinterpret_cast<const Tile *>(g);
-        m.d_band_sub[dir] = reinterpret_cast<const Tile *>(sb);
-        m.d_rest[dir] = reinterpret_cast<const Tile *>(r);
-        m.d_skip[dir] = reinterpret_cast<const uint64_t *>(k);
-        m.d_rest_take[dir] = reinterpret_cast<const uint32_t *>(tk);
+        const Plan &pn = m.plan;
+        const char *r = up(m.layout.rest_off, pn.rest_cut.data(), pn.rest_cut.size() * sizeof(RestTile));
+        if (r == bad) return fail(K2_E_HIP);
+        m.d_rest = reinterpret_cast<const RestTile *>(r);
+        for (int dir = 0; dir < 2; ++dir) {
+            const char *g = up(m.layout.groups_off[dir], pn.band_groups[dir].data(),
+                               pn.band_groups[dir].size() * sizeof(Tile));
+            const char *sb = up(m.layout.sub_off[dir], pn.band_sub[dir].data(), pn.band_sub[dir].size() * sizeof(Tile));
+            const char *o = up(m.layout.order_off[dir], pn.rest_order[dir].data(), pn.rest_order[dir].size() * 4);
+            const char *tk = up(m.layout.take_off[dir], pn.rest_take[dir].data(),
+                                pn.rest_take[dir].size() * sizeof(RestTake));
+            const char *k = up(m.layout.skip_off[dir], pn.skip[dir].data(), pn.skip[dir].size() * 8);
+            if (g == bad || sb == bad || o == bad || tk == bad || k == bad) return fail(K2_E_HIP);
+            m.d_band_groups[dir] = reinterpret_cast<const Tile *>(g);
+            m.d_band_sub[dir] = reinterpret_cast<const Tile *>(sb);
+            m.d_rest_order[dir] = reinterpret_cast<const uint32_t *>(o);
+            m.d_rest_take[dir] = reinterpret_cast<const RestTake *>(tk);
+            m.d_skip[dir] = reinterpret_cast<const uint64_t *>(k);
+        }
     }
     if (!m.plan.tiles.empty()) {
         hipError_t e = hipMemcpyAsync(const_cast<Tile *>(m.d_tiles), m.plan.tiles.data(),

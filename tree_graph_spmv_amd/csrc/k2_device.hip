@@ -1062,19 +1062,20 @@ __device__ __forceinline__ bool in_ranges(const uint64_t *__restrict__ r, uint32
     return a < n && uint32_t(r[a] >> 32) <= v;
 }
 
-// Tree-only rest tiles (a second depth-first cut of Sec. 3.4, in
-// output-block order): wave w of workgroup g takes tile 4 g + w of the list
-// (or of the tiles 'take' lists), then the tiles a whole grid of waves
-// further on, and descends each on its own as band_kernel does, with
-// frontiers of at most 'cap' absolute Morton codes per level in the wave's
-// LDS.  With 'skips' (after band groups) it skips the last-internal-level
-// ranges listed for the tile (skips + win_row, win_col of them; their
+// Tree-only rest tiles (a second depth-first cut of Sec. 3.4, taken in
+// output-block order): wave w of workgroup g takes entry 4 g + w of 'order'
+// (an index into the cut), or of 'take' (an index and the ranges to skip),
+// then the entries a whole grid of waves further on, and descends each tile
+// on its own as band_kernel does, with frontiers of at most 'cap' absolute
+// Morton codes per level in the wave's LDS.  A 'take' entry skips the
+// last-internal-level ranges skips[skip_row ..] (skip_count of them; their
 // fan-outs still count towards the leaf offsets).  Outputs go straight to y
 // (no window), so no workgroup barrier at all.
 template <class SR, int DIR, class Off, bool kFilter = false>
 __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
-    DevTree t, const Tile *__restrict__ tiles, const uint32_t *__restrict__ take, uint32_t n_tiles,
-    const uint64_t *__restrict__ skips, const uint64_t *__restrict__ tile_codes,
+    DevTree t, const RestTile *__restrict__ cut, const uint32_t *__restrict__ order,
+    const RestTake *__restrict__ take, uint32_t n_tiles, const uint64_t *__restrict__ skips,
+    const uint64_t *__restrict__ tile_codes,
     const uint32_t *__restrict__ bases, uint32_t cap, const typename SR::T *__restrict__ x,
     typename SR::T *__restrict__ y, uint32_t B, uint32_t VL, int runs, const uint32_t *__restrict__ inmask) {
     using T = typename SR::T;
@@ -1090,11 +1091,19 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
     const Window<T> w{nullptr, 0, 0, runs != 0};
     uint32_t ring_head = 0, ring_fill = 0;
     for (uint32_t ti = blockIdx.x * kWaves + wave; ti < n_tiles; ti += gridDim.x * kWaves) {
-        const Tile tl = tiles[take ? take[ti] : ti];
-        if (skips && tl.win_col == kWholeRest) continue;   // all of it skipped
-        const uint32_t nskip = skips ? tl.win_col : 0u;
-        int d = int(tl.level);
-        uint32_t lo = tl.first, cnt = tl.count;
+        uint32_t idx, skip_row = 0, nskip = 0;
+        if (take) {
+            const RestTake tk = take[ti];
+            idx = tk.tile;
+            skip_row = tk.skip_row;
+            nskip = tk.skip_count;
+        } else {
+            idx = order[ti];
+        }
+        const RestTile tl = cut[idx];
+        const int d0 = int(tl.level());
+        int d = d0;
+        uint32_t lo = tl.first, cnt = tl.count();
         uint64_t *cur = front, *nxt = front + cap;
         // the signature word of node start + lane of level dd (clamped): a
         // level's first chunk is loaded while the level above is expanded
@@ -1111,7 +1120,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
             return valid ? uint32_t(word >> (((lo + i) & 15u) * 4u)) & 15u : 0u;
         };
         while (d < last) {
-            const uint32_t base = bases ? bases[tl.base_off + uint32_t(d - int(tl.level))]
+            const uint32_t base = bases ? bases[tl.base_off + uint32_t(d - d0)]
                                         : wave_child_offset(t, d, lo);
             const uint64_t wnext = first_word(d + 1, base);
             const uint64_t *__restrict__ wd = t.words[d];
@@ -1141,7 +1150,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
             ++d;
         }
         // the last internal level: each node's cells into the ring
-        const uint32_t leaf0 = bases ? bases[tl.base_off + uint32_t(last - int(tl.level))]
+        const uint32_t leaf0 = bases ? bases[tl.base_off + uint32_t(last - d0)]
                                      : wave_child_offset(t, last, lo);
         const uint64_t *__restrict__ wd = t.words[last];
         uint32_t running = 0;
@@ -1152,7 +1161,7 @@ __global__ __launch_bounds__(kThreads, kOccupancy) void rest_kernel(
             const uint64_t code = valid ? cur[i] : 0ull;
             uint32_t total;
             const uint32_t ex = wave_scan(__popc(sg), total);
-            const bool skip = valid && nskip && in_ranges(skips + tl.win_row, nskip, lo + i);
+            const bool skip = valid && nskip && in_ranges(skips + skip_row, nskip, lo + i);
             const uint32_t off = leaf0 + running + ex;
             const uint32_t dw = (off >> 3) < last_dw ? (off >> 3) : last_dw;
             const uint32_t lo32 = leaf_dw[dw], hi32 = leaf_dw[dw < last_dw ? dw + 1u : last_dw];
@@ -1737,22 +1746,23 @@ int run_descent(const Matrix &m, uint32_t B, const void *x, void *y, uint64_t *e
         return run_tiles<SR, DIR, EMIT, Off>(m.dev, m.d_tiles, p.tiles.size(), m.d_codes, m.d_bases, p.tile_nodes,
                                              x, y, B, emit, p.row_runs, st);
     // a list of tiles of at most rest_cap nodes per level, a wave each
-    auto waves = [&](const uint32_t *take, size_t n, const uint64_t *skips) -> int {
+    auto waves = [&](const RestTake *take, size_t n) -> int {
         if (n == 0) return hipSuccess;
         auto kr = inmask ? rest_kernel<SR, DIR, Off, !SR::kWindowUnchecked> : rest_kernel<SR, DIR, Off, false>;
         const size_t lds = size_t(kWaves) * 2 * p.rest_cap * sizeof(uint64_t);
         int e = set_lds_limit(reinterpret_cast<const void *>(kr), lds);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kr, dim3(grid_for((n + kWaves - 1) / kWaves)), dim3(kThreads), lds, st, m.dev,
-                           m.d_rest[DIR], take, uint32_t(n), skips, m.d_codes, m.d_bases, p.rest_cap,
+                           m.d_rest, m.d_rest_order[DIR], take, uint32_t(n), m.d_skip[DIR], m.d_codes, m.d_bases,
+                           p.rest_cap,
                            static_cast<const T *>(x), static_cast<T *>(y), B, VL, p.row_runs ? 1 : 0, inmask);
         return hipGetLastError();
     };
     // the rest tiles the band groups leave, each skipping what the groups
     // cover; or all of them, skips ignored: the whole tree
     auto rest = [&](bool after_groups) -> int {
-        return after_groups ? waves(m.d_rest_take[DIR], p.rest_take[DIR].size(), m.d_skip[DIR])
-                            : waves(nullptr, p.rest_tiles[DIR].size(), nullptr);
+        return after_groups ? waves(m.d_rest_take[DIR], p.rest_take[DIR].size())
+                            : waves(nullptr, p.rest_order[DIR].size());
     };
     int use = 0;
     const size_t wb = SR::kTreeBands ? window_bytes(m, B, band_other_lds<Off>(m), &use) : 0;

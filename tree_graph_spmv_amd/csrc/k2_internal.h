@@ -45,9 +45,6 @@ uint64_t child_offset(const HostTree &t, int d, uint64_t i);
 // a window (win_log2 != kNoWindow) lies inside the 2^win_log2 x 2^win_log2
 // quadrant at (win_row, win_col) and accumulates its outputs in LDS.
 constexpr uint32_t kNoWindow = 0xFFFFFFFFu;
-// Skip count of a rest tile that band groups cover whole.
-constexpr uint32_t kWholeRest = 0xFFFFFFFFu;
-
 struct Tile {
     uint32_t first;
     uint32_t count;
@@ -59,6 +56,30 @@ struct Tile {
     uint32_t base_off;   // descent tiles with scan offsets: index into tile_bases
 };
 static_assert(sizeof(Tile) == 32, "tile layout");
+
+// A tile of the second depth-first cut (tree-only rest tiles, a wave's job):
+// 'count' (at most 256) nodes of 'level' from node 'first', their codes at
+// code_off, their scan offsets at base_off.  The cut is shared by both
+// directions; each direction orders it through a list of indexes.
+struct RestTile {
+    uint32_t first;
+    uint32_t code_off;
+    uint32_t base_off;
+    uint32_t shape;   // count | level << 16
+    K2_HD uint32_t count() const { return shape & 0xFFFFu; }
+    K2_HD uint32_t level() const { return shape >> 16; }
+};
+static_assert(sizeof(RestTile) == 16, "rest tile layout");
+
+// A rest tile that band groups cover in part: its index in the cut and its
+// skip ranges (skip_count ranges from skip_row of the direction's list).
+struct RestTake {
+    uint32_t tile;
+    uint32_t skip_row;
+    uint32_t skip_count;
+    uint32_t unused;
+};
+static_assert(sizeof(RestTake) == 16, "rest take layout");
 
 // A segment of a cached tile: up to kSegNodes consecutive nodes of the last
 // internal level, one wave's job, with the level-order index of the first
@@ -116,18 +137,19 @@ struct Plan {
     // fields) descends the dense quadrants of one row / column band into one
     // LDS window, with frontiers of at most band_cap nodes.  The rest: a
     // second depth-first cut with at most rest_cap nodes per level, in
-    // output-block order, each skipping the last-internal-level nodes listed
-    // for it in skip[dir] (ranges (lo << 32) | hi, sorted): rest_tiles[dir]
-    // holds them as tiles with win_row = first skip range, win_col = skip
-    // count, or kWholeRest for a tile wholly inside windowed quadrants.
-    // Plus-times products take after the groups the tiles rest_take[dir]
-    // lists (the others, in block order); products without groups take the
-    // whole list, its skips ignored: the whole second cut.
+    // rest_cut, taken in output-block order (rest_order[dir]).  After band
+    // groups, plus-times products take the tiles rest_take[dir] lists (those
+    // the groups do not cover whole, in block order), each skipping the
+    // last-internal-level nodes listed for it in skip[dir] (ranges
+    // (lo << 32) | hi, sorted); products without groups take rest_order[dir]
+    // whole: the whole second cut.
     uint32_t band_cap = 0;
     // rest tiles hold at most rest_cap nodes per level (a wave's frontier)
     uint32_t rest_cap = 0;
-    std::vector<Tile> band_groups[2], band_sub[2], rest_tiles[2];
-    std::vector<uint32_t> rest_take[2];
+    std::vector<Tile> band_groups[2], band_sub[2];
+    std::vector<RestTile> rest_cut;
+    std::vector<uint32_t> rest_order[2];
+    std::vector<RestTake> rest_take[2];
     std::vector<uint64_t> skip[2];
     // Strays (cached level, band_strays): per direction the segments of the
     // nodes outside every band tile's ranges, and the number of bands of
@@ -154,8 +176,8 @@ struct Layout {
     uint64_t words_off[kMaxLevels] = {};   // level words (levels >= top)
     uint64_t dir_off[kMaxLevels] = {};     // directories (internal levels >= top)
     uint64_t codes_off = 0, tiles_off = 0, cached_off = 0, bases_off = 0;
-    uint64_t groups_off[2] = {0, 0}, sub_off[2] = {0, 0}, rest_off[2] = {0, 0}, skip_off[2] = {0, 0};
-    uint64_t take_off[2] = {0, 0};
+    uint64_t groups_off[2] = {0, 0}, sub_off[2] = {0, 0}, skip_off[2] = {0, 0};
+    uint64_t rest_off = 0, order_off[2] = {0, 0}, take_off[2] = {0, 0};
     uint64_t cached_tiles_off[2] = {0, 0}, cached_segs_off[2] = {0, 0};
     uint64_t stray_segs_off[2] = {0, 0}, stray_off_off[2] = {0, 0}, stray_cur_off[2] = {0, 0};
     uint64_t strays_off[2] = {0, 0};
@@ -197,9 +219,10 @@ struct Matrix {
     const Tile *d_tiles = nullptr;
     const uint32_t *d_bases = nullptr;   // scan offsets of the descent tiles, or null
     const Tile *d_band_groups[2] = {nullptr, nullptr}, *d_band_sub[2] = {nullptr, nullptr};
-    const Tile *d_rest[2] = {nullptr, nullptr};
+    const RestTile *d_rest = nullptr;
+    const uint32_t *d_rest_order[2] = {nullptr, nullptr};
     const uint64_t *d_skip[2] = {nullptr, nullptr};
-    const uint32_t *d_rest_take[2] = {nullptr, nullptr};
+    const RestTake *d_rest_take[2] = {nullptr, nullptr};
     const Tile *d_cached_tiles[2] = {nullptr, nullptr};
     const Seg *d_cached_segs[2] = {nullptr, nullptr};
     const StrayRec *d_strays[2] = {nullptr, nullptr};   // grouped by band

@@ -437,6 +437,9 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         }
         for (int dir = 0; dir < 2; ++dir) block_order(rest_cut, dir, rest_order[dir]);
         if (plan_bases(rest_cut) != K2_OK) return K2_E_UNSUPPORTED;
+        p.rest_cut.reserve(rest_cut.size());
+        for (const Tile &tl : rest_cut) p.rest_cut.push_back({tl.first, tl.code_off, tl.base_off, tl.count | (tl.level << 16)});
+        for (int dir = 0; dir < 2; ++dir) p.rest_order[dir] = rest_order[dir];
     }
     // group boundaries: tile indexes where a new group starts (and the end)
     auto order_cached = [&](int dir, std::vector<size_t> groups) {
@@ -454,31 +457,25 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
     };
     const bool cache = o.cache_last_level != 0;
     p.band_cap = std::min<uint32_t>(o.tile_nodes, 256);   // per-wave frontiers (band kernel)
-    // Tree-only products: the rest tiles in block order, minus the
-    // last-internal-level ranges 'wr' (sorted) that band groups cover; with
-    // groups, the list of those they do not cover whole.
+    // Tree-only plus-times products after band groups: the rest tiles in
+    // block order that the last-internal-level ranges 'wr' (sorted, those
+    // the groups cover) do not cover whole, each with its ranges to skip.
     auto rest_plain = [&](int dir, const std::vector<std::pair<uint64_t, uint64_t>> &wr) {
+        if (wr.empty()) return;
         for (uint32_t idx : rest_order[dir]) {
             const uint64_t a = rest_lo2[idx], b = a + rest_w[idx];
             auto it = std::lower_bound(wr.begin(), wr.end(), a,
                                        [](const std::pair<uint64_t, uint64_t> &r, uint64_t v) { return r.second <= v; });
-            Tile r = rest_cut[idx];
-            r.win_row = uint32_t(p.skip[dir].size());
-            r.win_col = 0;
+            RestTake tk{idx, uint32_t(p.skip[dir].size()), 0, 0};
             uint64_t covered = 0;
             for (; it != wr.end() && it->first < b; ++it) {
                 const uint64_t lo = std::max(a, it->first), hi = std::min(b, it->second);
                 p.skip[dir].push_back((lo << 32) | hi);
                 covered += hi - lo;
-                ++r.win_col;
+                ++tk.skip_count;
             }
-            if (covered == b - a && b > a) {   // wholly inside band groups
-                p.skip[dir].resize(r.win_row);
-                r.win_col = kWholeRest;
-            } else if (!wr.empty()) {
-                p.rest_take[dir].push_back(uint32_t(p.rest_tiles[dir].size()));
-            }
-            p.rest_tiles[dir].push_back(r);
+            if (covered == b - a && b > a) p.skip[dir].resize(tk.skip_row);   // wholly inside band groups
+            else p.rest_take[dir].push_back(tk);
         }
     };
     // Scan offsets of the band groups' sub-tiles (the rest tiles are copies of
@@ -490,7 +487,6 @@ k2_status make_plan(const HostTree &t, const k2_plan_opts &o, Plan *out) {
         return K2_OK;
     };
     if (qlog < 0) {
-        for (int dir = 0; dir < 2; ++dir) rest_plain(dir, {});
         if (cache)
             for (int dir = 0; dir < 2; ++dir) {
                 pl.cached_run(dir, 0, n2);
@@ -830,10 +826,11 @@ void layout_for(const HostTree &t, int top, const Plan &plan, bool cached, Layou
     for (int dir = 0; dir < 2; ++dir) {
         l.groups_off[dir] = take(sizeof(Tile) * plan.band_groups[dir].size(), l.mem.tiles);
         l.sub_off[dir] = take(sizeof(Tile) * plan.band_sub[dir].size(), l.mem.tiles);
-        l.rest_off[dir] = take(sizeof(Tile) * plan.rest_tiles[dir].size(), l.mem.tiles);
+        l.order_off[dir] = take(4 * plan.rest_order[dir].size(), l.mem.tiles);
+        l.take_off[dir] = take(sizeof(RestTake) * plan.rest_take[dir].size(), l.mem.tiles);
         l.skip_off[dir] = take(8 * plan.skip[dir].size(), l.mem.tiles);
-        l.take_off[dir] = take(4 * plan.rest_take[dir].size(), l.mem.tiles);
     }
+    l.rest_off = take(sizeof(RestTile) * plan.rest_cut.size(), l.mem.tiles);
     for (int dir = 0; dir < 2; ++dir) {
         l.cached_tiles_off[dir] = take(cached ? sizeof(Tile) * plan.cached_tiles[dir].size() : 0, l.mem.tiles);
         l.cached_segs_off[dir] = take(cached ? sizeof(Seg) * plan.cached_segs[dir].size() : 0, l.mem.tiles);
