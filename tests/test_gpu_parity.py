@@ -276,8 +276,9 @@ def test_multi_tile_bands(dev):
 def test_wide_batch_windows(dev):
     """Batches 75 and 76 on a web-like 2^14 graph: a 512-row band window of
     75-76 vectors leaves no room for the band kernel's frontiers (tree-only
-    plus-times products then take the groups' sub-tiles and the rest tiles
-    a wave each, without windows) but fits the cached kernel's window.
+    plus-times products then skip the band groups and take every tile of
+    the rest cut, a wave each, skipping nothing) but fits the cached
+    kernel's window.
     Whole outputs against the oracle, both directions, tree-only and
     cached."""
     import tree_graph_spmv_amd as k2
