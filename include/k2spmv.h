@@ -77,9 +77,10 @@ typedef enum { K2_MODE_AUTO = 0, K2_MODE_TREE_ONLY = 1, K2_MODE_CACHED = 2 } k2_
 typedef struct {
     /* Tiled descent (Sec. 3.4): a tile is a contiguous node range whose
        subtree holds at most tile_nodes nodes on every level; one workgroup
-       descends a tile with its frontier in LDS.  Tree-only plus-times
-       products cut their band sub-tiles and rest tiles at 256 nodes per
-       level instead, one wave each.  256..4096, power of 2.  Default 1024. */
+       descends a tile with its frontier in LDS (the cached level's creation,
+       streamed products).  Tree-only products cut their band sub-tiles and
+       rest tiles at min(tile_nodes, 256) nodes per level instead, one wave
+       each.  256..4096, power of 2.  Default 1024. */
     uint32_t tile_nodes;
     /* Host-side top (Sec. 3.4): the device starts from the deepest level with
        at most host_top_max nodes (never below the last internal level).
