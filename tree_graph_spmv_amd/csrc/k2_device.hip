@@ -78,7 +78,8 @@ struct PlusTimes {
 
 struct BooleanF32 {
     using T = float;
-    // tree-only products take the depth-first tiles (see PlusTimes)
+    // tree-only products take the whole rest cut, no band groups (see
+    // PlusTimes and Tropical)
     static constexpr bool kTreeBands = false;
     static constexpr bool kWindowUnchecked = false;
     static constexpr uint32_t kZeroBits = 0u;
@@ -99,7 +100,8 @@ struct BooleanF32 {
 
 struct BooleanU32 {
     using T = uint32_t;
-    // tree-only products take the depth-first tiles (see PlusTimes)
+    // tree-only products take the whole rest cut, no band groups (see
+    // PlusTimes and Tropical)
     static constexpr bool kTreeBands = false;
     static constexpr bool kWindowUnchecked = false;
     static constexpr uint32_t kZeroBits = 0u;
@@ -118,8 +120,9 @@ struct BooleanU32 {
 
 struct Tropical {
     using T = float;
-    // tree-only products take the depth-first tiles: contributions equal
-    // to the zero (x = +inf) issue no atomic, and relaxation steps skip most
+    // tree-only products take the whole rest cut, no band groups: the
+    // groups' windows would absorb atomics, but contributions equal to the
+    // zero (x = +inf) issue none, and relaxation steps skip most
     static constexpr bool kTreeBands = false;
     static constexpr bool kWindowUnchecked = false;
     static constexpr uint32_t kZeroBits = 0x7F800000u;   // +inf
