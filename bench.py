@@ -444,7 +444,7 @@ def stream_bench(args, k2, tree, opts, n, semiring, batch, directions, dev):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs the product on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     if args.copy_probe:
