@@ -273,6 +273,47 @@ def test_multi_tile_bands(dev):
                          "accumulate " + label)
 
 
+def test_tree_only_with_band_groups(dev):
+    """Tree-only products of a web-like 2^14 graph whose plan holds band
+    groups in both directions: plus-times takes the groups, then the rest
+    tiles they leave with their skip ranges; the other semirings take every
+    rest tile in block order and skip nothing.  Every semiring, both
+    directions, batches 1, 3 and 8, scan and directory offsets, overwriting
+    and accumulating, whole outputs against the oracle."""
+    import tree_graph_spmv_amd as k2
+    rng = np.random.default_rng(31)
+    n = 2 ** 14
+    rows, cols = synth.web(n, 16, window=1024, p_local=0.8, seed=11)
+    tree = k2.Tree(rows, cols, n, n)
+    ref = oracle.OracleTree(rows, cols, n, n)
+    combine = {"plus_times": lambda a, b: a.astype(np.float64) + b,
+               "boolean": np.maximum, "boolean_u32": np.bitwise_or, "tropical": np.minimum}
+    for offsets in ("scan", "directory"):
+        opts = k2.plan_defaults(offsets=offsets)
+        for w in (0, 1):
+            assert len(tree.plan(opts, 5 + w)[1]), "the plan must hold band groups"
+            rest = tree.plan(opts, 3 + w)[1]
+            assert (rest[:, 5] == 0xFFFFFFFF).any() and (rest[:, 5] != 0xFFFFFFFF).any(), \
+                "rest tiles both inside and outside the groups"
+        m = k2.Matrix(tree, opts, device=dev)
+        for sr, direction, B in itertools.product(ALL_SEMIRINGS, ("right", "left"), (1, 3, 8)):
+            x = make_x(rng, sr, n, B)
+            xd = to_device(x, dev)
+            want = ref.spmv(x, ORC_SEMIRING[sr], ORC_DIR[direction], B)
+            label = f"tree with groups {offsets} {sr} {direction} B={B}"
+            y = m.spmv(xd, direction=direction, semiring=sr, batch=B, mode="tree")
+            torch.cuda.synchronize()
+            check_parity(from_device(y, sr), want, sr, label)
+            y0 = make_x(rng, sr, n, B)
+            if sr == "boolean":
+                y0 = (y0 != 0).astype(np.float32)
+            ya = to_device(y0, dev)
+            m.spmv(xd, ya, direction=direction, semiring=sr, batch=B, mode="tree", accumulate=True)
+            torch.cuda.synchronize()
+            check_parity(from_device(ya, sr), combine[sr](y0.reshape(want.shape), want), sr,
+                         "accumulate " + label)
+
+
 def test_wide_batch_windows(dev):
     """Batches 75 and 76 on a web-like 2^14 graph: a 512-row band window of
     75-76 vectors leaves no room for the band kernel's frontiers (tree-only
