@@ -132,7 +132,8 @@ def test_device_tree_and_cached_blocks(dev):
 def test_web_n20_d16(dev):
     """Web-like 2^20 (about 15M distinct edges): right and left plus-times,
     tree-only and cached, against the oracle's full product, overwriting y
-    and accumulating into it."""
+    and accumulating into it; the tropical and packed Boolean semirings
+    tree-only (their 79k rest tiles take several per wave)."""
     import tree_graph_spmv_amd as k2
     rows, cols, n = synth.workload_edges("web_n20_d16")
     tree = k2.Tree(rows, cols, n, n)
@@ -162,6 +163,12 @@ def test_web_n20_d16(dev):
         y = st.spmv(xd, direction=direction)
         torch.cuda.synchronize()
         check_parity(from_device(y, "plus_times"), want, "plus_times", f"web_n20_d16 {direction} streamed")
+        for sr in ("tropical", "boolean_u32"):
+            xs = make_x(np.random.default_rng(17), sr, n, 1)
+            want = ref.spmv(xs, ORC_SEMIRING[sr], ORC_DIR[direction], 1, threads=16)
+            y = m.spmv(to_device(xs, dev), direction=direction, semiring=sr, mode="tree")
+            torch.cuda.synchronize()
+            check_parity(from_device(y, sr), want, sr, f"web_n20_d16 {sr} {direction} tree")
 
 
 def test_accumulate(dev):
